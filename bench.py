@@ -1,0 +1,344 @@
+"""Benchmark: chunked SGMV LoRA hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: host plan (native
+planner) -> one async upload of the plan -> LoRA-A shrink -> LoRA-B expand
+(scaling, stacked slice offsets, in place into base) -> LoRA-A embedding
+gather.  The headline workload is the decode batch: 256 one-token requests on
+8 adapters drawn uniformly, rank 16, stacked qkv 4096 -> [4096, 1024, 1024],
+bf16; the embedding gather uses vocab 128256 and rank 16.  Inputs rotate over
+48 independent sets (> the 256 MB MALL) so kernels read HBM, not cache.
+
+Prints ONE JSON line.  `value` is tokens/s of whole steps (wall clock over
+the timed steps, inputs resident in HBM); kernel durations come from HIP
+events on the stream the kernels run on.  `--secondary` adds the prefill
+gate_up workload (32 requests of 64..2048 tokens, rank 64, chunk 128).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=48, help="rotated input sets")
+    ap.add_argument("--secondary", action="store_true", help="also time the prefill workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB device copy (for counter calibration)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------- algorithmic work
+
+def algo_counts(b, proj, emb_rank):
+    """Algorithmic bytes / flops of each kernel for one batch (padding and
+    zero-fill not counted): x read once, each active adapter's weights read
+    once, h written and read once, base read and written once."""
+    ranks = np.asarray(b.lora_ranks)
+    tok_rank = np.repeat(ranks[np.asarray(b.req_slots)], b.seq_lens).astype(np.int64)
+    sum_rho = int(tok_rank.sum())
+    active = sorted(set(b.req_slots))
+    act_rho = int(sum(min(ranks[a], proj.rank) for a in active))
+    s, K, c, N = b.num_tokens, proj.in_dim, proj.num_slices, proj.out_dim
+    shrink_b = 2 * s * K + 2 * c * K * act_rho + 2 * c * sum_rho + 4 * s
+    expand_b = 2 * c * sum_rho + 2 * N * act_rho + 4 * s * N + 4 * s
+    emb_rho = np.minimum(tok_rank, emb_rank)
+    emb_b = int(np.sum(8 + 4 + 4 * emb_rho))
+    return {"shrink": {"bytes": shrink_b, "flops": 2 * K * c * sum_rho},
+            "expand": {"bytes": expand_b, "flops": 2 * N * sum_rho},
+            "embedding": {"bytes": emb_b, "flops": 0}}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "segmented_gather_gemm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed counter runs, if they were
+    taken on the current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if line.startswith("#") or "=" not in line:
+            continue
+        k, v = line.split("=", 1)
+        rec[k.strip()] = v.strip()
+    if rec.get("source_sha") != kernel_source_hash():
+        return None
+    key = f"{workload}.{kernel}.hbm_bytes_per_launch"
+    return float(rec[key]) if key in rec else None
+
+
+# ---------------------------------------------------------------- GPU legs
+
+def make_sets(n_sets, device):
+    import torch
+    from synth import draw_batch, draw_embedding, draw_ids, draw_projection
+    from synth.workloads import rotation_batch
+    base_b = draw_batch("decode")
+    # one LoRA-A embedding table (33 MB) shared by all sets; ids differ per set
+    _, A_emb = draw_embedding(base_b)
+    A_emb = A_emb.to(device)
+    sets = []
+    for i in range(n_sets):
+        b = base_b if i == 0 else rotation_batch(base_b, i)
+        proj = b.projections[0]
+        t = draw_projection(b, proj)
+        sets.append({"b": b, "proj": proj,
+                     **{k: v.to(device) for k, v in t.items()},
+                     "ids": draw_ids(b).to(device), "A_emb": A_emb,
+                     "e": torch.empty((b.num_tokens, A_emb.shape[1]), dtype=torch.bfloat16,
+                                      device=device)})
+    return sets
+
+
+def run_decode(args, device):
+    import torch
+    import segmented_gather_gemm_amd as sgg
+
+    sets = make_sets(args.sets, device)
+    b0 = sets[0]["b"]
+    be = sgg.ChunkedSgmvLoRA(b0.num_loras, b0.max_chunk_size, device)
+    vocab = b0.vocab_size or 128256
+    stream = torch.cuda.current_stream(device)
+    names = ("shrink", "expand", "embedding")
+    h_bufs = [torch.empty((st["b"].num_tokens, st["A"].shape[1]), dtype=torch.bfloat16,
+                          device=device) for st in sets]
+    ws = sgg.default_workspace(device, 64 << 20)
+
+    def step(i, events=None):
+        st = sets[i % len(sets)]
+        b, proj = st["b"], st["proj"]
+        info = be.prepare_lora_batch(None, b.req_slots, b.lora_ranks, b.scalings,
+                                     is_decode=True)
+        ev = events[i] if events is not None else None
+        if ev:
+            ev[0].record(stream)
+        h = sgg.lora_shrink(st["x"], st["A"], info, proj.num_slices, out=h_bufs[i % len(sets)],
+                            workspace=ws)
+        if ev:
+            ev[1].record(stream)
+        sgg.lora_expand(h, st["B"], info, proj.slice_offsets, proj.max_slice, st["base"])
+        if ev:
+            ev[2].record(stream)
+        sgg.lora_a_embedding(st["ids"], st["A_emb"], info, vocab, out=st["e"])
+        if ev:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: whole steps, wall clock
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # kernel durations: the same steps again with events around each kernel
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, events)
+    torch.cuda.synchronize()
+    dur = {n: [] for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            dur[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)   # microseconds
+
+    # host planner alone (native plan + staging), for the record
+    t1 = time.perf_counter()
+    for i in range(50):
+        st = sets[i % len(sets)]
+        sgg.lora_plan_segments(None, st["b"].req_slots, b0.num_loras, True, b0.max_chunk_size)
+    plan_us = (time.perf_counter() - t1) / 50 * 1e6
+
+    counts = [algo_counts(st["b"], st["proj"], st["A_emb"].shape[1]) for st in sets]
+    avg = {n: float(np.mean(dur[n])) for n in names}
+    med = {n: float(np.median(dur[n])) for n in names}
+    per = {}
+    for n in names:
+        by = float(np.mean([c[n]["bytes"] for c in counts]))
+        fl = float(np.mean([c[n]["flops"] for c in counts]))
+        per[n] = {"avg_us": round(avg[n], 3), "median_us": round(med[n], 3),
+                  "algo_bytes": int(by), "algo_flops": int(fl),
+                  "gbs": round(by / (avg[n] * 1e-6) / 1e9, 1),
+                  "tflops": round(fl / (avg[n] * 1e-6) / 1e12, 3)}
+    se_us = avg["shrink"] + avg["expand"]
+    se_bytes = per["shrink"]["algo_bytes"] + per["expand"]["algo_bytes"]
+    return {
+        "wall_s": wall, "tokens": b0.num_tokens, "kernels": per, "plan_host_us": round(plan_us, 2),
+        "shrink_expand": {"us": round(se_us, 3),
+                          "gbs": round(se_bytes / (se_us * 1e-6) / 1e9, 1),
+                          "hbm_frac": round(se_bytes / (se_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "tokens_per_s_kernels": round(b0.num_tokens / (se_us * 1e-6), 1)},
+    }
+
+
+def run_prefill(device, steps=20, warmup=3):
+    import torch
+    import segmented_gather_gemm_amd as sgg
+    from synth import draw_batch, draw_projection
+
+    b = draw_batch("prefill", max_chunk_size=128)
+    proj = b.projections[0]
+    t = {k: v.to(device) for k, v in draw_projection(b, proj).items()}
+    be = sgg.ChunkedSgmvLoRA(b.num_loras, 128, device)
+    info = be.prepare_lora_batch(b.seq_lens, b.req_slots, b.lora_ranks, b.scalings)
+    h = torch.empty((b.num_tokens, t["A"].shape[1]), dtype=torch.bfloat16, device=device)
+    stream = torch.cuda.current_stream(device)
+    for _ in range(warmup):
+        sgg.lora_shrink(t["x"], t["A"], info, 2, out=h)
+        sgg.lora_expand(h, t["B"], info, proj.slice_offsets, proj.max_slice, t["base"])
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        sgg.lora_shrink(t["x"], t["A"], info, 2, out=h)
+        ev[i][1].record(stream)
+        sgg.lora_expand(h, t["B"], info, proj.slice_offsets, proj.max_slice, t["base"])
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    c = algo_counts(b, proj, 16)
+    out = {"workload": "prefill gate_up, 32 requests (s=%d), 32 adapters Zipf(1.1), r=64, "
+                       "4096 -> 2x14336, chunk 128" % b.num_tokens}
+    for j, n in enumerate(("shrink", "expand")):
+        us = float(np.mean([e[j].elapsed_time(e[j + 1]) * 1e3 for e in ev]))
+        by, fl = c[n]["bytes"], c[n]["flops"]
+        out[n] = {"avg_us": round(us, 2), "gbs": round(by / (us * 1e-6) / 1e9, 1),
+                  "hbm_frac": round(by / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                  "tflops": round(fl / (us * 1e-6) / 1e12, 2),
+                  "mfma_frac": round(fl / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    tot = out["shrink"]["avg_us"] + out["expand"]["avg_us"]
+    out["tokens_per_s"] = round(b.num_tokens / (tot * 1e-6), 1)
+    return out
+
+
+def copy_probe(device):
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=device)
+    bb = torch.empty_like(a)
+    for _ in range(5):
+        bb.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+
+
+# ----------------------------------------------------------------- CPU leg
+
+def cpu_baseline(seconds):
+    """The oracle (plan oracle + fp64 math oracle) on the decode workload's
+    rotated batches, single-threaded BLAS, until `seconds` have elapsed."""
+    from threadpoolctl import threadpool_limits
+    from oracle import lora as ol
+    from oracle import plan as op
+    from synth import draw_batch, draw_embedding, draw_projection, to_f64
+    from synth.workloads import rotation_batch
+
+    base_b = draw_batch("decode")
+    prepared = []
+    for i in range(2):
+        b = base_b if i == 0 else rotation_batch(base_b, i)
+        proj = b.projections[0]
+        t = draw_projection(b, proj)
+        ids, A_emb = draw_embedding(b)
+        prepared.append((b, proj, {k: to_f64(v) for k, v in t.items()}, ids.numpy(),
+                         to_f64(A_emb)))
+    done = 0
+    tokens = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            b, proj, t, ids, A_emb = prepared[done % len(prepared)]
+            op.plan(None, b.req_slots, True, b.max_chunk_size)
+            ol.lora_forward(t["x"], t["A"], t["B"], t["base"], b.seq_lens, b.req_slots,
+                            b.lora_ranks, b.scalings, proj.slice_offsets)
+            ol.embedding_a(ids, A_emb, b.seq_lens, b.req_slots, b.lora_ranks, 128256)
+            done += 1
+            tokens += b.num_tokens
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": round(tokens / el, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} full decode steps (256 tokens each: plan + qkv shrink/expand + "
+                      f"embedding gather, fp64 NumPy), {el:.1f} s, BLAS limited to 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
+              f"single-GPU, with no sharding or collectives", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    device = torch.device("cuda:0")
+    if args.copy_probe:
+        copy_probe(device)
+        return
+    print(f"# decode: {args.sets} input sets, warmup {args.warmup}, steps {args.steps}",
+          file=sys.stderr, flush=True)
+    res = run_decode(args, device)
+    ms = res["wall_s"] / args.steps * 1e3
+    value = res["tokens"] * args.steps / res["wall_s"]
+    k = res["kernels"]
+    dom = max(("shrink", "expand", "embedding"), key=lambda n: k[n]["avg_us"])
+    achieved = k[dom]["gbs"]
+    line = {
+        "metric": "LoRA tokens/s (decode qkv shrink+expand + embedding gather, whole step)",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode: 256 requests x 1 token, 8 adapters uniform, r=16, "
+                               "stacked qkv 4096 -> [4096,1024,1024] (c=3), chunk cap 128; "
+                               "LoRA-A embedding vocab 128256 r=16; "
+                               f"{args.sets} rotated input sets",
+                   "tokens_per_step": res["tokens"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for(dom, "decode")},
+        "kernels": k,
+        "shrink_expand": res["shrink_expand"],
+        "plan_host_us": res["plan_host_us"],
+    }
+    if args.secondary:
+        print("# prefill", file=sys.stderr, flush=True)
+        line["prefill"] = run_prefill(device)
+    if not args.no_cpu:
+        print("# cpu baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+/*
+ * sgg_lora.h -- chunked SGMV (segmented gather matrix-vector / GEMM) LoRA
+ * for AMD Instinct MI355X (gfx950).  Plain C ABI.
+ *
+ * The operations are the LoRA backend calls of sglang's chunked LoRA
+ * backend, as described on the web pages about it:
+ *   - the "chunked_backend.py" page, class ChunkedSgmvLoRABackend: the batch
+ *     plan (prepare_lora_batch, _determine_chunk_size, _get_permutation,
+ *     _get_segments_info, _build_req_seg_indptr) and the kernel calls
+ *     (run_lora_a_sgemm, run_lora_b_sgemm, run_qkv_lora, run_gate_up_lora,
+ *     run_lora_a_embedding);
+ *   - the "base_backend.py" page, class BaseLoRABackend: the shape contract
+ *     of every call;
+ *   - the "lora_manager.py" page, LoRAManager.prepare_lora_batch: per-slot
+ *     rank and scaling tables (rank 0 and scaling 0 mean "no adapter").
+ *
+ * Notation: s = number of tokens, K = in_dim, c = number of stacked slices,
+ * R = padded LoRA rank (the rank dimension of the weight tensors), L =
+ * number of adapter slots.  Token t belongs to adapter slot a(t); rho_a =
+ * min(lora_ranks[a], R), sigma_a = scalings[a].
+ *
+ * Conventions shared by every call
+ *   - Status: 0 on success, a negative SGG_ERR_* code otherwise;
+ *     lora_last_error() then returns a message for the calling thread.
+ *   - Ownership: the caller owns every buffer.  The library keeps no state
+ *     between calls except the per-thread error message.
+ *   - Element type: every floating-point tensor is bf16 (2 bytes, stored as
+ *     raw bits) except `scalings` (float32).  Index arrays are int32, token
+ *     ids int64.  Accumulation is float32; results are rounded to bf16 with
+ *     round-to-nearest-even.
+ *   - Layout: row-major.  Activation rows have a leading dimension (ld*, in
+ *     elements); weight tensors are dense.  Vector loads need 16-byte
+ *     aligned device pointers, K, R, ld* multiples of 8 (else
+ *     SGG_ERR_UNSUPPORTED).
+ *   - Device calls take device pointers (except where "host" is said),
+ *     enqueue work on `stream` (a hipStream_t; NULL = the null stream),
+ *     return without synchronising and never allocate memory.  Arguments
+ *     are validated on the host before anything is enqueued.  Values that
+ *     live in device memory (plan arrays, ranks, ids) are not read by the
+ *     host: kernels skip tokens whose permutation entry lies outside
+ *     [0, s), treat a segment slot outside [0, L) as rank 0, clamp ranks to
+ *     [0, R] and give zeros for token ids outside [0, vocab_size).  A
+ *     segment longer than `chunk_size` is still processed in full.
+ *   - Row order: h, the output and every activation use the original token
+ *     order; `permutation` (sorted position -> token) is only a gather /
+ *     scatter index.
+ */
+#ifndef SGG_LORA_H_
+#define SGG_LORA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGG_OK 0
+#define SGG_ERR_INVALID (-1)     /* bad argument: null pointer, bad size, stride, offsets */
+#define SGG_ERR_UNSUPPORTED (-2) /* well-formed but not implemented (alignment, extra vocab) */
+#define SGG_ERR_CAPACITY (-3)    /* output capacity too small, slot id out of range */
+#define SGG_ERR_HIP (-4)         /* the HIP runtime reported an error at launch */
+
+#define SGG_MIN_CHUNK_SIZE 16    /* smallest chunk the heuristic picks */
+#define SGG_MAX_SLICES 8         /* most stacked slices one call takes */
+
+/* Message describing the last non-zero status returned on this thread. */
+const char* lora_last_error(void);
+
+/*
+ * lora_plan_segments -- the batch plan, on the host.
+ * (chunked_backend.py page: _determine_chunk_size_for_tokens,
+ *  _get_permutation, _get_segments_info, _build_req_seg_indptr, and the
+ *  graph branch of prepare_lora_batch for padding.)
+ *
+ *   seq_lens[num_reqs]    host; tokens per request, >= 0.  May be NULL in
+ *                         decode mode (one token per request); in decode
+ *                         mode every length must be 1.
+ *   req_slots[num_reqs]   host; adapter slot of each request, in [0, max_loras).
+ *   is_decode             nonzero: the chunk rule keys on num_reqs;
+ *                         zero (extend): it keys on the total token count.
+ *   max_chunk_size        the server cap on the chunk size.
+ *   chunk_size_override   > 0 forces that chunk size; 0 uses the rule.
+ *   permutation[perm_capacity]  out: sorted position -> token index, a stable
+ *                         ascending sort of tokens by slot (s entries).
+ *   seg_indptr[seg_capacity+1], seg_slots[seg_capacity]  out: CSR segment
+ *                         boundaries over sorted positions and each segment's
+ *                         slot.  Runs of equal slots are cut into segments of
+ *                         chunk tokens with the remainder last.  Entries past
+ *                         the segment count are padded: slot 0 and zero
+ *                         length (boundary = s).
+ *   req_seg_indptr[num_reqs+1]  out (may be NULL): [0, cumsum(seq_lens)].
+ *   out_num_segments, out_chunk_size, out_num_tokens  out (each may be NULL).
+ * Errors: SGG_ERR_INVALID for bad lengths / sizes, SGG_ERR_CAPACITY when a
+ * slot is outside [0, max_loras) or a capacity is too small.  Deterministic:
+ * the same inputs always give the same arrays.  Thread-safe.
+ */
+int lora_plan_segments(const int32_t* seq_lens, const int32_t* req_slots, int32_t num_reqs,
+                       int32_t max_loras, int32_t is_decode, int32_t max_chunk_size,
+                       int32_t chunk_size_override,
+                       int32_t* permutation, int64_t perm_capacity,
+                       int32_t* seg_indptr, int32_t* seg_slots, int32_t seg_capacity,
+                       int32_t* req_seg_indptr,
+                       int32_t* out_num_segments, int32_t* out_chunk_size,
+                       int64_t* out_num_tokens);
+
+/*
+ * Upper bound on the number of segments of any plan over num_tokens tokens
+ * with at most max_loras distinct slots and chunks of at least min_chunk
+ * tokens (SGG_MIN_CHUNK_SIZE unless an override is used).  Host only.
+ */
+int64_t lora_plan_max_segments(int64_t num_tokens, int32_t max_loras, int32_t min_chunk);
+
+/*
+ * lora_shrink -- LoRA-A segmented gather GEMM.
+ * (chunked_backend.py page: run_lora_a_sgemm, and the shrink step of
+ *  run_qkv_lora / run_gate_up_lora; base_backend.py page: run_lora_a_sgemm
+ *  shape contract.)
+ *
+ *   h[t, k*R + j] = sum_{q<K} A[a(t), k*R + j, q] * x[t, q]   for j < rho_a
+ *   h[t, k*R + j] = 0                                         for rho_a <= j < R
+ * for every slice k < c (c = num_slices).  Rank padding of A is never read.
+ *
+ *   x          (s, K) bf16, row stride ldx >= K.
+ *   A          (L, c*R, K) bf16, dense.
+ *   h          (s, c*R) bf16 out, row stride ldh >= c*R.  Every row of every
+ *              token covered by the plan is written.
+ *   seg_indptr[num_segments+1], seg_slots[num_segments], permutation[s]:
+ *              the plan (device memory), as lora_plan_segments makes it.
+ *   lora_ranks[L] int32 (device).
+ *   chunk_size the plan's chunk size (tiling hint; an upper bound on
+ *              segment length for efficiency, not for correctness).
+ *   workspace  device scratch of at least lora_shrink_workspace_bytes()
+ *              bytes (may be NULL when that is 0).  Its first use must see
+ *              it zero-filled; every call leaves it ready for the next one.
+ *              Calls that share a workspace must not overlap in time.
+ */
+int64_t lora_shrink_workspace_bytes(int64_t s, int64_t in_dim, int32_t num_slices, int32_t R,
+                                    int32_t num_segments, int32_t chunk_size);
+int lora_shrink(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh,
+                int64_t s, int64_t in_dim, int32_t num_loras, int32_t num_slices, int32_t R,
+                const int32_t* seg_indptr, const int32_t* seg_slots, int32_t num_segments,
+                const int32_t* permutation, const int32_t* lora_ranks, int32_t chunk_size,
+                void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * lora_expand -- LoRA-B segmented gather GEMM with scaling, added in place.
+ * (chunked_backend.py page: run_lora_b_sgemm with slice offsets [0, out],
+ *  and the expand step of run_qkv_lora / run_gate_up_lora; base_backend.py
+ *  page: run_lora_b_sgemm shape contract.)
+ *
+ *   out[t, o_k + n] += sigma_a * sum_{j < rho_a} B[a, o_k + n, j] * h[t, k*R + j]
+ * for slice k < c and n < o_{k+1} - o_k.  Columns at or past o_c and every
+ * row of a rank-0 slot are left bit-for-bit unchanged.  Rank padding of B
+ * and h is never read.
+ *
+ *   h          (s, c*R) bf16, row stride ldh >= c*R.
+ *   B          (L, N, R) bf16 dense, N >= o_c.
+ *   base_output (s, >= o_c) bf16, row stride ldo, read and written in place.
+ *   slice_offsets[num_slices+1]  HOST int32, o_0 = 0, non-decreasing,
+ *              1 <= num_slices <= SGG_MAX_SLICES.
+ *   max_slice_size  >= the widest slice (a launch bound; results do not
+ *              depend on it).
+ *   scalings[L] float32 (device).
+ */
+int lora_expand(const void* h, int64_t ldh, const void* B, int64_t N, void* base_output,
+                int64_t ldo, int64_t s, int32_t num_loras, int32_t R,
+                const int32_t* slice_offsets, int32_t num_slices, int32_t max_slice_size,
+                const int32_t* seg_indptr, const int32_t* seg_slots, int32_t num_segments,
+                const int32_t* permutation, const int32_t* lora_ranks, const float* scalings,
+                int32_t chunk_size, void* stream);
+
+/*
+ * lora_qkv -- stacked LoRA for qkv (c = 3) or gate_up (c = 2) projections:
+ * shrink then expand with the same plan.
+ * (chunked_backend.py page: run_qkv_lora, run_gate_up_lora;
+ *  base_backend.py page: their shape contracts.  A plain projection is
+ *  c = 1 with offsets [0, out].)
+ *
+ *   x (s, K), A (L, c*R, K), B (L, N, R), base_output (s, >= o_c) as in
+ *   lora_shrink / lora_expand.  The intermediate h (bf16, s x c*R) lives in
+ *   `workspace`, which must hold lora_qkv_workspace_bytes() bytes, zero-
+ *   filled on first use, and is not shared by overlapping calls.
+ */
+int64_t lora_qkv_workspace_bytes(int64_t s, int64_t in_dim, int32_t num_slices, int32_t R,
+                                 int32_t num_segments, int32_t chunk_size);
+int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B, int64_t N,
+             void* base_output, int64_t ldo, int64_t s, int64_t in_dim, int32_t num_loras,
+             int32_t R, const int32_t* slice_offsets, int32_t num_slices,
+             int32_t max_slice_size, const int32_t* seg_indptr, const int32_t* seg_slots,
+             int32_t num_segments, const int32_t* permutation, const int32_t* lora_ranks,
+             const float* scalings, int32_t chunk_size, void* workspace,
+             int64_t workspace_bytes, void* stream);
+
+/*
+ * lora_a_embedding -- LoRA-A embedding lookup.
+ * (chunked_backend.py page: run_lora_a_embedding; base_backend.py page:
+ *  run_lora_a_embedding shape contract.)
+ *
+ *   out[t, j] = A_emb[a(t), j, input_ids[t]]   for j < rho_a and
+ *                                              0 <= input_ids[t] < vocab_size
+ *   out[t, j] = 0                              otherwise.
+ *
+ *   input_ids  (s,) int64 (device).
+ *   A_emb      (L, R, V) bf16 dense, V >= vocab_size.
+ *   out        (s, R) bf16, row stride ldo >= R.
+ *   has_extra_embeddings  must be 0: added-vocabulary embeddings are not
+ *              supported by the chunked backend (SGG_ERR_UNSUPPORTED).
+ */
+int lora_a_embedding(const int64_t* input_ids, const void* A_emb, int64_t V, void* out,
+                     int64_t ldo, int64_t s, int32_t num_loras, int32_t R,
+                     int64_t vocab_size, const int32_t* seg_indptr, const int32_t* seg_slots,
+                     int32_t num_segments, const int32_t* permutation,
+                     const int32_t* lora_ranks, int32_t has_extra_embeddings, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGG_LORA_H_ */

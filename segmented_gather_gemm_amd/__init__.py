@@ -1,0 +1,27 @@
+"""Chunked SGMV (segmented gather GEMM) LoRA for AMD Instinct MI355X (gfx950).
+
+The work is done by ``libsgg_lora.so`` (C ABI in ``include/sgg_lora.h``): a
+host planner and hand-written HIP kernels.  This package only marshals
+arguments to it; importing it fails if the library has not been built
+(``python segmented_gather_gemm_amd/build.py``).
+"""
+
+from ._lib import SggError, lib
+from .backend import ChunkedSgmvLoRA
+from .binding import (
+    LoRABatchInfo,
+    default_workspace,
+    lora_a_embedding,
+    lora_expand,
+    lora_plan_max_segments,
+    lora_plan_segments,
+    lora_qkv,
+    lora_shrink,
+)
+
+lib()  # load now: a missing library is an import error, never a silent fallback
+
+__all__ = [
+    "ChunkedSgmvLoRA", "LoRABatchInfo", "SggError", "default_workspace", "lora_a_embedding",
+    "lora_expand", "lora_plan_max_segments", "lora_plan_segments", "lora_qkv", "lora_shrink",
+]

@@ -1,0 +1,271 @@
+"""Thin Python binding over the C ABI: argument marshalling only.
+
+Each function has the name of the C entry point it calls and does no
+arithmetic of its own.  Tensors must be bf16 (int32 / int64 / float32 for
+plan arrays, ids and scalings) on a ROCm device; the call is enqueued on
+torch's current stream of that device.
+"""
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from ._lib import check, lib
+
+_P32 = ctypes.POINTER(ctypes.c_int32)
+_P64 = ctypes.POINTER(ctypes.c_int64)
+
+
+@dataclass
+class LoRABatchInfo:
+    """Device-resident plan of one batch (the pages' LoRABatchInfo fields).
+
+    ``weight_indices`` is the per-segment slot array, ``max_len`` the chunk
+    size.  Segment arrays may be longer than ``num_segments`` (padding).
+    """
+    bs: int
+    num_tokens: int
+    num_segments: int
+    max_len: int
+    seg_indptr: torch.Tensor
+    weight_indices: torch.Tensor
+    permutation: torch.Tensor
+    lora_ranks: torch.Tensor
+    scalings: torch.Tensor
+    req_seg_indptr: Optional[torch.Tensor] = None
+    req_weight_indices: Optional[torch.Tensor] = None
+    use_cuda_graph: bool = False
+
+
+def _vp(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _host_i32(values):
+    arr = np.ascontiguousarray(np.asarray(values, dtype=np.int32))
+    return arr, arr.ctypes.data_as(_P32)
+
+
+def _cpu_i32_ptr(t):
+    if t is None:
+        return ctypes.cast(0, _P32)
+    assert t.dtype == torch.int32 and t.device.type == "cpu" and t.is_contiguous()
+    return ctypes.cast(t.data_ptr(), _P32)
+
+
+def _need_bf16(name, t, dims):
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device")
+    if t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimensions, got shape {tuple(t.shape)}")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in its last dimension")
+
+
+def _need_dense(name, t):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def lora_plan_max_segments(num_tokens, max_loras, min_chunk=16):
+    return int(lib().lora_plan_max_segments(int(num_tokens), int(max_loras), int(min_chunk)))
+
+
+def lora_plan_segments(seq_lens, req_slots, max_loras, is_decode, max_chunk_size,
+                       chunk_size_override=0, seg_capacity=None, out=None):
+    """Plan a batch on the host.
+
+    ``out`` may hold preallocated contiguous int32 CPU tensors ``permutation``,
+    ``seg_indptr``, ``seg_slots``, ``req_seg_indptr`` (e.g. views of one
+    pinned staging buffer); otherwise NumPy arrays are allocated.  Returns a
+    dict with those arrays and ``num_segments``, ``chunk_size``,
+    ``num_tokens``.
+    """
+    slots, p_slots = _host_i32(req_slots)
+    bs = len(slots)
+    if seq_lens is None:
+        lens, p_lens = None, ctypes.cast(0, _P32)
+        s_hint = bs
+    else:
+        lens, p_lens = _host_i32(seq_lens)
+        if len(lens) != bs:
+            raise ValueError("seq_lens and req_slots differ in length")
+        s_hint = int(lens.astype(np.int64).sum())
+    min_chunk = chunk_size_override if chunk_size_override > 0 else 16
+    cap = (lora_plan_max_segments(s_hint, max_loras, min_chunk)
+           if seg_capacity is None else int(seg_capacity))
+    if out is None:
+        out = {"permutation": np.zeros(max(s_hint, 1), np.int32),
+               "seg_indptr": np.zeros(cap + 1, np.int32),
+               "seg_slots": np.zeros(max(cap, 1), np.int32),
+               "req_seg_indptr": np.zeros(bs + 1, np.int32)}
+
+    def ptr(a):
+        if isinstance(a, np.ndarray):
+            return a.ctypes.data_as(_P32)
+        return _cpu_i32_ptr(a)
+
+    n_seg, chunk, n_tok = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    perm = out["permutation"]
+    check(lib().lora_plan_segments(
+        p_lens, p_slots, bs, int(max_loras), 1 if is_decode else 0, int(max_chunk_size),
+        int(chunk_size_override), ptr(perm), int(perm.shape[0]) if s_hint else 0,
+        ptr(out["seg_indptr"]), ptr(out["seg_slots"]), cap, ptr(out["req_seg_indptr"]),
+        ctypes.byref(n_seg), ctypes.byref(chunk), ctypes.byref(n_tok)))
+    res = dict(out)
+    res.update(num_segments=n_seg.value, chunk_size=chunk.value, num_tokens=n_tok.value,
+               capacity=cap)
+    return res
+
+
+# ----------------------------------------------------------------- workspace
+
+_workspaces = {}
+
+
+def default_workspace(device, nbytes):
+    """A zero-initialised, grow-only scratch buffer per device.
+
+    Calls that use the same workspace must not overlap: use it from one
+    stream, or pass a separate workspace per stream.
+    """
+    device = torch.device(device)
+    key = (device.type, device.index if device.index is not None else torch.cuda.current_device())
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        size = max(int(nbytes), 1 << 20)
+        if ws is not None:
+            size = max(size, 2 * ws.numel())
+        ws = torch.zeros(size, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _offsets(slice_offsets):
+    if isinstance(slice_offsets, torch.Tensor):
+        slice_offsets = slice_offsets.detach().to("cpu")  # host copy (synchronises if on device)
+    arr, ptr = _host_i32(slice_offsets)
+    if arr.ndim != 1 or len(arr) < 2:
+        raise ValueError("slice_offsets needs at least two entries")
+    return arr, ptr
+
+
+# ---------------------------------------------------------------- device calls
+
+def lora_shrink(x, weights, batch_info: LoRABatchInfo, num_slices=1, out=None, workspace=None):
+    """LoRA-A: x (s, K), weights (L, c*R, K) -> h (s, c*R), original token order."""
+    _need_bf16("x", x, 2)
+    _need_bf16("weights", weights, 3)
+    _need_dense("weights", weights)
+    s, K = x.shape
+    L, CR, K2 = weights.shape
+    if K2 != K:
+        raise ValueError(f"weights in_dim {K2} != x in_dim {K}")
+    if CR % num_slices:
+        raise ValueError(f"weights rows {CR} not a multiple of num_slices {num_slices}")
+    if s != batch_info.num_tokens:
+        raise ValueError(f"x has {s} rows, the plan has {batch_info.num_tokens} tokens")
+    R = CR // num_slices
+    if out is None:
+        out = torch.empty((s, CR), dtype=torch.bfloat16, device=x.device)
+    _need_bf16("out", out, 2)
+    need = int(lib().lora_shrink_workspace_bytes(s, K, num_slices, R, batch_info.num_segments,
+                                                 batch_info.max_len))
+    ws = workspace if workspace is not None or need == 0 else default_workspace(x.device, need)
+    check(lib().lora_shrink(
+        _vp(x), x.stride(0), _vp(weights), _vp(out), out.stride(0), s, K, L, num_slices, R,
+        _vp(batch_info.seg_indptr), _vp(batch_info.weight_indices), batch_info.num_segments,
+        _vp(batch_info.permutation), _vp(batch_info.lora_ranks), batch_info.max_len,
+        _vp(ws), ws.numel() if ws is not None else 0, _stream(x.device)))
+    return out
+
+
+def lora_expand(h, weights, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
+                base_output=None):
+    """LoRA-B: base_output[:, o_k:o_{k+1}] += scaling * h-slice k @ B-slice k^T, in place.
+
+    ``base_output=None`` gives a zero-filled output (the update alone).
+    """
+    _need_bf16("h", h, 2)
+    _need_bf16("weights", weights, 3)
+    _need_dense("weights", weights)
+    offs, p_offs = _offsets(slice_offsets)
+    c = len(offs) - 1
+    s = h.shape[0]
+    L, N, R = weights.shape
+    if s != batch_info.num_tokens:
+        raise ValueError(f"h has {s} rows, the plan has {batch_info.num_tokens} tokens")
+    if base_output is None:
+        base_output = torch.zeros((s, int(offs[-1])), dtype=torch.bfloat16, device=h.device)
+    _need_bf16("base_output", base_output, 2)
+    if base_output.shape[0] != s:
+        raise ValueError("base_output rows differ from h rows")
+    check(lib().lora_expand(
+        _vp(h), h.stride(0), _vp(weights), N, _vp(base_output), base_output.stride(0), s, L, R,
+        p_offs, c, int(max_slice_size), _vp(batch_info.seg_indptr),
+        _vp(batch_info.weight_indices), batch_info.num_segments, _vp(batch_info.permutation),
+        _vp(batch_info.lora_ranks), _vp(batch_info.scalings), batch_info.max_len,
+        _stream(h.device)))
+    return base_output
+
+
+def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
+             base_output=None, workspace=None):
+    """Stacked shrink + expand with one plan (qkv: 3 slices, gate_up: 2)."""
+    _need_bf16("x", x, 2)
+    _need_bf16("A", A, 3)
+    _need_bf16("B", B, 3)
+    _need_dense("A", A)
+    _need_dense("B", B)
+    offs, p_offs = _offsets(slice_offsets)
+    c = len(offs) - 1
+    s, K = x.shape
+    L, CR, K2 = A.shape
+    _, N, R = B.shape
+    if K2 != K or CR != c * R:
+        raise ValueError(f"A shape {tuple(A.shape)} does not match x ({K}) and c*R ({c}*{R})")
+    if s != batch_info.num_tokens:
+        raise ValueError(f"x has {s} rows, the plan has {batch_info.num_tokens} tokens")
+    if base_output is None:
+        base_output = torch.zeros((s, int(offs[-1])), dtype=torch.bfloat16, device=x.device)
+    _need_bf16("base_output", base_output, 2)
+    need = int(lib().lora_qkv_workspace_bytes(s, K, c, R, batch_info.num_segments,
+                                              batch_info.max_len))
+    ws = workspace if workspace is not None else default_workspace(x.device, max(need, 1))
+    check(lib().lora_qkv(
+        _vp(x), x.stride(0), _vp(A), _vp(B), N, _vp(base_output), base_output.stride(0), s, K,
+        L, R, p_offs, c, int(max_slice_size), _vp(batch_info.seg_indptr),
+        _vp(batch_info.weight_indices), batch_info.num_segments, _vp(batch_info.permutation),
+        _vp(batch_info.lora_ranks), _vp(batch_info.scalings), batch_info.max_len, _vp(ws),
+        ws.numel(), _stream(x.device)))
+    return base_output
+
+
+def lora_a_embedding(input_ids, weights, batch_info: LoRABatchInfo, vocab_size,
+                     extra_embeddings=None, out=None):
+    """LoRA-A embedding lookup: ids (s,), weights (L, R, V) -> (s, R)."""
+    if input_ids.dtype != torch.int64 or input_ids.device.type != "cuda":
+        raise TypeError("input_ids must be an int64 tensor on a ROCm device")
+    _need_bf16("weights", weights, 3)
+    _need_dense("weights", weights)
+    s = input_ids.shape[0]
+    L, R, V = weights.shape
+    if s != batch_info.num_tokens:
+        raise ValueError(f"{s} ids, the plan has {batch_info.num_tokens} tokens")
+    if out is None:
+        out = torch.empty((s, R), dtype=torch.bfloat16, device=weights.device)
+    check(lib().lora_a_embedding(
+        _vp(input_ids.contiguous()), _vp(weights), V, _vp(out), out.stride(0), s, L, R,
+        int(vocab_size), _vp(batch_info.seg_indptr), _vp(batch_info.weight_indices),
+        batch_info.num_segments, _vp(batch_info.permutation), _vp(batch_info.lora_ranks),
+        0 if extra_embeddings is None else 1, _stream(weights.device)))
+    return out

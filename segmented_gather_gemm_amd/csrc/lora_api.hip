@@ -1,0 +1,338 @@
+// C-ABI device entry points: argument validation (host only, before anything
+// is enqueued), tile choice and kernel launches.
+#include <cinttypes>
+
+#include "sgg_internal.h"
+#include "sgg_kernels.h"
+#include "../../include/sgg_lora.h"
+
+using sgg::fail;
+
+namespace {
+
+#define SGG_CHECK(cond, code, ...) \
+  do {                             \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+int check_plan(int64_t s, int32_t num_segments, const int32_t* seg_indptr,
+               const int32_t* seg_slots, const int32_t* permutation, const int32_t* lora_ranks,
+               int32_t num_loras, int32_t chunk_size) {
+  SGG_CHECK(s >= 0 && s <= INT32_MAX, SGG_ERR_INVALID, "s=%" PRId64 " outside [0, 2^31)", s);
+  SGG_CHECK(num_segments >= 0, SGG_ERR_INVALID, "num_segments=%d is negative", num_segments);
+  SGG_CHECK(num_loras > 0, SGG_ERR_INVALID, "num_loras=%d must be positive", num_loras);
+  SGG_CHECK(chunk_size > 0, SGG_ERR_INVALID, "chunk_size=%d must be positive", chunk_size);
+  SGG_CHECK(seg_indptr && seg_slots && permutation && lora_ranks, SGG_ERR_INVALID,
+            "a plan array (seg_indptr, seg_slots, permutation, lora_ranks) is NULL");
+  return SGG_OK;
+}
+
+int check_shrink(const void* x, int64_t ldx, const void* A, const void* h, int64_t ldh,
+                 int64_t s, int64_t K, int32_t num_loras, int32_t c, int32_t R) {
+  SGG_CHECK(A && ((x && h) || s == 0), SGG_ERR_INVALID, "x, A or h is NULL");
+  SGG_CHECK(K > 0, SGG_ERR_INVALID, "in_dim=%" PRId64 " must be positive", K);
+  SGG_CHECK(c >= 1 && c <= SGG_MAX_SLICES, SGG_ERR_INVALID, "num_slices=%d outside [1, %d]", c,
+            SGG_MAX_SLICES);
+  SGG_CHECK(R > 0, SGG_ERR_INVALID, "R=%d must be positive", R);
+  SGG_CHECK(ldx >= K, SGG_ERR_INVALID, "ldx=%" PRId64 " < in_dim=%" PRId64, ldx, K);
+  SGG_CHECK(ldh >= static_cast<int64_t>(c) * R, SGG_ERR_INVALID,
+            "ldh=%" PRId64 " < num_slices*R=%d", ldh, c * R);
+  SGG_CHECK(K % 8 == 0 && ldx % 8 == 0 && R % 8 == 0 && ldh % 8 == 0, SGG_ERR_UNSUPPORTED,
+            "in_dim, ldx, R and ldh must be multiples of 8 (got %" PRId64 ", %" PRId64
+            ", %d, %" PRId64 ")", K, ldx, R, ldh);
+  SGG_CHECK(sgg::aligned16(x) && sgg::aligned16(A) && sgg::aligned16(h), SGG_ERR_UNSUPPORTED,
+            "x, A and h must be 16-byte aligned");
+  (void)s;
+  (void)num_loras;
+  return SGG_OK;
+}
+
+int check_expand(const void* h, int64_t ldh, const void* B, int64_t N, const void* out,
+                 int64_t ldo, int32_t R, const int32_t* offs, int32_t c, int32_t max_slice,
+                 const float* scalings, int64_t s) {
+  SGG_CHECK(B && scalings && (h || s == 0), SGG_ERR_INVALID, "h, B or scalings is NULL");
+  SGG_CHECK(out || s == 0, SGG_ERR_INVALID,
+            "base_output is NULL (pass a zero-filled tensor instead)");
+  SGG_CHECK(offs, SGG_ERR_INVALID, "slice_offsets is NULL");
+  SGG_CHECK(c >= 1 && c <= SGG_MAX_SLICES, SGG_ERR_INVALID, "num_slices=%d outside [1, %d]", c,
+            SGG_MAX_SLICES);
+  SGG_CHECK(R > 0, SGG_ERR_INVALID, "R=%d must be positive", R);
+  SGG_CHECK(offs[0] == 0, SGG_ERR_INVALID, "slice_offsets[0]=%d must be 0", offs[0]);
+  int32_t widest = 0;
+  for (int k = 0; k < c; ++k) {
+    SGG_CHECK(offs[k + 1] >= offs[k], SGG_ERR_INVALID,
+              "slice_offsets must be non-decreasing (offs[%d]=%d > offs[%d]=%d)", k, offs[k],
+              k + 1, offs[k + 1]);
+    if (offs[k + 1] - offs[k] > widest) widest = offs[k + 1] - offs[k];
+  }
+  SGG_CHECK(max_slice >= widest, SGG_ERR_INVALID, "max_slice_size=%d < widest slice %d",
+            max_slice, widest);
+  SGG_CHECK(N >= offs[c], SGG_ERR_INVALID, "B has %" PRId64 " rows < last offset %d", N, offs[c]);
+  SGG_CHECK(ldo >= offs[c], SGG_ERR_INVALID, "ldo=%" PRId64 " < last offset %d", ldo, offs[c]);
+  SGG_CHECK(ldh >= static_cast<int64_t>(c) * R, SGG_ERR_INVALID,
+            "ldh=%" PRId64 " < num_slices*R=%d", ldh, c * R);
+  SGG_CHECK(R % 8 == 0 && ldh % 8 == 0, SGG_ERR_UNSUPPORTED,
+            "R and ldh must be multiples of 8 (got %d, %" PRId64 ")", R, ldh);
+  SGG_CHECK(R <= 128, SGG_ERR_UNSUPPORTED, "R=%d above 128 is not supported", R);
+  SGG_CHECK(sgg::aligned16(h) && sgg::aligned16(B), SGG_ERR_UNSUPPORTED,
+            "h and B must be 16-byte aligned");
+  SGG_CHECK((reinterpret_cast<uintptr_t>(out) & 1u) == 0, SGG_ERR_UNSUPPORTED,
+            "base_output must be 2-byte aligned");
+  return SGG_OK;
+}
+
+sgg::ExpandTiling choose_expand_tiling(const int32_t* offs, int c, int num_segments, int R,
+                                       int32_t* tile_start, int32_t* total) {
+  sgg::ExpandTiling t{};
+  t.ks = R <= 32 ? 1 : (R <= 64 ? 2 : 4);
+  t.nfw = 1;
+  for (int nfw : {4, 2, 1}) {
+    int64_t tiles = 0;
+    for (int k = 0; k < c; ++k) tiles += (offs[k + 1] - offs[k] + 64 * nfw - 1) / (64 * nfw);
+    if (nfw == 1 || tiles * num_segments >= 512) {
+      t.nfw = nfw;
+      break;
+    }
+  }
+  int32_t acc = 0;
+  for (int k = 0; k < c; ++k) {
+    tile_start[k] = acc;
+    acc += (offs[k + 1] - offs[k] + 64 * t.nfw - 1) / (64 * t.nfw);
+  }
+  tile_start[c] = acc;
+  *total = acc;
+  t.grid = static_cast<int64_t>(acc) * num_segments;
+  return t;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SGG_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return SGG_OK;
+}
+
+int do_shrink(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh, int64_t s,
+              int64_t K, int32_t num_loras, int32_t c, int32_t R, const int32_t* seg_indptr,
+              const int32_t* seg_slots, int32_t num_segments, const int32_t* permutation,
+              const int32_t* lora_ranks, int32_t chunk_size, int32_t* counters,
+              void* partial, int64_t partial_avail, hipStream_t stream) {
+  const sgg::ShrinkTiling t = sgg::choose_shrink_tiling(s, K, c * R, num_segments, chunk_size);
+  if (t.ksplit > 1) {
+    SGG_CHECK(counters != nullptr && partial != nullptr && partial_avail >= t.partial_bytes,
+              SGG_ERR_CAPACITY, "shrink workspace too small: %" PRId64
+              " partial bytes needed, %" PRId64 " available", t.partial_bytes,
+              partial ? partial_avail : 0);
+  }
+  SGG_CHECK(t.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "shrink grid too large");
+  sgg::ShrinkParams p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.A = static_cast<const uint16_t*>(A);
+  p.h = static_cast<uint16_t*>(h);
+  p.partial = static_cast<float*>(partial);
+  p.counters = counters;
+  p.counter_cap = sgg::kCounterCap;
+  p.seg_indptr = seg_indptr;
+  p.seg_slots = seg_slots;
+  p.perm = permutation;
+  p.ranks = lora_ranks;
+  p.ldx = ldx;
+  p.ldh = ldh;
+  p.s = s;
+  p.K = K;
+  p.kps = t.kps;
+  p.L = num_loras;
+  p.R = R;
+  p.CR = c * R;
+  p.num_segments = num_segments;
+  p.mblocks = t.mblocks;
+  p.nblocks = t.nblocks;
+  p.ksplit = t.ksplit;
+  return launch_status(sgg::launch_shrink(p, t, stream), "shrink");
+}
+
+int do_expand(const void* h, int64_t ldh, const void* B, int64_t N, void* out, int64_t ldo,
+              int64_t s, int32_t num_loras, int32_t R, const int32_t* offs, int32_t c,
+              const int32_t* seg_indptr, const int32_t* seg_slots, int32_t num_segments,
+              const int32_t* permutation, const int32_t* lora_ranks, const float* scalings,
+              hipStream_t stream) {
+  sgg::ExpandParams p{};
+  const sgg::ExpandTiling t =
+      choose_expand_tiling(offs, c, num_segments, R, p.tile_start, &p.total_tiles);
+  SGG_CHECK(t.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "expand grid too large");
+  bool vec4 = (reinterpret_cast<uintptr_t>(out) & 7u) == 0 && ldo % 4 == 0;
+  for (int k = 0; k <= c; ++k) {
+    p.offs[k] = offs[k];
+    vec4 = vec4 && offs[k] % 4 == 0;
+  }
+  p.h = static_cast<const uint16_t*>(h);
+  p.B = static_cast<const uint16_t*>(B);
+  p.out = static_cast<uint16_t*>(out);
+  p.seg_indptr = seg_indptr;
+  p.seg_slots = seg_slots;
+  p.perm = permutation;
+  p.ranks = lora_ranks;
+  p.scalings = scalings;
+  p.ldh = ldh;
+  p.ldo = ldo;
+  p.s = s;
+  p.N = N;
+  p.L = num_loras;
+  p.R = R;
+  p.c = c;
+  p.num_segments = num_segments;
+  p.vec4 = vec4 ? 1 : 0;
+  return launch_status(sgg::launch_expand(p, t, stream), "expand");
+}
+
+}  // namespace
+
+extern "C" int64_t lora_shrink_workspace_bytes(int64_t s, int64_t in_dim, int32_t num_slices,
+                                               int32_t R, int32_t num_segments,
+                                               int32_t chunk_size) {
+  if (s <= 0 || in_dim <= 0 || num_slices <= 0 || R <= 0 || num_segments <= 0 || chunk_size <= 0)
+    return 0;
+  const sgg::ShrinkTiling t =
+      sgg::choose_shrink_tiling(s, in_dim, num_slices * R, num_segments, chunk_size);
+  return t.ksplit > 1 ? sgg::kCounterBytes + t.partial_bytes : 0;
+}
+
+extern "C" int64_t lora_qkv_workspace_bytes(int64_t s, int64_t in_dim, int32_t num_slices,
+                                            int32_t R, int32_t num_segments, int32_t chunk_size) {
+  if (s <= 0 || num_slices <= 0 || R <= 0) return 0;
+  int64_t partial = 0;
+  if (in_dim > 0 && num_segments > 0 && chunk_size > 0)
+    partial = sgg::choose_shrink_tiling(s, in_dim, num_slices * R, num_segments, chunk_size)
+                  .partial_bytes;
+  return sgg::kCounterBytes + sgg::round_up(s * num_slices * R * 2, 256) + partial;
+}
+
+extern "C" int lora_shrink(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh,
+                           int64_t s, int64_t in_dim, int32_t num_loras, int32_t num_slices,
+                           int32_t R, const int32_t* seg_indptr, const int32_t* seg_slots,
+                           int32_t num_segments, const int32_t* permutation,
+                           const int32_t* lora_ranks, int32_t chunk_size, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+  int rc = check_plan(s, num_segments, seg_indptr, seg_slots, permutation, lora_ranks, num_loras,
+                      chunk_size);
+  if (rc) return rc;
+  rc = check_shrink(x, ldx, A, h, ldh, s, in_dim, num_loras, num_slices, R);
+  if (rc) return rc;
+  if (s == 0 || num_segments == 0) return sgg::ok();
+  SGG_CHECK(workspace == nullptr || sgg::aligned16(workspace), SGG_ERR_UNSUPPORTED,
+            "workspace must be 16-byte aligned");
+  const int64_t part_avail = workspace_bytes - sgg::kCounterBytes;
+  rc = do_shrink(x, ldx, A, h, ldh, s, in_dim, num_loras, num_slices, R, seg_indptr, seg_slots,
+                 num_segments, permutation, lora_ranks, chunk_size,
+                 static_cast<int32_t*>(workspace),
+                 workspace && part_avail > 0 ? static_cast<char*>(workspace) + sgg::kCounterBytes
+                                             : nullptr,
+                 part_avail, static_cast<hipStream_t>(stream));
+  return rc ? rc : sgg::ok();
+}
+
+extern "C" int lora_expand(const void* h, int64_t ldh, const void* B, int64_t N,
+                           void* base_output, int64_t ldo, int64_t s, int32_t num_loras,
+                           int32_t R, const int32_t* slice_offsets, int32_t num_slices,
+                           int32_t max_slice_size, const int32_t* seg_indptr,
+                           const int32_t* seg_slots, int32_t num_segments,
+                           const int32_t* permutation, const int32_t* lora_ranks,
+                           const float* scalings, int32_t chunk_size, void* stream) {
+  int rc = check_plan(s, num_segments, seg_indptr, seg_slots, permutation, lora_ranks, num_loras,
+                      chunk_size);
+  if (rc) return rc;
+  rc = check_expand(h, ldh, B, N, base_output, ldo, R, slice_offsets, num_slices, max_slice_size,
+                    scalings, s);
+  if (rc) return rc;
+  if (s == 0 || num_segments == 0 || slice_offsets[num_slices] == 0) return sgg::ok();
+  rc = do_expand(h, ldh, B, N, base_output, ldo, s, num_loras, R, slice_offsets, num_slices,
+                 seg_indptr, seg_slots, num_segments, permutation, lora_ranks, scalings,
+                 static_cast<hipStream_t>(stream));
+  return rc ? rc : sgg::ok();
+}
+
+extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B, int64_t N,
+                        void* base_output, int64_t ldo, int64_t s, int64_t in_dim,
+                        int32_t num_loras, int32_t R, const int32_t* slice_offsets,
+                        int32_t num_slices, int32_t max_slice_size, const int32_t* seg_indptr,
+                        const int32_t* seg_slots, int32_t num_segments,
+                        const int32_t* permutation, const int32_t* lora_ranks,
+                        const float* scalings, int32_t chunk_size, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
+  int rc = check_plan(s, num_segments, seg_indptr, seg_slots, permutation, lora_ranks, num_loras,
+                      chunk_size);
+  if (rc) return rc;
+  const int64_t hbytes = sgg::round_up(s * num_slices * R * 2, 256);
+  SGG_CHECK(workspace != nullptr || s == 0, SGG_ERR_INVALID, "workspace is NULL");
+  SGG_CHECK(workspace == nullptr || sgg::aligned16(workspace), SGG_ERR_UNSUPPORTED,
+            "workspace must be 16-byte aligned");
+  const void* hcheck = workspace ? static_cast<const void*>(static_cast<char*>(workspace) +
+                                                            sgg::kCounterBytes)
+                                 : x;
+  rc = check_shrink(x, ldx, A, hcheck, static_cast<int64_t>(num_slices) * R, s, in_dim,
+                    num_loras, num_slices, R);
+  if (rc) return rc;
+  rc = check_expand(hcheck, static_cast<int64_t>(num_slices) * R, B, N, base_output, ldo, R,
+                    slice_offsets, num_slices, max_slice_size, scalings, s);
+  if (rc) return rc;
+  if (s == 0 || num_segments == 0) return sgg::ok();
+  const int64_t need = lora_qkv_workspace_bytes(s, in_dim, num_slices, R, num_segments, chunk_size);
+  SGG_CHECK(workspace_bytes >= need, SGG_ERR_CAPACITY,
+            "qkv workspace of %" PRId64 " bytes needed, %" PRId64 " given", need, workspace_bytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // Workspace: [split-K counters][h, s x c*R bf16][split-K partials]
+  char* ws = static_cast<char*>(workspace);
+  void* h = ws + sgg::kCounterBytes;
+  rc = do_shrink(x, ldx, A, h, static_cast<int64_t>(num_slices) * R, s, in_dim, num_loras,
+                 num_slices, R, seg_indptr, seg_slots, num_segments, permutation, lora_ranks,
+                 chunk_size, reinterpret_cast<int32_t*>(ws), ws + sgg::kCounterBytes + hbytes,
+                 workspace_bytes - sgg::kCounterBytes - hbytes, st);
+  if (rc) return rc;
+  if (slice_offsets[num_slices] == 0) return sgg::ok();
+  rc = do_expand(h, static_cast<int64_t>(num_slices) * R, B, N, base_output, ldo, s, num_loras, R,
+                 slice_offsets, num_slices, seg_indptr, seg_slots, num_segments, permutation,
+                 lora_ranks, scalings, st);
+  return rc ? rc : sgg::ok();
+}
+
+extern "C" int lora_a_embedding(const int64_t* input_ids, const void* A_emb, int64_t V, void* out,
+                                int64_t ldo, int64_t s, int32_t num_loras, int32_t R,
+                                int64_t vocab_size, const int32_t* seg_indptr,
+                                const int32_t* seg_slots, int32_t num_segments,
+                                const int32_t* permutation, const int32_t* lora_ranks,
+                                int32_t has_extra_embeddings, void* stream) {
+  SGG_CHECK(!has_extra_embeddings, SGG_ERR_UNSUPPORTED,
+            "extra (added-vocabulary) embeddings are not supported by the chunked backend");
+  int rc = check_plan(s, num_segments, seg_indptr, seg_slots, permutation, lora_ranks, num_loras,
+                      1);
+  if (rc) return rc;
+  SGG_CHECK(A_emb && ((input_ids && out) || s == 0), SGG_ERR_INVALID,
+            "input_ids, A_emb or out is NULL");
+  SGG_CHECK(R > 0, SGG_ERR_INVALID, "R=%d must be positive", R);
+  SGG_CHECK(vocab_size >= 0 && vocab_size <= V, SGG_ERR_INVALID,
+            "vocab_size=%" PRId64 " outside [0, V=%" PRId64 "]", vocab_size, V);
+  SGG_CHECK(ldo >= R, SGG_ERR_INVALID, "ldo=%" PRId64 " < R=%d", ldo, R);
+  SGG_CHECK((reinterpret_cast<uintptr_t>(out) & 1u) == 0 &&
+                (reinterpret_cast<uintptr_t>(A_emb) & 1u) == 0 &&
+                (reinterpret_cast<uintptr_t>(input_ids) & 7u) == 0,
+            SGG_ERR_UNSUPPORTED, "misaligned pointer");
+  if (s == 0 || num_segments == 0) return sgg::ok();
+  sgg::EmbeddingParams p{};
+  p.ids = input_ids;
+  p.A = static_cast<const uint16_t*>(A_emb);
+  p.out = static_cast<uint16_t*>(out);
+  p.seg_indptr = seg_indptr;
+  p.seg_slots = seg_slots;
+  p.perm = permutation;
+  p.ranks = lora_ranks;
+  p.V = V;
+  p.vocab = vocab_size;
+  p.ldo = ldo;
+  p.s = s;
+  p.L = num_loras;
+  p.R = R;
+  p.num_segments = num_segments;
+  const int64_t avg = (s + num_segments - 1) / num_segments;
+  int64_t parts = (avg * R + 1023) / 1024;
+  p.parts = static_cast<int32_t>(parts < 1 ? 1 : (parts > 64 ? 64 : parts));
+  rc = launch_status(sgg::launch_embedding(p, static_cast<hipStream_t>(stream)), "embedding");
+  return rc ? rc : sgg::ok();
+}

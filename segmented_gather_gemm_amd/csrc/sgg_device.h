@@ -1,0 +1,67 @@
+// Device-side helpers for the gfx950 kernels: bf16 bit handling, 16-byte
+// fragment loads, the MFMA operand types and the XCD-aware block mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace sgg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
+
+// bf16 bits -> float (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) {
+  return __uint_as_float(bits << 16);
+}
+
+// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// 8 bf16 values (16 bytes) from a 16-byte aligned address.
+__device__ __forceinline__ uint4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Zero the elements at positions >= keep (keep in any range) of 8 packed bf16.
+__device__ __forceinline__ uint4 keep_first(uint4 v, int keep) {
+  if (keep >= 8) return v;
+  if (keep <= 0) return make_uint4(0, 0, 0, 0);
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int lo = 2 * i, hi = 2 * i + 1;
+    uint32_t m = (lo < keep ? 0x0000ffffu : 0u) | (hi < keep ? 0xffff0000u : 0u);
+    w[i] &= m;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D (16x16, f32) += A (16x32) * B (32x16), bf16 inputs.  Lane l supplies row
+// (l % 16) of A and column (l % 16) of B, each with the 8 consecutive k of
+// group (l / 16); it receives D rows 4*(l/16) .. 4*(l/16)+3 of column l % 16.
+__device__ __forceinline__ f32x4 mfma16x16x32(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Blocks are handed to the XCDs round-robin (block b runs on XCD b % 8).
+// Return a logical index such that each XCD receives one contiguous range of
+// logical indices, so neighbouring work items (which share weight tiles)
+// meet in the same L2.  A bijection on [0, G).
+__device__ __forceinline__ int xcd_contiguous(int b, int G) {
+  int q = G / kXcds, r = G % kXcds;
+  int x = b % kXcds, l = b / kXcds;
+  return x < r ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
+}
+
+}  // namespace sgg

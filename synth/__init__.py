@@ -12,6 +12,7 @@ from .workloads import (  # noqa: F401
     Projection,
     draw_batch,
     draw_embedding,
+    draw_ids,
     draw_projection,
     to_f64,
 )

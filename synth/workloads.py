@@ -239,15 +239,20 @@ def draw_projection(batch: Batch, proj: Projection, layer=0, proj_index=None,
     return out
 
 
+def draw_ids(batch: Batch, vocab_size=None):
+    """Token ids (s,) int64 uniform over the vocabulary."""
+    V = vocab_size or batch.vocab_size or 128256
+    g = np.random.default_rng([batch.seed, 0, 0, KIND_IDS])
+    return torch.from_numpy(g.integers(0, V, size=batch.num_tokens).astype(np.int64))
+
+
 def draw_embedding(batch: Batch, vocab_size=None, emb_rank=None):
     """Token ids (s,) int64 uniform over the vocabulary and A_emb (L, R_e, V)."""
     V = vocab_size or batch.vocab_size or 128256
     Re = emb_rank or batch.emb_rank or 16
-    g = np.random.default_rng([batch.seed, 0, 0, KIND_IDS])
-    ids = torch.from_numpy(g.integers(0, V, size=batch.num_tokens).astype(np.int64))
     A_emb = _weights([batch.seed, 0, 0, KIND_EMB], batch.num_loras, Re, V, 0.02,
                      batch.lora_ranks, Re, False, True)
-    return ids, A_emb
+    return draw_ids(batch, V), A_emb
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:

@@ -1,0 +1,285 @@
+"""CPU tests of the C-ABI library: it loads, exports what the header declares,
+plans bit-exactly like the oracle, and rejects bad arguments on the host
+before anything reaches a GPU (no compute call here needs a device)."""
+
+import ctypes
+import itertools
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgg_lora.h")
+LIBPATH = os.path.join(ROOT, "segmented_gather_gemm_amd", "libsgg_lora.so")
+
+
+def _ensure_built():
+    if not os.path.exists(LIBPATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+
+_ensure_built()
+
+import segmented_gather_gemm_amd as sgg  # noqa: E402
+from segmented_gather_gemm_amd import _lib  # noqa: E402
+from oracle import plan as op  # noqa: E402
+from synth import CONFIGS, draw_batch  # noqa: E402
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert {"lora_plan_segments", "lora_shrink", "lora_expand", "lora_qkv",
+            "lora_a_embedding", "lora_last_error"} <= set(names)
+    handle = ctypes.CDLL(LIBPATH)
+    for name in names:
+        assert hasattr(handle, name), name
+    # the binding declares every exported entry point, with the same names
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+# ------------------------------------------------------------ planner parity
+
+def _native(lens, slots, max_loras, is_decode, cap_chunk, override=0, capacity=None):
+    return sgg.lora_plan_segments(lens, slots, max_loras, is_decode, cap_chunk, override,
+                                  seg_capacity=capacity)
+
+
+def _compare(lens, slots, max_loras, is_decode, cap_chunk, override=0, capacity=None):
+    nat = _native(lens, slots, max_loras, is_decode, cap_chunk, override, capacity)
+    cap = nat["capacity"]
+    ref = op.plan(lens, slots, is_decode, cap_chunk, override, capacity=cap)
+    s = ref["num_tokens"]
+    assert nat["num_tokens"] == s
+    assert nat["chunk_size"] == ref["chunk_size"]
+    assert nat["num_segments"] == ref["num_segments"]
+    assert list(nat["permutation"][:s]) == ref["permutation"]
+    assert list(nat["seg_indptr"][:cap + 1]) == ref["seg_indptr"]
+    assert list(nat["seg_slots"][:cap]) == ref["seg_slots"]
+    assert list(nat["req_seg_indptr"]) == ref["req_seg_indptr"]
+    return nat
+
+
+def test_plan_page_examples():
+    nat = _compare([2, 1, 3], [0, 1, 0], 2, False, 128, override=3)
+    assert list(nat["permutation"]) == [0, 1, 3, 4, 5, 2]
+    assert nat["num_segments"] == 3
+    assert list(nat["seg_indptr"][:4]) == [0, 3, 5, 6]
+    assert list(nat["seg_slots"][:3]) == [0, 0, 1]
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+def test_plan_workloads(name):
+    b = draw_batch(name)
+    caps = [16, 32, 64, 128] if name == "prefill" else [b.max_chunk_size]
+    for cap in caps:
+        _compare(None if b.is_decode else b.seq_lens, b.req_slots, b.num_loras, b.is_decode, cap)
+
+
+def test_plan_exhaustive_tiny():
+    for bs in range(0, 4):
+        for lens in itertools.product(range(4), repeat=bs):
+            for slots in itertools.product(range(3), repeat=bs):
+                for override in (1, 2, 3, 0):
+                    _compare(list(lens), list(slots), 3, False, 128, override)
+
+
+def test_plan_random_fuzz():
+    rng = random.Random(3)
+    for _ in range(300):
+        bs = rng.randint(0, 60)
+        L = rng.randint(1, 12)
+        lens = [rng.choice([0, 1, 1, 3, 16, 17, 100, 300]) for _ in range(bs)]
+        slots = [rng.randrange(L) for _ in range(bs)]
+        cap_chunk = rng.choice([1, 8, 16, 17, 32, 48, 64, 128, 256])
+        override = rng.choice([0, 0, 0, 1, 5, 16])
+        _compare(lens, slots, L, False, cap_chunk, override)
+
+
+def test_plan_decode_and_padding():
+    slots = [3, 1, 3, 0, 2] * 20
+    _compare(None, slots, 4, True, 128)
+    nat = _compare([3, 5, 1, 7], [0, 1, 0, 1], 2, False, 16, capacity=6)
+    assert list(nat["seg_slots"]) == [0, 1, 0, 0, 0, 0]
+    assert list(nat["seg_indptr"]) == [0, 4, 16, 16, 16, 16, 16]
+    nat = _compare([], [], 4, False, 128)
+    assert nat["num_segments"] == 0 and nat["num_tokens"] == 0
+
+
+def test_plan_errors():
+    with pytest.raises(sgg.SggError) as e:
+        _native([1, 2], [0, 5], 4, False, 128)
+    assert e.value.code == -3 and "req_slots[1]=5" in str(e.value)
+    with pytest.raises(sgg.SggError) as e:
+        _native([1, -2], [0, 1], 4, False, 128)
+    assert e.value.code == -1
+    with pytest.raises(sgg.SggError) as e:
+        _native([1, 2], [0, 1], 4, True, 128)
+    assert e.value.code == -1 and "decode" in str(e.value)
+    with pytest.raises(sgg.SggError) as e:
+        _native([40, 40], [0, 1], 4, False, 128, override=16, capacity=3)
+    assert e.value.code == -3
+
+
+def test_plan_segment_bound_holds():
+    rng = random.Random(5)
+    for _ in range(200):
+        bs = rng.randint(1, 50)
+        L = rng.randint(1, 20)
+        lens = [rng.randint(0, 200) for _ in range(bs)]
+        slots = [rng.randrange(L) for _ in range(bs)]
+        ref = op.plan(lens, slots, False, rng.choice([16, 32, 128]))
+        assert ref["num_segments"] <= sgg.lora_plan_max_segments(sum(lens), L, 16)
+
+
+# ------------------------------------------------------ argument validation
+
+L = _lib.lib()
+FAKE = ctypes.c_void_p(0x10000)      # 16-byte aligned, never dereferenced on the host
+NULL = ctypes.c_void_p(0)
+
+
+def _shrink(**kw):
+    a = dict(x=FAKE, ldx=256, A=FAKE, h=FAKE, ldh=8, s=16, K=256, L=2, c=1, R=8,
+             indptr=FAKE, slots=FAKE, nseg=2, perm=FAKE, ranks=FAKE, chunk=16,
+             ws=NULL, wsb=0)
+    a.update(kw)
+    return L.lora_shrink(a["x"], a["ldx"], a["A"], a["h"], a["ldh"], a["s"], a["K"], a["L"],
+                         a["c"], a["R"], a["indptr"], a["slots"], a["nseg"], a["perm"],
+                         a["ranks"], a["chunk"], a["ws"], a["wsb"], NULL)
+
+
+def _expand(offs=(0, 256), **kw):
+    arr = (ctypes.c_int32 * len(offs))(*offs)
+    a = dict(h=FAKE, ldh=8, B=FAKE, N=256, out=FAKE, ldo=256, s=16, L=2, R=8, c=len(offs) - 1,
+             maxs=256, indptr=FAKE, slots=FAKE, nseg=2, perm=FAKE, ranks=FAKE, scal=FAKE,
+             chunk=16)
+    a.update(kw)
+    return L.lora_expand(a["h"], a["ldh"], a["B"], a["N"], a["out"], a["ldo"], a["s"], a["L"],
+                         a["R"], arr, a["c"], a["maxs"], a["indptr"], a["slots"], a["nseg"],
+                         a["perm"], a["ranks"], a["scal"], a["chunk"], NULL)
+
+
+def _err():
+    return L.lora_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(x=NULL), -1, "NULL"),
+    (dict(K=0), -1, "in_dim"),
+    (dict(c=0), -1, "num_slices"),
+    (dict(c=9, ldh=72), -1, "num_slices"),
+    (dict(ldx=128), -1, "ldx"),
+    (dict(ldh=4), -1, "ldh"),
+    (dict(K=252, ldx=252), -2, "multiples of 8"),
+    (dict(R=12, ldh=12), -2, "multiples of 8"),
+    (dict(x=ctypes.c_void_p(0x10008)), -2, "aligned"),
+    (dict(indptr=NULL), -1, "plan array"),
+    (dict(nseg=-1), -1, "num_segments"),
+    (dict(L=0), -1, "num_loras"),
+    (dict(chunk=0), -1, "chunk_size"),
+    (dict(s=-1), -1, "s="),
+    (dict(s=256, K=4096, ldx=4096, c=3, R=16, ldh=48, nseg=8, chunk=128), -3, "workspace"),
+])
+def test_shrink_rejects(kw, code, text):
+    assert _shrink(**kw) == code
+    assert text in _err()
+
+
+def test_shrink_empty_is_noop():
+    assert _shrink(s=0) == 0
+    assert _shrink(nseg=0) == 0
+
+
+@pytest.mark.parametrize("offs,kw,code,text", [
+    ((0, 256), dict(out=NULL), -1, "base_output is NULL"),
+    ((1, 256), {}, -1, "slice_offsets[0]"),
+    ((0, 200, 100), {}, -1, "non-decreasing"),
+    ((0, 256), dict(maxs=255), -1, "max_slice_size"),
+    ((0, 256), dict(N=255), -1, "rows"),
+    ((0, 256), dict(ldo=255), -1, "ldo"),
+    ((0, 128, 256), dict(ldh=8), -1, "ldh"),
+    ((0, 256), dict(R=136, ldh=136), -2, "above 128"),
+    ((0, 256), dict(B=ctypes.c_void_p(0x10002)), -2, "aligned"),
+    ((0, 256), dict(out=ctypes.c_void_p(0x10001)), -2, "aligned"),
+    ((0, 256), dict(scal=NULL), -1, "NULL"),
+    ((0,) * 10, dict(c=9, maxs=0), -1, "num_slices"),
+])
+def test_expand_rejects(offs, kw, code, text):
+    assert _expand(offs, **kw) == code
+    assert text in _err()
+
+
+def test_expand_empty_is_noop():
+    assert _expand(s=0) == 0
+    assert _expand((0, 0)) == 0
+
+
+def test_embedding_rejects():
+    def emb(extra=0, **kw):
+        a = dict(ids=FAKE, A=FAKE, V=1000, out=FAKE, ldo=16, s=4, L=2, R=16, vocab=1000,
+                 indptr=FAKE, slots=FAKE, nseg=1, perm=FAKE, ranks=FAKE)
+        a.update(kw)
+        return L.lora_a_embedding(a["ids"], a["A"], a["V"], a["out"], a["ldo"], a["s"], a["L"],
+                                  a["R"], a["vocab"], a["indptr"], a["slots"], a["nseg"],
+                                  a["perm"], a["ranks"], extra, NULL)
+    assert emb(extra=1) == -2 and "extra" in _err()
+    assert emb(vocab=1001) == -1 and "vocab_size" in _err()
+    assert emb(ldo=8) == -1 and "ldo" in _err()
+    assert emb(ids=NULL) == -1
+    assert emb(s=0) == 0
+
+
+def test_qkv_rejects():
+    offs = (ctypes.c_int32 * 4)(0, 4096, 5120, 6144)
+    args = [FAKE, 4096, FAKE, FAKE, 6144, FAKE, 6144, 256, 4096, 8, 16, offs, 3, 4096,
+            FAKE, FAKE, 8, FAKE, FAKE, FAKE, 128]
+    assert L.lora_qkv(*args, NULL, 0, NULL) == -1 and "workspace" in _err()
+    need = L.lora_qkv_workspace_bytes(256, 4096, 3, 16, 8, 128)
+    assert need > 256 * 48 * 2
+    assert L.lora_qkv(*args, FAKE, need - 1, NULL) == -3 and "workspace" in _err()
+
+
+def test_workspace_sizes():
+    # decode shapes split K across workgroups and need scratch; prefill shapes do not
+    assert L.lora_shrink_workspace_bytes(256, 4096, 3, 16, 8, 128) > 0
+    assert L.lora_shrink_workspace_bytes(33792, 4096, 2, 64, 300, 128) == 0
+    assert L.lora_shrink_workspace_bytes(0, 4096, 3, 16, 8, 128) == 0
+
+
+def test_error_is_thread_local():
+    import threading
+    assert _shrink(K=0) == -1
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(_err()))
+    t.start()
+    t.join()
+    assert seen == [""]
+    assert "in_dim" in _err()
+
+
+def test_library_never_imports_oracle():
+    imp_oracle = re.compile(r"^\s*(from|import)\s+oracle\b", re.M)
+    imp_lib = re.compile(r"^\s*(from|import)\s+(segmented_gather_gemm_amd|synth)\b", re.M)
+    pkg = os.path.join(ROOT, "segmented_gather_gemm_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith(".py"):
+                assert not imp_oracle.search(open(os.path.join(dirpath, f)).read()), f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith(".py"):
+            assert not imp_lib.search(open(os.path.join(ROOT, "oracle", f)).read()), f
+
+
+def test_np_dtypes_roundtrip():
+    nat = _native(np.array([2, 3], np.int64), np.array([1, 0], np.int64), 2, False, 16)
+    assert list(nat["permutation"][:5]) == [2, 3, 4, 0, 1]

