@@ -131,6 +131,8 @@ class ChunkedSgmvLoRA:
             return dev[o:o + (size if n is None else n)]
 
         n_seg = plan["num_segments"]
+        indptr = view("seg_indptr")[:n_seg + 1].numpy()
+        longest = int((indptr[1:] - indptr[:-1]).max()) if n_seg > 0 else 0
         info = LoRABatchInfo(
             bs=bs, num_tokens=s,
             num_segments=cap if use_cuda_graph else n_seg,
@@ -139,7 +141,8 @@ class ChunkedSgmvLoRA:
             permutation=dview("permutation", s), lora_ranks=dview("ranks"),
             scalings=dview("scalings").view(torch.float32),
             req_seg_indptr=dview("req_seg_indptr", bs + 1),
-            req_weight_indices=dview("req_slots", bs), use_cuda_graph=use_cuda_graph)
+            req_weight_indices=dview("req_slots", bs), use_cuda_graph=use_cuda_graph,
+            max_seg_len=0 if use_cuda_graph else longest)
         info.planned_segments = n_seg
         self.batch_info = info
         return info

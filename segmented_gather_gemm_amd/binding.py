@@ -38,6 +38,12 @@ class LoRABatchInfo:
     req_seg_indptr: Optional[torch.Tensor] = None
     req_weight_indices: Optional[torch.Tensor] = None
     use_cuda_graph: bool = False
+    max_seg_len: int = 0          # longest planned segment (0: unknown, use max_len)
+
+    @property
+    def tile_hint(self):
+        """Upper bound on segment length handed to the kernels for tiling."""
+        return self.max_seg_len if self.max_seg_len > 0 else self.max_len
 
 
 def _vp(t):
@@ -179,12 +185,12 @@ def lora_shrink(x, weights, batch_info: LoRABatchInfo, num_slices=1, out=None, w
         out = torch.empty((s, CR), dtype=torch.bfloat16, device=x.device)
     _need_bf16("out", out, 2)
     need = int(lib().lora_shrink_workspace_bytes(s, K, num_slices, R, batch_info.num_segments,
-                                                 batch_info.max_len))
+                                                 batch_info.tile_hint))
     ws = workspace if workspace is not None or need == 0 else default_workspace(x.device, need)
     check(lib().lora_shrink(
         _vp(x), x.stride(0), _vp(weights), _vp(out), out.stride(0), s, K, L, num_slices, R,
         _vp(batch_info.seg_indptr), _vp(batch_info.weight_indices), batch_info.num_segments,
-        _vp(batch_info.permutation), _vp(batch_info.lora_ranks), batch_info.max_len,
+        _vp(batch_info.permutation), _vp(batch_info.lora_ranks), batch_info.tile_hint,
         _vp(ws), ws.numel() if ws is not None else 0, _stream(x.device)))
     return out
 
@@ -213,7 +219,7 @@ def lora_expand(h, weights, batch_info: LoRABatchInfo, slice_offsets, max_slice_
         _vp(h), h.stride(0), _vp(weights), N, _vp(base_output), base_output.stride(0), s, L, R,
         p_offs, c, int(max_slice_size), _vp(batch_info.seg_indptr),
         _vp(batch_info.weight_indices), batch_info.num_segments, _vp(batch_info.permutation),
-        _vp(batch_info.lora_ranks), _vp(batch_info.scalings), batch_info.max_len,
+        _vp(batch_info.lora_ranks), _vp(batch_info.scalings), batch_info.tile_hint,
         _stream(h.device)))
     return base_output
 
@@ -239,13 +245,13 @@ def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
         base_output = torch.zeros((s, int(offs[-1])), dtype=torch.bfloat16, device=x.device)
     _need_bf16("base_output", base_output, 2)
     need = int(lib().lora_qkv_workspace_bytes(s, K, c, R, batch_info.num_segments,
-                                              batch_info.max_len))
+                                              batch_info.tile_hint))
     ws = workspace if workspace is not None else default_workspace(x.device, max(need, 1))
     check(lib().lora_qkv(
         _vp(x), x.stride(0), _vp(A), _vp(B), N, _vp(base_output), base_output.stride(0), s, K,
         L, R, p_offs, c, int(max_slice_size), _vp(batch_info.seg_indptr),
         _vp(batch_info.weight_indices), batch_info.num_segments, _vp(batch_info.permutation),
-        _vp(batch_info.lora_ranks), _vp(batch_info.scalings), batch_info.max_len, _vp(ws),
+        _vp(batch_info.lora_ranks), _vp(batch_info.scalings), batch_info.tile_hint, _vp(ws),
         ws.numel(), _stream(x.device)))
     return base_output
 

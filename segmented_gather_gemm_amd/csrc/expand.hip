@@ -2,13 +2,21 @@
 // h[t, k*R + j] over the segments of a chunked plan (chunked_backend.py page:
 // run_lora_b_sgemm and the expand step of run_qkv_lora / run_gate_up_lora).
 //
-// One workgroup (4 waves) owns one segment and one tile of 64*NFW columns of
-// one slice.  Each wave loads the B fragments of its 16*NFW columns into
-// registers once (the rank is the short contraction dimension) and then walks
-// the segment 16 tokens at a time: one 16-byte h fragment per lane, KS MFMAs
-// per 16 columns, and a read-modify-write of the base rows.  The MFMA is set
-// up as out^T = B * h^T so that each lane ends with 4 consecutive columns of
-// one token: the base update is an 8-byte access per lane.
+// One workgroup (4 waves) owns one segment and one tile of 128*P columns of
+// one slice; each wave owns 32*P of those columns and keeps their B rows in
+// registers as MFMA fragments (the rank is the short contraction dimension).
+// The segment is walked 128 tokens at a time: the h rows of those tokens
+// (slice k's R columns) are fetched once per workgroup, coalesced, into a
+// swizzled LDS tile that all waves read their fragments from.  Then, 16
+// tokens at a time, each wave computes out^T = B * h^T on the MFMA and
+// transposes the accumulators through a padded LDS tile so that the base
+// rows are read and written coalesced: 4*P lanes cover the 64*P contiguous
+// bytes of one row.  The base rows of the next 16 tokens are in flight while
+// the current ones are computed and stored.
+//
+// Work order: each XCD takes a contiguous range of (segment, tile) items with
+// tiles fastest, so the workgroups resident on an XCD sweep whole rows of the
+// base tensor and share the segment's h rows and its adapter's B tiles in L2.
 #include "sgg_device.h"
 #include "sgg_kernels.h"
 
@@ -16,107 +24,169 @@ namespace sgg {
 
 namespace {
 
-template <int NFW, int KS>
+template <int P, int KS>
 __global__ __launch_bounds__(256) void expand_kernel(ExpandParams p) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  constexpr int TNW = 32 * P;                  // columns per wave
+  constexpr int CPR = 4 * KS;                  // 16-byte chunks per LDS h row (R <= 32*KS)
+  constexpr int RPS = 16 / CPR > 0 ? 16 / CPR : 1;  // h rows sharing one swizzle value
+  constexpr int LPR = 4 * P;                   // lanes per base row segment (16 B each)
+  constexpr int RPL = 64 / LPR;                // base rows per wave load
+  constexpr int BLD = 16 / RPL;                // base loads per 16 tokens
+  constexpr int APAD = TNW + 4;                // floats per row of the transpose tile
+  __shared__ uint4 htile[128 * CPR];
+  __shared__ int prow[128];
+  __shared__ __attribute__((aligned(16))) float acct[4][16 * APAD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int L = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int seg = L % p.num_segments;
-  const int tile = L / p.num_segments;
+  const int seg = L / p.total_tiles;
+  const int tile = L % p.total_tiles;
 
   int k = 0;
   while (k + 1 < p.c && tile >= p.tile_start[k + 1]) ++k;
-  const int col0 = p.offs[k] + (tile - p.tile_start[k]) * (64 * NFW) + 16 * NFW * wave;
+  const int colt = p.offs[k] + (tile - p.tile_start[k]) * (128 * P);
+  const int colw = colt + TNW * wave;
   const int colend = p.offs[k + 1];
-  if (col0 >= colend) return;
 
   // segment bounds, clamped to [0, s) so a malformed plan stays in bounds
   const int lo = max(p.seg_indptr[seg], 0);
   const int hi = min(static_cast<int64_t>(p.seg_indptr[seg + 1]), p.s);
-  if (hi <= lo) return;
+  if (hi <= lo || colt >= colend) return;
   const int slot = p.seg_slots[seg];
   int rho = (slot >= 0 && slot < p.L) ? p.ranks[slot] : 0;
   rho = rho < 0 ? 0 : (rho > p.R ? p.R : rho);
   if (rho == 0) return;  // base model: output rows stay untouched
   const float sigma = p.scalings[slot];
-  const int j8 = 8 * (lane >> 4);
+  const bool active = colw < colend;  // wave has columns (uniform); keeps joining barriers
+  const int m = lane & 15;
+  const int q = lane >> 4;
 
-  // B fragments: rows n of slice k, rank columns j8 + 32*ks .. +7.
-  uint4 bw[NFW][KS];
+  // B fragments: fragment g row m is column colw + 16*g + m; rank chunk 8q + 32ks.
+  uint4 bw[2 * P][KS];
 #pragma unroll
-  for (int g = 0; g < NFW; ++g) {
-    const int n = col0 + 16 * g + (lane & 15);
-    const uint16_t* brow = p.B + (static_cast<int64_t>(slot) * p.N + n) * p.R;
+  for (int g = 0; g < 2 * P; ++g) {
+    const int n = colw + 16 * g + m;
+    const uint16_t* brow = p.B + (static_cast<int64_t>(slot) * p.N + (n < colend ? n : 0)) * p.R;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int j = 32 * ks + j8;
+      const int j = 32 * ks + 8 * q;
       bw[g][ks] = make_uint4(0, 0, 0, 0);
-      if (n < colend && j < rho) bw[g][ks] = keep_first(load16(brow + j), rho - j);
+      if (active && n < colend && j < rho) bw[g][ks] = keep_first(load16(brow + j), rho - j);
     }
   }
 
-  const int hcol = k * p.R;
-  for (int m0 = lo; m0 < hi; m0 += 16) {
-    const int tok = m0 + (lane & 15);
-    int row = -1;
-    if (tok < hi) {
-      const int r = p.perm[tok];
-      if (r >= 0 && r < p.s) row = r;
+  // Base-row role of this lane: row (RPL*i + lane/LPR) of a 16-token group,
+  // columns colw + 8*(lane%LPR) .. +7.
+  const int brw = lane / LPR;
+  const int bc = colw + 8 * (lane % LPR);
+  const bool bvec = p.vec8 && bc + 8 <= colend;
+  const int hch = p.R >> 3;  // 16-byte chunks of one h row slice
+  float* at = acct[wave];
+
+  for (int c0 = lo; c0 < hi; c0 += 128) {
+    const int ntok = hi - c0 < 128 ? hi - c0 : 128;
+    __syncthreads();  // previous chunk's tiles are no longer read
+    if (tid < ntok) {
+      const int r = p.perm[c0 + tid];
+      prow[tid] = (r >= 0 && r < p.s) ? r : -1;
     }
-    uint4 hv[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int j = 32 * ks + j8;
-      hv[ks] = make_uint4(0, 0, 0, 0);
-      if (row >= 0 && j < rho)
-        hv[ks] = keep_first(load16(p.h + static_cast<int64_t>(row) * p.ldh + hcol + j), rho - j);
+    for (int piece = tid; piece < ntok * hch; piece += 256) {
+      const int row = piece / hch, c = piece % hch;
+      const int r = p.perm[c0 + row];
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r >= 0 && r < p.s) v = load16(p.h + static_cast<int64_t>(r) * p.ldh + k * p.R + 8 * c);
+      htile[row * CPR + (c ^ ((row / RPS) % CPR))] = v;
     }
-    uint16_t* orow = p.out + static_cast<int64_t>(row < 0 ? 0 : row) * p.ldo;
-    // Base values first, so their latency overlaps the MFMAs.
-    uint2 bv[NFW];
+    __syncthreads();
+    if (!active) continue;
+
+    const int nf = (ntok + 15) >> 4;
+    uint4 bv0[BLD], bv1[BLD];
+    auto fetch = [&](int f, uint4 (&bv)[BLD]) {
 #pragma unroll
-    for (int g = 0; g < NFW; ++g) {
-      const int c4 = col0 + 16 * g + 4 * (lane >> 4);
-      bv[g] = make_uint2(0, 0);
-      if (row >= 0 && p.vec4 && c4 + 4 <= colend)
-        bv[g] = *reinterpret_cast<const uint2*>(orow + c4);
-    }
+      for (int i = 0; i < BLD; ++i) {
+        const int rr = 16 * f + RPL * i + brw;
+        const int r = rr < ntok ? prow[rr] : -1;
+        bv[i] = make_uint4(0, 0, 0, 0);
+        if (r >= 0 && bvec)
+          bv[i] = *reinterpret_cast<const uint4*>(p.out + static_cast<int64_t>(r) * p.ldo + bc);
+      }
+    };
+    auto step = [&](int f, const uint4 (&bv)[BLD]) {
+      // h fragment: row 16f + m, rank chunk 8q + 32ks
+      const int hr = 16 * f + m;
+      const bool hv_ok = hr < ntok && prow[hr] >= 0;
+      uint4 hv[KS];
 #pragma unroll
-    for (int g = 0; g < NFW; ++g) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < KS; ++ks) {
+        const int j = 32 * ks + 8 * q;
+        const int c = 4 * ks + q;
+        hv[ks] = make_uint4(0, 0, 0, 0);
+        if (hv_ok && j < rho) hv[ks] = keep_first(htile[hr * CPR + (c ^ ((hr / RPS) % CPR))], rho - j);
+      }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(bw[g][ks], hv[ks], acc);
-      const int c4 = col0 + 16 * g + 4 * (lane >> 4);
-      if (row < 0 || c4 >= colend) continue;
-      if (p.vec4 && c4 + 4 <= colend) {
-        const float y0 = bf16_to_f32(bv[g].x & 0xffffu) + sigma * acc[0];
-        const float y1 = bf16_to_f32(bv[g].x >> 16) + sigma * acc[1];
-        const float y2 = bf16_to_f32(bv[g].y & 0xffffu) + sigma * acc[2];
-        const float y3 = bf16_to_f32(bv[g].y >> 16) + sigma * acc[3];
-        uint2 o;
-        o.x = f32_to_bf16(y0) | (f32_to_bf16(y1) << 16);
-        o.y = f32_to_bf16(y2) | (f32_to_bf16(y3) << 16);
-        *reinterpret_cast<uint2*>(orow + c4) = o;
-      } else {
+      for (int g = 0; g < 2 * P; ++g) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (c4 + i < colend) {
-            const float y = bf16_to_f32(orow[c4 + i]) + sigma * acc[i];
-            orow[c4 + i] = static_cast<uint16_t>(f32_to_bf16(y));
+        for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(bw[g][ks], hv[ks], acc);
+        *reinterpret_cast<f32x4*>(at + m * APAD + 16 * g + 4 * q) = acc;
+      }
+      // transposed read: 8 consecutive columns of one token per lane
+#pragma unroll
+      for (int i = 0; i < BLD; ++i) {
+        const int rl = RPL * i + brw;
+        const int rr = 16 * f + rl;
+        const int r = rr < ntok ? prow[rr] : -1;
+        if (r < 0 || bc >= colend) continue;
+        const float* src = at + rl * APAD + 8 * (lane % LPR);
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(src + 4);
+        uint16_t* dst = p.out + static_cast<int64_t>(r) * p.ldo + bc;
+        if (bvec) {
+          const uint4 b = bv[i];
+          uint4 o;
+          o.x = f32_to_bf16(bf16_to_f32(b.x & 0xffffu) + sigma * a0[0]) |
+                (f32_to_bf16(bf16_to_f32(b.x >> 16) + sigma * a0[1]) << 16);
+          o.y = f32_to_bf16(bf16_to_f32(b.y & 0xffffu) + sigma * a0[2]) |
+                (f32_to_bf16(bf16_to_f32(b.y >> 16) + sigma * a0[3]) << 16);
+          o.z = f32_to_bf16(bf16_to_f32(b.z & 0xffffu) + sigma * a1[0]) |
+                (f32_to_bf16(bf16_to_f32(b.z >> 16) + sigma * a1[1]) << 16);
+          o.w = f32_to_bf16(bf16_to_f32(b.w & 0xffffu) + sigma * a1[2]) |
+                (f32_to_bf16(bf16_to_f32(b.w >> 16) + sigma * a1[3]) << 16);
+          *reinterpret_cast<uint4*>(dst) = o;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (bc + e < colend) {
+              const float v = e < 4 ? a0[e & 3] : a1[e & 3];
+              const float y = bf16_to_f32(dst[e]) + sigma * v;
+              dst[e] = static_cast<uint16_t>(f32_to_bf16(y));
+            }
           }
         }
+      }
+    };
+    fetch(0, bv0);
+    for (int f = 0; f < nf; f += 2) {
+      if (f + 1 < nf) fetch(f + 1, bv1);
+      step(f, bv0);
+      if (f + 1 < nf) {
+        if (f + 2 < nf) fetch(f + 2, bv0);
+        step(f + 1, bv1);
       }
     }
   }
 }
 
-template <int NFW>
-hipError_t launch_w(const ExpandParams& p, int ks, int64_t grid, hipStream_t stream) {
+template <int P>
+hipError_t launch_p(const ExpandParams& p, int ks, int64_t grid, hipStream_t stream) {
   const dim3 g(static_cast<unsigned>(grid)), b(256);
   switch (ks) {
-    case 1: hipLaunchKernelGGL((expand_kernel<NFW, 1>), g, b, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((expand_kernel<NFW, 2>), g, b, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((expand_kernel<NFW, 4>), g, b, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((expand_kernel<P, 1>), g, b, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((expand_kernel<P, 2>), g, b, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((expand_kernel<P, 4>), g, b, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -126,10 +196,10 @@ hipError_t launch_w(const ExpandParams& p, int ks, int64_t grid, hipStream_t str
 
 hipError_t launch_expand(const ExpandParams& p, const ExpandTiling& t, hipStream_t stream) {
   if (t.grid <= 0) return hipSuccess;
-  switch (t.nfw) {
-    case 1: return launch_w<1>(p, t.ks, t.grid, stream);
-    case 2: return launch_w<2>(p, t.ks, t.grid, stream);
-    case 4: return launch_w<4>(p, t.ks, t.grid, stream);
+  switch (t.pairs) {
+    case 1: return launch_p<1>(p, t.ks, t.grid, stream);
+    case 2: return launch_p<2>(p, t.ks, t.grid, stream);
+    case 4: return launch_p<4>(p, t.ks, t.grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

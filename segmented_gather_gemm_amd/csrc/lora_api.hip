@@ -22,8 +22,10 @@ int check_plan(int64_t s, int32_t num_segments, const int32_t* seg_indptr,
   SGG_CHECK(num_segments >= 0, SGG_ERR_INVALID, "num_segments=%d is negative", num_segments);
   SGG_CHECK(num_loras > 0, SGG_ERR_INVALID, "num_loras=%d must be positive", num_loras);
   SGG_CHECK(chunk_size > 0, SGG_ERR_INVALID, "chunk_size=%d must be positive", chunk_size);
-  SGG_CHECK(seg_indptr && seg_slots && permutation && lora_ranks, SGG_ERR_INVALID,
-            "a plan array (seg_indptr, seg_slots, permutation, lora_ranks) is NULL");
+  // an empty plan (no tokens or no segments) may come with NULL arrays
+  SGG_CHECK((seg_indptr && seg_slots && lora_ranks) || num_segments == 0, SGG_ERR_INVALID,
+            "a plan array (seg_indptr, seg_slots, lora_ranks) is NULL");
+  SGG_CHECK(permutation || s == 0, SGG_ERR_INVALID, "permutation is NULL");
   return SGG_OK;
 }
 
@@ -81,23 +83,27 @@ int check_expand(const void* h, int64_t ldh, const void* B, int64_t N, const voi
   return SGG_OK;
 }
 
+// Columns per workgroup: 128 * pairs; 256 when that still gives at least four
+// workgroups per CU, else 128 (measured: 512 is slower for prefill shapes).
+// Rank steps of 32.
 sgg::ExpandTiling choose_expand_tiling(const int32_t* offs, int c, int num_segments, int R,
                                        int32_t* tile_start, int32_t* total) {
   sgg::ExpandTiling t{};
   t.ks = R <= 32 ? 1 : (R <= 64 ? 2 : 4);
-  t.nfw = 1;
-  for (int nfw : {4, 2, 1}) {
+  t.pairs = 1;
+  for (int pairs : {2}) {
     int64_t tiles = 0;
-    for (int k = 0; k < c; ++k) tiles += (offs[k + 1] - offs[k] + 64 * nfw - 1) / (64 * nfw);
-    if (nfw == 1 || tiles * num_segments >= 512) {
-      t.nfw = nfw;
+    for (int k = 0; k < c; ++k) tiles += (offs[k + 1] - offs[k] + 128 * pairs - 1) / (128 * pairs);
+    if (tiles * num_segments >= 1024) {
+      t.pairs = pairs;
       break;
     }
   }
+  const int tn = 128 * t.pairs;
   int32_t acc = 0;
   for (int k = 0; k < c; ++k) {
     tile_start[k] = acc;
-    acc += (offs[k + 1] - offs[k] + 64 * t.nfw - 1) / (64 * t.nfw);
+    acc += (offs[k + 1] - offs[k] + tn - 1) / tn;
   }
   tile_start[c] = acc;
   *total = acc;
@@ -158,10 +164,10 @@ int do_expand(const void* h, int64_t ldh, const void* B, int64_t N, void* out, i
   const sgg::ExpandTiling t =
       choose_expand_tiling(offs, c, num_segments, R, p.tile_start, &p.total_tiles);
   SGG_CHECK(t.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "expand grid too large");
-  bool vec4 = (reinterpret_cast<uintptr_t>(out) & 7u) == 0 && ldo % 4 == 0;
+  bool vec8 = sgg::aligned16(out) && ldo % 8 == 0;
   for (int k = 0; k <= c; ++k) {
     p.offs[k] = offs[k];
-    vec4 = vec4 && offs[k] % 4 == 0;
+    vec8 = vec8 && offs[k] % 8 == 0;
   }
   p.h = static_cast<const uint16_t*>(h);
   p.B = static_cast<const uint16_t*>(B);
@@ -179,7 +185,7 @@ int do_expand(const void* h, int64_t ldh, const void* B, int64_t N, void* out, i
   p.R = R;
   p.c = c;
   p.num_segments = num_segments;
-  p.vec4 = vec4 ? 1 : 0;
+  p.vec8 = vec8 ? 1 : 0;
   return launch_status(sgg::launch_expand(p, t, stream), "expand");
 }
 

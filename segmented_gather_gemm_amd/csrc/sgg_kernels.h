@@ -44,7 +44,7 @@ struct ExpandParams {
   const float* scalings;
   int64_t ldh, ldo, s, N;
   int32_t L, R, c, num_segments;
-  int32_t vec4;               // 8-byte base access is aligned for every group of 4 columns
+  int32_t vec8;               // 16-byte base access is aligned for every group of 8 columns
   int32_t offs[kMaxSlices + 1];
   int32_t tile_start[kMaxSlices + 1];  // first column tile of each slice
   int32_t total_tiles;
@@ -74,7 +74,7 @@ struct ShrinkTiling {
 ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk);
 
 struct ExpandTiling {
-  int nfw, ks;       // 64-column groups per wave, 32-deep rank steps
+  int pairs, ks;     // 32-column fragment pairs per wave, 32-deep rank steps
   int64_t grid;
 };
 

@@ -4,12 +4,21 @@
 //
 // One workgroup (4 waves) owns a tile of up to 16*MF tokens of one segment
 // (gathered through the permutation) by 16*NF outputs of the c*R stacked
-// rank rows, over one range of K.  The four waves walk interleaved 32-deep
-// K steps of that range, each keeping the whole tile in its own MFMA
-// accumulators, so no operand is loaded twice and the main loop needs no
+// rank rows, over one range of K.  The four waves take interleaved 64-deep K
+// chunks of that range, each keeping the whole tile in its own MFMA
+// accumulators, so no operand is fetched twice and the K loop needs no
 // barrier; the four partial tiles are summed once through LDS at the end.
-// Both operands are K-contiguous in memory (x rows and A rows), so each lane
-// fetches its MFMA fragment as one 16-byte load straight from global memory.
+//
+// Memory path.  An MFMA fragment puts 16 different rows on adjacent lanes, so
+// loading fragments straight from row-major x / A costs one L1 access per
+// lane.  Instead each chunk is fetched coalesced -- 8 lanes cover the 128
+// contiguous bytes of one row, 8 rows per load -- into registers, written to
+// the wave's own LDS tile, and read back in fragment layout.  Chunk slots in
+// the LDS tile are XOR-swizzled by (row / 2) so that both the row-wise writes
+// and the 16-row fragment reads hit 16 distinct bank groups.  The loads of
+// chunk t+1 are in flight while chunk t is staged and multiplied; every load
+// is unconditional (out-of-range rows / k read a clamped in-bounds address and
+// are zeroed at the fragment read).
 //
 // When the segments alone cannot fill the GPU (decode batches) K is also
 // split across workgroups: each writes an f32 partial tile and bumps an
@@ -25,18 +34,28 @@ namespace {
 
 constexpr int kFragsPerRound = 8;  // accumulator fragments reduced per LDS round
 
+// Byte offset of 16-byte chunk c (0..7) of row r in a swizzled 128-byte-row tile.
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
+
 template <int MF, int NF>
 __global__ __launch_bounds__(256, 1) void shrink_kernel(ShrinkParams p) {
   constexpr int BM = 16 * MF;
   constexpr int NB = 16 * NF;
   constexpr int NFR = MF * NF;
+  constexpr int ROWS = BM + NB;          // tile rows per chunk: x rows, then A rows
+  constexpr int LOADS = ROWS / 8;        // coalesced 16-byte loads per lane per chunk
+  constexpr int XL = BM / 8;             // of which x rows
   constexpr int ROUNDS = (NFR + kFragsPerRound - 1) / kFragsPerRound;
-  __shared__ f32x4 red[4][kFragsPerRound][kWave];
+  constexpr int STAGE_BYTES = 4 * ROWS * 128;
+  constexpr int RED_BYTES = 4 * kFragsPerRound * kWave * 16;
+  __shared__ __attribute__((aligned(16))) char smem[STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES];
   __shared__ int last_flag;
+  f32x4 (*red)[kFragsPerRound][kWave] = reinterpret_cast<f32x4 (*)[kFragsPerRound][kWave]>(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  char* tile = smem + wave * ROWS * 128;
   int L = xcd_contiguous(blockIdx.x, gridDim.x);
   const int mb0 = L % p.mblocks;
   L /= p.mblocks;
@@ -57,84 +76,101 @@ __global__ __launch_bounds__(256, 1) void shrink_kernel(ShrinkParams p) {
 
   const int64_t kb = static_cast<int64_t>(split) * p.kps;
   const int64_t ke = kb + p.kps < p.K ? kb + p.kps : p.K;
-  const int koff = 8 * (lane >> 4);
+  // this wave's 64-deep chunks: k = kb + 64*(wave + 4*t)
+  const int64_t kw = kb + 64 * wave;
+  const int nchunks = kw < ke ? static_cast<int>((ke - kw + 255) / 256) : 0;
 
-  // Weight rows held by this lane (same for every row block).
-  const uint16_t* arow[NF];
+  // Loading role of this lane: row (8*i + lane/8) of the chunk tile, 16-byte
+  // piece lane%8 of the row's 128 bytes.
+  const int lrow = lane >> 3;
+  const int lcol = lane & 7;
+  // Fragment role: row (lane%16) of a fragment, k group (lane/16).
+  const int frow = lane & 15;
+  const int fgrp = lane >> 4;
+
+  // A rows of this lane's loads (fixed for the workgroup); rows beyond the
+  // slot's rank or past c*R read row 0 of the slot (zeroed at the fragment read).
+  const uint16_t* aslot = p.A + static_cast<int64_t>(a) * p.CR * p.K + 8 * lcol;
+  int arow[LOADS - XL];
+#pragma unroll
+  for (int i = XL; i < LOADS; ++i) {
+    const int n = nb * NB + (8 * i + lrow - BM);
+    arow[i - XL] = (n < p.CR && (n % p.R) < rho) ? n : 0;
+  }
   bool nvalid[NF];
 #pragma unroll
   for (int g = 0; g < NF; ++g) {
-    const int n = nb * NB + 16 * g + (lane & 15);
+    const int n = nb * NB + 16 * g + frow;
     nvalid[g] = n < p.CR && (n % p.R) < rho;
-    arow[g] = p.A + (static_cast<int64_t>(a) * p.CR + (nvalid[g] ? n : 0)) * p.K;
   }
+  const uint16_t* xlane = p.x + 8 * lcol;
 
   for (int mb = mb0; lo + mb * BM < hi; mb += p.mblocks) {
     const int m0 = lo + mb * BM;
     const int mcount = hi - m0 < BM ? hi - m0 : BM;
-    const int mf_act = (mcount + 15) >> 4;
 
-    const uint16_t* xrow[MF];
+    int xrow[XL];
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int mm = 8 * i + lrow;
+      const int r = mm < mcount ? p.perm[m0 + mm] : 0;
+      xrow[i] = (r >= 0 && r < p.s) ? r : 0;  // in-bounds stand-in, zeroed at the fragment read
+    }
     bool tvalid[MF];
 #pragma unroll
     for (int f = 0; f < MF; ++f) {
-      const int mm = 16 * f + (lane & 15);
-      tvalid[f] = false;
-      xrow[f] = p.x;
-      if (mm < mcount) {
+      const int mm = 16 * f + frow;
+      bool ok = mm < mcount;
+      if (ok) {
         const int r = p.perm[m0 + mm];
-        if (r >= 0 && r < p.s) {
-          tvalid[f] = true;
-          xrow[f] = p.x + static_cast<int64_t>(r) * p.ldx;
-        }
+        ok = r >= 0 && r < p.s;
       }
+      tvalid[f] = ok;
     }
 
     f32x4 acc[NFR];
 #pragma unroll
     for (int i = 0; i < NFR; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (rho > 0) {
-      // Two 32-deep steps per trip: all fragment loads of both are issued
-      // before the first MFMA so their latencies overlap.
-      for (int64_t k0 = kb + 32 * wave; k0 < ke; k0 += 256) {
-        const int64_t k1 = k0 + koff;
-        const int64_t k2 = k1 + 128;
-        const bool kv1 = k1 < ke, kv2 = k2 < ke;
-        uint4 xv1[MF], xv2[MF], av1[NF], av2[NF];
+    if (rho > 0 && nchunks > 0) {
+      // One register set of loads in flight: chunk t+1 is requested as soon
+      // as chunk t has been copied into the LDS tile, and arrives while chunk
+      // t is multiplied.
+      uint4 ld[LOADS];
+      auto issue = [&](int t) {
+        const int64_t k = kw + 256 * t + 8 * lcol;
+        const int64_t koff = (k <= p.K - 8 ? k : p.K - 8) - 8 * lcol;
 #pragma unroll
-        for (int f = 0; f < MF; ++f) {
-          xv1[f] = make_uint4(0, 0, 0, 0);
-          xv2[f] = make_uint4(0, 0, 0, 0);
-          if (f < mf_act && tvalid[f]) {
-            if (kv1) xv1[f] = load16(xrow[f] + k1);
-            if (kv2) xv2[f] = load16(xrow[f] + k2);
-          }
-        }
+        for (int i = 0; i < XL; ++i) ld[i] = load16(xlane + static_cast<int64_t>(xrow[i]) * p.ldx + koff);
 #pragma unroll
-        for (int g = 0; g < NF; ++g) {
-          av1[g] = make_uint4(0, 0, 0, 0);
-          av2[g] = make_uint4(0, 0, 0, 0);
-          if (nvalid[g]) {
-            if (kv1) av1[g] = load16(arow[g] + k1);
-            if (kv2) av2[g] = load16(arow[g] + k2);
-          }
-        }
+        for (int i = XL; i < LOADS; ++i) ld[i] = load16(aslot + static_cast<int64_t>(arow[i - XL]) * p.K + koff);
+      };
+      issue(0);
+      for (int t = 0; t < nchunks; ++t) {
 #pragma unroll
-        for (int f = 0; f < MF; ++f) {
-          if (f < mf_act) {
+        for (int i = 0; i < LOADS; ++i)
+          *reinterpret_cast<uint4*>(tile + swz(8 * i + lrow, lcol)) = ld[i];
+        if (t + 1 < nchunks) issue(t + 1);
+        const int64_t k0 = kw + 256 * t;
 #pragma unroll
-            for (int g = 0; g < NF; ++g) acc[f * NF + g] = mfma16x16x32(av1[g], xv1[f], acc[f * NF + g]);
-          }
-        }
-        if (k0 + 128 < ke) {
+        for (int st = 0; st < 2; ++st) {
+          const int c = 4 * st + fgrp;
+          const bool kv = k0 + 8 * c < ke;
+          uint4 xv[MF], av[NF];
 #pragma unroll
           for (int f = 0; f < MF; ++f) {
-            if (f < mf_act) {
-#pragma unroll
-              for (int g = 0; g < NF; ++g) acc[f * NF + g] = mfma16x16x32(av2[g], xv2[f], acc[f * NF + g]);
-            }
+            const uint4 v = *reinterpret_cast<const uint4*>(tile + swz(16 * f + frow, c));
+            xv[f] = (kv && tvalid[f]) ? v : make_uint4(0, 0, 0, 0);
           }
+#pragma unroll
+          for (int g = 0; g < NF; ++g) {
+            const uint4 v = *reinterpret_cast<const uint4*>(tile + swz(BM + 16 * g + frow, c));
+            av[g] = (kv && nvalid[g]) ? v : make_uint4(0, 0, 0, 0);
+          }
+#pragma unroll
+          for (int f = 0; f < MF; ++f)
+#pragma unroll
+            for (int g = 0; g < NF; ++g) acc[f * NF + g] = mfma16x16x32(av[g], xv[f], acc[f * NF + g]);
         }
       }
     }
@@ -170,15 +206,21 @@ __global__ __launch_bounds__(256, 1) void shrink_kernel(ShrinkParams p) {
           o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
           *reinterpret_cast<uint2*>(p.h + static_cast<int64_t>(r) * p.ldh + n) = o;
         } else {
+          // written through to the agent's coherence point (no dirty L2 lines)
           float* dst = p.partial + (static_cast<int64_t>(split) * p.s + (m0 + mm)) * p.CR + n;
-          *reinterpret_cast<f32x4*>(dst) = v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            __hip_atomic_store(dst + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
     if (direct) continue;
 
     // Split-K: publish this partial, count arrivals, the last one reduces.
-    __threadfence();
+    // One release (thread 0, after the barrier that orders the whole
+    // workgroup's partial stores before it) per workgroup, and one acquire
+    // in the last arriver only: agent-scope fences write back / invalidate
+    // the XCD's L2, so they are kept off every other path.
     __syncthreads();
     // (lo / BM + seg + mb) is distinct for every (segment, row block) of a
     // CSR plan, so every tile has its own counter; the clamp only keeps a
@@ -186,12 +228,14 @@ __global__ __launch_bounds__(256, 1) void shrink_kernel(ShrinkParams p) {
     int64_t cidx = (static_cast<int64_t>(lo / BM) + seg + mb) * p.nblocks + nb;
     if (cidx >= p.counter_cap) cidx = p.counter_cap - 1;
     if (tid == 0) {
-      const int old = atomicAdd(p.counters + cidx, 1);
-      last_flag = (old == p.ksplit - 1);
+      const int old = __hip_atomic_fetch_add(p.counters + cidx, 1, __ATOMIC_RELEASE,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = old == p.ksplit - 1;
+      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      last_flag = last;
     }
     __syncthreads();
     if (!last_flag) continue;
-    __threadfence();
     const int items = mcount * (NB / 4);
     for (int q = tid; q < items; q += 256) {
       const int mm = q / (NB / 4);
@@ -202,14 +246,16 @@ __global__ __launch_bounds__(256, 1) void shrink_kernel(ShrinkParams p) {
       f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int sp = 0; sp < p.ksplit; ++sp) {
         const float* src = p.partial + (static_cast<int64_t>(sp) * p.s + (m0 + mm)) * p.CR + n;
-        v += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] += __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       uint2 o;
       o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
       o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
       *reinterpret_cast<uint2*>(p.h + static_cast<int64_t>(r) * p.ldh + n) = o;
     }
-    if (tid == 0) atomicExch(p.counters + cidx, 0);
+    if (tid == 0) __hip_atomic_store(p.counters + cidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

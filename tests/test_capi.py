@@ -184,6 +184,7 @@ def _err():
     (dict(R=12, ldh=12), -2, "multiples of 8"),
     (dict(x=ctypes.c_void_p(0x10008)), -2, "aligned"),
     (dict(indptr=NULL), -1, "plan array"),
+    (dict(perm=NULL), -1, "permutation is NULL"),
     (dict(nseg=-1), -1, "num_segments"),
     (dict(L=0), -1, "num_loras"),
     (dict(chunk=0), -1, "chunk_size"),
