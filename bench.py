@@ -3,7 +3,10 @@
 A step is one pass of the whole path over one batch: host plan (native
 planner) -> one async upload of the plan -> LoRA-A shrink -> LoRA-B expand
 (scaling, stacked slice offsets, in place into base) -> LoRA-A embedding
-gather.  The headline workload is the decode batch: 256 one-token requests on
+gather.  The timed steps use the graph path: the three kernel launches are
+captured once per input set over a fixed-capacity plan buffer, and each step
+plans + uploads on the host and replays the graph.  Eager steps (no graph)
+are timed too and reported beside it.  The headline workload is the decode batch: 256 one-token requests on
 8 adapters drawn uniformly, rank 16, stacked qkv 4096 -> [4096, 1024, 1024],
 bf16; the embedding gather uses vocab 128256 and rank 16.  Inputs rotate over
 48 independent sets (> the 256 MB MALL) so kernels read HBM, not cache.
@@ -117,60 +120,105 @@ def make_sets(n_sets, device):
 
 
 def run_decode(args, device):
+    """Decode steps: eager (plan + upload + 3 kernel calls) and graph mode
+    (plan + upload, then one replay of the captured shrink / expand /
+    embedding launches).  Graph mode is the headline: it is the pages' own
+    serving path for decode batches."""
     import torch
     import segmented_gather_gemm_amd as sgg
 
     sets = make_sets(args.sets, device)
     b0 = sets[0]["b"]
-    be = sgg.ChunkedSgmvLoRA(b0.num_loras, b0.max_chunk_size, device)
     vocab = b0.vocab_size or 128256
     stream = torch.cuda.current_stream(device)
     names = ("shrink", "expand", "embedding")
-    h_bufs = [torch.empty((st["b"].num_tokens, st["A"].shape[1]), dtype=torch.bfloat16,
-                          device=device) for st in sets]
-    ws = sgg.default_workspace(device, 64 << 20)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=device)
+    for st in sets:
+        st["h"] = torch.empty((st["b"].num_tokens, st["A"].shape[1]), dtype=torch.bfloat16,
+                              device=device)
 
-    def step(i, events=None):
-        st = sets[i % len(sets)]
-        b, proj = st["b"], st["proj"]
-        info = be.prepare_lora_batch(None, b.req_slots, b.lora_ranks, b.scalings,
-                                     is_decode=True)
-        ev = events[i] if events is not None else None
+    def launch(st, info, ev=None):
+        proj = st["proj"]
         if ev:
             ev[0].record(stream)
-        h = sgg.lora_shrink(st["x"], st["A"], info, proj.num_slices, out=h_bufs[i % len(sets)],
-                            workspace=ws)
+        sgg.lora_shrink(st["x"], st["A"], info, proj.num_slices, out=st["h"], workspace=ws)
         if ev:
             ev[1].record(stream)
-        sgg.lora_expand(h, st["B"], info, proj.slice_offsets, proj.max_slice, st["base"])
+        sgg.lora_expand(st["h"], st["B"], info, proj.slice_offsets, proj.max_slice, st["base"])
         if ev:
             ev[2].record(stream)
         sgg.lora_a_embedding(st["ids"], st["A_emb"], info, vocab, out=st["e"])
         if ev:
             ev[3].record(stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    # ---- eager steps
+    be = sgg.ChunkedSgmvLoRA(b0.num_loras, b0.max_chunk_size, device)
 
-    # timed region: whole steps, wall clock
+    def eager_step(i):
+        st = sets[i % len(sets)]
+        info = be.prepare_lora_batch(None, st["b"].req_slots, st["b"].lora_ranks,
+                                     st["b"].scalings, is_decode=True)
+        launch(st, info)
+
+    for i in range(args.warmup):
+        eager_step(i)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        eager_step(i)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    eager_wall = time.perf_counter() - t0
 
-    # kernel durations: the same steps again with events around each kernel
+    # ---- graph mode: one capture per input set over the fixed-capacity plan
+    bg = sgg.ChunkedSgmvLoRA(b0.num_loras, b0.max_chunk_size, device)
+    ginfo = bg.init_cuda_graph_batch_info(b0.num_tokens, 1)
+
+    def plan_g(st):
+        bg.prepare_lora_batch(None, st["b"].req_slots, st["b"].lora_ranks, st["b"].scalings,
+                              is_decode=True, use_cuda_graph=True)
+
+    plan_g(sets[0])
+    side = torch.cuda.Stream(device)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        launch(sets[0], ginfo)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for st in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            launch(st, ginfo)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    def graph_step(i):
+        j = i % len(sets)
+        plan_g(sets[j])
+        graphs[j].replay()
+
+    for i in range(args.warmup):
+        graph_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graph_step(i)
+    torch.cuda.synchronize()
+    graph_wall = time.perf_counter() - t0
+
+    # ---- kernel durations in the graphs' launch configuration (events)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
-        step(i, events)
+        st = sets[i % len(sets)]
+        plan_g(st)
+        launch(st, ginfo, events[i])
     torch.cuda.synchronize()
     dur = {n: [] for n in names}
     for ev in events:
         for j, n in enumerate(names):
             dur[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)   # microseconds
 
-    # host planner alone (native plan + staging), for the record
+    # host planner alone (native plan, no upload), for the record
     t1 = time.perf_counter()
     for i in range(50):
         st = sets[i % len(sets)]
@@ -178,20 +226,20 @@ def run_decode(args, device):
     plan_us = (time.perf_counter() - t1) / 50 * 1e6
 
     counts = [algo_counts(st["b"], st["proj"], st["A_emb"].shape[1]) for st in sets]
-    avg = {n: float(np.mean(dur[n])) for n in names}
-    med = {n: float(np.median(dur[n])) for n in names}
     per = {}
     for n in names:
+        avg = float(np.mean(dur[n]))
         by = float(np.mean([c[n]["bytes"] for c in counts]))
         fl = float(np.mean([c[n]["flops"] for c in counts]))
-        per[n] = {"avg_us": round(avg[n], 3), "median_us": round(med[n], 3),
+        per[n] = {"avg_us": round(avg, 3), "median_us": round(float(np.median(dur[n])), 3),
                   "algo_bytes": int(by), "algo_flops": int(fl),
-                  "gbs": round(by / (avg[n] * 1e-6) / 1e9, 1),
-                  "tflops": round(fl / (avg[n] * 1e-6) / 1e12, 3)}
-    se_us = avg["shrink"] + avg["expand"]
+                  "gbs": round(by / (avg * 1e-6) / 1e9, 1),
+                  "tflops": round(fl / (avg * 1e-6) / 1e12, 3)}
+    se_us = per["shrink"]["avg_us"] + per["expand"]["avg_us"]
     se_bytes = per["shrink"]["algo_bytes"] + per["expand"]["algo_bytes"]
     return {
-        "wall_s": wall, "tokens": b0.num_tokens, "kernels": per, "plan_host_us": round(plan_us, 2),
+        "wall_s": graph_wall, "eager_wall_s": eager_wall, "tokens": b0.num_tokens,
+        "kernels": per, "plan_host_us": round(plan_us, 2),
         "shrink_expand": {"us": round(se_us, 3),
                           "gbs": round(se_bytes / (se_us * 1e-6) / 1e9, 1),
                           "hbm_frac": round(se_bytes / (se_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -308,6 +356,7 @@ def main():
     res = run_decode(args, device)
     ms = res["wall_s"] / args.steps * 1e3
     value = res["tokens"] * args.steps / res["wall_s"]
+    eager = res["tokens"] * args.steps / res["eager_wall_s"]
     k = res["kernels"]
     dom = max(("shrink", "expand", "embedding"), key=lambda n: k[n]["avg_us"])
     achieved = k[dom]["gbs"]
@@ -325,6 +374,9 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for(dom, "decode")},
+        "mode": "graph replay per step (host plan + one upload + captured kernels)",
+        "eager_tokens_per_s": round(eager, 1),
+        "eager_ms_per_step": round(res["eager_wall_s"] / args.steps * 1e3, 4),
         "kernels": k,
         "shrink_expand": res["shrink_expand"],
         "plan_host_us": res["plan_host_us"],

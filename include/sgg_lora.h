@@ -111,6 +111,47 @@ int lora_plan_segments(const int32_t* seq_lens, const int32_t* req_slots, int32_
 int64_t lora_plan_max_segments(int64_t num_tokens, int32_t max_loras, int32_t min_chunk);
 
 /*
+ * Plan buffer layout used by lora_plan_upload: int32 regions, each starting
+ * at a multiple of 64 elements, in this order:
+ *   0 permutation [token_capacity]     1 seg_indptr [seg_capacity + 1]
+ *   2 seg_slots [seg_capacity]         3 req_seg_indptr [req_capacity + 1]
+ *   4 req_slots [req_capacity]         5 lora_ranks [max_loras]
+ *   6 scalings [max_loras] (float32 bits)
+ * lora_plan_layout writes the 7 element offsets to offsets[0..6] and returns
+ * the total element count (host only; -1 for negative sizes).
+ */
+#define SGG_PLAN_REGIONS 7
+int64_t lora_plan_layout(int64_t token_capacity, int32_t seg_capacity, int32_t req_capacity,
+                         int32_t max_loras, int64_t* offsets);
+
+/*
+ * lora_plan_upload -- the batch plan (as lora_plan_segments, segment arrays
+ * padded to seg_capacity) written into a pinned host staging buffer in the
+ * layout above, together with the per-request slots and the per-slot rank
+ * and scaling tables, followed by ONE asynchronous host-to-device copy of the
+ * whole buffer to `device_plan` on `stream`.
+ * (chunked_backend.py page: prepare_lora_batch, which plans on the host and
+ *  copies the plan arrays to the device without blocking.)
+ *
+ *   host_staging   pinned host memory (hipHostMalloc) of buffer_bytes bytes.
+ *                  The caller must not modify it until the copy is done
+ *                  (e.g. by recording an event on `stream` after the call).
+ *   device_plan    device memory of buffer_bytes bytes.
+ *   buffer_bytes   at least 4 * lora_plan_layout(...).
+ *   lora_ranks, scalings  host arrays of max_loras entries.
+ *   out_info[4]    host out: num_segments, chunk_size, longest segment,
+ *                  num_tokens.
+ * Errors as lora_plan_segments, plus SGG_ERR_CAPACITY when the batch exceeds
+ * a capacity and SGG_ERR_HIP when the copy cannot be enqueued.
+ */
+int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slots, int32_t num_reqs,
+                     const int32_t* lora_ranks, const float* scalings, int32_t max_loras,
+                     int32_t is_decode, int32_t max_chunk_size, int32_t chunk_size_override,
+                     int64_t token_capacity, int32_t seg_capacity, int32_t req_capacity,
+                     void* host_staging, void* device_plan, int64_t buffer_bytes,
+                     int32_t* out_info, void* stream);
+
+/*
  * lora_shrink -- LoRA-A segmented gather GEMM.
  * (chunked_backend.py page: run_lora_a_sgemm, and the shrink step of
  *  run_qkv_lora / run_gate_up_lora; base_backend.py page: run_lora_a_sgemm

@@ -7,18 +7,24 @@ init_cuda_graph_batch_info).  Every step of the work runs in libsgg_lora:
 the plan in its host planner, the rest in its HIP kernels.
 
 Upload: the page copies six small host arrays to the device one by one.
-Here the planner writes every plan array into one pinned staging buffer and a
-single non-blocking host-to-device copy moves them; the device arrays are
-views of one device buffer.  Staging buffers rotate through a small ring and
-are reused only after the copy that last read them has completed, so
-planning the next batch never waits for the GPU.
+Here one native call (lora_plan_upload) plans straight into a pinned staging
+buffer and enqueues a single non-blocking host-to-device copy of all plan
+arrays and tables; the device arrays are views of one device buffer.  Staging
+buffers rotate through a small ring and are reused only after the copy that
+last read them has completed, so planning the next batch does not wait for
+the GPU.
 """
+
+import ctypes
 
 import numpy as np
 import torch
 
 from . import binding as B
+from ._lib import check, lib
 from .binding import LoRABatchInfo
+
+_P32 = ctypes.POINTER(ctypes.c_int32)
 
 MIN_CHUNK_SIZE = 16
 
@@ -41,13 +47,18 @@ class _Staging:
         if self.events[i] is not None:
             self.events[i].synchronize()
         if self.bufs[i] is None or self.bufs[i].numel() < n:
-            self.bufs[i] = torch.empty(max(n, 1024), dtype=torch.int32, pin_memory=True)
+            self.bufs[i] = torch.empty(max(n, 4096), dtype=torch.int32, pin_memory=True)
         return i, self.bufs[i]
 
     def done(self, i, stream):
-        ev = torch.cuda.Event()
+        ev = self.events[i]
+        if ev is None:
+            ev = self.events[i] = torch.cuda.Event()
         ev.record(stream)
-        self.events[i] = ev
+
+
+_NAMES = ("permutation", "seg_indptr", "seg_slots", "req_seg_indptr", "req_slots", "ranks",
+          "scalings")
 
 
 class ChunkedSgmvLoRA:
@@ -64,18 +75,22 @@ class ChunkedSgmvLoRA:
         self._graph_dev = None
         self._graph_cap = None
         self._staging = _Staging()
+        self._layouts = {}
+        self._info_arr = (ctypes.c_int32 * 4)()
 
     # ---------------------------------------------------------------- plan
-    def _layout(self, s, cap, bs):
-        L = self.max_loras_per_batch
-        off = {}
-        pos = 0
-        for name, n in (("permutation", s), ("seg_indptr", cap + 1), ("seg_slots", cap),
-                        ("req_seg_indptr", bs + 1), ("req_slots", bs), ("ranks", L),
-                        ("scalings", L)):
-            off[name] = (pos, n)
-            pos += _align(n)
-        return off, pos
+    def _layout(self, s_cap, seg_cap, req_cap):
+        key = (s_cap, seg_cap, req_cap)
+        lay = self._layouts.get(key)
+        if lay is None:
+            offs = (ctypes.c_int64 * 7)()
+            total = int(lib().lora_plan_layout(s_cap, seg_cap, req_cap, self.max_loras_per_batch,
+                                               offs))
+            sizes = (s_cap, seg_cap + 1, seg_cap, req_cap + 1, req_cap,
+                     self.max_loras_per_batch, self.max_loras_per_batch)
+            lay = (total, [(int(o), n) for o, n in zip(offs, sizes)])
+            self._layouts[key] = lay
+        return lay
 
     def prepare_lora_batch(self, seq_lens, weight_indices, lora_ranks, scalings,
                            is_decode=False, use_cuda_graph=False, chunk_size_override=0):
@@ -88,80 +103,90 @@ class ChunkedSgmvLoRA:
         L = self.max_loras_per_batch
         if len(lora_ranks) != L or len(scalings) != L:
             raise ValueError(f"lora_ranks and scalings need {L} entries")
-        bs = len(weight_indices)
-        s = bs if seq_lens is None else int(np.sum(np.asarray(seq_lens, dtype=np.int64)))
+        slots = np.ascontiguousarray(weight_indices, dtype=np.int32)
+        bs = len(slots)
+        lens = None if seq_lens is None else np.ascontiguousarray(seq_lens, dtype=np.int32)
+        s = bs if lens is None else int(lens.sum(dtype=np.int64))
         if use_cuda_graph:
             if self._graph_cap is None:
                 raise RuntimeError("call init_cuda_graph_batch_info first")
-            max_bs, max_tokens, cap = self._graph_cap
+            max_bs, max_tokens, seg_cap = self._graph_cap
             if bs > max_bs or s > max_tokens:
                 raise ValueError("batch exceeds the graph capacity")
-            s_alloc, bs_alloc = max_tokens, max_bs
+            s_cap, req_cap = max_tokens, max_bs
         else:
             min_chunk = chunk_size_override if chunk_size_override > 0 else MIN_CHUNK_SIZE
-            cap = B.lora_plan_max_segments(s, L, min_chunk)
-            s_alloc, bs_alloc = s, bs
-        off, total = self._layout(s_alloc, cap, bs_alloc)
-        slot, buf = self._staging.take(total)
-
-        def view(name, n=None):
-            o, size = off[name]
-            return buf[o:o + (size if n is None else n)]
-
-        plan = B.lora_plan_segments(
-            seq_lens, weight_indices, L, is_decode, self.max_chunk_size, chunk_size_override,
-            seg_capacity=cap,
-            out={"permutation": view("permutation", max(s, 1)),
-                 "seg_indptr": view("seg_indptr"), "seg_slots": view("seg_slots"),
-                 "req_seg_indptr": view("req_seg_indptr", bs + 1)})
-        view("req_slots", bs).copy_(torch.as_tensor(np.asarray(weight_indices, np.int32)))
-        view("ranks").copy_(torch.as_tensor(np.asarray(lora_ranks, np.int32)))
-        view("scalings").copy_(torch.as_tensor(np.asarray(scalings, np.float32)).view(torch.int32))
-
+            seg_cap = B.lora_plan_max_segments(s, L, min_chunk)
+            s_cap, req_cap = s, bs
+        total, regions = self._layout(s_cap, seg_cap, req_cap)
+        ring, stage = self._staging.take(total)
+        dev = self._graph_dev if use_cuda_graph else torch.empty(
+            total, dtype=torch.int32, device=self.device)
+        ranks = np.ascontiguousarray(lora_ranks, dtype=np.int32)
+        scal = np.ascontiguousarray(scalings, dtype=np.float32)
         stream = torch.cuda.current_stream(self.device)
+        info = self._info_arr
+        check(lib().lora_plan_upload(
+            ctypes.cast(0, _P32) if lens is None else lens.ctypes.data_as(_P32),
+            slots.ctypes.data_as(_P32), bs, ranks.ctypes.data_as(_P32),
+            scal.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), L, 1 if is_decode else 0,
+            self.max_chunk_size, int(chunk_size_override), s_cap, seg_cap, req_cap,
+            ctypes.c_void_p(stage.data_ptr()), ctypes.c_void_p(dev.data_ptr()), 4 * total,
+            info, ctypes.c_void_p(stream.cuda_stream)))
+        self._staging.done(ring, stream)
+        n_seg, chunk, longest = info[0], info[1], info[2]
         if use_cuda_graph:
-            dev = self._graph_dev
-        else:
-            dev = torch.empty(total, dtype=torch.int32, device=self.device)
-        dev[:total].copy_(buf[:total], non_blocking=True)
-        self._staging.done(slot, stream)
-
-        def dview(name, n=None):
-            o, size = off[name]
-            return dev[o:o + (size if n is None else n)]
-
-        n_seg = plan["num_segments"]
-        indptr = view("seg_indptr")[:n_seg + 1].numpy()
-        longest = int((indptr[1:] - indptr[:-1]).max()) if n_seg > 0 else 0
-        info = LoRABatchInfo(
+            # fixed views and launch shape: capacity segments over capacity tokens
+            batch = self.cuda_graph_batch_info
+            batch.bs, batch.max_len, batch.planned_segments = bs, chunk, n_seg
+            batch.planned_tokens = s
+            self.batch_info = batch
+            return batch
+        v = {name: dev[o:o + n] for name, (o, n) in zip(_NAMES, regions)}
+        batch = LoRABatchInfo(
             bs=bs, num_tokens=s,
-            num_segments=cap if use_cuda_graph else n_seg,
-            max_len=plan["chunk_size"],
-            seg_indptr=dview("seg_indptr"), weight_indices=dview("seg_slots"),
-            permutation=dview("permutation", s), lora_ranks=dview("ranks"),
-            scalings=dview("scalings").view(torch.float32),
-            req_seg_indptr=dview("req_seg_indptr", bs + 1),
-            req_weight_indices=dview("req_slots", bs), use_cuda_graph=use_cuda_graph,
+            num_segments=seg_cap if use_cuda_graph else n_seg,
+            max_len=chunk,
+            seg_indptr=v["seg_indptr"], weight_indices=v["seg_slots"],
+            permutation=v["permutation"][:s], lora_ranks=v["ranks"],
+            scalings=v["scalings"].view(torch.float32),
+            req_seg_indptr=v["req_seg_indptr"][:bs + 1],
+            req_weight_indices=v["req_slots"][:bs], use_cuda_graph=use_cuda_graph,
             max_seg_len=0 if use_cuda_graph else longest)
-        info.planned_segments = n_seg
-        self.batch_info = info
-        return info
+        batch.planned_segments = n_seg
+        batch.planned_tokens = s
+        self.batch_info = batch
+        return batch
 
     def init_cuda_graph_batch_info(self, max_bs_in_cuda_graph, num_tokens_per_bs):
         """Preallocate fixed-capacity device plan arrays for graph capture.
 
-        Capacity follows the page: ceil(tokens_per_bs / 16) segments per
-        request; unused segments are padded to zero length with slot 0, and
-        kernels are always launched over the full capacity so the launch
-        shape never changes between replays.
+        Capacity: the page's ceil(tokens_per_bs / 16) segments per request,
+        or the tighter bound ceil(tokens / 16) + max_loras when smaller (no
+        plan can exceed either).  Unused segments are padded to zero length
+        with slot 0, and kernels are launched over the full capacity so the
+        launch shape never changes between replays.
         """
         max_tokens = max_bs_in_cuda_graph * num_tokens_per_bs
         cap = (num_tokens_per_bs + MIN_CHUNK_SIZE - 1) // MIN_CHUNK_SIZE * max_bs_in_cuda_graph
-        cap = max(cap, B.lora_plan_max_segments(max_tokens, self.max_loras_per_batch,
+        cap = min(cap, B.lora_plan_max_segments(max_tokens, self.max_loras_per_batch,
                                                 MIN_CHUNK_SIZE))
         self._graph_cap = (max_bs_in_cuda_graph, max_tokens, cap)
-        _, total = self._layout(max_tokens, cap, max_bs_in_cuda_graph)
-        self._graph_dev = torch.zeros(total, dtype=torch.int32, device=self.device)
+        total, regions = self._layout(max_tokens, cap, max_bs_in_cuda_graph)
+        dev = torch.zeros(total, dtype=torch.int32, device=self.device)
+        self._graph_dev = dev
+        v = {name: dev[o:o + n] for name, (o, n) in zip(_NAMES, regions)}
+        # Kernels see the capacity: num_segments = cap (padding segments are
+        # empty), num_tokens = max_tokens (activations are allocated for the
+        # capacity), and a tiling hint of the largest chunk any batch can use.
+        hint = max(MIN_CHUNK_SIZE, min(self.max_chunk_size, 128))
+        self.cuda_graph_batch_info = LoRABatchInfo(
+            bs=max_bs_in_cuda_graph, num_tokens=max_tokens, num_segments=cap,
+            max_len=hint, seg_indptr=v["seg_indptr"], weight_indices=v["seg_slots"],
+            permutation=v["permutation"], lora_ranks=v["ranks"],
+            scalings=v["scalings"].view(torch.float32), req_seg_indptr=v["req_seg_indptr"],
+            req_weight_indices=v["req_slots"], use_cuda_graph=True, max_seg_len=hint)
+        return self.cuda_graph_batch_info
 
     # -------------------------------------------------------------- kernels
     def _info(self, pruned_batch_info=None):

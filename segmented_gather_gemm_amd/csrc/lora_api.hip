@@ -1,6 +1,7 @@
 // C-ABI device entry points: argument validation (host only, before anything
 // is enqueued), tile choice and kernel launches.
 #include <cinttypes>
+#include <cstring>
 
 #include "sgg_internal.h"
 #include "sgg_kernels.h"
@@ -341,4 +342,62 @@ extern "C" int lora_a_embedding(const int64_t* input_ids, const void* A_emb, int
   p.parts = static_cast<int32_t>(parts < 1 ? 1 : (parts > 64 ? 64 : parts));
   rc = launch_status(sgg::launch_embedding(p, static_cast<hipStream_t>(stream)), "embedding");
   return rc ? rc : sgg::ok();
+}
+
+// ------------------------------------------------------------- plan upload
+
+extern "C" int64_t lora_plan_layout(int64_t token_capacity, int32_t seg_capacity,
+                                    int32_t req_capacity, int32_t max_loras, int64_t* offsets) {
+  if (token_capacity < 0 || seg_capacity < 0 || req_capacity < 0 || max_loras < 0) return -1;
+  const int64_t sizes[SGG_PLAN_REGIONS] = {token_capacity, seg_capacity + 1, seg_capacity,
+                                           req_capacity + 1, req_capacity, max_loras, max_loras};
+  int64_t pos = 0;
+  for (int i = 0; i < SGG_PLAN_REGIONS; ++i) {
+    if (offsets) offsets[i] = pos;
+    pos += sgg::round_up(sizes[i], 64);
+  }
+  return pos;
+}
+
+extern "C" int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slots,
+                                int32_t num_reqs, const int32_t* lora_ranks,
+                                const float* scalings, int32_t max_loras, int32_t is_decode,
+                                int32_t max_chunk_size, int32_t chunk_size_override,
+                                int64_t token_capacity, int32_t seg_capacity,
+                                int32_t req_capacity, void* host_staging, void* device_plan,
+                                int64_t buffer_bytes, int32_t* out_info, void* stream) {
+  int64_t off[SGG_PLAN_REGIONS];
+  const int64_t total = lora_plan_layout(token_capacity, seg_capacity, req_capacity, max_loras, off);
+  SGG_CHECK(total >= 0, SGG_ERR_INVALID, "negative capacity");
+  SGG_CHECK(host_staging && device_plan && out_info, SGG_ERR_INVALID,
+            "host_staging, device_plan or out_info is NULL");
+  SGG_CHECK(lora_ranks && scalings, SGG_ERR_INVALID, "lora_ranks or scalings is NULL");
+  SGG_CHECK(buffer_bytes >= total * 4, SGG_ERR_CAPACITY,
+            "plan buffer of %" PRId64 " bytes, layout needs %" PRId64, buffer_bytes, total * 4);
+  SGG_CHECK(num_reqs <= req_capacity, SGG_ERR_CAPACITY, "%d requests > capacity %d", num_reqs,
+            req_capacity);
+  int32_t* h = static_cast<int32_t*>(host_staging);
+  int32_t n_seg = 0, chunk = 0;
+  int64_t n_tok = 0;
+  int rc = lora_plan_segments(seq_lens, req_slots, num_reqs, max_loras, is_decode, max_chunk_size,
+                              chunk_size_override, h + off[0], token_capacity, h + off[1],
+                              h + off[2], seg_capacity, h + off[3], &n_seg, &chunk, &n_tok);
+  if (rc) return rc;
+  for (int32_t r = 0; r < num_reqs; ++r) h[off[4] + r] = req_slots[r];
+  for (int32_t a = 0; a < max_loras; ++a) h[off[5] + a] = lora_ranks[a];
+  std::memcpy(h + off[6], scalings, sizeof(float) * static_cast<size_t>(max_loras));
+  int32_t longest = 0;
+  for (int32_t i = 0; i < n_seg; ++i) {
+    const int32_t len = h[off[1] + i + 1] - h[off[1] + i];
+    longest = len > longest ? len : longest;
+  }
+  const hipError_t e = hipMemcpyAsync(device_plan, host_staging, static_cast<size_t>(total) * 4,
+                                      hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(SGG_ERR_HIP, "plan upload failed: %s", hipGetErrorString(e));
+  out_info[0] = n_seg;
+  out_info[1] = chunk;
+  out_info[2] = longest;
+  out_info[3] = static_cast<int32_t>(n_tok);
+  return sgg::ok();
 }

@@ -282,44 +282,55 @@ hipError_t launch_m(const ShrinkParams& p, int nf, int64_t grid, hipStream_t str
 
 }  // namespace
 
-// Fragment counts: NF covers c*R (at most 8 fragments = 128 outputs per
-// column block), MF the chunk (at most 8 fragments = 128 tokens), with at
-// most 32 accumulator fragments per wave.  K is split across workgroups only
-// when segments x column blocks cannot give every CU a workgroup.
+// Tile choice.  Start from the largest tile (NF covering c*R up to 8
+// fragments, MF covering the longest segment up to 8, at most 32 accumulator
+// fragments per wave).  While the grid has fewer work items than CUs, split
+// columns (NF), then rows (MF), down to single fragments; only then split K
+// across workgroups, into at most 4 ranges (each extra range costs a partial
+// tile round trip).  Measured on decode shapes: small tiles with 4 K ranges
+// beat both one big tile and 16-32 K ranges.
 ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk) {
   ShrinkTiling t{};
-  const int need = (CR + 15) / 16;
   static const int kNf[] = {1, 2, 3, 4, 6, 8};
-  t.nf = 8;
-  for (int v : kNf) {
-    if (v >= need) {
-      t.nf = v;
-      break;
-    }
+  static const int kMf[] = {1, 2, 4, 8};
+  const int need_n = (CR + 15) / 16;
+  const int need_m = (chunk < 16 ? 16 : chunk + 15) / 16;
+  // column fragments: values that tile c*R exactly (no partly empty block)
+  auto nf_ok = [&](int v) { return v <= need_n ? need_n % v == 0 : v == kNf[0] || kNf[0] >= need_n; };
+  int ni = 5, mi = 3;
+  while (ni > 0 && (kNf[ni] > need_n && kNf[ni - 1] >= need_n)) --ni;  // smallest NF covering c*R
+  while (ni > 0 && !(kNf[ni] >= need_n || need_n % kNf[ni] == 0)) --ni;
+  while (mi > 0 && kMf[mi - 1] >= need_m) --mi;   // smallest MF covering the chunk (or 8)
+  while (kMf[mi] * kNf[ni] > 32) --mi;
+  auto units_for = [&](int nf, int mf) {
+    const int bm = 16 * mf;
+    const int64_t mblocks = (chunk + bm - 1) / bm;
+    const int64_t grid_units = static_cast<int64_t>(num_segments) * mblocks;
+    const int64_t real_units = (s + bm - 1) / bm + num_segments;
+    const int64_t nblocks = (CR + 16 * nf - 1) / (16 * nf);
+    return (grid_units < real_units ? grid_units : real_units) * nblocks;
+  };
+  while (units_for(kNf[ni], kMf[mi]) < 256 && ni > 0) {
+    --ni;
+    while (ni > 0 && !nf_ok(kNf[ni])) --ni;
   }
+  while (units_for(kNf[ni], kMf[mi]) < 256 && mi > 0) --mi;
+  t.nf = kNf[ni];
+  t.mf = kMf[mi];
   t.nblocks = (CR + 16 * t.nf - 1) / (16 * t.nf);
-  const int chunk16 = (chunk < 16 ? 16 : chunk + 15) / 16;
-  t.mf = 1;
-  for (int v : {8, 4, 2, 1}) {
-    if (v * t.nf <= 32 && v <= chunk16) {
-      t.mf = v;
-      break;
-    }
-  }
   const int bm = 16 * t.mf;
   t.mblocks = (chunk + bm - 1) / bm;
   if (t.mblocks < 1) t.mblocks = 1;
-  const int64_t units_grid = static_cast<int64_t>(num_segments) * t.mblocks;
-  const int64_t units_real = (s + bm - 1) / bm + num_segments;
-  const int64_t units = (units_grid < units_real ? units_grid : units_real) * t.nblocks;
-  const int64_t kgroups = (K + 127) / 128;
+  const int64_t units = units_for(t.nf, t.mf);
+  const int64_t kgroups = (K + 255) / 256;   // 256-deep groups: one 64-deep chunk per wave
   int64_t ksplit = 1;
   const int64_t counters = (s / bm + num_segments + 1) * t.nblocks;
   if (units > 0 && units < 256 && counters <= kCounterCap) {
     ksplit = (256 + units - 1) / units;
+    if (ksplit > 4) ksplit = 4;
     if (ksplit > kgroups) ksplit = kgroups;
   }
-  t.kps = (kgroups + ksplit - 1) / ksplit * 128;
+  t.kps = (kgroups + ksplit - 1) / ksplit * 256;
   t.ksplit = static_cast<int>((K + t.kps - 1) / t.kps);
   if (t.ksplit < 1) t.ksplit = 1;
   t.grid = static_cast<int64_t>(t.ksplit) * t.nblocks * num_segments * t.mblocks;

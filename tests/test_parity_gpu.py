@@ -385,3 +385,65 @@ def test_missing_base_gives_delta():
     t0 = dict(t, base=torch.zeros_like(t["base"]))
     _, want = oracle_forward(t0, b, proj)
     assert_close(y, want, "delta only")
+
+
+def test_graph_mode_replays_match_oracle():
+    """Capacity plan + captured kernels, replayed with different batches.
+
+    The plan upload runs eagerly before each replay (as on the pages' graph
+    path); base is reset eagerly, and every replay is checked on its own.
+    """
+    sgg = _sgg()
+    L, K, R, offs, Re, V = 6, 512, 16, [0, 256, 320, 384], 16, 1000
+    max_bs = 64
+    rng = np.random.default_rng(55)
+    proto = Batch("graph", 5555, [1] * max_bs, [0] * max_bs, True, L, [16, 16, 8, 0, 16, 16],
+                  [1.0, 0.5, 2.0, 1.0, 1.5, 1.0], 128, [Projection("qkv", K, offs, R)])
+    proj = proto.projections[0]
+    t = draw_projection(proto, proj)
+    x, A, Bw = (t[k].to(DEV) for k in ("x", "A", "B"))
+    base0 = t["base"].to(DEV)
+    base = base0.clone()
+    A_emb = torch.randn(L, Re, V).to(torch.bfloat16)
+    ids = torch.as_tensor(rng.integers(0, V, size=max_bs), dtype=torch.int64)
+    ids_d, A_emb_d = ids.to(DEV), A_emb.to(DEV)
+    h = torch.empty(max_bs, 3 * R, dtype=torch.bfloat16, device=DEV)
+    e = torch.empty(max_bs, Re, dtype=torch.bfloat16, device=DEV)
+    ws = torch.zeros(8 << 20, dtype=torch.uint8, device=DEV)
+    be = sgg.ChunkedSgmvLoRA(L, 128, DEV)
+    info = be.init_cuda_graph_batch_info(max_bs, 1)
+
+    def kernels():
+        sgg.lora_shrink(x, A, info, 3, out=h, workspace=ws)
+        sgg.lora_expand(h, Bw, info, offs, 256, base)
+        sgg.lora_a_embedding(ids_d, A_emb_d, info, V, out=e)
+
+    be.prepare_lora_batch(None, [0] * max_bs, proto.lora_ranks, proto.scalings, is_decode=True,
+                          use_cuda_graph=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kernels()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kernels()
+    torch.cuda.synchronize()
+    for trial in range(4):
+        slots = rng.integers(0, L, size=max_bs).tolist()
+        be.prepare_lora_batch(None, slots, proto.lora_ranks, proto.scalings, is_decode=True,
+                              use_cuda_graph=True)
+        base.copy_(base0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        b = Batch("g", 0, [1] * max_bs, slots, True, L, proto.lora_ranks, proto.scalings, 128,
+                  proto.projections)
+        want_h, want_y = oracle_forward(t, b, proj)
+        assert_close(h, want_h, f"graph replay {trial} h")
+        assert_close(base, want_y, f"graph replay {trial} y")
+        want_e = ol.embedding_a(ids.numpy(), to_f64(A_emb), b.seq_lens, slots, b.lora_ranks, V)
+        assert np.array_equal(to_f64(e), want_e), f"graph replay {trial} embedding"
+        # eager work between replays, on the default stream
+        torch.mm(torch.randn(64, 64, device=DEV), torch.randn(64, 64, device=DEV))
