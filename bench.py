@@ -3,10 +3,11 @@
 A step is one pass of the whole path over one batch: host plan (native
 planner) -> one async upload of the plan -> LoRA-A shrink -> LoRA-B expand
 (scaling, stacked slice offsets, in place into base) -> LoRA-A embedding
-gather.  The timed steps use the graph path: the three kernel launches are
-captured once per input set over a fixed-capacity plan buffer, and each step
-plans + uploads on the host and replays the graph.  Eager steps (no graph)
-are timed too and reported beside it.  The headline workload is the decode batch: 256 one-token requests on
+gather.  The timed steps are eager: one native call plans and uploads, one
+call runs the embedding gather and one runs lora_qkv (shrink then expand).
+Graph mode (the three launches captured once per input set over a
+fixed-capacity plan, replayed after each upload) is timed too and reported
+beside it.  The headline workload is the decode batch: 256 one-token requests on
 8 adapters drawn uniformly, rank 16, stacked qkv 4096 -> [4096, 1024, 1024],
 bf16; the embedding gather uses vocab 128256 and rank 16.  Inputs rotate over
 48 independent sets (> the 256 MB MALL) so kernels read HBM, not cache.
@@ -18,6 +19,7 @@ gate_up workload (32 requests of 64..2048 tokens, rank 64, chunk 128).
 """
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -119,11 +121,34 @@ def make_sets(n_sets, device):
     return sets
 
 
+def hold_stream(stream, ms):
+    """Enqueue a delay kernel of about `ms` milliseconds on `stream`; return
+    an event recorded after it (not yet complete while the delay runs)."""
+    import torch
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            torch.cuda._sleep(1 << 22)
+            b.record(stream)
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = (1 << 22) / max(a.elapsed_time(b), 1e-3)
+    done = torch.cuda.Event()
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
+        done.record(stream)
+    return done
+
+
+_SLEEP_CYCLES_PER_MS = None
+
+
 def run_decode(args, device):
-    """Decode steps: eager (plan + upload + 3 kernel calls) and graph mode
-    (plan + upload, then one replay of the captured shrink / expand /
-    embedding launches).  Graph mode is the headline: it is the pages' own
-    serving path for decode batches."""
+    """Decode steps.  Headline (eager): host plan + one upload, then the
+    embedding gather and the stacked shrink + expand (lora_qkv), one C call
+    each.  Secondary: graph mode (the three launches captured once per input
+    set over a fixed-capacity plan, replayed after each plan upload)."""
     import torch
     import segmented_gather_gemm_amd as sgg
 
@@ -136,30 +161,24 @@ def run_decode(args, device):
     for st in sets:
         st["h"] = torch.empty((st["b"].num_tokens, st["A"].shape[1]), dtype=torch.bfloat16,
                               device=device)
+        st["slots"] = np.asarray(st["b"].req_slots, np.int32)
+        st["ranks"] = np.asarray(st["b"].lora_ranks, np.int32)
+        st["scal"] = np.asarray(st["b"].scalings, np.float32)
 
-    def launch(st, info, ev=None):
-        proj = st["proj"]
-        if ev:
-            ev[0].record(stream)
-        sgg.lora_shrink(st["x"], st["A"], info, proj.num_slices, out=st["h"], workspace=ws)
-        if ev:
-            ev[1].record(stream)
-        sgg.lora_expand(st["h"], st["B"], info, proj.slice_offsets, proj.max_slice, st["base"])
-        if ev:
-            ev[2].record(stream)
-        sgg.lora_a_embedding(st["ids"], st["A_emb"], info, vocab, out=st["e"])
-        if ev:
-            ev[3].record(stream)
-
-    # ---- eager steps
+    # ---- eager steps (headline)
     be = sgg.ChunkedSgmvLoRA(b0.num_loras, b0.max_chunk_size, device)
 
     def eager_step(i):
         st = sets[i % len(sets)]
-        info = be.prepare_lora_batch(None, st["b"].req_slots, st["b"].lora_ranks,
-                                     st["b"].scalings, is_decode=True)
-        launch(st, info)
+        proj = st["proj"]
+        info = be.prepare_lora_batch(None, st["slots"], st["ranks"], st["scal"], is_decode=True)
+        sgg.lora_a_embedding(st["ids"], st["A_emb"], info, vocab, out=st["e"])
+        sgg.lora_qkv(st["x"], st["A"], st["B"], info, proj.slice_offsets, proj.max_slice,
+                     st["base"], workspace=ws)
 
+    # Set-up leaves many young objects; a full collection of them inside the
+    # timed steps would cost ~30 ms, so collect once before timing.
+    gc.collect()
     for i in range(args.warmup):
         eager_step(i)
     torch.cuda.synchronize()
@@ -169,26 +188,71 @@ def run_decode(args, device):
     torch.cuda.synchronize()
     eager_wall = time.perf_counter() - t0
 
-    # ---- graph mode: one capture per input set over the fixed-capacity plan
+    # ---- kernel durations, same plans and launch configuration, HIP events
+    # on the launch stream.  The plans are made first; then, per kernel, a
+    # delay kernel holds the stream while one launch per step is queued
+    # between two events, so the launches run back to back and the average
+    # launch duration is the interval over the number of launches.
+    infos = []
+    for i in range(args.steps):
+        st = sets[i % len(sets)]
+        infos.append(be.prepare_lora_batch(None, st["slots"], st["ranks"], st["scal"],
+                                           is_decode=True))
+    torch.cuda.synchronize()
+
+    def one(n, i):
+        st, info = sets[i % len(sets)], infos[i]
+        proj = st["proj"]
+        if n == "embedding":
+            sgg.lora_a_embedding(st["ids"], st["A_emb"], info, vocab, out=st["e"])
+        elif n == "shrink":
+            sgg.lora_shrink(st["x"], st["A"], info, proj.num_slices, out=st["h"], workspace=ws)
+        else:
+            sgg.lora_expand(st["h"], st["B"], info, proj.slice_offsets, proj.max_slice,
+                            st["base"])
+
+    dur = {}
+    back_to_back = True
+    for n in names:
+        for i in range(min(args.warmup, args.steps)):
+            one(n, i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        held = hold_stream(stream, 5.0 + 0.05 * args.steps)
+        e0.record(stream)
+        for i in range(args.steps):
+            one(n, i)
+        e1.record(stream)
+        back_to_back &= not held.query()   # the delay outlasted the enqueueing
+        torch.cuda.synchronize()
+        dur[n] = e0.elapsed_time(e1) * 1e3 / args.steps   # microseconds per launch
+    del infos
+
+    # ---- graph mode (secondary)
     bg = sgg.ChunkedSgmvLoRA(b0.num_loras, b0.max_chunk_size, device)
     ginfo = bg.init_cuda_graph_batch_info(b0.num_tokens, 1)
 
+    def launch_g(st):
+        proj = st["proj"]
+        sgg.lora_a_embedding(st["ids"], st["A_emb"], ginfo, vocab, out=st["e"])
+        sgg.lora_shrink(st["x"], st["A"], ginfo, proj.num_slices, out=st["h"], workspace=ws)
+        sgg.lora_expand(st["h"], st["B"], ginfo, proj.slice_offsets, proj.max_slice, st["base"])
+
     def plan_g(st):
-        bg.prepare_lora_batch(None, st["b"].req_slots, st["b"].lora_ranks, st["b"].scalings,
-                              is_decode=True, use_cuda_graph=True)
+        bg.prepare_lora_batch(None, st["slots"], st["ranks"], st["scal"], is_decode=True,
+                              use_cuda_graph=True)
 
     plan_g(sets[0])
     side = torch.cuda.Stream(device)
     side.wait_stream(stream)
     with torch.cuda.stream(side):
-        launch(sets[0], ginfo)
+        launch_g(sets[0])
     stream.wait_stream(side)
     torch.cuda.synchronize()
     graphs = []
     for st in sets:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            launch(st, ginfo)
+            launch_g(st)
         graphs.append(g)
     torch.cuda.synchronize()
 
@@ -197,6 +261,7 @@ def run_decode(args, device):
         plan_g(sets[j])
         graphs[j].replay()
 
+    gc.collect()
     for i in range(args.warmup):
         graph_step(i)
     torch.cuda.synchronize()
@@ -206,40 +271,28 @@ def run_decode(args, device):
     torch.cuda.synchronize()
     graph_wall = time.perf_counter() - t0
 
-    # ---- kernel durations in the graphs' launch configuration (events)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        st = sets[i % len(sets)]
-        plan_g(st)
-        launch(st, ginfo, events[i])
-    torch.cuda.synchronize()
-    dur = {n: [] for n in names}
-    for ev in events:
-        for j, n in enumerate(names):
-            dur[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)   # microseconds
-
-    # host planner alone (native plan, no upload), for the record
+    # host planner alone (native plan into pinned staging + upload), for the record
     t1 = time.perf_counter()
     for i in range(50):
         st = sets[i % len(sets)]
-        sgg.lora_plan_segments(None, st["b"].req_slots, b0.num_loras, True, b0.max_chunk_size)
+        be.prepare_lora_batch(None, st["slots"], st["ranks"], st["scal"], is_decode=True)
     plan_us = (time.perf_counter() - t1) / 50 * 1e6
+    torch.cuda.synchronize()
 
     counts = [algo_counts(st["b"], st["proj"], st["A_emb"].shape[1]) for st in sets]
     per = {}
     for n in names:
-        avg = float(np.mean(dur[n]))
+        avg = dur[n]
         by = float(np.mean([c[n]["bytes"] for c in counts]))
         fl = float(np.mean([c[n]["flops"] for c in counts]))
-        per[n] = {"avg_us": round(avg, 3), "median_us": round(float(np.median(dur[n])), 3),
-                  "algo_bytes": int(by), "algo_flops": int(fl),
+        per[n] = {"avg_us": round(avg, 3), "algo_bytes": int(by), "algo_flops": int(fl),
                   "gbs": round(by / (avg * 1e-6) / 1e9, 1),
                   "tflops": round(fl / (avg * 1e-6) / 1e12, 3)}
     se_us = per["shrink"]["avg_us"] + per["expand"]["avg_us"]
     se_bytes = per["shrink"]["algo_bytes"] + per["expand"]["algo_bytes"]
     return {
-        "wall_s": graph_wall, "eager_wall_s": eager_wall, "tokens": b0.num_tokens,
-        "kernels": per, "plan_host_us": round(plan_us, 2),
+        "wall_s": eager_wall, "graph_wall_s": graph_wall, "tokens": b0.num_tokens,
+        "kernels": per, "prepare_host_us": round(plan_us, 2), "back_to_back": back_to_back,
         "shrink_expand": {"us": round(se_us, 3),
                           "gbs": round(se_bytes / (se_us * 1e-6) / 1e9, 1),
                           "hbm_frac": round(se_bytes / (se_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -356,7 +409,7 @@ def main():
     res = run_decode(args, device)
     ms = res["wall_s"] / args.steps * 1e3
     value = res["tokens"] * args.steps / res["wall_s"]
-    eager = res["tokens"] * args.steps / res["eager_wall_s"]
+    graph = res["tokens"] * args.steps / res["graph_wall_s"]
     k = res["kernels"]
     dom = max(("shrink", "expand", "embedding"), key=lambda n: k[n]["avg_us"])
     achieved = k[dom]["gbs"]
@@ -374,12 +427,15 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for(dom, "decode")},
-        "mode": "graph replay per step (host plan + one upload + captured kernels)",
-        "eager_tokens_per_s": round(eager, 1),
-        "eager_ms_per_step": round(res["eager_wall_s"] / args.steps * 1e3, 4),
+        "mode": "eager: host plan + one upload, embedding gather, lora_qkv (shrink+expand)",
+        "graph_tokens_per_s": round(graph, 1),
+        "graph_ms_per_step": round(res["graph_wall_s"] / args.steps * 1e3, 4),
         "kernels": k,
+        "kernel_timing": ("HIP events on the launch stream around one launch per step, "
+                          "back to back behind a delay kernel" + ("" if res["back_to_back"] else
+                                            " (WARNING: delay ended before enqueueing did)")),
         "shrink_expand": res["shrink_expand"],
-        "plan_host_us": res["plan_host_us"],
+        "prepare_host_us": res["prepare_host_us"],
     }
     if args.secondary:
         print("# prefill", file=sys.stderr, flush=True)

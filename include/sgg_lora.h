@@ -128,8 +128,9 @@ int64_t lora_plan_layout(int64_t token_capacity, int32_t seg_capacity, int32_t r
  * lora_plan_upload -- the batch plan (as lora_plan_segments, segment arrays
  * padded to seg_capacity) written into a pinned host staging buffer in the
  * layout above, together with the per-request slots and the per-slot rank
- * and scaling tables, followed by ONE asynchronous host-to-device copy of the
- * whole buffer to `device_plan` on `stream`.
+ * and scaling tables, followed by ONE asynchronous host-to-device transfer of
+ * the whole buffer to `device_plan` on `stream` (a copy kernel that reads the
+ * pinned buffer through its device mapping; a runtime copy if it has none).
  * (chunked_backend.py page: prepare_lora_batch, which plans on the host and
  *  copies the plan arrays to the device without blocking.)
  *

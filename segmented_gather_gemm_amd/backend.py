@@ -34,9 +34,15 @@ def _align(n, m=64):
 
 
 class _Staging:
-    """Ring of pinned int32 buffers, each guarded by the event of its last copy."""
+    """Ring of pinned int32 buffers, each guarded by the event of its last copy.
 
-    def __init__(self, slots=3):
+    A slot is reused only after the copy that last read it has completed.
+    The wait polls the event instead of blocking in the driver: a sleeping
+    wait wakes up tens of microseconds late, which a serving loop that plans
+    each batch while the previous one runs cannot afford.
+    """
+
+    def __init__(self, slots=8):
         self.bufs = [None] * slots
         self.events = [None] * slots
         self.i = 0
@@ -44,8 +50,10 @@ class _Staging:
     def take(self, n):
         i = self.i
         self.i = (i + 1) % len(self.bufs)
-        if self.events[i] is not None:
-            self.events[i].synchronize()
+        ev = self.events[i]
+        if ev is not None:
+            while not ev.query():
+                pass
         if self.bufs[i] is None or self.bufs[i].numel() < n:
             self.bufs[i] = torch.empty(max(n, 4096), dtype=torch.int32, pin_memory=True)
         return i, self.bufs[i]
@@ -126,6 +134,7 @@ class ChunkedSgmvLoRA:
         scal = np.ascontiguousarray(scalings, dtype=np.float32)
         stream = torch.cuda.current_stream(self.device)
         info = self._info_arr
+        # fast path below; NumPy int32 / float32 arrays avoid per-call conversion
         check(lib().lora_plan_upload(
             ctypes.cast(0, _P32) if lens is None else lens.ctypes.data_as(_P32),
             slots.ctypes.data_as(_P32), bs, ranks.ctypes.data_as(_P32),
@@ -177,9 +186,13 @@ class ChunkedSgmvLoRA:
         self._graph_dev = dev
         v = {name: dev[o:o + n] for name, (o, n) in zip(_NAMES, regions)}
         # Kernels see the capacity: num_segments = cap (padding segments are
-        # empty), num_tokens = max_tokens (activations are allocated for the
-        # capacity), and a tiling hint of the largest chunk any batch can use.
-        hint = max(MIN_CHUNK_SIZE, min(self.max_chunk_size, 128))
+        # empty) and num_tokens = max_tokens (activations are allocated for
+        # the capacity).
+        # typical segment length (tokens per adapter slot); longer segments
+        # are still covered, by the same workgroups looping
+        cap_chunk = max(MIN_CHUNK_SIZE, min(self.max_chunk_size, 128))
+        per_slot = -(-max_tokens // max(self.max_loras_per_batch, 1))
+        hint = max(MIN_CHUNK_SIZE, min(cap_chunk, -(-per_slot // 16) * 16))
         self.cuda_graph_batch_info = LoRABatchInfo(
             bs=max_bs_in_cuda_graph, num_tokens=max_tokens, num_segments=cap,
             max_len=hint, seg_indptr=v["seg_indptr"], weight_indices=v["seg_slots"],

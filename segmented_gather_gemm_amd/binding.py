@@ -51,7 +51,9 @@ def _vp(t):
 
 
 def _stream(device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    """Raw handle of torch's current stream on `device` (the launch stream)."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(idx))
 
 
 def _host_i32(values):
@@ -67,13 +69,13 @@ def _cpu_i32_ptr(t):
 
 
 def _need_bf16(name, t, dims):
-    if t.dtype != torch.bfloat16:
-        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a ROCm device")
-    if t.dim() != dims:
-        raise ValueError(f"{name} must have {dims} dimensions, got shape {tuple(t.shape)}")
-    if t.stride(-1) != 1:
+    if t.dtype is not torch.bfloat16 or not t.is_cuda or t.dim() != dims or t.stride(-1) != 1:
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a ROCm device")
+        if t.dim() != dims:
+            raise ValueError(f"{name} must have {dims} dimensions, got shape {tuple(t.shape)}")
         raise ValueError(f"{name} must have unit stride in its last dimension")
 
 
@@ -156,12 +158,23 @@ def default_workspace(device, nbytes):
     return ws
 
 
+_offset_cache = {}
+
+
 def _offsets(slice_offsets):
+    """Host int32 copy of the slice offsets (cached for lists and tuples)."""
+    key = tuple(slice_offsets) if isinstance(slice_offsets, (list, tuple)) else None
+    if key is not None:
+        hit = _offset_cache.get(key)
+        if hit is not None:
+            return hit
     if isinstance(slice_offsets, torch.Tensor):
         slice_offsets = slice_offsets.detach().to("cpu")  # host copy (synchronises if on device)
     arr, ptr = _host_i32(slice_offsets)
     if arr.ndim != 1 or len(arr) < 2:
         raise ValueError("slice_offsets needs at least two entries")
+    if key is not None and len(_offset_cache) < 256:
+        _offset_cache[key] = (arr, ptr)
     return arr, ptr
 
 

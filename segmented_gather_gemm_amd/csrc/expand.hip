@@ -17,6 +17,8 @@
 // Work order: each XCD takes a contiguous range of (segment, tile) items with
 // tiles fastest, so the workgroups resident on an XCD sweep whole rows of the
 // base tensor and share the segment's h rows and its adapter's B tiles in L2.
+// With few segments (e.g. a capacity-padded graph launch, whose trailing
+// segments are empty) segments are dealt round-robin to the XCDs instead.
 #include "sgg_device.h"
 #include "sgg_kernels.h"
 
@@ -40,9 +42,15 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int L = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int seg = L / p.total_tiles;
-  const int tile = L % p.total_tiles;
+  int seg, tile;
+  if (p.round_robin) {
+    segment_round_robin(blockIdx.x, p.total_tiles, &seg, &tile);
+    if (seg >= p.num_segments) return;
+  } else {
+    const int L = xcd_contiguous(blockIdx.x, gridDim.x);
+    seg = L / p.total_tiles;
+    tile = L % p.total_tiles;
+  }
 
   int k = 0;
   while (k + 1 < p.c && tile >= p.tile_start[k + 1]) ++k;
@@ -263,6 +271,32 @@ hipError_t launch_embedding(const EmbeddingParams& p, hipStream_t stream) {
   const int64_t grid = static_cast<int64_t>(p.num_segments) * p.parts;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(embedding_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- plan upload
+// Copies the plan from pinned host memory to the device plan buffer.  A plain
+// kernel on the caller's stream (system-scope loads, so each read sees the
+// host's latest writes): small host-to-device copies through the runtime
+// were seen to busy-wait on the host for the stream to drain.
+
+namespace {
+
+__global__ __launch_bounds__(256) void plan_copy_kernel(const int32_t* src, int32_t* dst, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+}  // namespace
+
+hipError_t launch_plan_copy(const int32_t* src_dev_view, int32_t* dst, int64_t n,
+                            hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 1023) / 1024;
+  if (blocks > 256) blocks = 256;
+  hipLaunchKernelGGL(plan_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     src_dev_view, dst, n);
   return hipGetLastError();
 }
 

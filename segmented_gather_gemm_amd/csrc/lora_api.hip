@@ -108,7 +108,7 @@ sgg::ExpandTiling choose_expand_tiling(const int32_t* offs, int c, int num_segme
   }
   tile_start[c] = acc;
   *total = acc;
-  t.grid = static_cast<int64_t>(acc) * num_segments;
+  t.grid = sgg::grid_for(num_segments, acc);
   return t;
 }
 
@@ -137,6 +137,7 @@ int do_shrink(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh, i
   p.partial = static_cast<float*>(partial);
   p.counters = counters;
   p.counter_cap = sgg::kCounterCap;
+  p.round_robin = num_segments < sgg::kRoundRobinBelow ? 1 : 0;
   p.seg_indptr = seg_indptr;
   p.seg_slots = seg_slots;
   p.perm = permutation;
@@ -187,6 +188,7 @@ int do_expand(const void* h, int64_t ldh, const void* B, int64_t N, void* out, i
   p.c = c;
   p.num_segments = num_segments;
   p.vec8 = vec8 ? 1 : 0;
+  p.round_robin = num_segments < sgg::kRoundRobinBelow ? 1 : 0;
   return launch_status(sgg::launch_expand(p, t, stream), "expand");
 }
 
@@ -391,8 +393,18 @@ extern "C" int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slot
     const int32_t len = h[off[1] + i + 1] - h[off[1] + i];
     longest = len > longest ? len : longest;
   }
-  const hipError_t e = hipMemcpyAsync(device_plan, host_staging, static_cast<size_t>(total) * 4,
-                                      hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+  // One transfer: a copy kernel reading the pinned buffer through its device
+  // mapping; a runtime copy only if the buffer has no device mapping.
+  void* src = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&src, host_staging, 0);
+  if (e == hipSuccess && src != nullptr) {
+    e = sgg::launch_plan_copy(static_cast<const int32_t*>(src), static_cast<int32_t*>(device_plan),
+                              total, static_cast<hipStream_t>(stream));
+  } else {
+    (void)hipGetLastError();  // clear the failed lookup
+    e = hipMemcpyAsync(device_plan, host_staging, static_cast<size_t>(total) * 4,
+                       hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+  }
   if (e != hipSuccess)
     return fail(SGG_ERR_HIP, "plan upload failed: %s", hipGetErrorString(e));
   out_info[0] = n_seg;

@@ -64,4 +64,15 @@ __device__ __forceinline__ int xcd_contiguous(int b, int G) {
   return x < r ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
 }
 
+// Segments dealt round-robin to the XCDs: block b (on XCD b % 8) takes
+// segment (b % 8) + 8 * ((b / 8) / per) and item (b / 8) % per of it, so the
+// items of one segment share an XCD and the first segments -- the real ones
+// when trailing segments are capacity padding -- spread over all XCDs.
+// Launch with 8 * ceil(num_segments / 8) * per blocks.
+__device__ __forceinline__ void segment_round_robin(int b, int per, int* seg, int* item) {
+  const int x = b % kXcds, local = b / kXcds;
+  *seg = x + kXcds * (local / per);
+  *item = local % per;
+}
+
 }  // namespace sgg

@@ -13,7 +13,9 @@
 // loading fragments straight from row-major x / A costs one L1 access per
 // lane.  Instead each chunk is fetched coalesced -- 8 lanes cover the 128
 // contiguous bytes of one row, 8 rows per load -- into registers, written to
-// the wave's own LDS tile, and read back in fragment layout.  Chunk slots in
+// the wave's own LDS tile, and read back in fragment layout.  Small tiles
+// fetch several chunks per round trip (about 128 tile rows' worth), so a
+// decode-sized K range is requested in one go.  Chunk slots in
 // the LDS tile are XOR-swizzled by (row / 2) so that both the row-wise writes
 // and the 16-row fragment reads hit 16 distinct bank groups.  The loads of
 // chunk t+1 are in flight while chunk t is staged and multiplied; every load
@@ -45,8 +47,9 @@ __global__ __launch_bounds__(256, 1) void shrink_kernel(ShrinkParams p) {
   constexpr int ROWS = BM + NB;          // tile rows per chunk: x rows, then A rows
   constexpr int LOADS = ROWS / 8;        // coalesced 16-byte loads per lane per chunk
   constexpr int XL = BM / 8;             // of which x rows
+  constexpr int CH = ROWS >= 128 ? 1 : 128 / ROWS;  // chunks fetched per round trip
   constexpr int ROUNDS = (NFR + kFragsPerRound - 1) / kFragsPerRound;
-  constexpr int STAGE_BYTES = 4 * ROWS * 128;
+  constexpr int STAGE_BYTES = 4 * CH * ROWS * 128;
   constexpr int RED_BYTES = 4 * kFragsPerRound * kWave * 16;
   __shared__ __attribute__((aligned(16))) char smem[STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES];
   __shared__ int last_flag;
@@ -55,14 +58,20 @@ __global__ __launch_bounds__(256, 1) void shrink_kernel(ShrinkParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  char* tile = smem + wave * ROWS * 128;
-  int L = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int mb0 = L % p.mblocks;
-  L /= p.mblocks;
-  const int seg = L % p.num_segments;
-  L /= p.num_segments;
-  const int nb = L % p.nblocks;
-  const int split = L / p.nblocks;
+  char* tile = smem + wave * CH * ROWS * 128;
+  int seg, item;
+  if (p.round_robin) {
+    segment_round_robin(blockIdx.x, p.mblocks * p.nblocks * p.ksplit, &seg, &item);
+    if (seg >= p.num_segments) return;
+  } else {
+    const int L = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int per = p.mblocks * p.nblocks * p.ksplit;
+    seg = L / per;
+    item = L % per;
+  }
+  const int mb0 = item % p.mblocks;
+  const int nb = (item / p.mblocks) % p.nblocks;
+  const int split = item / (p.mblocks * p.nblocks);
 
   // segment bounds, clamped to [0, s) so a malformed plan stays in bounds
   const int lo = max(p.seg_indptr[seg], 0);
@@ -133,44 +142,57 @@ __global__ __launch_bounds__(256, 1) void shrink_kernel(ShrinkParams p) {
     for (int i = 0; i < NFR; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (rho > 0 && nchunks > 0) {
-      // One register set of loads in flight: chunk t+1 is requested as soon
-      // as chunk t has been copied into the LDS tile, and arrives while chunk
-      // t is multiplied.
-      uint4 ld[LOADS];
+      // One register set of loads in flight: the CH chunks of stage t+1 are
+      // requested as soon as stage t has been copied into the LDS tiles, and
+      // arrive while stage t is multiplied.
+      const int nstages = (nchunks + CH - 1) / CH;
+      uint4 ld[CH][LOADS];
       auto issue = [&](int t) {
-        const int64_t k = kw + 256 * t + 8 * lcol;
-        const int64_t koff = (k <= p.K - 8 ? k : p.K - 8) - 8 * lcol;
 #pragma unroll
-        for (int i = 0; i < XL; ++i) ld[i] = load16(xlane + static_cast<int64_t>(xrow[i]) * p.ldx + koff);
+        for (int cc = 0; cc < CH; ++cc) {
+          const int64_t k = kw + 256 * (CH * t + cc) + 8 * lcol;
+          const int64_t koff = (k <= p.K - 8 ? k : p.K - 8) - 8 * lcol;
 #pragma unroll
-        for (int i = XL; i < LOADS; ++i) ld[i] = load16(aslot + static_cast<int64_t>(arow[i - XL]) * p.K + koff);
+          for (int i = 0; i < XL; ++i)
+            ld[cc][i] = load16(xlane + static_cast<int64_t>(xrow[i]) * p.ldx + koff);
+#pragma unroll
+          for (int i = XL; i < LOADS; ++i)
+            ld[cc][i] = load16(aslot + static_cast<int64_t>(arow[i - XL]) * p.K + koff);
+        }
       };
       issue(0);
-      for (int t = 0; t < nchunks; ++t) {
+      for (int t = 0; t < nstages; ++t) {
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i)
-          *reinterpret_cast<uint4*>(tile + swz(8 * i + lrow, lcol)) = ld[i];
-        if (t + 1 < nchunks) issue(t + 1);
-        const int64_t k0 = kw + 256 * t;
+        for (int cc = 0; cc < CH; ++cc)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int c = 4 * st + fgrp;
-          const bool kv = k0 + 8 * c < ke;
-          uint4 xv[MF], av[NF];
+          for (int i = 0; i < LOADS; ++i)
+            *reinterpret_cast<uint4*>(tile + cc * ROWS * 128 + swz(8 * i + lrow, lcol)) = ld[cc][i];
+        if (t + 1 < nstages) issue(t + 1);
 #pragma unroll
-          for (int f = 0; f < MF; ++f) {
-            const uint4 v = *reinterpret_cast<const uint4*>(tile + swz(16 * f + frow, c));
-            xv[f] = (kv && tvalid[f]) ? v : make_uint4(0, 0, 0, 0);
+        for (int cc = 0; cc < CH; ++cc) {
+          const int64_t k0 = kw + 256 * (CH * t + cc);
+          if (k0 >= ke) break;  // wave-uniform
+          const char* ct = tile + cc * ROWS * 128;
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const int c = 4 * st + fgrp;
+            const bool kv = k0 + 8 * c < ke;
+            uint4 xv[MF], av[NF];
+#pragma unroll
+            for (int f = 0; f < MF; ++f) {
+              const uint4 v = *reinterpret_cast<const uint4*>(ct + swz(16 * f + frow, c));
+              xv[f] = (kv && tvalid[f]) ? v : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int g = 0; g < NF; ++g) {
+              const uint4 v = *reinterpret_cast<const uint4*>(ct + swz(BM + 16 * g + frow, c));
+              av[g] = (kv && nvalid[g]) ? v : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int f = 0; f < MF; ++f)
+#pragma unroll
+              for (int g = 0; g < NF; ++g) acc[f * NF + g] = mfma16x16x32(av[g], xv[f], acc[f * NF + g]);
           }
-#pragma unroll
-          for (int g = 0; g < NF; ++g) {
-            const uint4 v = *reinterpret_cast<const uint4*>(tile + swz(BM + 16 * g + frow, c));
-            av[g] = (kv && nvalid[g]) ? v : make_uint4(0, 0, 0, 0);
-          }
-#pragma unroll
-          for (int f = 0; f < MF; ++f)
-#pragma unroll
-            for (int g = 0; g < NF; ++g) acc[f * NF + g] = mfma16x16x32(av[g], xv[f], acc[f * NF + g]);
         }
       }
     }
@@ -333,7 +355,7 @@ ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments
   t.kps = (kgroups + ksplit - 1) / ksplit * 256;
   t.ksplit = static_cast<int>((K + t.kps - 1) / t.kps);
   if (t.ksplit < 1) t.ksplit = 1;
-  t.grid = static_cast<int64_t>(t.ksplit) * t.nblocks * num_segments * t.mblocks;
+  t.grid = grid_for(num_segments, static_cast<int64_t>(t.ksplit) * t.nblocks * t.mblocks);
   if (t.ksplit > 1) t.partial_bytes = round_up(static_cast<int64_t>(t.ksplit) * s * CR * 4, 256);
   return t;
 }
