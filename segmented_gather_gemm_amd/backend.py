@@ -8,11 +8,14 @@ the plan in its host planner, the rest in its HIP kernels.
 
 Upload: the page copies six small host arrays to the device one by one.
 Here one native call (lora_plan_upload) plans straight into a pinned staging
-buffer and enqueues a single non-blocking host-to-device copy of all plan
-arrays and tables; the device arrays are views of one device buffer.  Staging
-buffers rotate through a small ring and are reused only after the copy that
-last read them has completed, so planning the next batch does not wait for
-the GPU.
+buffer and enqueues a single non-blocking host-to-device transfer of all plan
+arrays and tables; the device arrays are views of one device buffer.  Plan
+buffers (staging + device) rotate through a ring of 8 slots; a slot is reused
+only after the transfer that last read it has completed, so planning the next
+batch does not wait for the GPU.  A batch's device plan stays intact while
+fewer than 8 further batches have been prepared, or for as long as its
+kernels run on the stream it was prepared on (later uploads are ordered
+after them).
 """
 
 import ctypes
@@ -34,29 +37,40 @@ def _align(n, m=64):
 
 
 class _Staging:
-    """Ring of pinned int32 buffers, each guarded by the event of its last copy.
+    """Ring of plan buffers: pinned host staging plus a device plan buffer per
+    slot, each slot guarded by the event of its last upload.
 
-    A slot is reused only after the copy that last read it has completed.
-    The wait polls the event instead of blocking in the driver: a sleeping
-    wait wakes up tens of microseconds late, which a serving loop that plans
-    each batch while the previous one runs cannot afford.
+    A slot is reused only after the upload that last read its staging buffer
+    has completed.  Its device buffer is then rewritten by an upload enqueued
+    after every kernel launched before it on the same stream, so the kernels
+    of a batch read its plan intact as long as they run on the stream the
+    batch was prepared on.  The wait polls the event instead of blocking in
+    the driver: a sleeping wait wakes up tens of microseconds late, which a
+    serving loop that plans each batch while the previous one runs cannot
+    afford.
     """
 
-    def __init__(self, slots=8):
-        self.bufs = [None] * slots
+    def __init__(self, device, slots=8):
+        self.device = device
+        self.host = [None] * slots
+        self.dev = [None] * slots
         self.events = [None] * slots
+        self.infos = [{} for _ in range(slots)]   # layout key -> LoRABatchInfo views
         self.i = 0
 
     def take(self, n):
         i = self.i
-        self.i = (i + 1) % len(self.bufs)
+        self.i = (i + 1) % len(self.host)
         ev = self.events[i]
         if ev is not None:
             while not ev.query():
                 pass
-        if self.bufs[i] is None or self.bufs[i].numel() < n:
-            self.bufs[i] = torch.empty(max(n, 4096), dtype=torch.int32, pin_memory=True)
-        return i, self.bufs[i]
+        if self.host[i] is None or self.host[i].numel() < n:
+            size = max(n, 4096)
+            self.host[i] = torch.empty(size, dtype=torch.int32, pin_memory=True)
+            self.dev[i] = torch.empty(size, dtype=torch.int32, device=self.device)
+            self.infos[i] = {}
+        return i
 
     def done(self, i, stream):
         ev = self.events[i]
@@ -82,7 +96,7 @@ class ChunkedSgmvLoRA:
         self.cuda_graph_batch_info = None
         self._graph_dev = None
         self._graph_cap = None
-        self._staging = _Staging()
+        self._staging = _Staging(self.device)
         self._layouts = {}
         self._info_arr = (ctypes.c_int32 * 4)()
 
@@ -126,23 +140,22 @@ class ChunkedSgmvLoRA:
             min_chunk = chunk_size_override if chunk_size_override > 0 else MIN_CHUNK_SIZE
             seg_cap = B.lora_plan_max_segments(s, L, min_chunk)
             s_cap, req_cap = s, bs
+        key = (s_cap, seg_cap, req_cap)
         total, regions = self._layout(s_cap, seg_cap, req_cap)
-        ring, stage = self._staging.take(total)
-        dev = self._graph_dev if use_cuda_graph else torch.empty(
-            total, dtype=torch.int32, device=self.device)
+        stg = self._staging
+        ring = stg.take(total)
+        dev = self._graph_dev if use_cuda_graph else stg.dev[ring]
         ranks = np.ascontiguousarray(lora_ranks, dtype=np.int32)
         scal = np.ascontiguousarray(scalings, dtype=np.float32)
-        stream = torch.cuda.current_stream(self.device)
+        idx = self.device.index if self.device.index is not None else torch.cuda.current_device()
+        stream = torch._C._cuda_getCurrentRawStream(idx)
         info = self._info_arr
-        # fast path below; NumPy int32 / float32 arrays avoid per-call conversion
         check(lib().lora_plan_upload(
-            ctypes.cast(0, _P32) if lens is None else lens.ctypes.data_as(_P32),
-            slots.ctypes.data_as(_P32), bs, ranks.ctypes.data_as(_P32),
-            scal.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), L, 1 if is_decode else 0,
-            self.max_chunk_size, int(chunk_size_override), s_cap, seg_cap, req_cap,
-            ctypes.c_void_p(stage.data_ptr()), ctypes.c_void_p(dev.data_ptr()), 4 * total,
-            info, ctypes.c_void_p(stream.cuda_stream)))
-        self._staging.done(ring, stream)
+            None if lens is None else lens.ctypes.data, slots.ctypes.data, bs, ranks.ctypes.data,
+            scal.ctypes.data, L, 1 if is_decode else 0, self.max_chunk_size,
+            int(chunk_size_override), s_cap, seg_cap, req_cap, stg.host[ring].data_ptr(),
+            dev.data_ptr(), 4 * dev.numel(), info, stream))
+        stg.done(ring, torch.cuda.current_stream(self.device))
         n_seg, chunk, longest = info[0], info[1], info[2]
         if use_cuda_graph:
             # fixed views and launch shape: capacity segments over capacity tokens
@@ -151,17 +164,19 @@ class ChunkedSgmvLoRA:
             batch.planned_tokens = s
             self.batch_info = batch
             return batch
-        v = {name: dev[o:o + n] for name, (o, n) in zip(_NAMES, regions)}
-        batch = LoRABatchInfo(
-            bs=bs, num_tokens=s,
-            num_segments=seg_cap if use_cuda_graph else n_seg,
-            max_len=chunk,
-            seg_indptr=v["seg_indptr"], weight_indices=v["seg_slots"],
-            permutation=v["permutation"][:s], lora_ranks=v["ranks"],
-            scalings=v["scalings"].view(torch.float32),
-            req_seg_indptr=v["req_seg_indptr"][:bs + 1],
-            req_weight_indices=v["req_slots"][:bs], use_cuda_graph=use_cuda_graph,
-            max_seg_len=0 if use_cuda_graph else longest)
+        # eager: the slot's views for this layout are built once and reused
+        batch = stg.infos[ring].get(key)
+        if batch is None:
+            v = {name: dev[o:o + n] for name, (o, n) in zip(_NAMES, regions)}
+            batch = LoRABatchInfo(
+                bs=bs, num_tokens=s, num_segments=n_seg, max_len=chunk,
+                seg_indptr=v["seg_indptr"], weight_indices=v["seg_slots"],
+                permutation=v["permutation"], lora_ranks=v["ranks"],
+                scalings=v["scalings"].view(torch.float32),
+                req_seg_indptr=v["req_seg_indptr"], req_weight_indices=v["req_slots"],
+                use_cuda_graph=False, max_seg_len=longest)
+            stg.infos[ring][key] = batch
+        batch.num_segments, batch.max_len, batch.max_seg_len = n_seg, chunk, longest
         batch.planned_segments = n_seg
         batch.planned_tokens = s
         self.batch_info = batch

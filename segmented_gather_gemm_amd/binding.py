@@ -47,13 +47,14 @@ class LoRABatchInfo:
 
 
 def _vp(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    """Device address of a tensor (0 for None), passed as an integer."""
+    return t.data_ptr() if t is not None else 0
 
 
 def _stream(device):
     """Raw handle of torch's current stream on `device` (the launch stream)."""
     idx = device.index if device.index is not None else torch.cuda.current_device()
-    return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(idx))
+    return torch._C._cuda_getCurrentRawStream(idx)
 
 
 def _host_i32(values):
@@ -197,9 +198,12 @@ def lora_shrink(x, weights, batch_info: LoRABatchInfo, num_slices=1, out=None, w
     if out is None:
         out = torch.empty((s, CR), dtype=torch.bfloat16, device=x.device)
     _need_bf16("out", out, 2)
-    need = int(lib().lora_shrink_workspace_bytes(s, K, num_slices, R, batch_info.num_segments,
-                                                 batch_info.tile_hint))
-    ws = workspace if workspace is not None or need == 0 else default_workspace(x.device, need)
+    ws = workspace
+    if ws is None:   # the library checks the size of a caller's workspace itself
+        need = int(lib().lora_shrink_workspace_bytes(s, K, num_slices, R,
+                                                     batch_info.num_segments,
+                                                     batch_info.tile_hint))
+        ws = default_workspace(x.device, need) if need else None
     check(lib().lora_shrink(
         _vp(x), x.stride(0), _vp(weights), _vp(out), out.stride(0), s, K, L, num_slices, R,
         _vp(batch_info.seg_indptr), _vp(batch_info.weight_indices), batch_info.num_segments,
@@ -257,9 +261,11 @@ def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
     if base_output is None:
         base_output = torch.zeros((s, int(offs[-1])), dtype=torch.bfloat16, device=x.device)
     _need_bf16("base_output", base_output, 2)
-    need = int(lib().lora_qkv_workspace_bytes(s, K, c, R, batch_info.num_segments,
-                                              batch_info.tile_hint))
-    ws = workspace if workspace is not None else default_workspace(x.device, max(need, 1))
+    ws = workspace
+    if ws is None:   # the library checks the size of a caller's workspace itself
+        need = int(lib().lora_qkv_workspace_bytes(s, K, c, R, batch_info.num_segments,
+                                                  batch_info.tile_hint))
+        ws = default_workspace(x.device, max(need, 1))
     check(lib().lora_qkv(
         _vp(x), x.stride(0), _vp(A), _vp(B), N, _vp(base_output), base_output.stride(0), s, K,
         L, R, p_offs, c, int(max_slice_size), _vp(batch_info.seg_indptr),
