@@ -63,27 +63,35 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandParams p) {
   const int hi = min(static_cast<int64_t>(p.seg_indptr[seg + 1]), p.s);
   if (hi <= lo || colt >= colend) return;
   const int slot = p.seg_slots[seg];
-  int rho = (slot >= 0 && slot < p.L) ? p.ranks[slot] : 0;
-  rho = rho < 0 ? 0 : (rho > p.R ? p.R : rho);
-  if (rho == 0) return;  // base model: output rows stay untouched
-  const float sigma = p.scalings[slot];
+  const bool slot_ok = slot >= 0 && slot < p.L;
   const bool active = colw < colend;  // wave has columns (uniform); keeps joining barriers
   const int m = lane & 15;
   const int q = lane >> 4;
 
   // B fragments: fragment g row m is column colw + 16*g + m; rank chunk 8q + 32ks.
+  // Requested before the slot's rank arrives (every column j < R is in
+  // bounds); columns at or beyond the rank are zeroed once it is known.
   uint4 bw[2 * P][KS];
 #pragma unroll
   for (int g = 0; g < 2 * P; ++g) {
     const int n = colw + 16 * g + m;
-    const uint16_t* brow = p.B + (static_cast<int64_t>(slot) * p.N + (n < colend ? n : 0)) * p.R;
+    const uint16_t* brow =
+        p.B + (static_cast<int64_t>(slot_ok ? slot : 0) * p.N + (n < colend ? n : 0)) * p.R;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int j = 32 * ks + 8 * q;
       bw[g][ks] = make_uint4(0, 0, 0, 0);
-      if (active && n < colend && j < rho) bw[g][ks] = keep_first(load16(brow + j), rho - j);
+      if (active && n < colend && j < p.R) bw[g][ks] = load16(brow + j);
     }
   }
+  int rho = slot_ok ? p.ranks[slot] : 0;
+  rho = rho < 0 ? 0 : (rho > p.R ? p.R : rho);
+  if (rho == 0) return;  // base model: output rows stay untouched
+  const float sigma = p.scalings[slot];
+#pragma unroll
+  for (int g = 0; g < 2 * P; ++g)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bw[g][ks] = keep_first(bw[g][ks], rho - (32 * ks + 8 * q));
 
   // Base-row role of this lane: row (RPL*i + lane/LPR) of a 16-token group,
   // columns colw + 8*(lane%LPR) .. +7.
@@ -100,12 +108,32 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandParams p) {
       const int r = p.perm[c0 + tid];
       prow[tid] = (r >= 0 && r < p.s) ? r : -1;
     }
-    for (int piece = tid; piece < ntok * hch; piece += 256) {
-      const int row = piece / hch, c = piece % hch;
-      const int r = p.perm[c0 + row];
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r >= 0 && r < p.s) v = load16(p.h + static_cast<int64_t>(r) * p.ldh + k * p.R + 8 * c);
-      htile[row * CPR + (c ^ ((row / RPS) % CPR))] = v;
+    if (p.hpart) {
+      // split-K partials, indexed by sorted position: no gather needed
+      for (int piece = tid; piece < ntok * hch; piece += 256) {
+        const int row = piece / hch, c = piece % hch;
+        const float* src = p.hpart + static_cast<int64_t>(c0 + row) * p.ldp + k * p.R + 8 * c;
+        f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+        for (int sp = 0; sp < p.hsplit; ++sp) {
+          const float* q = src + static_cast<int64_t>(sp) * p.s * p.ldp;
+          s0 += *reinterpret_cast<const f32x4*>(q);
+          s1 += *reinterpret_cast<const f32x4*>(q + 4);
+        }
+        uint4 v;
+        v.x = f32_to_bf16(s0[0]) | (f32_to_bf16(s0[1]) << 16);
+        v.y = f32_to_bf16(s0[2]) | (f32_to_bf16(s0[3]) << 16);
+        v.z = f32_to_bf16(s1[0]) | (f32_to_bf16(s1[1]) << 16);
+        v.w = f32_to_bf16(s1[2]) | (f32_to_bf16(s1[3]) << 16);
+        htile[row * CPR + (c ^ ((row / RPS) % CPR))] = v;
+      }
+    } else {
+      for (int piece = tid; piece < ntok * hch; piece += 256) {
+        const int row = piece / hch, c = piece % hch;
+        const int r = p.perm[c0 + row];
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r >= 0 && r < p.s) v = load16(p.h + static_cast<int64_t>(r) * p.ldh + k * p.R + 8 * c);
+        htile[row * CPR + (c ^ ((row / RPS) % CPR))] = v;
+      }
     }
     __syncthreads();
     if (!active) continue;
@@ -282,10 +310,23 @@ hipError_t launch_embedding(const EmbeddingParams& p, hipStream_t stream) {
 
 namespace {
 
+// Each thread issues its four loads before any store, so a small plan costs
+// one host-memory round trip rather than one per element.
 __global__ __launch_bounds__(256) void plan_copy_kernel(const int32_t* src, int32_t* dst, int64_t n) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * 256)
-    dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  const int64_t step = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i0 < n; i0 += 4 * step) {
+    int32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * step;
+      v[u] = i < n ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * step;
+      if (i < n) dst[i] = v[u];
+    }
+  }
 }
 
 }  // namespace
@@ -294,7 +335,7 @@ hipError_t launch_plan_copy(const int32_t* src_dev_view, int32_t* dst, int64_t n
                             hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + 1023) / 1024;
-  if (blocks > 256) blocks = 256;
+  if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(plan_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                      src_dev_view, dst, n);
   return hipGetLastError();

@@ -121,7 +121,7 @@ int do_shrink(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh, i
               int64_t K, int32_t num_loras, int32_t c, int32_t R, const int32_t* seg_indptr,
               const int32_t* seg_slots, int32_t num_segments, const int32_t* permutation,
               const int32_t* lora_ranks, int32_t chunk_size, int32_t* counters,
-              void* partial, int64_t partial_avail, hipStream_t stream) {
+              void* partial, int64_t partial_avail, bool partials_only, hipStream_t stream) {
   const sgg::ShrinkTiling t = sgg::choose_shrink_tiling(s, K, c * R, num_segments, chunk_size);
   if (t.ksplit > 1) {
     SGG_CHECK(counters != nullptr && partial != nullptr && partial_avail >= t.partial_bytes,
@@ -154,6 +154,7 @@ int do_shrink(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh, i
   p.mblocks = t.mblocks;
   p.nblocks = t.nblocks;
   p.ksplit = t.ksplit;
+  p.partials_only = partials_only && t.ksplit > 1 ? 1 : 0;
   return launch_status(sgg::launch_shrink(p, t, stream), "shrink");
 }
 
@@ -161,7 +162,7 @@ int do_expand(const void* h, int64_t ldh, const void* B, int64_t N, void* out, i
               int64_t s, int32_t num_loras, int32_t R, const int32_t* offs, int32_t c,
               const int32_t* seg_indptr, const int32_t* seg_slots, int32_t num_segments,
               const int32_t* permutation, const int32_t* lora_ranks, const float* scalings,
-              hipStream_t stream) {
+              const float* hpart, int32_t hsplit, hipStream_t stream) {
   sgg::ExpandParams p{};
   const sgg::ExpandTiling t =
       choose_expand_tiling(offs, c, num_segments, R, p.tile_start, &p.total_tiles);
@@ -172,6 +173,9 @@ int do_expand(const void* h, int64_t ldh, const void* B, int64_t N, void* out, i
     vec8 = vec8 && offs[k] % 8 == 0;
   }
   p.h = static_cast<const uint16_t*>(h);
+  p.hpart = hpart;
+  p.hsplit = hpart ? hsplit : 0;
+  p.ldp = static_cast<int64_t>(c) * R;
   p.B = static_cast<const uint16_t*>(B);
   p.out = static_cast<uint16_t*>(out);
   p.seg_indptr = seg_indptr;
@@ -234,7 +238,7 @@ extern "C" int lora_shrink(const void* x, int64_t ldx, const void* A, void* h, i
                  static_cast<int32_t*>(workspace),
                  workspace && part_avail > 0 ? static_cast<char*>(workspace) + sgg::kCounterBytes
                                              : nullptr,
-                 part_avail, static_cast<hipStream_t>(stream));
+                 part_avail, false, static_cast<hipStream_t>(stream));
   return rc ? rc : sgg::ok();
 }
 
@@ -254,7 +258,7 @@ extern "C" int lora_expand(const void* h, int64_t ldh, const void* B, int64_t N,
   if (s == 0 || num_segments == 0 || slice_offsets[num_slices] == 0) return sgg::ok();
   rc = do_expand(h, ldh, B, N, base_output, ldo, s, num_loras, R, slice_offsets, num_slices,
                  seg_indptr, seg_slots, num_segments, permutation, lora_ranks, scalings,
-                 static_cast<hipStream_t>(stream));
+                 nullptr, 0, static_cast<hipStream_t>(stream));
   return rc ? rc : sgg::ok();
 }
 
@@ -287,18 +291,22 @@ extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B
   SGG_CHECK(workspace_bytes >= need, SGG_ERR_CAPACITY,
             "qkv workspace of %" PRId64 " bytes needed, %" PRId64 " given", need, workspace_bytes);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // Workspace: [split-K counters][h, s x c*R bf16][split-K partials]
+  // Workspace: [split-K counters][h, s x c*R bf16][split-K partials].  With
+  // K split, the expand sums the shrink's partials itself (h is not written).
   char* ws = static_cast<char*>(workspace);
   void* h = ws + sgg::kCounterBytes;
+  float* part = reinterpret_cast<float*>(ws + sgg::kCounterBytes + hbytes);
+  const int ksplit =
+      sgg::choose_shrink_tiling(s, in_dim, num_slices * R, num_segments, chunk_size).ksplit;
   rc = do_shrink(x, ldx, A, h, static_cast<int64_t>(num_slices) * R, s, in_dim, num_loras,
                  num_slices, R, seg_indptr, seg_slots, num_segments, permutation, lora_ranks,
-                 chunk_size, reinterpret_cast<int32_t*>(ws), ws + sgg::kCounterBytes + hbytes,
-                 workspace_bytes - sgg::kCounterBytes - hbytes, st);
+                 chunk_size, reinterpret_cast<int32_t*>(ws), part,
+                 workspace_bytes - sgg::kCounterBytes - hbytes, true, st);
   if (rc) return rc;
   if (slice_offsets[num_slices] == 0) return sgg::ok();
   rc = do_expand(h, static_cast<int64_t>(num_slices) * R, B, N, base_output, ldo, s, num_loras, R,
                  slice_offsets, num_slices, seg_indptr, seg_slots, num_segments, permutation,
-                 lora_ranks, scalings, st);
+                 lora_ranks, scalings, ksplit > 1 ? part : nullptr, ksplit, st);
   return rc ? rc : sgg::ok();
 }
 

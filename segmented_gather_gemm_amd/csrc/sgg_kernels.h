@@ -31,6 +31,7 @@ struct ShrinkParams {
   int32_t ksplit;             // K ranges (one workgroup each)
   int32_t counter_cap;        // entries in `counters`
   int32_t round_robin;        // segment-to-XCD mapping: 1 round-robin, 0 contiguous ranges
+  int32_t partials_only;      // ksplit > 1: leave the partials for the expand, write no h
 };
 
 // LoRA-B expand (scale, add into base) over the segments of a plan.
@@ -43,6 +44,12 @@ struct ExpandParams {
   const int32_t* perm;
   const int32_t* ranks;
   const float* scalings;
+  // Optional: h as the shrink's f32 split-K partials [hsplit][s][ldp], rows
+  // in sorted (plan) order; summed in split order and rounded to bf16 while
+  // staging, exactly as the shrink's own reduction would.  Null: read h.
+  const float* hpart;
+  int64_t ldp;
+  int32_t hsplit;
   int64_t ldh, ldo, s, N;
   int32_t L, R, c, num_segments;
   int32_t vec8;               // 16-byte base access is aligned for every group of 8 columns

@@ -25,7 +25,10 @@
 // When the segments alone cannot fill the GPU (decode batches) K is also
 // split across workgroups: each writes an f32 partial tile and bumps an
 // arrival counter; the last to arrive sums the partials in split order
-// (deterministic) and writes bf16 h, then resets the counter.
+// (deterministic) and writes bf16 h, then resets the counter.  In the
+// stacked shrink + expand the partials are instead left for the expand,
+// which sums them in the same order while staging h (no counters, no
+// cross-workgroup round trip here).
 #include "sgg_device.h"
 #include "sgg_internal.h"
 #include "sgg_kernels.h"
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(256, 1) void shrink_kernel(ShrinkParams p) {
         }
       }
     }
-    if (direct) continue;
+    if (direct || p.partials_only) continue;
 
     // Split-K: publish this partial, count arrivals, the last one reduces.
     // One release (thread 0, after the barrier that orders the whole
