@@ -21,6 +21,7 @@
 // segments are empty) segments are dealt round-robin to the XCDs instead.
 #include "sgg_device.h"
 #include "sgg_kernels.h"
+#include "expand_tile.h"
 
 namespace sgg {
 
@@ -28,192 +29,10 @@ namespace {
 
 template <int P, int KS>
 __global__ __launch_bounds__(256) void expand_kernel(ExpandParams p) {
-  constexpr int TNW = 32 * P;                  // columns per wave
-  constexpr int CPR = 4 * KS;                  // 16-byte chunks per LDS h row (R <= 32*KS)
-  constexpr int RPS = 16 / CPR > 0 ? 16 / CPR : 1;  // h rows sharing one swizzle value
-  constexpr int LPR = 4 * P;                   // lanes per base row segment (16 B each)
-  constexpr int RPL = 64 / LPR;                // base rows per wave load
-  constexpr int BLD = 16 / RPL;                // base loads per 16 tokens
-  constexpr int APAD = TNW + 4;                // floats per row of the transpose tile
-  __shared__ uint4 htile[128 * CPR];
-  __shared__ int prow[128];
-  __shared__ __attribute__((aligned(16))) float acct[4][16 * APAD];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  __shared__ __attribute__((aligned(16))) char smem[detail::ExpandShape<P, KS>::SMEM];
   int seg, tile;
-  if (p.round_robin) {
-    segment_round_robin(blockIdx.x, p.total_tiles, &seg, &tile);
-    if (seg >= p.num_segments) return;
-  } else {
-    const int L = xcd_contiguous(blockIdx.x, gridDim.x);
-    seg = L / p.total_tiles;
-    tile = L % p.total_tiles;
-  }
-
-  int k = 0;
-  while (k + 1 < p.c && tile >= p.tile_start[k + 1]) ++k;
-  const int colt = p.offs[k] + (tile - p.tile_start[k]) * (128 * P);
-  const int colw = colt + TNW * wave;
-  const int colend = p.offs[k + 1];
-
-  // segment bounds, clamped to [0, s) so a malformed plan stays in bounds
-  const int lo = max(p.seg_indptr[seg], 0);
-  const int hi = min(static_cast<int64_t>(p.seg_indptr[seg + 1]), p.s);
-  if (hi <= lo || colt >= colend) return;
-  const int slot = p.seg_slots[seg];
-  const bool slot_ok = slot >= 0 && slot < p.L;
-  const bool active = colw < colend;  // wave has columns (uniform); keeps joining barriers
-  const int m = lane & 15;
-  const int q = lane >> 4;
-
-  // B fragments: fragment g row m is column colw + 16*g + m; rank chunk 8q + 32ks.
-  // Requested before the slot's rank arrives (every column j < R is in
-  // bounds); columns at or beyond the rank are zeroed once it is known.
-  uint4 bw[2 * P][KS];
-#pragma unroll
-  for (int g = 0; g < 2 * P; ++g) {
-    const int n = colw + 16 * g + m;
-    const uint16_t* brow =
-        p.B + (static_cast<int64_t>(slot_ok ? slot : 0) * p.N + (n < colend ? n : 0)) * p.R;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int j = 32 * ks + 8 * q;
-      bw[g][ks] = make_uint4(0, 0, 0, 0);
-      if (active && n < colend && j < p.R) bw[g][ks] = load16(brow + j);
-    }
-  }
-  int rho = slot_ok ? p.ranks[slot] : 0;
-  rho = rho < 0 ? 0 : (rho > p.R ? p.R : rho);
-  if (rho == 0) return;  // base model: output rows stay untouched
-  const float sigma = p.scalings[slot];
-#pragma unroll
-  for (int g = 0; g < 2 * P; ++g)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bw[g][ks] = keep_first(bw[g][ks], rho - (32 * ks + 8 * q));
-
-  // Base-row role of this lane: row (RPL*i + lane/LPR) of a 16-token group,
-  // columns colw + 8*(lane%LPR) .. +7.
-  const int brw = lane / LPR;
-  const int bc = colw + 8 * (lane % LPR);
-  const bool bvec = p.vec8 && bc + 8 <= colend;
-  const int hch = p.R >> 3;  // 16-byte chunks of one h row slice
-  float* at = acct[wave];
-
-  for (int c0 = lo; c0 < hi; c0 += 128) {
-    const int ntok = hi - c0 < 128 ? hi - c0 : 128;
-    __syncthreads();  // previous chunk's tiles are no longer read
-    if (tid < ntok) {
-      const int r = p.perm[c0 + tid];
-      prow[tid] = (r >= 0 && r < p.s) ? r : -1;
-    }
-    if (p.hpart) {
-      // split-K partials, indexed by sorted position: no gather needed
-      for (int piece = tid; piece < ntok * hch; piece += 256) {
-        const int row = piece / hch, c = piece % hch;
-        const float* src = p.hpart + static_cast<int64_t>(c0 + row) * p.ldp + k * p.R + 8 * c;
-        f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-        for (int sp = 0; sp < p.hsplit; ++sp) {
-          const float* q = src + static_cast<int64_t>(sp) * p.s * p.ldp;
-          s0 += *reinterpret_cast<const f32x4*>(q);
-          s1 += *reinterpret_cast<const f32x4*>(q + 4);
-        }
-        uint4 v;
-        v.x = f32_to_bf16(s0[0]) | (f32_to_bf16(s0[1]) << 16);
-        v.y = f32_to_bf16(s0[2]) | (f32_to_bf16(s0[3]) << 16);
-        v.z = f32_to_bf16(s1[0]) | (f32_to_bf16(s1[1]) << 16);
-        v.w = f32_to_bf16(s1[2]) | (f32_to_bf16(s1[3]) << 16);
-        htile[row * CPR + (c ^ ((row / RPS) % CPR))] = v;
-      }
-    } else {
-      for (int piece = tid; piece < ntok * hch; piece += 256) {
-        const int row = piece / hch, c = piece % hch;
-        const int r = p.perm[c0 + row];
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r >= 0 && r < p.s) v = load16(p.h + static_cast<int64_t>(r) * p.ldh + k * p.R + 8 * c);
-        htile[row * CPR + (c ^ ((row / RPS) % CPR))] = v;
-      }
-    }
-    __syncthreads();
-    if (!active) continue;
-
-    const int nf = (ntok + 15) >> 4;
-    uint4 bv0[BLD], bv1[BLD];
-    auto fetch = [&](int f, uint4 (&bv)[BLD]) {
-#pragma unroll
-      for (int i = 0; i < BLD; ++i) {
-        const int rr = 16 * f + RPL * i + brw;
-        const int r = rr < ntok ? prow[rr] : -1;
-        bv[i] = make_uint4(0, 0, 0, 0);
-        if (r >= 0 && bvec)
-          bv[i] = *reinterpret_cast<const uint4*>(p.out + static_cast<int64_t>(r) * p.ldo + bc);
-      }
-    };
-    auto step = [&](int f, const uint4 (&bv)[BLD]) {
-      // h fragment: row 16f + m, rank chunk 8q + 32ks
-      const int hr = 16 * f + m;
-      const bool hv_ok = hr < ntok && prow[hr] >= 0;
-      uint4 hv[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int j = 32 * ks + 8 * q;
-        const int c = 4 * ks + q;
-        hv[ks] = make_uint4(0, 0, 0, 0);
-        if (hv_ok && j < rho) hv[ks] = keep_first(htile[hr * CPR + (c ^ ((hr / RPS) % CPR))], rho - j);
-      }
-#pragma unroll
-      for (int g = 0; g < 2 * P; ++g) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(bw[g][ks], hv[ks], acc);
-        *reinterpret_cast<f32x4*>(at + m * APAD + 16 * g + 4 * q) = acc;
-      }
-      // transposed read: 8 consecutive columns of one token per lane
-#pragma unroll
-      for (int i = 0; i < BLD; ++i) {
-        const int rl = RPL * i + brw;
-        const int rr = 16 * f + rl;
-        const int r = rr < ntok ? prow[rr] : -1;
-        if (r < 0 || bc >= colend) continue;
-        const float* src = at + rl * APAD + 8 * (lane % LPR);
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(src);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(src + 4);
-        uint16_t* dst = p.out + static_cast<int64_t>(r) * p.ldo + bc;
-        if (bvec) {
-          const uint4 b = bv[i];
-          uint4 o;
-          o.x = f32_to_bf16(bf16_to_f32(b.x & 0xffffu) + sigma * a0[0]) |
-                (f32_to_bf16(bf16_to_f32(b.x >> 16) + sigma * a0[1]) << 16);
-          o.y = f32_to_bf16(bf16_to_f32(b.y & 0xffffu) + sigma * a0[2]) |
-                (f32_to_bf16(bf16_to_f32(b.y >> 16) + sigma * a0[3]) << 16);
-          o.z = f32_to_bf16(bf16_to_f32(b.z & 0xffffu) + sigma * a1[0]) |
-                (f32_to_bf16(bf16_to_f32(b.z >> 16) + sigma * a1[1]) << 16);
-          o.w = f32_to_bf16(bf16_to_f32(b.w & 0xffffu) + sigma * a1[2]) |
-                (f32_to_bf16(bf16_to_f32(b.w >> 16) + sigma * a1[3]) << 16);
-          *reinterpret_cast<uint4*>(dst) = o;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (bc + e < colend) {
-              const float v = e < 4 ? a0[e & 3] : a1[e & 3];
-              const float y = bf16_to_f32(dst[e]) + sigma * v;
-              dst[e] = static_cast<uint16_t>(f32_to_bf16(y));
-            }
-          }
-        }
-      }
-    };
-    fetch(0, bv0);
-    for (int f = 0; f < nf; f += 2) {
-      if (f + 1 < nf) fetch(f + 1, bv1);
-      step(f, bv0);
-      if (f + 1 < nf) {
-        if (f + 2 < nf) fetch(f + 2, bv0);
-        step(f + 1, bv1);
-      }
-    }
-  }
+  if (!detail::expand_item_of(p, blockIdx.x, gridDim.x, &seg, &tile)) return;
+  detail::expand_tile<P, KS>(p, seg, tile, smem);
 }
 
 template <int P>

@@ -117,19 +117,12 @@ int launch_status(hipError_t e, const char* what) {
   return SGG_OK;
 }
 
-int do_shrink(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh, int64_t s,
-              int64_t K, int32_t num_loras, int32_t c, int32_t R, const int32_t* seg_indptr,
-              const int32_t* seg_slots, int32_t num_segments, const int32_t* permutation,
-              const int32_t* lora_ranks, int32_t chunk_size, int32_t* counters,
-              void* partial, int64_t partial_avail, bool partials_only, hipStream_t stream) {
-  const sgg::ShrinkTiling t = sgg::choose_shrink_tiling(s, K, c * R, num_segments, chunk_size);
-  if (t.ksplit > 1) {
-    SGG_CHECK(counters != nullptr && partial != nullptr && partial_avail >= t.partial_bytes,
-              SGG_ERR_CAPACITY, "shrink workspace too small: %" PRId64
-              " partial bytes needed, %" PRId64 " available", t.partial_bytes,
-              partial ? partial_avail : 0);
-  }
-  SGG_CHECK(t.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "shrink grid too large");
+sgg::ShrinkParams shrink_params(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh,
+                                int64_t s, int64_t K, int32_t num_loras, int32_t c, int32_t R,
+                                const int32_t* seg_indptr, const int32_t* seg_slots,
+                                int32_t num_segments, const int32_t* permutation,
+                                const int32_t* lora_ranks, int32_t* counters, void* partial,
+                                bool partials_only, const sgg::ShrinkTiling& t) {
   sgg::ShrinkParams p{};
   p.x = static_cast<const uint16_t*>(x);
   p.A = static_cast<const uint16_t*>(A);
@@ -155,18 +148,39 @@ int do_shrink(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh, i
   p.nblocks = t.nblocks;
   p.ksplit = t.ksplit;
   p.partials_only = partials_only && t.ksplit > 1 ? 1 : 0;
+  return p;
+}
+
+int do_shrink(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh, int64_t s,
+              int64_t K, int32_t num_loras, int32_t c, int32_t R, const int32_t* seg_indptr,
+              const int32_t* seg_slots, int32_t num_segments, const int32_t* permutation,
+              const int32_t* lora_ranks, int32_t chunk_size, int32_t* counters,
+              void* partial, int64_t partial_avail, hipStream_t stream) {
+  const sgg::ShrinkTiling t = sgg::choose_shrink_tiling(s, K, c * R, num_segments, chunk_size);
+  if (t.ksplit > 1) {
+    SGG_CHECK(counters != nullptr && partial != nullptr && partial_avail >= t.partial_bytes,
+              SGG_ERR_CAPACITY, "shrink workspace too small: %" PRId64
+              " partial bytes needed, %" PRId64 " available", t.partial_bytes,
+              partial ? partial_avail : 0);
+  }
+  SGG_CHECK(t.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "shrink grid too large");
+  const sgg::ShrinkParams p =
+      shrink_params(x, ldx, A, h, ldh, s, K, num_loras, c, R, seg_indptr, seg_slots,
+                    num_segments, permutation, lora_ranks, counters, partial, false, t);
   return launch_status(sgg::launch_shrink(p, t, stream), "shrink");
 }
 
-int do_expand(const void* h, int64_t ldh, const void* B, int64_t N, void* out, int64_t ldo,
-              int64_t s, int32_t num_loras, int32_t R, const int32_t* offs, int32_t c,
-              const int32_t* seg_indptr, const int32_t* seg_slots, int32_t num_segments,
-              const int32_t* permutation, const int32_t* lora_ranks, const float* scalings,
-              const float* hpart, int32_t hsplit, hipStream_t stream) {
+// Expand parameters; also fills the tiling.  `hpart` (may be null): h as the
+// shrink's split-K partials.
+sgg::ExpandParams expand_params(const void* h, int64_t ldh, const void* B, int64_t N, void* out,
+                                int64_t ldo, int64_t s, int32_t num_loras, int32_t R,
+                                const int32_t* offs, int32_t c, const int32_t* seg_indptr,
+                                const int32_t* seg_slots, int32_t num_segments,
+                                const int32_t* permutation, const int32_t* lora_ranks,
+                                const float* scalings, const float* hpart, int32_t hsplit,
+                                sgg::ExpandTiling* tiling) {
   sgg::ExpandParams p{};
-  const sgg::ExpandTiling t =
-      choose_expand_tiling(offs, c, num_segments, R, p.tile_start, &p.total_tiles);
-  SGG_CHECK(t.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "expand grid too large");
+  *tiling = choose_expand_tiling(offs, c, num_segments, R, p.tile_start, &p.total_tiles);
   bool vec8 = sgg::aligned16(out) && ldo % 8 == 0;
   for (int k = 0; k <= c; ++k) {
     p.offs[k] = offs[k];
@@ -193,6 +207,19 @@ int do_expand(const void* h, int64_t ldh, const void* B, int64_t N, void* out, i
   p.num_segments = num_segments;
   p.vec8 = vec8 ? 1 : 0;
   p.round_robin = num_segments < sgg::kRoundRobinBelow ? 1 : 0;
+  return p;
+}
+
+int do_expand(const void* h, int64_t ldh, const void* B, int64_t N, void* out, int64_t ldo,
+              int64_t s, int32_t num_loras, int32_t R, const int32_t* offs, int32_t c,
+              const int32_t* seg_indptr, const int32_t* seg_slots, int32_t num_segments,
+              const int32_t* permutation, const int32_t* lora_ranks, const float* scalings,
+              const float* hpart, int32_t hsplit, hipStream_t stream) {
+  sgg::ExpandTiling t{};
+  const sgg::ExpandParams p =
+      expand_params(h, ldh, B, N, out, ldo, s, num_loras, R, offs, c, seg_indptr, seg_slots,
+                    num_segments, permutation, lora_ranks, scalings, hpart, hsplit, &t);
+  SGG_CHECK(t.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "expand grid too large");
   return launch_status(sgg::launch_expand(p, t, stream), "expand");
 }
 
@@ -238,7 +265,7 @@ extern "C" int lora_shrink(const void* x, int64_t ldx, const void* A, void* h, i
                  static_cast<int32_t*>(workspace),
                  workspace && part_avail > 0 ? static_cast<char*>(workspace) + sgg::kCounterBytes
                                              : nullptr,
-                 part_avail, false, static_cast<hipStream_t>(stream));
+                 part_avail, static_cast<hipStream_t>(stream));
   return rc ? rc : sgg::ok();
 }
 
@@ -294,19 +321,27 @@ extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B
   // Workspace: [split-K counters][h, s x c*R bf16][split-K partials].  With
   // K split, the expand sums the shrink's partials itself (h is not written).
   char* ws = static_cast<char*>(workspace);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws);
   void* h = ws + sgg::kCounterBytes;
   float* part = reinterpret_cast<float*>(ws + sgg::kCounterBytes + hbytes);
-  const int ksplit =
-      sgg::choose_shrink_tiling(s, in_dim, num_slices * R, num_segments, chunk_size).ksplit;
-  rc = do_shrink(x, ldx, A, h, static_cast<int64_t>(num_slices) * R, s, in_dim, num_loras,
-                 num_slices, R, seg_indptr, seg_slots, num_segments, permutation, lora_ranks,
-                 chunk_size, reinterpret_cast<int32_t*>(ws), part,
-                 workspace_bytes - sgg::kCounterBytes - hbytes, true, st);
+  const int64_t CR = static_cast<int64_t>(num_slices) * R;
+  const sgg::ShrinkTiling ts = sgg::choose_shrink_tiling(s, in_dim, num_slices * R,
+                                                         num_segments, chunk_size);
+  SGG_CHECK(ts.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "shrink grid too large");
+  if (slice_offsets[num_slices] == 0) return sgg::ok();  // no output columns: nothing changes
+  const bool split = ts.ksplit > 1;
+  const sgg::ShrinkParams ps =
+      shrink_params(x, ldx, A, h, CR, s, in_dim, num_loras, num_slices, R, seg_indptr,
+                    seg_slots, num_segments, permutation, lora_ranks, counters, part, true, ts);
+  sgg::ExpandTiling te{};
+  const sgg::ExpandParams pe =
+      expand_params(h, CR, B, N, base_output, ldo, s, num_loras, R, slice_offsets, num_slices,
+                    seg_indptr, seg_slots, num_segments, permutation, lora_ranks, scalings,
+                    split ? part : nullptr, ts.ksplit, &te);
+  SGG_CHECK(te.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "expand grid too large");
+  rc = launch_status(sgg::launch_shrink(ps, ts, st), "shrink");
   if (rc) return rc;
-  if (slice_offsets[num_slices] == 0) return sgg::ok();
-  rc = do_expand(h, static_cast<int64_t>(num_slices) * R, B, N, base_output, ldo, s, num_loras, R,
-                 slice_offsets, num_slices, seg_indptr, seg_slots, num_segments, permutation,
-                 lora_ranks, scalings, ksplit > 1 ? part : nullptr, ksplit, st);
+  rc = launch_status(sgg::launch_expand(pe, te, st), "expand");
   return rc ? rc : sgg::ok();
 }
 

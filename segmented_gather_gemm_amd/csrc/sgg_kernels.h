@@ -99,6 +99,7 @@ struct ExpandTiling {
 hipError_t launch_shrink(const ShrinkParams& p, const ShrinkTiling& t, hipStream_t stream);
 hipError_t launch_expand(const ExpandParams& p, const ExpandTiling& t, hipStream_t stream);
 hipError_t launch_embedding(const EmbeddingParams& p, hipStream_t stream);
+
 // Copy n int32 from pinned host memory (given by its device-side address) to
 // device memory, as a kernel on `stream`.
 hipError_t launch_plan_copy(const int32_t* src_dev_view, int32_t* dst, int64_t n,

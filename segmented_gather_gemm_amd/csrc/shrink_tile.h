@@ -1,0 +1,280 @@
+// LoRA-A shrink work item (one tile of one segment) and its block mapping.
+// The algorithm is described at the top of shrink.hip.
+#pragma once
+
+#include "sgg_device.h"
+#include "sgg_kernels.h"
+
+namespace sgg {
+namespace detail {
+
+constexpr int kFragsPerRound = 8;  // accumulator fragments reduced per LDS round
+
+// Byte offset of 16-byte chunk c (0..7) of row r in a swizzled 128-byte-row tile.
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
+
+template <int MF, int NF>
+struct ShrinkShape {
+  static constexpr int BM = 16 * MF;
+  static constexpr int NB = 16 * NF;
+  static constexpr int NFR = MF * NF;
+  static constexpr int ROWS = BM + NB;          // tile rows per chunk: x rows, then A rows
+  static constexpr int LOADS = ROWS / 8;        // coalesced 16-byte loads per lane per chunk
+  static constexpr int XL = BM / 8;             // of which x rows
+  static constexpr int CH = ROWS >= 128 ? 1 : 128 / ROWS;  // chunks fetched per round trip
+  static constexpr int ROUNDS = (NFR + kFragsPerRound - 1) / kFragsPerRound;
+  static constexpr int STAGE_BYTES = 4 * CH * ROWS * 128;
+  static constexpr int RED_BYTES = 4 * kFragsPerRound * kWave * 16;
+  static constexpr int SMEM = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
+};
+
+// Work item of block b in a grid of G blocks: false for the padding blocks of
+// a round-robin grid.
+__device__ __forceinline__ bool shrink_item_of(const ShrinkParams& p, int b, int G, int* seg,
+                                               int* item) {
+  const int per = p.mblocks * p.nblocks * p.ksplit;
+  if (p.round_robin) {
+    segment_round_robin(b, per, seg, item);
+    return *seg < p.num_segments;
+  }
+  const int L = xcd_contiguous(b, G);
+  *seg = L / per;
+  *item = L % per;
+  return true;
+}
+
+// Tile `item` of segment `seg`; `smem` holds ShrinkShape<MF, NF>::SMEM bytes.
+// Every early return is uniform over the workgroup.
+template <int MF, int NF>
+__device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int seg, int item, char* smem,
+                                            int* last_flag_ptr) {
+  using S = ShrinkShape<MF, NF>;
+  constexpr int BM = S::BM;
+  constexpr int NB = S::NB;
+  constexpr int NFR = S::NFR;
+  constexpr int ROWS = S::ROWS;
+  constexpr int LOADS = S::LOADS;
+  constexpr int XL = S::XL;
+  constexpr int CH = S::CH;
+  constexpr int ROUNDS = S::ROUNDS;
+  int& last_flag = *last_flag_ptr;
+  f32x4 (*red)[kFragsPerRound][kWave] = reinterpret_cast<f32x4 (*)[kFragsPerRound][kWave]>(smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  char* tile = smem + wave * CH * ROWS * 128;
+  const int mb0 = item % p.mblocks;
+  const int nb = (item / p.mblocks) % p.nblocks;
+  const int split = item / (p.mblocks * p.nblocks);
+
+  // segment bounds, clamped to [0, s) so a malformed plan stays in bounds
+  const int lo = max(p.seg_indptr[seg], 0);
+  const int hi = min(static_cast<int64_t>(p.seg_indptr[seg + 1]), p.s);
+  if (hi <= lo) return;
+  const int slot = p.seg_slots[seg];
+  int rho = (slot >= 0 && slot < p.L) ? p.ranks[slot] : 0;
+  rho = rho < 0 ? 0 : (rho > p.R ? p.R : rho);
+  const int a = rho > 0 ? slot : 0;
+  if (rho == 0 && split != 0) return;  // split 0 alone writes the zero rows
+
+  const int64_t kb = static_cast<int64_t>(split) * p.kps;
+  const int64_t ke = kb + p.kps < p.K ? kb + p.kps : p.K;
+  // this wave's 64-deep chunks: k = kb + 64*(wave + 4*t)
+  const int64_t kw = kb + 64 * wave;
+  const int nchunks = kw < ke ? static_cast<int>((ke - kw + 255) / 256) : 0;
+
+  // Loading role of this lane: row (8*i + lane/8) of the chunk tile, 16-byte
+  // piece lane%8 of the row's 128 bytes.
+  const int lrow = lane >> 3;
+  const int lcol = lane & 7;
+  // Fragment role: row (lane%16) of a fragment, k group (lane/16).
+  const int frow = lane & 15;
+  const int fgrp = lane >> 4;
+
+  // A rows of this lane's loads (fixed for the workgroup); rows beyond the
+  // slot's rank or past c*R read row 0 of the slot (zeroed at the fragment read).
+  const uint16_t* aslot = p.A + static_cast<int64_t>(a) * p.CR * p.K + 8 * lcol;
+  int arow[LOADS - XL];
+#pragma unroll
+  for (int i = XL; i < LOADS; ++i) {
+    const int n = nb * NB + (8 * i + lrow - BM);
+    arow[i - XL] = (n < p.CR && (n % p.R) < rho) ? n : 0;
+  }
+  bool nvalid[NF];
+#pragma unroll
+  for (int g = 0; g < NF; ++g) {
+    const int n = nb * NB + 16 * g + frow;
+    nvalid[g] = n < p.CR && (n % p.R) < rho;
+  }
+  const uint16_t* xlane = p.x + 8 * lcol;
+
+  for (int mb = mb0; lo + mb * BM < hi; mb += p.mblocks) {
+    const int m0 = lo + mb * BM;
+    const int mcount = hi - m0 < BM ? hi - m0 : BM;
+
+    int xrow[XL];
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int mm = 8 * i + lrow;
+      const int r = mm < mcount ? p.perm[m0 + mm] : 0;
+      xrow[i] = (r >= 0 && r < p.s) ? r : 0;  // in-bounds stand-in, zeroed at the fragment read
+    }
+    bool tvalid[MF];
+#pragma unroll
+    for (int f = 0; f < MF; ++f) {
+      const int mm = 16 * f + frow;
+      bool ok = mm < mcount;
+      if (ok) {
+        const int r = p.perm[m0 + mm];
+        ok = r >= 0 && r < p.s;
+      }
+      tvalid[f] = ok;
+    }
+
+    f32x4 acc[NFR];
+#pragma unroll
+    for (int i = 0; i < NFR; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (rho > 0 && nchunks > 0) {
+      // One register set of loads in flight: the CH chunks of stage t+1 are
+      // requested as soon as stage t has been copied into the LDS tiles, and
+      // arrive while stage t is multiplied.
+      const int nstages = (nchunks + CH - 1) / CH;
+      uint4 ld[CH][LOADS];
+      auto issue = [&](int t) {
+#pragma unroll
+        for (int cc = 0; cc < CH; ++cc) {
+          const int64_t k = kw + 256 * (CH * t + cc) + 8 * lcol;
+          const int64_t koff = (k <= p.K - 8 ? k : p.K - 8) - 8 * lcol;
+#pragma unroll
+          for (int i = 0; i < XL; ++i)
+            ld[cc][i] = load16(xlane + static_cast<int64_t>(xrow[i]) * p.ldx + koff);
+#pragma unroll
+          for (int i = XL; i < LOADS; ++i)
+            ld[cc][i] = load16(aslot + static_cast<int64_t>(arow[i - XL]) * p.K + koff);
+        }
+      };
+      issue(0);
+      for (int t = 0; t < nstages; ++t) {
+#pragma unroll
+        for (int cc = 0; cc < CH; ++cc)
+#pragma unroll
+          for (int i = 0; i < LOADS; ++i)
+            *reinterpret_cast<uint4*>(tile + cc * ROWS * 128 + swz(8 * i + lrow, lcol)) = ld[cc][i];
+        if (t + 1 < nstages) issue(t + 1);
+#pragma unroll
+        for (int cc = 0; cc < CH; ++cc) {
+          const int64_t k0 = kw + 256 * (CH * t + cc);
+          if (k0 >= ke) break;  // wave-uniform
+          const char* ct = tile + cc * ROWS * 128;
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const int c = 4 * st + fgrp;
+            const bool kv = k0 + 8 * c < ke;
+            uint4 xv[MF], av[NF];
+#pragma unroll
+            for (int f = 0; f < MF; ++f) {
+              const uint4 v = *reinterpret_cast<const uint4*>(ct + swz(16 * f + frow, c));
+              xv[f] = (kv && tvalid[f]) ? v : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int g = 0; g < NF; ++g) {
+              const uint4 v = *reinterpret_cast<const uint4*>(ct + swz(BM + 16 * g + frow, c));
+              av[g] = (kv && nvalid[g]) ? v : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int f = 0; f < MF; ++f)
+#pragma unroll
+              for (int g = 0; g < NF; ++g) acc[f * NF + g] = mfma16x16x32(av[g], xv[f], acc[f * NF + g]);
+          }
+        }
+      }
+    }
+
+    // Sum the four waves' tiles through LDS, a few fragments per round, and
+    // emit 4 consecutive outputs of one token per (fragment, lane) item.
+    const bool direct = p.ksplit == 1 || rho == 0;
+#pragma unroll
+    for (int rd = 0; rd < ROUNDS; ++rd) {
+      __syncthreads();
+#pragma unroll
+      for (int fr = 0; fr < kFragsPerRound; ++fr) {
+        const int F = rd * kFragsPerRound + fr;
+        if (F < NFR) red[wave][fr][lane] = acc[F];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kFragsPerRound * kWave / 256; ++u) {
+        const int q = tid + 256 * u;
+        const int fr = q >> 6, l = q & 63;
+        const int F = rd * kFragsPerRound + fr;
+        if (F >= NFR) continue;
+        const int f = F / NF, g = F % NF;
+        const int mm = 16 * f + (l & 15);
+        const int n = nb * NB + 16 * g + 4 * (l >> 4);
+        if (mm >= mcount || n >= p.CR) continue;
+        const f32x4 v = red[0][fr][l] + red[1][fr][l] + red[2][fr][l] + red[3][fr][l];
+        if (direct) {
+          const int r = p.perm[m0 + mm];
+          if (r < 0 || r >= p.s) continue;
+          uint2 o;
+          o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+          o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+          *reinterpret_cast<uint2*>(p.h + static_cast<int64_t>(r) * p.ldh + n) = o;
+        } else {
+          // written through to the agent's coherence point (no dirty L2 lines)
+          float* dst = p.partial + (static_cast<int64_t>(split) * p.s + (m0 + mm)) * p.CR + n;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            __hip_atomic_store(dst + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    if (direct || p.partials_only) continue;
+
+    // Split-K: publish this partial, count arrivals, the last one reduces.
+    // One release (thread 0, after the barrier that orders the whole
+    // workgroup's partial stores before it) per workgroup, and one acquire
+    // in the last arriver only: agent-scope fences write back / invalidate
+    // the XCD's L2, so they are kept off every other path.
+    __syncthreads();
+    // (lo / BM + seg + mb) is distinct for every (segment, row block) of a
+    // CSR plan, so every tile has its own counter; the clamp only keeps a
+    // malformed plan in bounds.
+    int64_t cidx = (static_cast<int64_t>(lo / BM) + seg + mb) * p.nblocks + nb;
+    if (cidx >= p.counter_cap) cidx = p.counter_cap - 1;
+    if (tid == 0) {
+      const int old = __hip_atomic_fetch_add(p.counters + cidx, 1, __ATOMIC_RELEASE,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = old == p.ksplit - 1;
+      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      last_flag = last;
+    }
+    __syncthreads();
+    if (!last_flag) continue;
+    const int items = mcount * (NB / 4);
+    for (int q = tid; q < items; q += 256) {
+      const int mm = q / (NB / 4);
+      const int n = nb * NB + 4 * (q % (NB / 4));
+      if (n >= p.CR) continue;
+      const int r = p.perm[m0 + mm];
+      if (r < 0 || r >= p.s) continue;
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int sp = 0; sp < p.ksplit; ++sp) {
+        const float* src = p.partial + (static_cast<int64_t>(sp) * p.s + (m0 + mm)) * p.CR + n;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] += __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      uint2 o;
+      o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+      o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+      *reinterpret_cast<uint2*>(p.h + static_cast<int64_t>(r) * p.ldh + n) = o;
+    }
+    if (tid == 0) __hip_atomic_store(p.counters + cidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+}  // namespace detail
+}  // namespace sgg

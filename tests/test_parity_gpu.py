@@ -131,6 +131,42 @@ def test_decode_full():
     assert torch.equal(h2, h) and torch.equal(y2, y)
 
 
+@pytest.mark.parametrize("case", [
+    # (seed, tokens, slots, c, R, K): decode-like batches whose shrink splits K
+    (61, 256, 8, 3, 16, 4096),
+    (62, 40, 3, 3, 16, 2048),
+    (63, 64, 4, 2, 32, 4096),
+    (64, 96, 16, 1, 64, 4096),
+    (65, 24, 2, 4, 16, 1024),
+])
+def test_stacked_call_matches_separate_calls(case):
+    """lora_qkv on small batches (split K: the expand sums the shrink's
+    partials itself) gives the same bits as lora_shrink (whose last
+    arriving workgroup sums them) followed by lora_expand, matches the
+    oracle, and leaves the workspace counter region at zero."""
+    sgg = _sgg()
+    seed, s, L, c, R, K = case
+    rng = np.random.default_rng(seed)
+    slots = rng.integers(0, L, size=s).tolist()
+    width = [4096 if k == 0 else 1024 for k in range(c)] if K == 4096 else [512] * c
+    offs = np.concatenate([[0], np.cumsum(width)]).tolist()
+    b, proj, t = _small_case(seed, [1] * s, slots, L, [R] * L,
+                             rng.uniform(0.5, 2.0, size=L).tolist(), K, offs, R)
+    be = backend(b)
+    info = plan_on(be, b)
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    h = sgg.lora_shrink(x, A, info, c, workspace=ws)
+    y_sep = sgg.lora_expand(h, Bw, info, offs, max(width), base.clone())
+    _, want_y = oracle_forward(t, b, proj)
+    assert_close(y_sep, want_y, f"case {seed} separate")
+    for rep in range(3):
+        y = sgg.lora_qkv(x, A, Bw, info, offs, max(width), base.clone(), workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_sep), (seed, rep)
+        assert not ws[:32768].any(), (seed, rep)
+
+
 @pytest.fixture(scope="module")
 def prefill_data():
     b = draw_batch("prefill")
