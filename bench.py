@@ -11,11 +11,13 @@ beside it.  The headline workload is the decode batch: 256 one-token requests on
 8 adapters drawn uniformly, rank 16, stacked qkv 4096 -> [4096, 1024, 1024],
 bf16; the embedding gather uses vocab 128256 and rank 16.  Inputs rotate over
 48 independent sets (> the 256 MB MALL) so kernels read HBM, not cache.
+Every run also times the prefill gate_up workload (chunk cap 128).
 
 Prints ONE JSON line.  `value` is tokens/s of whole steps (wall clock over
 the timed steps, inputs resident in HBM); kernel durations come from HIP
 events on the stream the kernels run on.  `--secondary` adds the prefill
-gate_up workload (32 requests of 64..2048 tokens, rank 64, chunk 128).
+chunk sweep (16 / 32 / 64 / 128), the skewed batch (o_proj, down_proj) and
+the full Llama-3-8B-shaped layer sweep with the embedding gather.
 """
 
 import argparse
@@ -42,7 +44,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=48, help="rotated input sets")
-    ap.add_argument("--secondary", action="store_true", help="also time the prefill workload")
+    ap.add_argument("--secondary", action="store_true",
+                    help="also time the prefill chunk sweep, the skewed batch and the full "
+                         "layer sweep")
+    ap.add_argument("--full-layers", type=int, default=8,
+                    help="layers with distinct weights timed in the full layer sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -304,43 +310,136 @@ def run_decode(args, device):
     }
 
 
-def run_prefill(device, steps=20, warmup=3):
+def _rates(n_bytes, flops, us):
+    """GB/s, TFLOP/s and roofline fractions of one call of `us` microseconds.
+    fraction_of_attainable = max(bytes / HBM peak, flops / bf16 peak) / time."""
+    t = us * 1e-6
+    roof = max(n_bytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
+    return {"avg_us": round(us, 2), "gbs": round(n_bytes / t / 1e9, 1),
+            "hbm_frac": round(n_bytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(flops / t / 1e12, 2),
+            "mfma_frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "fraction_of_attainable": round(roof / t, 4)}
+
+
+def measure_projection(device, b, proj, t, max_chunk, steps, warmup, emb_rank=16):
+    """Events around each call, `steps` times after `warmup`: the shrink, the
+    expand and (stacked projections) the stacked call, on one planned batch.
+    Inputs: `t` = device tensors x, A, B, base of the projection."""
     import torch
     import segmented_gather_gemm_amd as sgg
-    from synth import draw_batch, draw_projection
 
-    b = draw_batch("prefill", max_chunk_size=128)
-    proj = b.projections[0]
-    t = {k: v.to(device) for k, v in draw_projection(b, proj).items()}
-    be = sgg.ChunkedSgmvLoRA(b.num_loras, 128, device)
-    info = be.prepare_lora_batch(b.seq_lens, b.req_slots, b.lora_ranks, b.scalings)
+    be = sgg.ChunkedSgmvLoRA(b.num_loras, max_chunk, device)
+    info = be.prepare_lora_batch(None if b.is_decode else b.seq_lens, b.req_slots,
+                                 b.lora_ranks, b.scalings, is_decode=b.is_decode)
+    c = proj.num_slices
     h = torch.empty((b.num_tokens, t["A"].shape[1]), dtype=torch.bfloat16, device=device)
+    ws = torch.zeros(256 << 20, dtype=torch.uint8, device=device)
     stream = torch.cuda.current_stream(device)
-    for _ in range(warmup):
-        sgg.lora_shrink(t["x"], t["A"], info, 2, out=h)
-        sgg.lora_expand(h, t["B"], info, proj.slice_offsets, proj.max_slice, t["base"])
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record(stream)
-        sgg.lora_shrink(t["x"], t["A"], info, 2, out=h)
-        ev[i][1].record(stream)
-        sgg.lora_expand(h, t["B"], info, proj.slice_offsets, proj.max_slice, t["base"])
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    c = algo_counts(b, proj, 16)
-    out = {"workload": "prefill gate_up, 32 requests (s=%d), 32 adapters Zipf(1.1), r=64, "
-                       "4096 -> 2x14336, chunk 128" % b.num_tokens}
-    for j, n in enumerate(("shrink", "expand")):
-        us = float(np.mean([e[j].elapsed_time(e[j + 1]) * 1e3 for e in ev]))
-        by, fl = c[n]["bytes"], c[n]["flops"]
-        out[n] = {"avg_us": round(us, 2), "gbs": round(by / (us * 1e-6) / 1e9, 1),
-                  "hbm_frac": round(by / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                  "tflops": round(fl / (us * 1e-6) / 1e12, 2),
-                  "mfma_frac": round(fl / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    calls = {
+        "shrink": lambda: sgg.lora_shrink(t["x"], t["A"], info, c, out=h, workspace=ws),
+        "expand": lambda: sgg.lora_expand(h, t["B"], info, proj.slice_offsets, proj.max_slice,
+                                          t["base"]),
+    }
+    if c > 1:
+        calls["stacked"] = lambda: sgg.lora_qkv(t["x"], t["A"], t["B"], info,
+                                                proj.slice_offsets, proj.max_slice, t["base"],
+                                                workspace=ws)
+    cnt = algo_counts(b, proj, emb_rank)
+    cnt["stacked"] = {k: cnt["shrink"][k] + cnt["expand"][k] for k in ("bytes", "flops")}
+    out = {"tokens": b.num_tokens, "segments": info.num_segments, "chunk": info.max_len}
+    for name, fn in calls.items():
+        for _ in range(warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]))
+        out[name] = _rates(cnt[name]["bytes"], cnt[name]["flops"], us)
     tot = out["shrink"]["avg_us"] + out["expand"]["avg_us"]
     out["tokens_per_s"] = round(b.num_tokens / (tot * 1e-6), 1)
     return out
+
+
+def _to(device, d):
+    return {k: v.to(device) for k, v in d.items()}
+
+
+def run_prefill(device, chunks=(128,), steps=20, warmup=3):
+    """Prefill gate_up (32 requests of 64..2048 tokens, 32 adapters Zipf(1.1),
+    r=64, 4096 -> 2 x 14336), one entry per server chunk cap."""
+    from synth import draw_batch, draw_projection
+    res = {}
+    t = None
+    for mc in chunks:
+        b = draw_batch("prefill", max_chunk_size=mc)
+        proj = b.projections[0]
+        if t is None:
+            t = _to(device, draw_projection(b, proj))
+        res[f"chunk{mc}"] = measure_projection(device, b, proj, t, mc, steps, warmup)
+    res["workload"] = ("prefill gate_up, 32 requests (s=%d), 32 adapters Zipf(1.1), r=64, "
+                       "4096 -> 2x14336" % b.num_tokens)
+    return res
+
+
+def run_skewed(device, steps=20, warmup=3):
+    """Skewed mixed batch: 8192 tokens, 90 % on one adapter, ranks 8..64 padded
+    to 64 (NaN padding), o_proj 4096 -> 4096 and down_proj 14336 -> 4096."""
+    from synth import draw_batch, draw_projection
+    b = draw_batch("skewed")
+    res = {"workload": "skewed: s=8192, 128 adapters, 90 % on one, ranks {8,16,32,64} "
+                       "padded to 64"}
+    for pi, proj in enumerate(b.projections):
+        t = _to(device, draw_projection(b, proj, proj_index=pi))
+        res[proj.name] = measure_projection(device, b, proj, t, b.max_chunk_size, steps, warmup)
+        del t
+    return res
+
+
+def run_full(device, layers, steps=5, warmup=1):
+    """Full layer sweep, Llama-3-8B shapes: per layer qkv, o, gate_up, down
+    over 4288 tokens (192 decode + 8 x 512), 64 adapters r=32.  `layers`
+    layers with distinct weights are timed; the per-layer figure is their
+    mean and the 32-layer figure is 32 x that mean."""
+    import torch
+    from synth import draw_batch, draw_embedding, draw_projection
+    import segmented_gather_gemm_amd as sgg
+    b = draw_batch("full")
+    per = {p.name: [] for p in b.projections}
+    for layer in range(layers):
+        for pi, proj in enumerate(b.projections):
+            t = _to(device, draw_projection(b, proj, layer=layer, proj_index=pi))
+            m = measure_projection(device, b, proj, t, b.max_chunk_size, steps, warmup)
+            per[proj.name].append(m["stacked"]["avg_us"] if proj.num_slices > 1 else
+                                  m["shrink"]["avg_us"] + m["expand"]["avg_us"])
+            del t
+    layer_us = float(sum(np.mean(v) for v in per.values()))
+    cnts = [algo_counts(b, p, 16) for p in b.projections]
+    layer_bytes = sum(c["shrink"]["bytes"] + c["expand"]["bytes"] for c in cnts)
+    layer_flops = sum(c["shrink"]["flops"] + c["expand"]["flops"] for c in cnts)
+    # embedding gather over the same plan
+    ids, A_emb = draw_embedding(b)
+    ids, A_emb = ids.to(device), A_emb.to(device)
+    be = sgg.ChunkedSgmvLoRA(b.num_loras, b.max_chunk_size, device)
+    info = be.prepare_lora_batch(b.seq_lens, b.req_slots, b.lora_ranks, b.scalings)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sgg.lora_a_embedding(ids, A_emb, info, b.vocab_size)
+    e0.record()
+    for _ in range(20):
+        sgg.lora_a_embedding(ids, A_emb, info, b.vocab_size)
+    e1.record()
+    torch.cuda.synchronize()
+    emb_us = e0.elapsed_time(e1) * 1e3 / 20
+    return {"workload": "full layer sweep: Llama-3-8B shapes, 4288 tokens, 64 adapters r=32; "
+                        f"{layers} layers with distinct weights timed",
+            "per_layer_us": {k: round(float(np.mean(v)), 2) for k, v in per.items()},
+            "layer": _rates(layer_bytes, layer_flops, layer_us),
+            "layers32_ms": round(32 * layer_us / 1e3, 3),
+            "tokens_per_s_32_layers": round(b.num_tokens / (32 * layer_us * 1e-6), 1),
+            "embedding_us": round(emb_us, 2)}
 
 
 def copy_probe(device):
@@ -441,9 +540,13 @@ def main():
         "shrink_expand": res["shrink_expand"],
         "prepare_host_us": res["prepare_host_us"],
     }
+    print("# prefill", file=sys.stderr, flush=True)
+    line["prefill"] = run_prefill(device, (16, 32, 64, 128) if args.secondary else (128,))
     if args.secondary:
-        print("# prefill", file=sys.stderr, flush=True)
-        line["prefill"] = run_prefill(device)
+        print("# skewed", file=sys.stderr, flush=True)
+        line["skewed"] = run_skewed(device)
+        print("# full layer sweep", file=sys.stderr, flush=True)
+        line["full"] = run_full(device, args.full_layers)
     if not args.no_cpu:
         print("# cpu baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
