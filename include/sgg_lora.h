@@ -117,10 +117,18 @@ int64_t lora_plan_max_segments(int64_t num_tokens, int32_t max_loras, int32_t mi
  *   2 seg_slots [seg_capacity]         3 req_seg_indptr [req_capacity + 1]
  *   4 req_slots [req_capacity]         5 lora_ranks [max_loras]
  *   6 scalings [max_loras] (float32 bits)
- * lora_plan_layout writes the 7 element offsets to offsets[0..6] and returns
+ *   7 work_indptr [seg_capacity + 1]   8 work_slots [seg_capacity]
+ * lora_plan_layout writes the 9 element offsets to offsets[0..8] and returns
  * the total element count (host only; -1 for negative sizes).
  */
-#define SGG_PLAN_REGIONS 7
+#define SGG_PLAN_REGIONS 9
+/* Work segments (regions 7, 8): the plan's segments with consecutive
+ * segments of one slot merged while the merged length stays within
+ * max(chunk_size, SGG_WORK_SEGMENT_TOKENS).  They partition the same sorted
+ * positions, so any kernel call gives the same result with them as with the
+ * plan's segments; with short chunks they let a workgroup reuse an adapter's
+ * weights across more tokens. */
+#define SGG_WORK_SEGMENT_TOKENS 128
 int64_t lora_plan_layout(int64_t token_capacity, int32_t seg_capacity, int32_t req_capacity,
                          int32_t max_loras, int64_t* offsets);
 
@@ -140,8 +148,11 @@ int64_t lora_plan_layout(int64_t token_capacity, int32_t seg_capacity, int32_t r
  *   device_plan    device memory of buffer_bytes bytes.
  *   buffer_bytes   at least 4 * lora_plan_layout(...).
  *   lora_ranks, scalings  host arrays of max_loras entries.
- *   out_info[4]    host out: num_segments, chunk_size, longest segment,
- *                  num_tokens.
+ *   out_info[6]    host out: num_segments, chunk_size, longest segment,
+ *                  num_tokens, number of work segments, longest work segment.
+ * Segment and work-segment arrays are padded to seg_capacity with empty
+ * segments of slot 0 (chunked_backend.py page: the CUDA-graph branch of
+ * prepare_lora_batch pads the same way).
  * Errors as lora_plan_segments, plus SGG_ERR_CAPACITY when the batch exceeds
  * a capacity and SGG_ERR_HIP when the copy cannot be enqueued.
  */

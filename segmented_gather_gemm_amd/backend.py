@@ -80,7 +80,7 @@ class _Staging:
 
 
 _NAMES = ("permutation", "seg_indptr", "seg_slots", "req_seg_indptr", "req_slots", "ranks",
-          "scalings")
+          "scalings", "work_indptr", "work_slots")
 
 
 class ChunkedSgmvLoRA:
@@ -98,18 +98,18 @@ class ChunkedSgmvLoRA:
         self._graph_cap = None
         self._staging = _Staging(self.device)
         self._layouts = {}
-        self._info_arr = (ctypes.c_int32 * 4)()
+        self._info_arr = (ctypes.c_int32 * 6)()
 
     # ---------------------------------------------------------------- plan
     def _layout(self, s_cap, seg_cap, req_cap):
         key = (s_cap, seg_cap, req_cap)
         lay = self._layouts.get(key)
         if lay is None:
-            offs = (ctypes.c_int64 * 7)()
+            offs = (ctypes.c_int64 * len(_NAMES))()
             total = int(lib().lora_plan_layout(s_cap, seg_cap, req_cap, self.max_loras_per_batch,
                                                offs))
             sizes = (s_cap, seg_cap + 1, seg_cap, req_cap + 1, req_cap,
-                     self.max_loras_per_batch, self.max_loras_per_batch)
+                     self.max_loras_per_batch, self.max_loras_per_batch, seg_cap + 1, seg_cap)
             lay = (total, [(int(o), n) for o, n in zip(offs, sizes)])
             self._layouts[key] = lay
         return lay
@@ -156,7 +156,7 @@ class ChunkedSgmvLoRA:
             int(chunk_size_override), s_cap, seg_cap, req_cap, stg.host[ring].data_ptr(),
             dev.data_ptr(), 4 * dev.numel(), info, stream))
         stg.done(ring, torch.cuda.current_stream(self.device))
-        n_seg, chunk, longest = info[0], info[1], info[2]
+        n_seg, chunk, longest, n_work, longest_work = info[0], info[1], info[2], info[4], info[5]
         if use_cuda_graph:
             # fixed views and launch shape: capacity segments over capacity tokens
             batch = self.cuda_graph_batch_info
@@ -174,9 +174,11 @@ class ChunkedSgmvLoRA:
                 permutation=v["permutation"], lora_ranks=v["ranks"],
                 scalings=v["scalings"].view(torch.float32),
                 req_seg_indptr=v["req_seg_indptr"], req_weight_indices=v["req_slots"],
-                use_cuda_graph=False, max_seg_len=longest)
+                use_cuda_graph=False, max_seg_len=longest, work_indptr=v["work_indptr"],
+                work_slots=v["work_slots"], num_work_segments=n_work, max_work_len=longest_work)
             stg.infos[ring][key] = batch
         batch.num_segments, batch.max_len, batch.max_seg_len = n_seg, chunk, longest
+        batch.num_work_segments, batch.max_work_len = n_work, longest_work
         batch.planned_segments = n_seg
         batch.planned_tokens = s
         self.batch_info = batch
@@ -213,7 +215,9 @@ class ChunkedSgmvLoRA:
             max_len=hint, seg_indptr=v["seg_indptr"], weight_indices=v["seg_slots"],
             permutation=v["permutation"], lora_ranks=v["ranks"],
             scalings=v["scalings"].view(torch.float32), req_seg_indptr=v["req_seg_indptr"],
-            req_weight_indices=v["req_slots"], use_cuda_graph=True, max_seg_len=hint)
+            req_weight_indices=v["req_slots"], use_cuda_graph=True, max_seg_len=hint,
+            work_indptr=v["work_indptr"], work_slots=v["work_slots"], num_work_segments=cap,
+            max_work_len=hint)
         return self.cuda_graph_batch_info
 
     # -------------------------------------------------------------- kernels

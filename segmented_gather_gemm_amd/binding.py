@@ -39,11 +39,25 @@ class LoRABatchInfo:
     req_weight_indices: Optional[torch.Tensor] = None
     use_cuda_graph: bool = False
     max_seg_len: int = 0          # longest planned segment (0: unknown, use max_len)
+    # Work segments (optional): the same sorted positions with consecutive
+    # segments of one slot merged (lora_plan_upload); kernels run over them
+    # when present, with the same results.
+    work_indptr: Optional[torch.Tensor] = None
+    work_slots: Optional[torch.Tensor] = None
+    num_work_segments: int = 0
+    max_work_len: int = 0
 
     @property
     def tile_hint(self):
         """Upper bound on segment length handed to the kernels for tiling."""
         return self.max_seg_len if self.max_seg_len > 0 else self.max_len
+
+    def kernel_segments(self):
+        """(indptr, slots, count, tile hint) of the segmentation the kernels run over."""
+        if self.work_indptr is not None:
+            hint = self.max_work_len if self.max_work_len > 0 else self.tile_hint
+            return self.work_indptr, self.work_slots, self.num_work_segments, hint
+        return self.seg_indptr, self.weight_indices, self.num_segments, self.tile_hint
 
 
 def _vp(t):
@@ -198,16 +212,14 @@ def lora_shrink(x, weights, batch_info: LoRABatchInfo, num_slices=1, out=None, w
     if out is None:
         out = torch.empty((s, CR), dtype=torch.bfloat16, device=x.device)
     _need_bf16("out", out, 2)
+    ind, sl, nseg, hint = batch_info.kernel_segments()
     ws = workspace
     if ws is None:   # the library checks the size of a caller's workspace itself
-        need = int(lib().lora_shrink_workspace_bytes(s, K, num_slices, R,
-                                                     batch_info.num_segments,
-                                                     batch_info.tile_hint))
+        need = int(lib().lora_shrink_workspace_bytes(s, K, num_slices, R, nseg, hint))
         ws = default_workspace(x.device, need) if need else None
     check(lib().lora_shrink(
         _vp(x), x.stride(0), _vp(weights), _vp(out), out.stride(0), s, K, L, num_slices, R,
-        _vp(batch_info.seg_indptr), _vp(batch_info.weight_indices), batch_info.num_segments,
-        _vp(batch_info.permutation), _vp(batch_info.lora_ranks), batch_info.tile_hint,
+        _vp(ind), _vp(sl), nseg, _vp(batch_info.permutation), _vp(batch_info.lora_ranks), hint,
         _vp(ws), ws.numel() if ws is not None else 0, _stream(x.device)))
     return out
 
@@ -232,12 +244,11 @@ def lora_expand(h, weights, batch_info: LoRABatchInfo, slice_offsets, max_slice_
     _need_bf16("base_output", base_output, 2)
     if base_output.shape[0] != s:
         raise ValueError("base_output rows differ from h rows")
+    ind, sl, nseg, hint = batch_info.kernel_segments()
     check(lib().lora_expand(
         _vp(h), h.stride(0), _vp(weights), N, _vp(base_output), base_output.stride(0), s, L, R,
-        p_offs, c, int(max_slice_size), _vp(batch_info.seg_indptr),
-        _vp(batch_info.weight_indices), batch_info.num_segments, _vp(batch_info.permutation),
-        _vp(batch_info.lora_ranks), _vp(batch_info.scalings), batch_info.tile_hint,
-        _stream(h.device)))
+        p_offs, c, int(max_slice_size), _vp(ind), _vp(sl), nseg, _vp(batch_info.permutation),
+        _vp(batch_info.lora_ranks), _vp(batch_info.scalings), hint, _stream(h.device)))
     return base_output
 
 
@@ -261,17 +272,16 @@ def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
     if base_output is None:
         base_output = torch.zeros((s, int(offs[-1])), dtype=torch.bfloat16, device=x.device)
     _need_bf16("base_output", base_output, 2)
+    ind, sl, nseg, hint = batch_info.kernel_segments()
     ws = workspace
     if ws is None:   # the library checks the size of a caller's workspace itself
-        need = int(lib().lora_qkv_workspace_bytes(s, K, c, R, batch_info.num_segments,
-                                                  batch_info.tile_hint))
+        need = int(lib().lora_qkv_workspace_bytes(s, K, c, R, nseg, hint))
         ws = default_workspace(x.device, max(need, 1))
     check(lib().lora_qkv(
         _vp(x), x.stride(0), _vp(A), _vp(B), N, _vp(base_output), base_output.stride(0), s, K,
-        L, R, p_offs, c, int(max_slice_size), _vp(batch_info.seg_indptr),
-        _vp(batch_info.weight_indices), batch_info.num_segments, _vp(batch_info.permutation),
-        _vp(batch_info.lora_ranks), _vp(batch_info.scalings), batch_info.tile_hint, _vp(ws),
-        ws.numel(), _stream(x.device)))
+        L, R, p_offs, c, int(max_slice_size), _vp(ind), _vp(sl), nseg,
+        _vp(batch_info.permutation), _vp(batch_info.lora_ranks), _vp(batch_info.scalings), hint,
+        _vp(ws), ws.numel(), _stream(x.device)))
     return base_output
 
 
@@ -288,9 +298,10 @@ def lora_a_embedding(input_ids, weights, batch_info: LoRABatchInfo, vocab_size,
         raise ValueError(f"{s} ids, the plan has {batch_info.num_tokens} tokens")
     if out is None:
         out = torch.empty((s, R), dtype=torch.bfloat16, device=weights.device)
+    ind, sl, nseg, _ = batch_info.kernel_segments()
     check(lib().lora_a_embedding(
         _vp(input_ids.contiguous()), _vp(weights), V, _vp(out), out.stride(0), s, L, R,
-        int(vocab_size), _vp(batch_info.seg_indptr), _vp(batch_info.weight_indices),
-        batch_info.num_segments, _vp(batch_info.permutation), _vp(batch_info.lora_ranks),
-        0 if extra_embeddings is None else 1, _stream(weights.device)))
+        int(vocab_size), _vp(ind), _vp(sl), nseg, _vp(batch_info.permutation),
+        _vp(batch_info.lora_ranks), 0 if extra_embeddings is None else 1,
+        _stream(weights.device)))
     return out

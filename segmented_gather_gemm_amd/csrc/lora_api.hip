@@ -395,7 +395,8 @@ extern "C" int64_t lora_plan_layout(int64_t token_capacity, int32_t seg_capacity
                                     int32_t req_capacity, int32_t max_loras, int64_t* offsets) {
   if (token_capacity < 0 || seg_capacity < 0 || req_capacity < 0 || max_loras < 0) return -1;
   const int64_t sizes[SGG_PLAN_REGIONS] = {token_capacity, seg_capacity + 1, seg_capacity,
-                                           req_capacity + 1, req_capacity, max_loras, max_loras};
+                                           req_capacity + 1, req_capacity, max_loras, max_loras,
+                                           seg_capacity + 1, seg_capacity};
   int64_t pos = 0;
   for (int i = 0; i < SGG_PLAN_REGIONS; ++i) {
     if (offsets) offsets[i] = pos;
@@ -436,6 +437,28 @@ extern "C" int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slot
     const int32_t len = h[off[1] + i + 1] - h[off[1] + i];
     longest = len > longest ? len : longest;
   }
+  // Work segments: merge consecutive segments of one slot up to `cap` tokens.
+  const int32_t* sind = h + off[1];
+  const int32_t* sslot = h + off[2];
+  int32_t* wind = h + off[7];
+  int32_t* wslot = h + off[8];
+  const int32_t cap = chunk > SGG_WORK_SEGMENT_TOKENS ? chunk : SGG_WORK_SEGMENT_TOKENS;
+  int32_t n_work = 0, longest_work = 0;
+  wind[0] = 0;
+  for (int32_t i = 0; i < n_seg;) {
+    int32_t j = i + 1;
+    while (j < n_seg && sslot[j] == sslot[i] && sind[j + 1] - sind[i] <= cap) ++j;
+    wslot[n_work] = sslot[i];
+    wind[n_work + 1] = sind[j];
+    const int32_t len = sind[j] - sind[i];
+    longest_work = len > longest_work ? len : longest_work;
+    ++n_work;
+    i = j;
+  }
+  for (int32_t i = n_work; i < seg_capacity; ++i) {
+    wslot[i] = 0;
+    wind[i + 1] = wind[n_work];
+  }
   // One transfer: a copy kernel reading the pinned buffer through its device
   // mapping; a runtime copy only if the buffer has no device mapping.
   void* src = nullptr;
@@ -454,5 +477,7 @@ extern "C" int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slot
   out_info[1] = chunk;
   out_info[2] = longest;
   out_info[3] = static_cast<int32_t>(n_tok);
+  out_info[4] = n_work;
+  out_info[5] = longest_work;
   return sgg::ok();
 }

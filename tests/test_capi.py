@@ -284,3 +284,19 @@ def test_library_never_imports_oracle():
 def test_np_dtypes_roundtrip():
     nat = _native(np.array([2, 3], np.int64), np.array([1, 0], np.int64), 2, False, 16)
     assert list(nat["permutation"][:5]) == [2, 3, 4, 0, 1]
+
+
+def test_plan_layout_regions():
+    """lora_plan_layout: 9 regions (plan, routing, tables, work segments),
+    64-element aligned, in the documented order and sizes."""
+    lib = _lib.lib()
+    offs = (ctypes.c_int64 * 9)()
+    total = lib.lora_plan_layout(300, 40, 20, 8, offs)
+    sizes = [300, 41, 40, 21, 20, 8, 8, 41, 40]
+    pos = 0
+    for i, n in enumerate(sizes):
+        assert offs[i] == pos, i
+        pos += (n + 63) // 64 * 64
+    assert total == pos
+    assert lib.lora_plan_layout(-1, 0, 0, 1, None) == -1
+

@@ -49,7 +49,29 @@ def check_plan(info, b, max_chunk, override=0):
     assert info.seg_indptr[:n + 1].cpu().tolist() == ref["seg_indptr"]
     assert info.weight_indices[:n].cpu().tolist() == ref["seg_slots"]
     assert info.req_seg_indptr.cpu().tolist() == ref["req_seg_indptr"]
+    check_work_segments(info, ref)
     return ref
+
+
+def check_work_segments(info, ref):
+    """The kernels' work segments: runs of the plan's segments of one slot,
+    merged greedily while within max(chunk, 128) tokens (a coarser partition
+    of the same sorted positions)."""
+    n = info.num_work_segments
+    wind = info.work_indptr[:n + 1].cpu().tolist()
+    wsl = info.work_slots[:n].cpu().tolist()
+    ind, sl = ref["seg_indptr"], ref["seg_slots"]
+    limit = max(ref["chunk_size"], 128)
+    assert wind[0] == 0 and wind[-1] == ind[-1]
+    pos = {v: i for i, v in enumerate(ind)}
+    assert all(v in pos for v in wind)
+    for w in range(n):
+        lo, hi = wind[w], wind[w + 1]
+        i0, i1 = pos[lo], pos[hi]
+        assert i1 > i0 and all(sl[i] == wsl[w] for i in range(i0, i1))
+        assert hi - lo <= limit
+        if i1 < len(sl):   # greedy: the next segment differs in slot or would not fit
+            assert sl[i1] != wsl[w] or ind[i1 + 1] - lo > limit
 
 
 def sample_rows(ref, s, n_random=768, seed=0):
@@ -284,6 +306,23 @@ def test_chunk_size_invariance(override):
     assert_close(y, want_y, f"chunk {override} y")
 
 
+def test_short_segments_in_groups():
+    """Many short segments (forced chunk 8) on few slots: the kernels tile
+    groups of consecutive segments and walk each same-slot run as one token
+    range (shrink groups of 2, expand groups of 8 here).  Every element is
+    compared with the oracle."""
+    rng = np.random.default_rng(81)
+    lens = rng.integers(1, 9, size=1800).tolist()
+    slots = rng.integers(0, 6, size=1800).tolist()
+    b, proj, t = _small_case(81, lens, slots, 6, [16, 16, 8, 16, 0, 16],
+                             [1.0, 0.5, 2.0, 1.5, 1.0, 0.25], 1024, [0, 1024, 2048], 16)
+    assert b.num_tokens > 8000
+    h, y = _gpu_forward(b, proj, t, override=8)
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, "grouped h")
+    assert_close(y, want_y, "grouped y")
+
+
 def test_request_permutation_and_merge():
     lens, slots = [7, 3, 20, 3, 50, 1], [1, 1, 0, 2, 0, 0]
     b, proj, t = _small_case(32, lens, slots, 3, [8, 8, 8], [1.0, 2.0, 0.5], 256,
@@ -356,7 +395,10 @@ def test_out_of_range_slot_is_no_adapter():
     b, proj, t = _small_case(37, [6, 10], [0, 1], 2, [16, 16], [1.0, 1.0], 256, [0, 128], 16)
     be = backend(b)
     info = plan_on(be, b)
-    info.weight_indices[:info.num_segments] = 7   # slot outside [0, 2): no adapter
+    # slot outside [0, 2) in the segments the kernels run over: no adapter
+    _, slots, n, _ = info.kernel_segments()
+    slots[:n] = 7
+    info.weight_indices[:info.num_segments] = 7
     x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
     h = sgg.lora_shrink(x, A, info, 1)
     y = sgg.lora_expand(h, Bw, info, [0, 128], 128, base.clone())
