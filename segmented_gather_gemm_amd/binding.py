@@ -298,10 +298,12 @@ def lora_a_embedding(input_ids, weights, batch_info: LoRABatchInfo, vocab_size,
         raise ValueError(f"{s} ids, the plan has {batch_info.num_tokens} tokens")
     if out is None:
         out = torch.empty((s, R), dtype=torch.bfloat16, device=weights.device)
-    ind, sl, nseg, _ = batch_info.kernel_segments()
+    # the plan's own segments: the gather parallelises over segments, so the
+    # finer partition is the faster one here
     check(lib().lora_a_embedding(
         _vp(input_ids.contiguous()), _vp(weights), V, _vp(out), out.stride(0), s, L, R,
-        int(vocab_size), _vp(ind), _vp(sl), nseg, _vp(batch_info.permutation),
+        int(vocab_size), _vp(batch_info.seg_indptr), _vp(batch_info.weight_indices),
+        batch_info.num_segments, _vp(batch_info.permutation),
         _vp(batch_info.lora_ranks), 0 if extra_embeddings is None else 1,
         _stream(weights.device)))
     return out

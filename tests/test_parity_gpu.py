@@ -53,15 +53,22 @@ def check_plan(info, b, max_chunk, override=0):
     return ref
 
 
+def _work_segment_tokens():
+    import os
+    import re
+    hdr = os.path.join(os.path.dirname(__file__), "..", "include", "sgg_lora.h")
+    return int(re.search(r"#define SGG_WORK_SEGMENT_TOKENS (\d+)", open(hdr).read()).group(1))
+
+
 def check_work_segments(info, ref):
     """The kernels' work segments: runs of the plan's segments of one slot,
-    merged greedily while within max(chunk, 128) tokens (a coarser partition
-    of the same sorted positions)."""
+    merged greedily while within max(chunk, SGG_WORK_SEGMENT_TOKENS) tokens
+    (a coarser partition of the same sorted positions)."""
     n = info.num_work_segments
     wind = info.work_indptr[:n + 1].cpu().tolist()
     wsl = info.work_slots[:n].cpu().tolist()
     ind, sl = ref["seg_indptr"], ref["seg_slots"]
-    limit = max(ref["chunk_size"], 128)
+    limit = max(ref["chunk_size"], _work_segment_tokens())
     assert wind[0] == 0 and wind[-1] == ind[-1]
     pos = {v: i for i, v in enumerate(ind)}
     assert all(v in pos for v in wind)
