@@ -7,7 +7,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsgg_lora.so")
-SOURCES = ["plan.cpp", "shrink.hip", "expand.hip", "lora_api.hip"]
+SOURCES = ["plan.cpp", "shrink.hip", "shrink_gemm.hip", "expand.hip", "lora_api.hip"]
 ARCH = os.environ.get("SGG_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

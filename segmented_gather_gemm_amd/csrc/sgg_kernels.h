@@ -83,7 +83,9 @@ struct EmbeddingParams {
 
 // Tile choice for the shrink (also sizes its workspace).
 struct ShrinkTiling {
-  int mf, nf;        // row / column fragments of 16
+  int gemm;          // 1: shrink_gemm_kernel with bm x bn tiles; 0: split-K shrink_kernel
+  int bm, bn;        // gemm tile (tokens x stacked rank rows)
+  int mf, nf;        // split-K kernel: row / column fragments of 16
   int mblocks, nblocks, ksplit;
   int64_t kps;
   int64_t partial_bytes;     // f32 partial tiles (0 unless ksplit > 1)
@@ -97,6 +99,8 @@ struct ExpandTiling {
 };
 
 hipError_t launch_shrink(const ShrinkParams& p, const ShrinkTiling& t, hipStream_t stream);
+hipError_t launch_shrink_gemm(const ShrinkParams& p, int bm, int bn, int64_t grid,
+                              hipStream_t stream);
 hipError_t launch_expand(const ExpandParams& p, const ExpandTiling& t, hipStream_t stream);
 hipError_t launch_embedding(const EmbeddingParams& p, hipStream_t stream);
 

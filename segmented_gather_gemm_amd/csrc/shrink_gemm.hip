@@ -1,0 +1,223 @@
+// LoRA-A shrink for batches that fill the GPU without splitting K (prefill,
+// mixed batches): h[t, k*R + j] = sum_q A[a(t), k*R + j, q] * x[t, q] over
+// the segments of a plan (chunked_backend.py page: run_lora_a_sgemm and the
+// shrink step of run_qkv_lora / run_gate_up_lora).
+//
+// A workgroup (4 waves) owns BM gathered tokens of one segment by BN stacked
+// rank rows and walks K in 64-deep steps.  Each step's x rows and A rows are
+// fetched once for the whole workgroup -- coalesced, 8 lanes per 128-byte
+// row -- into one of two XOR-swizzled LDS stages; every wave then reads its
+// (BM / WM) x (BN / WN) share of the tile as MFMA fragments
+// (mfma_f32_16x16x32_bf16).  The next step's loads are in flight while the
+// current step is multiplied, and one barrier per step separates the two.
+//
+// No operand is masked inside the K loop: a token row outside the segment
+// (or with an invalid permutation entry) reads an in-bounds stand-in row and
+// only feeds its own output row, which is never stored; an A row beyond the
+// slot's rank (or beyond c*R) only feeds its own output column, which is
+// stored as zero.  Only a ragged K tail (K % 64 != 0) zeroes the chunks past
+// K, in its last step.
+#include "sgg_device.h"
+#include "sgg_kernels.h"
+
+namespace sgg {
+
+namespace {
+
+// Byte offset of 16-byte chunk c (0..7) of row r in a swizzled 128-byte-row tile.
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
+
+template <int BM, int BN, int WM>
+__global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
+  constexpr int WN = 4 / WM;
+  constexpr int FM = BM / (16 * WM);        // token fragments per wave
+  constexpr int FN = BN / (16 * WN);        // rank-row fragments per wave
+  constexpr int ROWS = BM + BN;             // tile rows per step: x rows, then A rows
+  constexpr int XPER = BM / 32;             // 16-byte loads per thread per step: x rows
+  constexpr int APER = BN / 32;             //   and A rows
+  constexpr int STAGE = ROWS * 128;         // bytes of one LDS stage
+  static_assert(FM >= 1 && FN >= 1 && ROWS % 32 == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+
+  int seg, item;
+  {
+    const int per = p.mblocks * p.nblocks;
+    if (p.round_robin) {
+      segment_round_robin(blockIdx.x, per, &seg, &item);
+      if (seg >= p.num_segments) return;
+    } else {
+      const int L = xcd_contiguous(blockIdx.x, gridDim.x);
+      seg = L / per;
+      item = L % per;
+    }
+  }
+  const int mb0 = item % p.mblocks;
+  const int nb = item / p.mblocks;
+  // segment bounds, clamped to [0, s) so a malformed plan stays in bounds
+  const int lo = max(p.seg_indptr[seg], 0);
+  const int hi = min(static_cast<int64_t>(p.seg_indptr[seg + 1]), p.s);
+  if (hi <= lo) return;
+  const int slot = p.seg_slots[seg];
+  const bool slot_ok = slot >= 0 && slot < p.L;
+  int rho = slot_ok ? p.ranks[slot] : 0;
+  rho = rho < 0 ? 0 : (rho > p.R ? p.R : rho);
+
+  // Loading role: row (tid/8 + 32*j) of the step's tile, 16-byte chunk tid%8.
+  const int lrow = tid >> 3;
+  const int lcol = tid & 7;
+  // A rows of this thread's loads (tile rows BM + lrow + 32*j): fixed for the
+  // workgroup (in-bounds stand-in row 0 beyond c*R).
+  const uint16_t* arow[APER];
+#pragma unroll
+  for (int j = 0; j < APER; ++j) {
+    const int n = nb * BN + lrow + 32 * j;
+    arow[j] = p.A + (static_cast<int64_t>(slot_ok ? slot : 0) * p.CR + (n < p.CR ? n : 0)) * p.K +
+              8 * lcol;
+  }
+  const int nk = static_cast<int>((p.K + 63) / 64);
+  const bool ktail = (p.K & 63) != 0;
+
+  // Fragment role: row (lane%16) of a fragment, k group (lane/16).
+  const int frow = lane & 15;
+  const int fgrp = lane >> 4;
+  const int xr0 = wm * FM * 16;             // this wave's first token row in the tile
+  const int ar0 = BM + wn * FN * 16;        // this wave's first A row in the tile
+
+  for (int mb = mb0; lo + mb * BM < hi; mb += p.mblocks) {
+    const int m0 = lo + mb * BM;
+    const int mcount = hi - m0 < BM ? hi - m0 : BM;
+
+    if (rho == 0) {  // base model slot: zero rows of h
+      for (int q = tid; q < mcount * (BN / 4); q += 256) {
+        const int mm = q / (BN / 4);
+        const int n = nb * BN + 4 * (q % (BN / 4));
+        const int r = p.perm[m0 + mm];
+        if (n < p.CR && r >= 0 && r < p.s)
+          *reinterpret_cast<uint2*>(p.h + static_cast<int64_t>(r) * p.ldh + n) = make_uint2(0, 0);
+      }
+      continue;
+    }
+
+    // x rows of this thread's loads (tile rows lrow + 32*j; a stand-in row
+    // for tokens outside the segment)
+    const uint16_t* xrow[XPER];
+#pragma unroll
+    for (int j = 0; j < XPER; ++j) {
+      const int r = lrow + 32 * j;
+      const int pr = r < mcount ? p.perm[m0 + r] : p.perm[m0];
+      xrow[j] = p.x + static_cast<int64_t>((pr >= 0 && pr < p.s) ? pr : 0) * p.ldx + 8 * lcol;
+    }
+
+    uint4 xl[XPER], al[APER];
+    auto issue = [&](int kt) {
+      const int64_t k = static_cast<int64_t>(kt) * 64 + 8 * lcol;
+      const int64_t koff = (k <= p.K - 8 ? k : p.K - 8) - 8 * lcol;
+#pragma unroll
+      for (int j = 0; j < XPER; ++j) xl[j] = load16(xrow[j] + koff);
+#pragma unroll
+      for (int j = 0; j < APER; ++j) al[j] = load16(arow[j] + koff);
+      if (ktail && kt == nk - 1 && k >= p.K) {  // chunks past K contribute zero
+#pragma unroll
+        for (int j = 0; j < XPER; ++j) xl[j] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < APER; ++j) al[j] = make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto stash = [&](int buf) {
+      char* st = smem + buf * STAGE;
+#pragma unroll
+      for (int j = 0; j < XPER; ++j)
+        *reinterpret_cast<uint4*>(st + swz(lrow + 32 * j, lcol)) = xl[j];
+#pragma unroll
+      for (int j = 0; j < APER; ++j)
+        *reinterpret_cast<uint4*>(st + swz(BM + lrow + 32 * j, lcol)) = al[j];
+    };
+
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int f = 0; f < FM; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    __syncthreads();  // the previous row block's tiles are no longer read
+    issue(0);
+    stash(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) issue(kt + 1);
+      const char* st = smem + buf * STAGE;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c = 4 * ks + fgrp;
+        uint4 xv[FM], av[FN];
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+          xv[f] = *reinterpret_cast<const uint4*>(st + swz(xr0 + 16 * f + frow, c));
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+          av[i] = *reinterpret_cast<const uint4*>(st + swz(ar0 + 16 * i + frow, c));
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+          for (int f = 0; f < FM; ++f) acc[i][f] = mfma16x16x32(av[i], xv[f], acc[i][f]);
+      }
+      if (kt + 1 < nk) stash(buf ^ 1);
+      __syncthreads();
+    }
+
+    // Epilogue: lane holds rank rows n .. n+3 of token column m for each
+    // fragment; rows past the rank are stored as zero.
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      const int mm = xr0 + 16 * f + frow;
+      if (mm >= mcount) continue;
+      const int r = p.perm[m0 + mm];
+      if (r < 0 || r >= p.s) continue;
+      uint16_t* hrow = p.h + static_cast<int64_t>(r) * p.ldh;
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        const int n = nb * BN + (ar0 - BM) + 16 * i + 4 * fgrp;
+        if (n >= p.CR) continue;
+        const f32x4 v = acc[i][f];
+        const int j0 = n % p.R;  // rank index of n (n .. n+3 lie in one slice: R % 8 == 0)
+        uint2 o;
+        o.x = (j0 < rho ? f32_to_bf16(v[0]) : 0u) | ((j0 + 1 < rho ? f32_to_bf16(v[1]) : 0u) << 16);
+        o.y = (j0 + 2 < rho ? f32_to_bf16(v[2]) : 0u) | ((j0 + 3 < rho ? f32_to_bf16(v[3]) : 0u) << 16);
+        *reinterpret_cast<uint2*>(hrow + n) = o;
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM>
+hipError_t launch_g(const ShrinkParams& p, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((shrink_gemm_kernel<BM, BN, WM>), dim3(static_cast<unsigned>(grid)),
+                     dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Tile shapes with a kernel: (BM, BN) in {64, 128} x {32, 64, 128}; waves
+// split BN in two where BN allows, else all four split BM.
+hipError_t launch_shrink_gemm(const ShrinkParams& p, int bm, int bn, int64_t grid,
+                              hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  switch (bm * 1000 + bn) {
+    case 128128: return launch_g<128, 128, 2>(p, grid, stream);
+    case 128064: return launch_g<128, 64, 2>(p, grid, stream);
+    case 128032: return launch_g<128, 32, 4>(p, grid, stream);
+    case 64128: return launch_g<64, 128, 2>(p, grid, stream);
+    case 64064: return launch_g<64, 64, 2>(p, grid, stream);
+    case 64032: return launch_g<64, 32, 4>(p, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sgg

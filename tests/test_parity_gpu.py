@@ -313,6 +313,22 @@ def test_chunk_size_invariance(override):
     assert_close(y, want_y, f"chunk {override} y")
 
 
+def test_large_batch_ragged_k():
+    """A batch large enough for the whole-K GEMM shrink tiles, with K not a
+    multiple of 64 (the last K step is partly past K), NaN rank padding and
+    mixed ranks; every element against the oracle."""
+    rng = np.random.default_rng(91)
+    lens = rng.integers(40, 300, size=48).tolist()
+    slots = rng.integers(0, 40, size=48).tolist()
+    ranks = [(8, 16, 24, 32)[a % 4] for a in range(40)]
+    b, proj, t = _small_case(91, lens, slots, 40, ranks, rng.uniform(0.5, 2, 40).tolist(), 1000,
+                             [0, 768, 1536], 32, nan_pad=True)
+    h, y = _gpu_forward(b, proj, t)
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, "ragged-K GEMM h")
+    assert_close(y, want_y, "ragged-K GEMM y")
+
+
 def test_short_segments_in_groups():
     """Many short segments (forced chunk 8) on few slots: the kernels tile
     groups of consecutive segments and walk each same-slot run as one token
