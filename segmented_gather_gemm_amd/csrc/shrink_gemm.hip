@@ -27,7 +27,7 @@ namespace {
 // Byte offset of 16-byte chunk c (0..7) of row r in a swizzled 128-byte-row tile.
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
 
-template <int BM, int BN, int WM>
+template <int BM, int BN, int WM, int DEPTH>
 __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
   constexpr int WN = 4 / WM;
   constexpr int FM = BM / (16 * WM);        // token fragments per wave
@@ -113,44 +113,34 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
       xrow[j] = p.x + static_cast<int64_t>((pr >= 0 && pr < p.s) ? pr : 0) * p.ldx + 8 * lcol;
     }
 
-    uint4 xl[XPER], al[APER];
-    auto issue = [&](int kt) {
+    // DEPTH register sets: with two, step t+2 is requested while step t is
+    // multiplied and step t+1 (requested one step earlier) waits to be
+    // staged; with one, step t+1 is requested while step t is multiplied.
+    uint4 xl[DEPTH][XPER], al[DEPTH][APER];
+    auto issue = [&](int kt, uint4 (&xs)[XPER], uint4 (&as)[APER]) {
       const int64_t k = static_cast<int64_t>(kt) * 64 + 8 * lcol;
       const int64_t koff = (k <= p.K - 8 ? k : p.K - 8) - 8 * lcol;
 #pragma unroll
-      for (int j = 0; j < XPER; ++j) xl[j] = load16(xrow[j] + koff);
+      for (int j = 0; j < XPER; ++j) xs[j] = load16(xrow[j] + koff);
 #pragma unroll
-      for (int j = 0; j < APER; ++j) al[j] = load16(arow[j] + koff);
+      for (int j = 0; j < APER; ++j) as[j] = load16(arow[j] + koff);
       if (ktail && kt == nk - 1 && k >= p.K) {  // chunks past K contribute zero
 #pragma unroll
-        for (int j = 0; j < XPER; ++j) xl[j] = make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < XPER; ++j) xs[j] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < APER; ++j) al[j] = make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < APER; ++j) as[j] = make_uint4(0, 0, 0, 0);
       }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int buf, const uint4 (&xs)[XPER], const uint4 (&as)[APER]) {
       char* st = smem + buf * STAGE;
 #pragma unroll
       for (int j = 0; j < XPER; ++j)
-        *reinterpret_cast<uint4*>(st + swz(lrow + 32 * j, lcol)) = xl[j];
+        *reinterpret_cast<uint4*>(st + swz(lrow + 32 * j, lcol)) = xs[j];
 #pragma unroll
       for (int j = 0; j < APER; ++j)
-        *reinterpret_cast<uint4*>(st + swz(BM + lrow + 32 * j, lcol)) = al[j];
+        *reinterpret_cast<uint4*>(st + swz(BM + lrow + 32 * j, lcol)) = as[j];
     };
-
-    f32x4 acc[FN][FM];
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int f = 0; f < FM; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    __syncthreads();  // the previous row block's tiles are no longer read
-    issue(0);
-    stash(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) issue(kt + 1);
+    auto mma = [&](int buf, f32x4 (&acc)[FN][FM]) {
       const char* st = smem + buf * STAGE;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -167,8 +157,43 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
 #pragma unroll
           for (int f = 0; f < FM; ++f) acc[i][f] = mfma16x16x32(av[i], xv[f], acc[i][f]);
       }
-      if (kt + 1 < nk) stash(buf ^ 1);
+    };
+
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int f = 0; f < FM; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    __syncthreads();  // the previous row block's tiles are no longer read
+    if constexpr (DEPTH == 2) {
+      issue(0, xl[0], al[0]);
+      if (nk > 1) issue(1, xl[DEPTH - 1], al[DEPTH - 1]);
+      stash(0, xl[0], al[0]);
       __syncthreads();
+      // Step kt is in LDS stage kt & 1 and step kt + 1 in register set
+      // (kt + 1) & 1; unrolled by two so that the register sets are fixed.
+      for (int kt = 0; kt < nk; kt += 2) {
+        if (kt + 2 < nk) issue(kt + 2, xl[0], al[0]);
+        mma(0, acc);
+        if (kt + 1 >= nk) break;
+        stash(1, xl[DEPTH - 1], al[DEPTH - 1]);
+        __syncthreads();
+        if (kt + 3 < nk) issue(kt + 3, xl[DEPTH - 1], al[DEPTH - 1]);
+        mma(1, acc);
+        if (kt + 2 < nk) stash(0, xl[0], al[0]);
+        __syncthreads();
+      }
+    } else {
+      issue(0, xl[0], al[0]);
+      stash(0, xl[0], al[0]);
+      __syncthreads();
+      for (int kt = 0; kt < nk; ++kt) {
+        if (kt + 1 < nk) issue(kt + 1, xl[0], al[0]);
+        mma(kt & 1, acc);
+        if (kt + 1 < nk) stash((kt + 1) & 1, xl[0], al[0]);
+        __syncthreads();
+      }
     }
 
     // Epilogue: lane holds rank rows n .. n+3 of token column m for each
@@ -195,9 +220,9 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
   }
 }
 
-template <int BM, int BN, int WM>
+template <int BM, int BN, int WM, int DEPTH>
 hipError_t launch_g(const ShrinkParams& p, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((shrink_gemm_kernel<BM, BN, WM>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((shrink_gemm_kernel<BM, BN, WM, DEPTH>), dim3(static_cast<unsigned>(grid)),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
 }
@@ -205,17 +230,18 @@ hipError_t launch_g(const ShrinkParams& p, int64_t grid, hipStream_t stream) {
 }  // namespace
 
 // Tile shapes with a kernel: (BM, BN) in {64, 128} x {32, 64, 128}; waves
-// split BN in two where BN allows, else all four split BM.
+// split BN in two where BN allows, else all four split BM.  Two register
+// sets of prefetch except for 128 x 128 (one set: two would spill).
 hipError_t launch_shrink_gemm(const ShrinkParams& p, int bm, int bn, int64_t grid,
                               hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   switch (bm * 1000 + bn) {
-    case 128128: return launch_g<128, 128, 2>(p, grid, stream);
-    case 128064: return launch_g<128, 64, 2>(p, grid, stream);
-    case 128032: return launch_g<128, 32, 4>(p, grid, stream);
-    case 64128: return launch_g<64, 128, 2>(p, grid, stream);
-    case 64064: return launch_g<64, 64, 2>(p, grid, stream);
-    case 64032: return launch_g<64, 32, 4>(p, grid, stream);
+    case 128128: return launch_g<128, 128, 2, 1>(p, grid, stream);
+    case 128064: return launch_g<128, 64, 2, 2>(p, grid, stream);
+    case 128032: return launch_g<128, 32, 4, 2>(p, grid, stream);
+    case 64128: return launch_g<64, 128, 2, 2>(p, grid, stream);
+    case 64064: return launch_g<64, 64, 2, 2>(p, grid, stream);
+    case 64032: return launch_g<64, 32, 4, 2>(p, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

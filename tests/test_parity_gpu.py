@@ -315,13 +315,13 @@ def test_chunk_size_invariance(override):
 
 def test_large_batch_ragged_k():
     """A batch large enough for the whole-K GEMM shrink tiles, with K not a
-    multiple of 64 (the last K step is partly past K), NaN rank padding and
-    mixed ranks; every element against the oracle."""
+    multiple of 64 (17 K steps, the last partly past K), NaN rank padding
+    and mixed ranks; every element against the oracle."""
     rng = np.random.default_rng(91)
     lens = rng.integers(40, 300, size=48).tolist()
     slots = rng.integers(0, 40, size=48).tolist()
     ranks = [(8, 16, 24, 32)[a % 4] for a in range(40)]
-    b, proj, t = _small_case(91, lens, slots, 40, ranks, rng.uniform(0.5, 2, 40).tolist(), 1000,
+    b, proj, t = _small_case(91, lens, slots, 40, ranks, rng.uniform(0.5, 2, 40).tolist(), 1064,
                              [0, 768, 1536], 32, nan_pad=True)
     h, y = _gpu_forward(b, proj, t)
     want_h, want_y = oracle_forward(t, b, proj)
