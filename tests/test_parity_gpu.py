@@ -329,6 +329,35 @@ def test_large_batch_ragged_k():
     assert_close(y, want_y, "ragged-K GEMM y")
 
 
+def test_long_k_small_grid():
+    """Long K (129 K steps, the last partly past K) on a small grid, NaN rank
+    padding, a rank-0 slot: the standalone shrink and the stacked call
+    against the oracle on every element and against each other bit for bit;
+    the workspace counters are left at zero."""
+    sgg = _sgg()
+    rng = np.random.default_rng(95)
+    lens = rng.integers(60, 140, size=40).tolist()
+    slots = rng.integers(0, 10, size=40).tolist()
+    ranks = [16, 16, 8, 16, 16, 0, 16, 12, 16, 16]
+    b, proj, t = _small_case(95, lens, slots, 10, ranks, rng.uniform(0.5, 2, 10).tolist(), 8232,
+                             [0, 640, 1280], 16, nan_pad=True)
+    be = backend(b)
+    info = plan_on(be, b)
+    check_plan(info, b, 128)
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    h = sgg.lora_shrink(x, A, info, 2, workspace=ws)
+    y_sep = sgg.lora_expand(h, Bw, info, proj.slice_offsets, proj.max_slice, base.clone())
+    y = sgg.lora_qkv(x, A, Bw, info, proj.slice_offsets, proj.max_slice, base.clone(),
+                     workspace=ws)
+    torch.cuda.synchronize()
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, "long-K h")
+    assert_close(y_sep, want_y, "long-K y (separate)")
+    assert torch.equal(y, y_sep)
+    assert not ws[:32768].any()
+
+
 def test_short_segments_in_groups():
     """Many short segments (forced chunk 8) on few slots: the kernels tile
     groups of consecutive segments and walk each same-slot run as one token
