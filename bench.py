@@ -409,12 +409,15 @@ def run_full(device, layers, steps=5, warmup=1):
     import segmented_gather_gemm_amd as sgg
     b = draw_batch("full")
     per = {p.name: [] for p in b.projections}
+    parts = {p.name: {"shrink": [], "expand": []} for p in b.projections}
     for layer in range(layers):
         for pi, proj in enumerate(b.projections):
             t = _to(device, draw_projection(b, proj, layer=layer, proj_index=pi))
             m = measure_projection(device, b, proj, t, b.max_chunk_size, steps, warmup)
             per[proj.name].append(m["stacked"]["avg_us"] if proj.num_slices > 1 else
                                   m["shrink"]["avg_us"] + m["expand"]["avg_us"])
+            for n in ("shrink", "expand"):
+                parts[proj.name][n].append(m[n]["avg_us"])
             del t
     layer_us = float(sum(np.mean(v) for v in per.values()))
     cnts = [algo_counts(b, p, 16) for p in b.projections]
@@ -436,6 +439,8 @@ def run_full(device, layers, steps=5, warmup=1):
     return {"workload": "full layer sweep: Llama-3-8B shapes, 4288 tokens, 64 adapters r=32; "
                         f"{layers} layers with distinct weights timed",
             "per_layer_us": {k: round(float(np.mean(v)), 2) for k, v in per.items()},
+            "per_layer_kernels_us": {k: {n: round(float(np.mean(v)), 2) for n, v in d.items()}
+                                     for k, d in parts.items()},
             "layer": _rates(layer_bytes, layer_flops, layer_us),
             "layers32_ms": round(32 * layer_us / 1e3, 3),
             "tokens_per_s_32_layers": round(b.num_tokens / (32 * layer_us * 1e-6), 1),
