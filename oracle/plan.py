@@ -14,7 +14,11 @@ Follows the ``chunked_backend.py`` page (class ``ChunkedSgmvLoRABackend``):
                          with the remainder last; CSR boundaries);
 * per-request routing -- ``_build_req_seg_indptr``;
 * graph padding       -- the CUDA-graph branch of ``prepare_lora_batch``
-                         (unused segment slots get adapter 0 and zero length).
+                         (unused segment slots get adapter 0 and zero length);
+* lm_head plans       -- ``_prepare_lm_head_batch_info`` / ``_build_lm_head_batch_info``
+                         (identity permutation; segments from the page's
+                         unprinted ``merge_and_chunk_segments``, read plainly:
+                         see ``merge_and_chunk``).
 
 Readings where the page is silent: in decode mode every request carries one
 token; requests of length zero contribute no tokens; ``chunk_override > 0``
@@ -152,3 +156,67 @@ def plan(seq_lens, req_slots, is_decode, max_chunk_size, chunk_override=0,
         "chunk_size": chunk,
         "num_tokens": num_tokens,
     }
+
+
+# ----------------------------------------------------------- lm_head plans
+
+def merge_and_chunk(req_slots, lens, chunk):
+    """Segments of the pruned lm_head tokens, which stay in original order.
+
+    ``_prepare_lm_head_batch_info`` (``chunked_backend.py`` page) builds them
+    with ``merge_and_chunk_segments(weight_indices, pruned_lens, chunk)``, a
+    helper the page imports but does not print.  Plain reading, taken here:
+    requests with no pruned token carry nothing and are dropped; consecutive
+    requests of one slot are merged into a run; each run is cut into pieces of
+    ``chunk`` tokens, the remainder last.  Returns (per-segment slot,
+    per-segment length).
+    """
+    runs = []
+    for slot, n in zip(req_slots, lens):
+        if n < 0:
+            raise ValueError("negative length")
+        if n == 0:
+            continue
+        if runs and runs[-1][0] == slot:
+            runs[-1][1] += n
+        else:
+            runs.append([slot, n])
+    seg_slots, seg_lens = [], []
+    for slot, n in runs:
+        pieces = (n + chunk - 1) // chunk
+        for q in range(pieces):
+            seg_slots.append(slot)
+            seg_lens.append(chunk if q < pieces - 1 else n - (pieces - 1) * chunk)
+    return seg_slots, seg_lens
+
+
+def lm_head_plan(pruned_lens, req_slots, max_chunk_size, chunk_override=0, capacity=None):
+    """Plan of the pruned lm_head pass (``_prepare_lm_head_batch_info`` and
+    ``_build_lm_head_batch_info``): the chunk from the token-count rule over
+    the pruned total, segments from ``merge_and_chunk``, CSR boundaries from
+    their lengths, and the identity permutation (the pruned tokens are in
+    original order).  Per-pass plans for logprob chunking are the same plan
+    over the requests of one pass.  ``capacity`` pads as in ``plan``."""
+    if len(pruned_lens) != len(req_slots):
+        raise ValueError("one length per request")
+    total = sum(pruned_lens)
+    chunk = chunk_override if chunk_override > 0 else chunk_size_for_tokens(total, max_chunk_size)
+    seg_slots, seg_lens = merge_and_chunk(req_slots, pruned_lens, chunk)
+    indptr = [0]
+    for length in seg_lens:
+        indptr.append(indptr[-1] + length)
+    num_segments = len(seg_slots)
+    if capacity is not None:
+        if capacity < num_segments:
+            raise ValueError("segment capacity too small")
+        seg_slots = seg_slots + [0] * (capacity - num_segments)
+        indptr = indptr + [indptr[-1]] * (capacity - num_segments)
+    return {
+        "permutation": list(range(total)),
+        "seg_indptr": indptr,
+        "seg_slots": seg_slots,
+        "num_segments": num_segments,
+        "chunk_size": chunk,
+        "num_tokens": total,
+    }
+

@@ -474,3 +474,54 @@ def test_pins_pass_on_oracle():
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name):
     assert not _pins_pass(_mutant_module(MUTANTS[name])), name
+
+
+# ------------------------------------------------------------- lm_head plans
+
+def test_lm_head_plan_hand_example():
+    ex = json.load(open(os.path.join(GOLDEN, "lm_head_plan_example.json")))
+    got = op.lm_head_plan(ex["pruned_lens"], ex["req_slots"], 128, ex["chunk_size_override"])
+    for k, v in ex["expected"].items():
+        assert got[k] == v, k
+
+
+def test_lm_head_segments_are_runs_of_the_original_order():
+    """Brute force over tiny batches: merging consecutive same-slot requests
+    and chunking the runs equals cutting the runs of equal slots of the
+    token sequence in ORIGINAL order (no sort) into chunks -- the plan's
+    segment rule applied to the unsorted slot sequence."""
+    for bs in range(0, 5):
+        for lens in itertools.product(range(0, 4), repeat=bs):
+            for slots in itertools.product(range(0, 3), repeat=bs):
+                for chunk in (1, 2, 3, 16):
+                    seg_slots, seg_lens = op.merge_and_chunk(list(slots), list(lens), chunk)
+                    want_slots, want_indptr = op.segments(op.token_slots(lens, slots), chunk)
+                    assert seg_slots == want_slots
+                    got_indptr = [0]
+                    for n in seg_lens:
+                        got_indptr.append(got_indptr[-1] + n)
+                    assert got_indptr == want_indptr
+
+
+def test_lm_head_plan_invariants_and_chunk_rule():
+    rng = random.Random(7)
+    for _ in range(200):
+        bs = rng.randint(1, 40)
+        lens = [rng.choice([0, 1, 1, 1, 2, 5, 40, 300]) for _ in range(bs)]
+        slots = [rng.randrange(4) for _ in range(bs)]
+        for cap in (16, 64, 128):
+            pl = op.lm_head_plan(lens, slots, cap)
+            total = sum(lens)
+            assert pl["chunk_size"] == op.chunk_size_for_tokens(total, cap)
+            assert pl["permutation"] == list(range(total))
+            ind = pl["seg_indptr"]
+            assert ind[0] == 0 and ind[-1] == total
+            assert all(0 < ind[i + 1] - ind[i] <= pl["chunk_size"] for i in range(pl["num_segments"]))
+            # tokens of a segment all belong to requests of the segment's slot
+            rows = op.token_slots(lens, slots)
+            for i in range(pl["num_segments"]):
+                assert set(rows[ind[i]:ind[i + 1]]) == {pl["seg_slots"][i]}
+    padded = op.lm_head_plan([3, 0, 4], [1, 0, 1], 128, capacity=5)
+    assert padded["seg_slots"] == [1, 0, 0, 0, 0]
+    assert padded["seg_indptr"] == [0, 7, 7, 7, 7, 7]
+
