@@ -164,6 +164,45 @@ int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slots, int32_t 
                      int32_t* out_info, void* stream);
 
 /*
+ * lora_plan_lm_head -- plan of a pruned lm_head pass.
+ * (chunked_backend.py page: _prepare_lm_head_batch_info and
+ *  _build_lm_head_batch_info.)
+ *
+ * The pruned tokens (pruned_lens[r] of request r, r < num_reqs, requests
+ * laid out one after another) stay in original order: permutation[t] = t.
+ * Segments: the page's merge_and_chunk_segments, which it imports but does
+ * not print, read plainly -- requests with no pruned token are dropped,
+ * consecutive requests of one slot form a run, each run is cut into pieces
+ * of `chunk` tokens, the remainder last.  The chunk follows the token-count
+ * rule over the pruned total (as lora_plan_segments in extend mode), or
+ * chunk_size_override when positive.  A per-pass plan (logprob chunking) is
+ * this plan over the requests of one pass.  Arrays, capacities, padding and
+ * errors as lora_plan_segments (a segment capacity of
+ * lora_plan_max_segments(total, num_reqs, min_chunk) always suffices).
+ * Host only, synchronous.
+ */
+int lora_plan_lm_head(const int32_t* pruned_lens, const int32_t* req_slots, int32_t num_reqs,
+                      int32_t max_loras, int32_t max_chunk_size, int32_t chunk_size_override,
+                      int32_t* permutation, int64_t perm_capacity,
+                      int32_t* seg_indptr, int32_t* seg_slots, int32_t seg_capacity,
+                      int32_t* out_num_segments, int32_t* out_chunk_size,
+                      int64_t* out_num_tokens);
+
+/*
+ * lora_plan_lm_head_upload -- as lora_plan_upload, for the lm_head plan of
+ * lora_plan_lm_head: the same buffer layout (req_seg_indptr holds the
+ * boundaries of each request's pruned tokens), work segments and single
+ * transfer on `stream`.
+ */
+int lora_plan_lm_head_upload(const int32_t* pruned_lens, const int32_t* req_slots,
+                             int32_t num_reqs, const int32_t* lora_ranks, const float* scalings,
+                             int32_t max_loras, int32_t max_chunk_size,
+                             int32_t chunk_size_override, int64_t token_capacity,
+                             int32_t seg_capacity, int32_t req_capacity, void* host_staging,
+                             void* device_plan, int64_t buffer_bytes, int32_t* out_info,
+                             void* stream);
+
+/*
  * lora_shrink -- LoRA-A segmented gather GEMM.
  * (chunked_backend.py page: run_lora_a_sgemm, and the shrink step of
  *  run_qkv_lora / run_gate_up_lora; base_backend.py page: run_lora_a_sgemm

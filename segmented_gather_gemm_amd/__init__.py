@@ -13,6 +13,7 @@ from .binding import (
     default_workspace,
     lora_a_embedding,
     lora_expand,
+    lora_plan_lm_head,
     lora_plan_max_segments,
     lora_plan_segments,
     lora_qkv,
@@ -23,5 +24,6 @@ lib()  # load now: a missing library is an import error, never a silent fallback
 
 __all__ = [
     "ChunkedSgmvLoRA", "LoRABatchInfo", "SggError", "default_workspace", "lora_a_embedding",
-    "lora_expand", "lora_plan_max_segments", "lora_plan_segments", "lora_qkv", "lora_shrink",
+    "lora_expand", "lora_plan_lm_head", "lora_plan_max_segments", "lora_plan_segments",
+    "lora_qkv", "lora_shrink",
 ]

@@ -13,11 +13,17 @@ SIGNATURES = {
     "lora_plan_segments": (ctypes.c_int, [
         _pi32, _pi32, _i32, _i32, _i32, _i32, _i32,
         _pi32, _i64, _pi32, _pi32, _i32, _pi32, _pi32, _pi32, _pi64]),
+    "lora_plan_lm_head": (ctypes.c_int, [
+        _pi32, _pi32, _i32, _i32, _i32, _i32,
+        _pi32, _i64, _pi32, _pi32, _i32, _pi32, _pi32, _pi64]),
     "lora_plan_max_segments": (_i64, [_i64, _i32, _i32]),
     "lora_plan_layout": (_i64, [_i64, _i32, _i32, _i32, _pi64]),
     # host arrays are passed as addresses (NumPy .ctypes.data) on this hot call
     "lora_plan_upload": (ctypes.c_int, [
         _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+        _i64, _i32, _i32, _vp, _vp, _i64, _vp, _vp]),
+    "lora_plan_lm_head_upload": (ctypes.c_int, [
+        _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
         _i64, _i32, _i32, _vp, _vp, _i64, _vp, _vp]),
     "lora_shrink_workspace_bytes": (_i64, [_i64, _i64, _i32, _i32, _i32, _i32]),
     "lora_shrink": (ctypes.c_int, [

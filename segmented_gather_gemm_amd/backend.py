@@ -3,7 +3,9 @@
 Method names and arguments follow the ``ChunkedSgmvLoRABackend`` /
 ``BaseLoRABackend`` pages (prepare_lora_batch, run_lora_a_sgemm,
 run_lora_b_sgemm, run_qkv_lora, run_gate_up_lora, run_lora_a_embedding,
-init_cuda_graph_batch_info).  Every step of the work runs in libsgg_lora:
+init_cuda_graph_batch_info); the pruned lm_head plans of
+``_prepare_lm_head_batch_info`` are prepare_lm_head_batch and
+prepare_lm_head_pass_batches.  Every step of the work runs in libsgg_lora:
 the plan in its host planner, the rest in its HIP kernels.
 
 Upload: the page copies six small host arrays to the device one by one.
@@ -93,6 +95,8 @@ class ChunkedSgmvLoRA:
         self.max_chunk_size = int(max_chunk_size)
         self.device = torch.device(device)
         self.batch_info = None
+        self.lm_head_batch_info = None
+        self.lm_head_pass_batch_infos = None
         self.cuda_graph_batch_info = None
         self._graph_dev = None
         self._graph_cap = None
@@ -183,6 +187,67 @@ class ChunkedSgmvLoRA:
         batch.planned_tokens = s
         self.batch_info = batch
         return batch
+
+    # ------------------------------------------------------------ lm_head
+    def prepare_lm_head_batch(self, pruned_lens, weight_indices, lora_ranks, scalings,
+                              chunk_size_override=0):
+        """Plan and upload the pruned lm_head pass (``_prepare_lm_head_batch_info``):
+        ``pruned_lens[r]`` tokens of request r reach the lm_head, in original
+        order (identity permutation); segments are runs of consecutive
+        same-slot requests cut into chunks.  The result is also kept as
+        ``lm_head_batch_info``; pass it as ``pruned_batch_info`` to
+        run_lora_a_sgemm / run_lora_b_sgemm."""
+        batch = self._lm_head_plan(pruned_lens, weight_indices, lora_ranks, scalings,
+                                   chunk_size_override)
+        self.lm_head_batch_info = batch
+        return batch
+
+    def prepare_lm_head_pass_batches(self, passes, lora_ranks, scalings):
+        """Per-pass lm_head plans for logprob chunking: one plan per
+        (weight_indices, pruned_lens) pass, each over that pass's requests
+        (the page plans each pass the same way as the whole batch)."""
+        out = [self._lm_head_plan(lens, wi, lora_ranks, scalings, 0) for wi, lens in passes]
+        self.lm_head_pass_batch_infos = out
+        return out
+
+    def _lm_head_plan(self, pruned_lens, weight_indices, lora_ranks, scalings, override):
+        L = self.max_loras_per_batch
+        if len(lora_ranks) != L or len(scalings) != L:
+            raise ValueError(f"lora_ranks and scalings need {L} entries")
+        slots = np.ascontiguousarray(weight_indices, dtype=np.int32)
+        lens = np.ascontiguousarray(pruned_lens, dtype=np.int32)
+        if len(lens) != len(slots):
+            raise ValueError("pruned_lens and weight_indices differ in length")
+        bs = len(slots)
+        s = int(lens.sum(dtype=np.int64))
+        min_chunk = override if override > 0 else MIN_CHUNK_SIZE
+        # runs of consecutive requests are not bounded by the slot count
+        seg_cap = B.lora_plan_max_segments(s, max(bs, 1), min_chunk)
+        total, regions = self._layout(s, seg_cap, bs)
+        stg = self._staging
+        ring = stg.take(total)
+        dev = stg.dev[ring]
+        ranks = np.ascontiguousarray(lora_ranks, dtype=np.int32)
+        scal = np.ascontiguousarray(scalings, dtype=np.float32)
+        idx = self.device.index if self.device.index is not None else torch.cuda.current_device()
+        stream = torch._C._cuda_getCurrentRawStream(idx)
+        info = self._info_arr
+        check(lib().lora_plan_lm_head_upload(
+            lens.ctypes.data, slots.ctypes.data, bs, ranks.ctypes.data, scal.ctypes.data, L,
+            self.max_chunk_size, int(override), s, seg_cap, bs, stg.host[ring].data_ptr(),
+            dev.data_ptr(), 4 * dev.numel(), info, stream))
+        stg.done(ring, torch.cuda.current_stream(self.device))
+        n_seg, chunk, longest, n_work, longest_work = info[0], info[1], info[2], info[4], info[5]
+        v = {name: dev[o:o + n] for name, (o, n) in zip(_NAMES, regions)}
+        # a fresh LoRABatchInfo (not one of the eager step's cached views)
+        return LoRABatchInfo(
+            bs=bs, num_tokens=s, num_segments=n_seg, max_len=chunk,
+            seg_indptr=v["seg_indptr"], weight_indices=v["seg_slots"],
+            permutation=v["permutation"], lora_ranks=v["ranks"],
+            scalings=v["scalings"].view(torch.float32), req_seg_indptr=v["req_seg_indptr"],
+            req_weight_indices=v["req_slots"], use_cuda_graph=False, max_seg_len=longest,
+            work_indptr=v["work_indptr"], work_slots=v["work_slots"], num_work_segments=n_work,
+            max_work_len=longest_work)
 
     def init_cuda_graph_batch_info(self, max_bs_in_cuda_graph, num_tokens_per_bs):
         """Preallocate fixed-capacity device plan arrays for graph capture.

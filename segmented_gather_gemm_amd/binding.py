@@ -150,6 +150,35 @@ def lora_plan_segments(seq_lens, req_slots, max_loras, is_decode, max_chunk_size
     return res
 
 
+def lora_plan_lm_head(pruned_lens, req_slots, max_loras, max_chunk_size, chunk_size_override=0,
+                      seg_capacity=None):
+    """Plan a pruned lm_head pass on the host (identity permutation).
+
+    Returns a dict with ``permutation``, ``seg_indptr``, ``seg_slots`` (NumPy
+    arrays), ``num_segments``, ``chunk_size``, ``num_tokens``, ``capacity``.
+    """
+    slots, p_slots = _host_i32(req_slots)
+    lens, p_lens = _host_i32(pruned_lens)
+    if len(lens) != len(slots):
+        raise ValueError("pruned_lens and req_slots differ in length")
+    s = int(lens.astype(np.int64).sum())
+    min_chunk = chunk_size_override if chunk_size_override > 0 else 16
+    cap = (lora_plan_max_segments(s, max(len(slots), 1), min_chunk)
+           if seg_capacity is None else int(seg_capacity))
+    perm = np.zeros(max(s, 1), np.int32)
+    ind = np.zeros(cap + 1, np.int32)
+    sl = np.zeros(max(cap, 1), np.int32)
+    n_seg, chunk, n_tok = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    check(lib().lora_plan_lm_head(
+        p_lens, p_slots, len(slots), int(max_loras), int(max_chunk_size),
+        int(chunk_size_override), perm.ctypes.data_as(_P32), s, ind.ctypes.data_as(_P32),
+        sl.ctypes.data_as(_P32), cap, ctypes.byref(n_seg), ctypes.byref(chunk),
+        ctypes.byref(n_tok)))
+    return {"permutation": perm[:s], "seg_indptr": ind, "seg_slots": sl,
+            "num_segments": n_seg.value, "chunk_size": chunk.value, "num_tokens": n_tok.value,
+            "capacity": cap}
+
+
 # ----------------------------------------------------------------- workspace
 
 _workspaces = {}

@@ -405,13 +405,17 @@ extern "C" int64_t lora_plan_layout(int64_t token_capacity, int32_t seg_capacity
   return pos;
 }
 
-extern "C" int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slots,
-                                int32_t num_reqs, const int32_t* lora_ranks,
-                                const float* scalings, int32_t max_loras, int32_t is_decode,
-                                int32_t max_chunk_size, int32_t chunk_size_override,
-                                int64_t token_capacity, int32_t seg_capacity,
-                                int32_t req_capacity, void* host_staging, void* device_plan,
-                                int64_t buffer_bytes, int32_t* out_info, void* stream) {
+namespace {
+
+// Plan into the staging buffer (`lm_head`: the pruned lm_head plan, else the
+// chunked plan), add the tables and the work segments, then one transfer.
+int plan_upload(bool lm_head, const int32_t* seq_lens, const int32_t* req_slots,
+                int32_t num_reqs, const int32_t* lora_ranks, const float* scalings,
+                int32_t max_loras, int32_t is_decode, int32_t max_chunk_size,
+                int32_t chunk_size_override, int64_t token_capacity, int32_t seg_capacity,
+                int32_t req_capacity, void* host_staging, void* device_plan,
+                int64_t buffer_bytes, int32_t* out_info, void* stream) {
+
   int64_t off[SGG_PLAN_REGIONS];
   const int64_t total = lora_plan_layout(token_capacity, seg_capacity, req_capacity, max_loras, off);
   SGG_CHECK(total >= 0, SGG_ERR_INVALID, "negative capacity");
@@ -425,9 +429,24 @@ extern "C" int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slot
   int32_t* h = static_cast<int32_t*>(host_staging);
   int32_t n_seg = 0, chunk = 0;
   int64_t n_tok = 0;
-  int rc = lora_plan_segments(seq_lens, req_slots, num_reqs, max_loras, is_decode, max_chunk_size,
-                              chunk_size_override, h + off[0], token_capacity, h + off[1],
-                              h + off[2], seg_capacity, h + off[3], &n_seg, &chunk, &n_tok);
+  int rc;
+  if (lm_head) {
+    rc = lora_plan_lm_head(seq_lens, req_slots, num_reqs, max_loras, max_chunk_size,
+                           chunk_size_override, h + off[0], token_capacity, h + off[1],
+                           h + off[2], seg_capacity, &n_seg, &chunk, &n_tok);
+    if (rc == 0) {  // request boundaries over the pruned tokens
+      int64_t acc = 0;
+      h[off[3]] = 0;
+      for (int32_t r = 0; r < num_reqs; ++r) {
+        acc += seq_lens[r];
+        h[off[3] + r + 1] = static_cast<int32_t>(acc);
+      }
+    }
+  } else {
+    rc = lora_plan_segments(seq_lens, req_slots, num_reqs, max_loras, is_decode, max_chunk_size,
+                            chunk_size_override, h + off[0], token_capacity, h + off[1],
+                            h + off[2], seg_capacity, h + off[3], &n_seg, &chunk, &n_tok);
+  }
   if (rc) return rc;
   for (int32_t r = 0; r < num_reqs; ++r) h[off[4] + r] = req_slots[r];
   for (int32_t a = 0; a < max_loras; ++a) h[off[5] + a] = lora_ranks[a];
@@ -480,4 +499,33 @@ extern "C" int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slot
   out_info[4] = n_work;
   out_info[5] = longest_work;
   return sgg::ok();
+}
+
+}  // namespace
+
+extern "C" int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slots,
+                                int32_t num_reqs, const int32_t* lora_ranks,
+                                const float* scalings, int32_t max_loras, int32_t is_decode,
+                                int32_t max_chunk_size, int32_t chunk_size_override,
+                                int64_t token_capacity, int32_t seg_capacity,
+                                int32_t req_capacity, void* host_staging, void* device_plan,
+                                int64_t buffer_bytes, int32_t* out_info, void* stream) {
+  return plan_upload(false, seq_lens, req_slots, num_reqs, lora_ranks, scalings, max_loras,
+                     is_decode, max_chunk_size, chunk_size_override, token_capacity,
+                     seg_capacity, req_capacity, host_staging, device_plan, buffer_bytes,
+                     out_info, stream);
+}
+
+extern "C" int lora_plan_lm_head_upload(const int32_t* pruned_lens, const int32_t* req_slots,
+                                        int32_t num_reqs, const int32_t* lora_ranks,
+                                        const float* scalings, int32_t max_loras,
+                                        int32_t max_chunk_size, int32_t chunk_size_override,
+                                        int64_t token_capacity, int32_t seg_capacity,
+                                        int32_t req_capacity, void* host_staging,
+                                        void* device_plan, int64_t buffer_bytes,
+                                        int32_t* out_info, void* stream) {
+  SGG_CHECK(num_reqs == 0 || pruned_lens != nullptr, SGG_ERR_INVALID, "pruned_lens is NULL");
+  return plan_upload(true, pruned_lens, req_slots, num_reqs, lora_ranks, scalings, max_loras, 0,
+                     max_chunk_size, chunk_size_override, token_capacity, seg_capacity,
+                     req_capacity, host_staging, device_plan, buffer_bytes, out_info, stream);
 }

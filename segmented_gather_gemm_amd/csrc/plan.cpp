@@ -153,3 +153,86 @@ extern "C" int lora_plan_segments(const int32_t* seq_lens, const int32_t* req_sl
   if (out_num_tokens) *out_num_tokens = s;
   return sgg::ok();
 }
+
+// Plan of a pruned lm_head pass (chunked_backend.py page:
+// _prepare_lm_head_batch_info, _build_lm_head_batch_info).  The pruned tokens
+// stay in original order (identity permutation).  Segments come from the
+// page's merge_and_chunk_segments, which it imports but does not print; the
+// plain reading is taken: requests with no pruned token are dropped,
+// consecutive requests of one slot form a run, and each run is cut into
+// pieces of `chunk` tokens, remainder last.  The chunk follows the
+// token-count rule over the pruned total.
+extern "C" int lora_plan_lm_head(const int32_t* pruned_lens, const int32_t* req_slots,
+                                 int32_t num_reqs, int32_t max_loras, int32_t max_chunk_size,
+                                 int32_t chunk_size_override, int32_t* permutation,
+                                 int64_t perm_capacity, int32_t* seg_indptr, int32_t* seg_slots,
+                                 int32_t seg_capacity, int32_t* out_num_segments,
+                                 int32_t* out_chunk_size, int64_t* out_num_tokens) {
+  using sgg::fail;
+  if (num_reqs < 0) return fail(SGG_ERR_INVALID, "num_reqs=%d is negative", num_reqs);
+  if (max_loras <= 0) return fail(SGG_ERR_INVALID, "max_loras=%d must be positive", max_loras);
+  if (num_reqs > 0 && (req_slots == nullptr || pruned_lens == nullptr))
+    return fail(SGG_ERR_INVALID, "pruned_lens or req_slots is NULL");
+  if (chunk_size_override < 0)
+    return fail(SGG_ERR_INVALID, "chunk_size_override=%d is negative", chunk_size_override);
+  if (seg_capacity < 0) return fail(SGG_ERR_INVALID, "seg_capacity=%d is negative", seg_capacity);
+  if (seg_indptr == nullptr || (seg_capacity > 0 && seg_slots == nullptr))
+    return fail(SGG_ERR_INVALID, "seg_indptr / seg_slots is NULL");
+
+  int64_t s = 0;
+  for (int32_t r = 0; r < num_reqs; ++r) {
+    if (pruned_lens[r] < 0)
+      return fail(SGG_ERR_INVALID, "pruned_lens[%d]=%d is negative", r, pruned_lens[r]);
+    if (req_slots[r] < 0 || req_slots[r] >= max_loras)
+      return fail(SGG_ERR_CAPACITY, "req_slots[%d]=%d outside [0, %d)", r, req_slots[r],
+                  max_loras);
+    s += pruned_lens[r];
+  }
+  if (s > INT32_MAX) return fail(SGG_ERR_INVALID, "%lld tokens exceed int32 indexing",
+                                 static_cast<long long>(s));
+  if (s > 0 && permutation == nullptr) return fail(SGG_ERR_INVALID, "permutation is NULL");
+  if (perm_capacity < s)
+    return fail(SGG_ERR_CAPACITY, "permutation capacity %lld < %lld tokens",
+                static_cast<long long>(perm_capacity), static_cast<long long>(s));
+  const int32_t chunk = chunk_size_override > 0 ? chunk_size_override
+                                                : sgg::chunk_for_tokens(s, max_chunk_size);
+
+  // count the segments first (runs of one slot, chunked)
+  int64_t n_seg = 0;
+  for (int32_t r = 0; r < num_reqs;) {
+    if (pruned_lens[r] == 0) { ++r; continue; }
+    const int32_t slot = req_slots[r];
+    int64_t run = 0;
+    while (r < num_reqs && (pruned_lens[r] == 0 || req_slots[r] == slot)) run += pruned_lens[r++];
+    n_seg += (run + chunk - 1) / chunk;
+  }
+  if (n_seg > seg_capacity)
+    return fail(SGG_ERR_CAPACITY, "plan needs %lld segments, capacity is %d",
+                static_cast<long long>(n_seg), seg_capacity);
+
+  for (int64_t t = 0; t < s; ++t) permutation[t] = static_cast<int32_t>(t);
+  int64_t i = 0, start = 0;
+  seg_indptr[0] = 0;
+  for (int32_t r = 0; r < num_reqs;) {
+    if (pruned_lens[r] == 0) { ++r; continue; }
+    const int32_t slot = req_slots[r];
+    int64_t run = 0;
+    while (r < num_reqs && (pruned_lens[r] == 0 || req_slots[r] == slot)) run += pruned_lens[r++];
+    while (run > 0) {
+      const int64_t len = run < chunk ? run : chunk;
+      seg_slots[i] = slot;
+      start += len;
+      seg_indptr[i + 1] = static_cast<int32_t>(start);
+      ++i;
+      run -= len;
+    }
+  }
+  for (; i < seg_capacity; ++i) {
+    seg_slots[i] = 0;
+    seg_indptr[i + 1] = static_cast<int32_t>(s);
+  }
+  if (out_num_segments) *out_num_segments = static_cast<int32_t>(n_seg);
+  if (out_chunk_size) *out_chunk_size = chunk;
+  if (out_num_tokens) *out_num_tokens = s;
+  return sgg::ok();
+}

@@ -300,3 +300,47 @@ def test_plan_layout_regions():
     assert total == pos
     assert lib.lora_plan_layout(-1, 0, 0, 1, None) == -1
 
+
+def _lm_head_native(lens, slots, L, cap, override=0):
+    got = sgg.lora_plan_lm_head(lens, slots, L, cap, override)
+    n = got["num_segments"]
+    return {"permutation": got["permutation"].tolist(),
+            "seg_indptr": got["seg_indptr"][:n + 1].tolist(),
+            "seg_slots": got["seg_slots"][:n].tolist(), "num_segments": n,
+            "chunk_size": got["chunk_size"], "num_tokens": got["num_tokens"]}
+
+
+def test_lm_head_planner_matches_oracle_exhaustive():
+    """Every tiny pruned batch (bs <= 4, lengths 0..3, slots 0..2) and forced
+    chunks: the native lm_head planner equals the oracle bit for bit."""
+    for bs in range(0, 5):
+        for lens in itertools.product(range(0, 4), repeat=bs):
+            for slots in itertools.product(range(0, 3), repeat=bs):
+                for override in (0, 1, 2, 3):
+                    want = op.lm_head_plan(list(lens), list(slots), 128, override)
+                    got = _lm_head_native(list(lens), list(slots), 3, 128, override)
+                    for k in got:
+                        assert got[k] == want[k], (lens, slots, override, k)
+
+
+def test_lm_head_planner_matches_oracle_random():
+    rng = random.Random(11)
+    for _ in range(300):
+        bs = rng.randint(1, 64)
+        lens = [rng.choice([0, 1, 1, 1, 3, 20, 150, 700]) for _ in range(bs)]
+        slots = [rng.randrange(6) for _ in range(bs)]
+        cap = rng.choice([8, 16, 32, 64, 128, 256])
+        want = op.lm_head_plan(lens, slots, cap)
+        got = _lm_head_native(lens, slots, 6, cap)
+        for k in got:
+            assert got[k] == want[k], k
+
+
+def test_lm_head_planner_errors():
+    with pytest.raises(sgg.SggError):
+        sgg.lora_plan_lm_head([1, -1], [0, 0], 2, 128)
+    with pytest.raises(sgg.SggError):
+        sgg.lora_plan_lm_head([1, 1], [0, 2], 2, 128)     # slot outside [0, 2)
+    with pytest.raises(sgg.SggError):
+        sgg.lora_plan_lm_head([5, 5], [0, 1], 2, 128, seg_capacity=1)
+

@@ -375,6 +375,50 @@ def test_short_segments_in_groups():
     assert_close(y, want_y, "grouped y")
 
 
+def test_lm_head_pruned_pass():
+    """The pruned lm_head pass: tokens stay in original order (identity
+    permutation) and segments are runs of consecutive same-slot requests cut
+    into chunks.  Plan arrays bit-exact with the oracle; shrink and expand
+    over that plan against the oracle's per-token math on every element;
+    then per-pass plans over three request ranges, likewise."""
+    rng = np.random.default_rng(101)
+    bs = 96
+    slots = np.repeat(rng.integers(0, 6, size=40), rng.integers(1, 5, size=40))[:bs].tolist()
+    lens = rng.choice([0, 1, 1, 1, 1, 2, 7, 40, 180], size=bs).tolist()
+    ranks = [16, 8, 16, 0, 16, 12]
+    b, proj, t = _small_case(101, lens, slots, 6, ranks, rng.uniform(0.5, 2, 6).tolist(), 2048,
+                             [0, 5000], 16, nan_pad=True)
+    be = backend(b)
+    info = be.prepare_lm_head_batch(lens, slots, b.lora_ranks, b.scalings)
+    ref = op.lm_head_plan(lens, slots, 128)
+    n = info.num_segments
+    assert n == ref["num_segments"] and info.max_len == ref["chunk_size"]
+    assert info.permutation.cpu().tolist() == ref["permutation"]
+    assert info.seg_indptr[:n + 1].cpu().tolist() == ref["seg_indptr"]
+    assert info.weight_indices[:n].cpu().tolist() == ref["seg_slots"]
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    h = be.run_lora_a_sgemm(x, A, pruned_batch_info=info)
+    y = be.run_lora_b_sgemm(h, Bw, base_output=base.clone(), pruned_batch_info=info)
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, "lm_head h")
+    assert_close(y, want_y, "lm_head y")
+
+    cuts = [0, 30, 70, bs]
+    passes = [(slots[a:z], lens[a:z]) for a, z in zip(cuts, cuts[1:])]
+    infos = be.prepare_lm_head_pass_batches(passes, b.lora_ranks, b.scalings)
+    cum = np.concatenate([[0], np.cumsum(lens)])
+    for (wi, pl), pinfo, a, z in zip(passes, infos, cuts, cuts[1:]):
+        pref = op.lm_head_plan(pl, wi, 128)
+        pn = pinfo.num_segments
+        assert pinfo.seg_indptr[:pn + 1].cpu().tolist() == pref["seg_indptr"]
+        assert pinfo.weight_indices[:pn].cpu().tolist() == pref["seg_slots"]
+        rows = torch.arange(int(cum[a]), int(cum[z]), device=DEV)
+        if rows.numel() == 0:
+            continue
+        hp = be.run_lora_a_sgemm(x.index_select(0, rows).contiguous(), A, pruned_batch_info=pinfo)
+        assert_close(hp, want_h[int(cum[a]):int(cum[z])], f"lm_head pass {a}..{z} h")
+
+
 def test_request_permutation_and_merge():
     lens, slots = [7, 3, 20, 3, 50, 1], [1, 1, 0, 2, 0, 0]
     b, proj, t = _small_case(32, lens, slots, 3, [8, 8, 8], [1.0, 2.0, 0.5], 256,
