@@ -521,7 +521,105 @@ def test_lm_head_plan_invariants_and_chunk_rule():
             rows = op.token_slots(lens, slots)
             for i in range(pl["num_segments"]):
                 assert set(rows[ind[i]:ind[i + 1]]) == {pl["seg_slots"][i]}
+            # a segment is followed by one of its own slot only when it is a full chunk
+            for i in range(pl["num_segments"] - 1):
+                if pl["seg_slots"][i] == pl["seg_slots"][i + 1]:
+                    assert ind[i + 1] - ind[i] == pl["chunk_size"]
     padded = op.lm_head_plan([3, 0, 4], [1, 0, 1], 128, capacity=5)
     assert padded["seg_slots"] == [1, 0, 0, 0, 0]
     assert padded["seg_indptr"] == [0, 7, 7, 7, 7, 7]
 
+
+
+# ------------------------------------------ planted mistakes in the planner
+
+def _plan_pins_pass(mod):
+    """Run the page's worked examples, the hand-derived plans and the chunk
+    table against a planner module (expected values written by hand)."""
+    try:
+        ex = _load("plan_worked_examples.json")
+        pe, se, tiny = ex["permutation_example"], ex["segments_example"], ex["tiny_plan_hand_derived"]
+        p = mod.plan(pe["seq_lens"], pe["seq_weight_indices"], False, 128,
+                     chunk_override=se["chunk_size"])
+        if (p["permutation"], p["seg_slots"], p["seg_indptr"]) != (
+                pe["permutation"], se["weight_indices"], se["seg_indptr"]):
+            return False
+        p = mod.plan(tiny["seq_lens"], tiny["req_slots"], tiny["is_decode"], tiny["max_chunk_size"])
+        if any(p[k] != tiny[k] for k in ("chunk_size", "permutation", "seg_indptr", "seg_slots",
+                                         "req_seg_indptr")):
+            return False
+        for cap, row in CHUNK_TABLE.items():
+            if [mod.chunk_size_for_tokens(n, cap) for n in CHUNK_TABLE_TOKENS] != row:
+                return False
+        # graph padding: slot 0, zero-length segments (worked by hand)
+        p = mod.plan([2, 1, 3], [1, 0, 1], False, 128, capacity=5)
+        if (p["permutation"], p["seg_slots"], p["seg_indptr"]) != (
+                [2, 0, 1, 3, 4, 5], [0, 1, 0, 0, 0], [0, 1, 6, 6, 6, 6]):
+            return False
+        lm = _load("lm_head_plan_example.json")
+        got = mod.lm_head_plan(lm["pruned_lens"], lm["req_slots"], 128, lm["chunk_size_override"])
+        if any(got[k] != v for k, v in lm["expected"].items()):
+            return False
+        # a zero-token request of another slot does not split a run
+        got = mod.lm_head_plan([3, 0, 4], [1, 0, 1], 128)
+        if (got["seg_slots"], got["seg_indptr"]) != ([1], [0, 7]):
+            return False
+        # the chunk follows the pruned token count (300 tokens -> 128), not the request count
+        got = mod.lm_head_plan([300], [0], 128)
+        if (got["chunk_size"], got["seg_indptr"]) != (128, [0, 128, 256, 300]):
+            return False
+    except Exception:
+        return False
+    return True
+
+
+PLAN_MUTANTS = {
+    "sort descending": [
+        ("pairs = sorted((slot, t) for t, slot in enumerate(rows))",
+         "pairs = sorted(((slot, t) for t, slot in enumerate(rows)), reverse=True)")],
+    "ties in reverse token order": [
+        ("pairs = sorted((slot, t) for t, slot in enumerate(rows))",
+         "pairs = [(a, -b) for a, b in sorted((slot, -t) for t, slot in enumerate(rows))]")],
+    "remainder first": [
+        ("seg_lens.append(chunk if q < pieces - 1 else run - (pieces - 1) * chunk)",
+         "seg_lens.append(run - (pieces - 1) * chunk if q == 0 else chunk)")],
+    "256 threshold exclusive": [("if num_tokens >= 256:", "if num_tokens > 256:")],
+    "server cap ignored": [("return min(max_chunk_size, wanted)", "return wanted")],
+    "graph padding repeats the last slot": [
+        ("seg_slots = seg_slots + [0] * (capacity - num_segments)",
+         "seg_slots = seg_slots + seg_slots[-1:] * (capacity - num_segments)")],
+    "request boundaries count requests": [
+        ("out.append(out[-1] + length)", "out.append(out[-1] + 1)")],
+    "lm_head runs not merged": [("if runs and runs[-1][0] == slot:", "if False:")],
+    "lm_head zero-token requests kept": [
+        ("        if n == 0:\n            continue\n", "")],
+    "lm_head remainder first": [
+        ("seg_lens.append(chunk if q < pieces - 1 else n - (pieces - 1) * chunk)",
+         "seg_lens.append(n - (pieces - 1) * chunk if q == 0 else chunk)")],
+    "lm_head chunk from request count": [
+        ("chunk_size_for_tokens(total, max_chunk_size)",
+         "chunk_size_for_tokens(len(pruned_lens), max_chunk_size)")],
+    "lm_head tokens sorted by slot": [
+        ('"permutation": list(range(total)),',
+         '"permutation": gather_permutation(token_slots(pruned_lens, req_slots))[0],')],
+}
+
+
+def _plan_mutant_module(edits):
+    import types
+    src = open(op.__file__).read()
+    for old, new in edits:
+        assert old in src, old
+        src = src.replace(old, new, 1)
+    mod = types.ModuleType("plan_mutant")
+    exec(compile(src, "plan_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def test_plan_pins_pass_on_oracle():
+    assert _plan_pins_pass(op)
+
+
+@pytest.mark.parametrize("name", sorted(PLAN_MUTANTS))
+def test_plan_pins_catch_planted_mistake(name):
+    assert not _plan_pins_pass(_plan_mutant_module(PLAN_MUTANTS[name])), name
