@@ -78,9 +78,13 @@ def algo_counts(b, proj, emb_rank):
 
 
 def kernel_source_hash():
+    """First 16 hex digits of sha256 over the sources of libsgg_lora.so (the
+    planner, kernels and launch code; not the CPython call module)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "segmented_gather_gemm_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if not f.endswith((".hip", ".cpp", ".h")):
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -297,7 +301,7 @@ def run_decode(args, device):
         per[n] = {"avg_us": round(avg, 3), "algo_bytes": int(by), "algo_flops": int(fl),
                   "gbs": round(by / (avg * 1e-6) / 1e9, 1),
                   "tflops": round(fl / (avg * 1e-6) / 1e12, 3)}
-    # the stacked call as the step runs it (one fused launch for split-K tilings)
+    # the stacked call as the step runs it (shrink then expand, two launches)
     se_us = dur["qkv"]
     se_bytes = per["shrink"]["algo_bytes"] + per["expand"]["algo_bytes"]
     return {

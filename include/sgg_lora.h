@@ -142,14 +142,21 @@ int64_t lora_plan_layout(int64_t token_capacity, int32_t seg_capacity, int32_t r
  * (chunked_backend.py page: prepare_lora_batch, which plans on the host and
  *  copies the plan arrays to the device without blocking.)
  *
- *   host_staging   pinned host memory (hipHostMalloc) of buffer_bytes bytes.
- *                  The caller must not modify it until the copy is done
- *                  (e.g. by recording an event on `stream` after the call).
- *   device_plan    device memory of buffer_bytes bytes.
+ *   host_staging   pinned host memory (hipHostMalloc) of buffer_bytes bytes,
+ *                  8-byte aligned.  The caller must not modify it until the
+ *                  copy has read it: wait for done_flag, or for an event
+ *                  recorded on `stream` after the call.
+ *   device_plan    device memory of buffer_bytes bytes, 8-byte aligned.
  *   buffer_bytes   at least 4 * lora_plan_layout(...).
  *   lora_ranks, scalings  host arrays of max_loras entries.
  *   out_info[6]    host out: num_segments, chunk_size, longest segment,
  *                  num_tokens, number of work segments, longest work segment.
+ *   done_flag      NULL, or one int32 of pinned host memory mapped for the
+ *                  device: the copy writes done_value there (system scope)
+ *                  once it has read the whole staging buffer, so a caller
+ *                  that cycles through several staging buffers can tell when
+ *                  one is free again by reading host memory, without an
+ *                  event.  Not pinned and mapped: SGG_ERR_INVALID.
  * Segment and work-segment arrays are padded to seg_capacity with empty
  * segments of slot 0 (chunked_backend.py page: the CUDA-graph branch of
  * prepare_lora_batch pads the same way).
@@ -161,7 +168,7 @@ int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slots, int32_t 
                      int32_t is_decode, int32_t max_chunk_size, int32_t chunk_size_override,
                      int64_t token_capacity, int32_t seg_capacity, int32_t req_capacity,
                      void* host_staging, void* device_plan, int64_t buffer_bytes,
-                     int32_t* out_info, void* stream);
+                     int32_t* out_info, int32_t* done_flag, int32_t done_value, void* stream);
 
 /*
  * lora_plan_lm_head -- plan of a pruned lm_head pass.
@@ -191,8 +198,8 @@ int lora_plan_lm_head(const int32_t* pruned_lens, const int32_t* req_slots, int3
 /*
  * lora_plan_lm_head_upload -- as lora_plan_upload, for the lm_head plan of
  * lora_plan_lm_head: the same buffer layout (req_seg_indptr holds the
- * boundaries of each request's pruned tokens), work segments and single
- * transfer on `stream`.
+ * boundaries of each request's pruned tokens), work segments, done flag and
+ * single transfer on `stream`.
  */
 int lora_plan_lm_head_upload(const int32_t* pruned_lens, const int32_t* req_slots,
                              int32_t num_reqs, const int32_t* lora_ranks, const float* scalings,
@@ -200,7 +207,7 @@ int lora_plan_lm_head_upload(const int32_t* pruned_lens, const int32_t* req_slot
                              int32_t chunk_size_override, int64_t token_capacity,
                              int32_t seg_capacity, int32_t req_capacity, void* host_staging,
                              void* device_plan, int64_t buffer_bytes, int32_t* out_info,
-                             void* stream);
+                             int32_t* done_flag, int32_t done_value, void* stream);
 
 /*
  * lora_shrink -- LoRA-A segmented gather GEMM.

@@ -6,7 +6,7 @@ arguments to it; importing it fails if the library has not been built
 (``python segmented_gather_gemm_amd/build.py``).
 """
 
-from ._lib import SggError, lib
+from ._lib import SggError, calls, lib
 from .backend import ChunkedSgmvLoRA
 from .binding import (
     LoRABatchInfo,
@@ -21,6 +21,7 @@ from .binding import (
 )
 
 lib()  # load now: a missing library is an import error, never a silent fallback
+calls()
 
 __all__ = [
     "ChunkedSgmvLoRA", "LoRABatchInfo", "SggError", "default_workspace", "lora_a_embedding",

@@ -1,9 +1,15 @@
-"""ctypes view of libsgg_lora.so (the C ABI declared in include/sgg_lora.h)."""
+"""Views of libsgg_lora.so (the C ABI declared in include/sgg_lora.h).
+
+``lib()`` is a ctypes handle with every entry point; ``calls()`` is the
+CPython module ``_sggcall`` with the hot entry points (plan upload, shrink,
+expand, qkv, embedding), which take integer arguments and cost far less per
+call than ctypes.
+"""
 
 import ctypes
 import os
 
-from .build import LIB
+from .build import CALLMOD, LIB
 
 _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 _pi32, _pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
@@ -21,10 +27,10 @@ SIGNATURES = {
     # host arrays are passed as addresses (NumPy .ctypes.data) on this hot call
     "lora_plan_upload": (ctypes.c_int, [
         _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
-        _i64, _i32, _i32, _vp, _vp, _i64, _vp, _vp]),
+        _i64, _i32, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _vp]),
     "lora_plan_lm_head_upload": (ctypes.c_int, [
         _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
-        _i64, _i32, _i32, _vp, _vp, _i64, _vp, _vp]),
+        _i64, _i32, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _vp]),
     "lora_shrink_workspace_bytes": (_i64, [_i64, _i64, _i32, _i32, _i32, _i32]),
     "lora_shrink": (ctypes.c_int, [
         _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
@@ -68,6 +74,22 @@ def lib():
             fn.argtypes = args
         _lib = handle
     return _lib
+
+
+_calls = None
+
+
+def calls():
+    """The CPython call module over the library.  Raises if it has not been built."""
+    global _calls
+    if _calls is None:
+        if not os.path.exists(CALLMOD):
+            raise ImportError(
+                f"{CALLMOD} is missing: build it with `python segmented_gather_gemm_amd/build.py`")
+        lib()
+        from . import _sggcall
+        _calls = _sggcall
+    return _calls
 
 
 def check(rc):

@@ -21,12 +21,13 @@ after them).
 """
 
 import ctypes
+import time
 
 import numpy as np
 import torch
 
 from . import binding as B
-from ._lib import check, lib
+from ._lib import calls, check, lib
 from .binding import LoRABatchInfo
 
 _P32 = ctypes.POINTER(ctypes.c_int32)
@@ -40,33 +41,37 @@ def _align(n, m=64):
 
 class _Staging:
     """Ring of plan buffers: pinned host staging plus a device plan buffer per
-    slot, each slot guarded by the event of its last upload.
+    slot.
 
-    A slot is reused only after the upload that last read its staging buffer
-    has completed.  Its device buffer is then rewritten by an upload enqueued
-    after every kernel launched before it on the same stream, so the kernels
-    of a batch read its plan intact as long as they run on the stream the
-    batch was prepared on.  The wait polls the event instead of blocking in
-    the driver: a sleeping wait wakes up tens of microseconds late, which a
-    serving loop that plans each batch while the previous one runs cannot
-    afford.
+    A slot's staging buffer is reused only after the upload that last read it
+    has done so: the upload's copy kernel writes the slot's sequence number
+    into a pinned flag word once it has read the staging buffer, and taking
+    the slot polls that word in host memory (no event, no driver call: a
+    sleeping wait wakes up tens of microseconds late, which a serving loop
+    that plans each batch while the previous one runs cannot afford).  The
+    slot's device buffer is then rewritten by an upload enqueued after every
+    kernel launched before it on the same stream, so the kernels of a batch
+    read its plan intact as long as they run on the stream the batch was
+    prepared on.
     """
 
     def __init__(self, device, slots=8):
         self.device = device
         self.host = [None] * slots
         self.dev = [None] * slots
-        self.events = [None] * slots
         self.infos = [{} for _ in range(slots)]   # layout key -> LoRABatchInfo views
+        self.flags = torch.zeros(slots, dtype=torch.int32, pin_memory=True)
+        self.flag_view = self.flags.numpy()
+        self.flag_addr = self.flags.data_ptr()
+        self.seq = [0] * slots
         self.i = 0
 
     def take(self, n):
         i = self.i
         self.i = (i + 1) % len(self.host)
-        ev = self.events[i]
-        if ev is not None:
-            while not ev.query():
-                pass
+        want, flags = self.seq[i], self.flag_view
+        if flags[i] != want:
+            self._wait(i, want)
         if self.host[i] is None or self.host[i].numel() < n:
             size = max(n, 4096)
             self.host[i] = torch.empty(size, dtype=torch.int32, pin_memory=True)
@@ -74,11 +79,26 @@ class _Staging:
             self.infos[i] = {}
         return i
 
-    def done(self, i, stream):
-        ev = self.events[i]
-        if ev is None:
-            ev = self.events[i] = torch.cuda.Event()
-        ev.record(stream)
+    def _wait(self, i, want, limit_s=30.0):
+        """Poll slot i's flag; raise if the upload has not read its staging
+        buffer within `limit_s` seconds (its stream never ran it)."""
+        flags = self.flag_view
+        t0 = time.monotonic()
+        n = 0
+        while flags[i] != want:
+            n += 1
+            if n % 4096 == 0 and time.monotonic() - t0 > limit_s:
+                raise RuntimeError(
+                    f"plan staging slot {i}: the upload enqueued {limit_s:.0f} s ago has not "
+                    "run (is its stream blocked?)")
+
+    def signal(self, i):
+        """Flag address and value that the next upload from slot i writes."""
+        return self.flag_addr + 4 * i, (self.seq[i] + 1) & 0x7FFFFFFF
+
+    def done(self, i):
+        """The upload from slot i was enqueued: wait for its flag next time."""
+        self.seq[i] = (self.seq[i] + 1) & 0x7FFFFFFF
 
 
 _NAMES = ("permutation", "seg_indptr", "seg_slots", "req_seg_indptr", "req_slots", "ranks",
@@ -103,6 +123,7 @@ class ChunkedSgmvLoRA:
         self._staging = _Staging(self.device)
         self._layouts = {}
         self._info_arr = (ctypes.c_int32 * 6)()
+        self._info_addr = ctypes.addressof(self._info_arr)
 
     # ---------------------------------------------------------------- plan
     def _layout(self, s_cap, seg_cap, req_cap):
@@ -154,12 +175,13 @@ class ChunkedSgmvLoRA:
         idx = self.device.index if self.device.index is not None else torch.cuda.current_device()
         stream = torch._C._cuda_getCurrentRawStream(idx)
         info = self._info_arr
-        check(lib().lora_plan_upload(
+        flag, flag_value = stg.signal(ring)
+        check(calls().lora_plan_upload(
             None if lens is None else lens.ctypes.data, slots.ctypes.data, bs, ranks.ctypes.data,
             scal.ctypes.data, L, 1 if is_decode else 0, self.max_chunk_size,
             int(chunk_size_override), s_cap, seg_cap, req_cap, stg.host[ring].data_ptr(),
-            dev.data_ptr(), 4 * dev.numel(), info, stream))
-        stg.done(ring, torch.cuda.current_stream(self.device))
+            dev.data_ptr(), 4 * dev.numel(), self._info_addr, flag, flag_value, stream))
+        stg.done(ring)
         n_seg, chunk, longest, n_work, longest_work = info[0], info[1], info[2], info[4], info[5]
         if use_cuda_graph:
             # fixed views and launch shape: capacity segments over capacity tokens
@@ -232,11 +254,12 @@ class ChunkedSgmvLoRA:
         idx = self.device.index if self.device.index is not None else torch.cuda.current_device()
         stream = torch._C._cuda_getCurrentRawStream(idx)
         info = self._info_arr
-        check(lib().lora_plan_lm_head_upload(
+        flag, flag_value = stg.signal(ring)
+        check(calls().lora_plan_lm_head_upload(
             lens.ctypes.data, slots.ctypes.data, bs, ranks.ctypes.data, scal.ctypes.data, L,
             self.max_chunk_size, int(override), s, seg_cap, bs, stg.host[ring].data_ptr(),
-            dev.data_ptr(), 4 * dev.numel(), info, stream))
-        stg.done(ring, torch.cuda.current_stream(self.device))
+            dev.data_ptr(), 4 * dev.numel(), self._info_addr, flag, flag_value, stream))
+        stg.done(ring)
         n_seg, chunk, longest, n_work, longest_work = info[0], info[1], info[2], info[4], info[5]
         v = {name: dev[o:o + n] for name, (o, n) in zip(_NAMES, regions)}
         # a fresh LoRABatchInfo (not one of the eager step's cached views)

@@ -13,7 +13,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from ._lib import check, lib
+from ._lib import calls, check, lib
 
 _P32 = ctypes.POINTER(ctypes.c_int32)
 _P64 = ctypes.POINTER(ctypes.c_int64)
@@ -100,7 +100,7 @@ def _need_dense(name, t):
 
 
 def lora_plan_max_segments(num_tokens, max_loras, min_chunk=16):
-    return int(lib().lora_plan_max_segments(int(num_tokens), int(max_loras), int(min_chunk)))
+    return calls().lora_plan_max_segments(int(num_tokens), int(max_loras), int(min_chunk))
 
 
 def lora_plan_segments(seq_lens, req_slots, max_loras, is_decode, max_chunk_size,
@@ -206,7 +206,7 @@ _offset_cache = {}
 
 
 def _offsets(slice_offsets):
-    """Host int32 copy of the slice offsets (cached for lists and tuples)."""
+    """Host int32 copy of the slice offsets and its address (cached for lists and tuples)."""
     key = tuple(slice_offsets) if isinstance(slice_offsets, (list, tuple)) else None
     if key is not None:
         hit = _offset_cache.get(key)
@@ -214,12 +214,13 @@ def _offsets(slice_offsets):
             return hit
     if isinstance(slice_offsets, torch.Tensor):
         slice_offsets = slice_offsets.detach().to("cpu")  # host copy (synchronises if on device)
-    arr, ptr = _host_i32(slice_offsets)
+    arr = np.ascontiguousarray(np.asarray(slice_offsets, dtype=np.int32))
     if arr.ndim != 1 or len(arr) < 2:
         raise ValueError("slice_offsets needs at least two entries")
+    hit = (arr, arr.ctypes.data)
     if key is not None and len(_offset_cache) < 256:
-        _offset_cache[key] = (arr, ptr)
-    return arr, ptr
+        _offset_cache[key] = hit
+    return hit
 
 
 # ---------------------------------------------------------------- device calls
@@ -244,9 +245,9 @@ def lora_shrink(x, weights, batch_info: LoRABatchInfo, num_slices=1, out=None, w
     ind, sl, nseg, hint = batch_info.kernel_segments()
     ws = workspace
     if ws is None:   # the library checks the size of a caller's workspace itself
-        need = int(lib().lora_shrink_workspace_bytes(s, K, num_slices, R, nseg, hint))
+        need = calls().lora_shrink_workspace_bytes(s, K, num_slices, R, nseg, hint)
         ws = default_workspace(x.device, need) if need else None
-    check(lib().lora_shrink(
+    check(calls().lora_shrink(
         _vp(x), x.stride(0), _vp(weights), _vp(out), out.stride(0), s, K, L, num_slices, R,
         _vp(ind), _vp(sl), nseg, _vp(batch_info.permutation), _vp(batch_info.lora_ranks), hint,
         _vp(ws), ws.numel() if ws is not None else 0, _stream(x.device)))
@@ -274,7 +275,7 @@ def lora_expand(h, weights, batch_info: LoRABatchInfo, slice_offsets, max_slice_
     if base_output.shape[0] != s:
         raise ValueError("base_output rows differ from h rows")
     ind, sl, nseg, hint = batch_info.kernel_segments()
-    check(lib().lora_expand(
+    check(calls().lora_expand(
         _vp(h), h.stride(0), _vp(weights), N, _vp(base_output), base_output.stride(0), s, L, R,
         p_offs, c, int(max_slice_size), _vp(ind), _vp(sl), nseg, _vp(batch_info.permutation),
         _vp(batch_info.lora_ranks), _vp(batch_info.scalings), hint, _stream(h.device)))
@@ -304,9 +305,9 @@ def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
     ind, sl, nseg, hint = batch_info.kernel_segments()
     ws = workspace
     if ws is None:   # the library checks the size of a caller's workspace itself
-        need = int(lib().lora_qkv_workspace_bytes(s, K, c, R, nseg, hint))
+        need = calls().lora_qkv_workspace_bytes(s, K, c, R, nseg, hint)
         ws = default_workspace(x.device, max(need, 1))
-    check(lib().lora_qkv(
+    check(calls().lora_qkv(
         _vp(x), x.stride(0), _vp(A), _vp(B), N, _vp(base_output), base_output.stride(0), s, K,
         L, R, p_offs, c, int(max_slice_size), _vp(ind), _vp(sl), nseg,
         _vp(batch_info.permutation), _vp(batch_info.lora_ranks), _vp(batch_info.scalings), hint,
@@ -329,7 +330,7 @@ def lora_a_embedding(input_ids, weights, batch_info: LoRABatchInfo, vocab_size,
         out = torch.empty((s, R), dtype=torch.bfloat16, device=weights.device)
     # the plan's own segments: the gather parallelises over segments, so the
     # finer partition is the faster one here
-    check(lib().lora_a_embedding(
+    check(calls().lora_a_embedding(
         _vp(input_ids.contiguous()), _vp(weights), V, _vp(out), out.stride(0), s, L, R,
         int(vocab_size), _vp(batch_info.seg_indptr), _vp(batch_info.weight_indices),
         batch_info.num_segments, _vp(batch_info.permutation),

@@ -1,12 +1,16 @@
-"""Compile libsgg_lora.so (host planner + gfx950 HIP kernels) in the package directory."""
+"""Compile libsgg_lora.so (host planner + gfx950 HIP kernels) and the CPython
+call module over it, in the package directory."""
 
 import os
 import subprocess
 import sys
+import sysconfig
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsgg_lora.so")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
+CALLMOD = os.path.join(PKG, "_sggcall" + sysconfig.get_config_var("EXT_SUFFIX"))
 SOURCES = ["plan.cpp", "shrink.hip", "shrink_gemm.hip", "expand.hip", "lora_api.hip"]
 ARCH = os.environ.get("SGG_OFFLOAD_ARCH", "gfx950")
 
@@ -24,18 +28,29 @@ def hipcc():
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(verbose=False):
-    """Build the shared library; always recompiles.  Returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + srcs + ["-o", tmp]
+def _run(cmd, verbose, what):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+        raise RuntimeError(f"{what} failed with status {res.returncode}")
+
+
+def build(verbose=False):
+    """Build the shared library and the CPython call module; always
+    recompiles.  Returns the library's path."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    _run([hipcc()] + HIPCC_FLAGS + srcs + ["-o", tmp], verbose, "hipcc")
     os.replace(tmp, LIB)
+    # integer-argument entry points for the hot calls, linked to the library
+    tmp = CALLMOD + ".tmp"
+    _run([os.environ.get("CC", "gcc"), "-O2", "-shared", "-fPIC", "-Wall",
+          "-I", sysconfig.get_paths()["include"], "-I", INCLUDE,
+          os.path.join(CSRC, "pycall.c"), "-L", PKG, "-lsgg_lora",
+          "-Wl,-rpath,$ORIGIN", "-o", tmp], verbose, "cc")
+    os.replace(tmp, CALLMOD)
     return LIB
 
 

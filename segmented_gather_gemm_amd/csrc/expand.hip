@@ -31,7 +31,7 @@ template <int P, int KS>
 __global__ __launch_bounds__(256) void expand_kernel(ExpandParams p) {
   __shared__ __attribute__((aligned(16))) char smem[detail::ExpandShape<P, KS>::SMEM];
   int seg, tile;
-  if (!detail::expand_item_of(p, blockIdx.x, gridDim.x, &seg, &tile)) return;
+  if (!detail::expand_item_of(p, blockIdx.x, &seg, &tile)) return;
   detail::expand_tile<P, KS>(p, seg, tile, smem);
 }
 
@@ -129,34 +129,50 @@ hipError_t launch_embedding(const EmbeddingParams& p, hipStream_t stream) {
 
 namespace {
 
-// Each thread issues its four loads before any store, so a small plan costs
-// one host-memory round trip rather than one per element.
-__global__ __launch_bounds__(256) void plan_copy_kernel(const int32_t* src, int32_t* dst, int64_t n) {
-  const int64_t step = static_cast<int64_t>(gridDim.x) * 256;
-  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i0 < n; i0 += 4 * step) {
-    int32_t v[4];
+constexpr int kCopyThreads = 1024;
+constexpr int kCopyDepth = 8;  // 8-byte loads in flight per thread
+
+// One workgroup copies the whole plan.  Each thread requests kCopyDepth
+// 8-byte pieces before storing any, so a plan of up to 64 KB costs one
+// host-memory round trip.  Once every thread has stored its pieces the
+// staging buffer has been read in full; thread 0 then writes `done_value` to
+// `done` (host memory, system scope), if given, so the host can reuse the
+// staging buffer without an event.
+__global__ __launch_bounds__(kCopyThreads) void plan_copy_kernel(const int32_t* src, int32_t* dst,
+                                                                 int64_t n, int32_t* done,
+                                                                 int32_t done_value) {
+  const int64_t n2 = n >> 1;
+  const uint64_t* s2 = reinterpret_cast<const uint64_t*>(src);
+  uint64_t* d2 = reinterpret_cast<uint64_t*>(dst);
+  for (int64_t i0 = threadIdx.x; i0 < n2; i0 += static_cast<int64_t>(kCopyThreads) * kCopyDepth) {
+    uint64_t v[kCopyDepth];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = i0 + u * step;
-      v[u] = i < n ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : 0;
+    for (int u = 0; u < kCopyDepth; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * kCopyThreads;
+      v[u] = i < n2 ? __hip_atomic_load(s2 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : 0;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = i0 + u * step;
-      if (i < n) dst[i] = v[u];
+    for (int u = 0; u < kCopyDepth; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * kCopyThreads;
+      if (i < n2) d2[i] = v[u];
     }
+  }
+  if ((n & 1) && threadIdx.x == 0)
+    dst[n - 1] = __hip_atomic_load(src + n - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (done != nullptr) {
+    __syncthreads();  // every thread's loads have returned (their values are stored)
+    if (threadIdx.x == 0)
+      __hip_atomic_store(done, done_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
 }
 
 }  // namespace
 
 hipError_t launch_plan_copy(const int32_t* src_dev_view, int32_t* dst, int64_t n,
-                            hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  int64_t blocks = (n + 1023) / 1024;
-  if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(plan_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                     src_dev_view, dst, n);
+                            int32_t* done_dev_view, int32_t done_value, hipStream_t stream) {
+  if (n <= 0 && done_dev_view == nullptr) return hipSuccess;
+  hipLaunchKernelGGL(plan_copy_kernel, dim3(1), dim3(kCopyThreads), 0, stream, src_dev_view, dst,
+                     n < 0 ? 0 : n, done_dev_view, done_value);
   return hipGetLastError();
 }
 

@@ -23,18 +23,10 @@ struct ExpandShape {
   static constexpr int SMEM = HTILE_BYTES + PROW_BYTES + ACCT_BYTES;
 };
 
-// Work item of block b in a grid of G blocks: false for the padding blocks of
-// a round-robin grid.
-__device__ __forceinline__ bool expand_item_of(const ExpandParams& p, int b, int G, int* seg,
-                                               int* tile) {
-  if (p.round_robin) {
-    segment_round_robin(b, p.total_tiles, seg, tile);
-    return *seg < p.num_segments;
-  }
-  const int L = xcd_contiguous(b, G);
-  *seg = L / p.total_tiles;
-  *tile = L % p.total_tiles;
-  return true;
+// Work item of block b: false for the padding blocks of the grid.
+__device__ __forceinline__ bool expand_item_of(const ExpandParams& p, int b, int* seg, int* tile) {
+  segment_round_robin(b, p.total_tiles, seg, tile);
+  return *seg < p.num_segments;
 }
 
 // Column tile `tile` of segment `seg`; `smem` holds ExpandShape<P, KS>::SMEM

@@ -130,7 +130,6 @@ sgg::ShrinkParams shrink_params(const void* x, int64_t ldx, const void* A, void*
   p.partial = static_cast<float*>(partial);
   p.counters = counters;
   p.counter_cap = sgg::kCounterCap;
-  p.round_robin = num_segments < sgg::kRoundRobinBelow ? 1 : 0;
   p.seg_indptr = seg_indptr;
   p.seg_slots = seg_slots;
   p.perm = permutation;
@@ -206,7 +205,6 @@ sgg::ExpandParams expand_params(const void* h, int64_t ldh, const void* B, int64
   p.c = c;
   p.num_segments = num_segments;
   p.vec8 = vec8 ? 1 : 0;
-  p.round_robin = num_segments < sgg::kRoundRobinBelow ? 1 : 0;
   return p;
 }
 
@@ -414,7 +412,8 @@ int plan_upload(bool lm_head, const int32_t* seq_lens, const int32_t* req_slots,
                 int32_t max_loras, int32_t is_decode, int32_t max_chunk_size,
                 int32_t chunk_size_override, int64_t token_capacity, int32_t seg_capacity,
                 int32_t req_capacity, void* host_staging, void* device_plan,
-                int64_t buffer_bytes, int32_t* out_info, void* stream) {
+                int64_t buffer_bytes, int32_t* out_info, int32_t* done_flag,
+                int32_t done_value, void* stream) {
 
   int64_t off[SGG_PLAN_REGIONS];
   const int64_t total = lora_plan_layout(token_capacity, seg_capacity, req_capacity, max_loras, off);
@@ -422,6 +421,19 @@ int plan_upload(bool lm_head, const int32_t* seq_lens, const int32_t* req_slots,
   SGG_CHECK(host_staging && device_plan && out_info, SGG_ERR_INVALID,
             "host_staging, device_plan or out_info is NULL");
   SGG_CHECK(lora_ranks && scalings, SGG_ERR_INVALID, "lora_ranks or scalings is NULL");
+  SGG_CHECK(((reinterpret_cast<uintptr_t>(host_staging) | reinterpret_cast<uintptr_t>(device_plan)) &
+             7) == 0,
+            SGG_ERR_INVALID, "host_staging and device_plan must be 8-byte aligned");
+  int32_t* done_dev = nullptr;
+  if (done_flag != nullptr) {
+    void* m = nullptr;
+    const hipError_t me = hipHostGetDevicePointer(&m, done_flag, 0);
+    if (me != hipSuccess || m == nullptr) {
+      (void)hipGetLastError();
+      return fail(SGG_ERR_INVALID, "done_flag is not pinned host memory mapped for the device");
+    }
+    done_dev = static_cast<int32_t*>(m);
+  }
   SGG_CHECK(buffer_bytes >= total * 4, SGG_ERR_CAPACITY,
             "plan buffer of %" PRId64 " bytes, layout needs %" PRId64, buffer_bytes, total * 4);
   SGG_CHECK(num_reqs <= req_capacity, SGG_ERR_CAPACITY, "%d requests > capacity %d", num_reqs,
@@ -479,16 +491,20 @@ int plan_upload(bool lm_head, const int32_t* seq_lens, const int32_t* req_slots,
     wind[i + 1] = wind[n_work];
   }
   // One transfer: a copy kernel reading the pinned buffer through its device
-  // mapping; a runtime copy only if the buffer has no device mapping.
+  // mapping (it also raises the done flag); a runtime copy only if the buffer
+  // has no device mapping, followed by an empty copy that raises the flag.
   void* src = nullptr;
   hipError_t e = hipHostGetDevicePointer(&src, host_staging, 0);
   if (e == hipSuccess && src != nullptr) {
     e = sgg::launch_plan_copy(static_cast<const int32_t*>(src), static_cast<int32_t*>(device_plan),
-                              total, static_cast<hipStream_t>(stream));
+                              total, done_dev, done_value, static_cast<hipStream_t>(stream));
   } else {
     (void)hipGetLastError();  // clear the failed lookup
     e = hipMemcpyAsync(device_plan, host_staging, static_cast<size_t>(total) * 4,
                        hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess && done_dev != nullptr)
+      e = sgg::launch_plan_copy(nullptr, nullptr, 0, done_dev, done_value,
+                                static_cast<hipStream_t>(stream));
   }
   if (e != hipSuccess)
     return fail(SGG_ERR_HIP, "plan upload failed: %s", hipGetErrorString(e));
@@ -509,11 +525,12 @@ extern "C" int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slot
                                 int32_t max_chunk_size, int32_t chunk_size_override,
                                 int64_t token_capacity, int32_t seg_capacity,
                                 int32_t req_capacity, void* host_staging, void* device_plan,
-                                int64_t buffer_bytes, int32_t* out_info, void* stream) {
+                                int64_t buffer_bytes, int32_t* out_info, int32_t* done_flag,
+                                int32_t done_value, void* stream) {
   return plan_upload(false, seq_lens, req_slots, num_reqs, lora_ranks, scalings, max_loras,
                      is_decode, max_chunk_size, chunk_size_override, token_capacity,
                      seg_capacity, req_capacity, host_staging, device_plan, buffer_bytes,
-                     out_info, stream);
+                     out_info, done_flag, done_value, stream);
 }
 
 extern "C" int lora_plan_lm_head_upload(const int32_t* pruned_lens, const int32_t* req_slots,
@@ -523,9 +540,11 @@ extern "C" int lora_plan_lm_head_upload(const int32_t* pruned_lens, const int32_
                                         int64_t token_capacity, int32_t seg_capacity,
                                         int32_t req_capacity, void* host_staging,
                                         void* device_plan, int64_t buffer_bytes,
-                                        int32_t* out_info, void* stream) {
+                                        int32_t* out_info, int32_t* done_flag,
+                                        int32_t done_value, void* stream) {
   SGG_CHECK(num_reqs == 0 || pruned_lens != nullptr, SGG_ERR_INVALID, "pruned_lens is NULL");
   return plan_upload(true, pruned_lens, req_slots, num_reqs, lora_ranks, scalings, max_loras, 0,
                      max_chunk_size, chunk_size_override, token_capacity, seg_capacity,
-                     req_capacity, host_staging, device_plan, buffer_bytes, out_info, stream);
+                     req_capacity, host_staging, device_plan, buffer_bytes, out_info, done_flag,
+                     done_value, stream);
 }

@@ -55,24 +55,20 @@ __device__ __forceinline__ f32x4 mfma16x16x32(uint4 a, uint4 b, f32x4 c) {
 }
 
 // Blocks are handed to the XCDs round-robin (block b runs on XCD b % 8).
-// Return a logical index such that each XCD receives one contiguous range of
-// logical indices, so neighbouring work items (which share weight tiles)
-// meet in the same L2.  A bijection on [0, G).
-__device__ __forceinline__ int xcd_contiguous(int b, int G) {
-  int q = G / kXcds, r = G % kXcds;
-  int x = b % kXcds, l = b / kXcds;
-  return x < r ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
-}
-
-// Segments dealt round-robin to the XCDs: block b (on XCD b % 8) takes
+// Segments are dealt round-robin to the XCDs the same way: block b takes
 // segment (b % 8) + 8 * ((b / 8) / per) and item (b / 8) % per of it, so the
-// items of one segment share an XCD and the first segments -- the real ones
-// when trailing segments are capacity padding -- spread over all XCDs.
-// Launch with 8 * ceil(num_segments / 8) * per blocks.
+// items of one segment share an XCD (and its L2), while consecutive segments
+// -- the full chunks of a dominant adapter, or the real segments ahead of a
+// graph's capacity padding -- spread over all XCDs.  Measured against
+// dealing groups of consecutive segments (up to one contiguous range per
+// XCD): single segments are as fast or faster on every workload, and with
+// one adapter holding most tokens contiguous ranges make the expand take
+// 1.7x as long, its full chunks crowding onto two or three XCDs.
+// Launch with grid_for(num_segments, per) blocks.
 __device__ __forceinline__ void segment_round_robin(int b, int per, int* seg, int* item) {
-  const int x = b % kXcds, local = b / kXcds;
-  *seg = x + kXcds * (local / per);
-  *item = local % per;
+  const int x = b % kXcds, l = b / kXcds;
+  *seg = x + kXcds * (l / per);
+  *item = l % per;
 }
 
 }  // namespace sgg

@@ -30,7 +30,6 @@ struct ShrinkParams {
   int32_t nblocks;            // column blocks over CR
   int32_t ksplit;             // K ranges (one workgroup each)
   int32_t counter_cap;        // entries in `counters`
-  int32_t round_robin;        // segment-to-XCD mapping: 1 round-robin, 0 contiguous ranges
   int32_t partials_only;      // ksplit > 1: leave the partials for the expand, write no h
 };
 
@@ -56,16 +55,10 @@ struct ExpandParams {
   int32_t offs[kMaxSlices + 1];
   int32_t tile_start[kMaxSlices + 1];  // first column tile of each slice
   int32_t total_tiles;
-  int32_t round_robin;        // segment-to-XCD mapping: 1 round-robin, 0 contiguous ranges
 };
-// Below this many segments, work is dealt to XCDs segment by segment
-// (balance); at or above it, each XCD takes a contiguous range (L2 sharing of
-// an adapter's weights across its consecutive segments).
-constexpr int kRoundRobinBelow = 64;
+// Grid of a segment_round_robin launch: whole rounds of 8 segments.
 inline int64_t grid_for(int num_segments, int64_t per_segment) {
-  if (num_segments < kRoundRobinBelow)
-    return static_cast<int64_t>((num_segments + 7) / 8) * 8 * per_segment;
-  return static_cast<int64_t>(num_segments) * per_segment;
+  return static_cast<int64_t>((num_segments + 7) / 8) * 8 * per_segment;
 }
 
 // LoRA-A embedding lookup over the segments of a plan.
@@ -105,8 +98,10 @@ hipError_t launch_expand(const ExpandParams& p, const ExpandTiling& t, hipStream
 hipError_t launch_embedding(const EmbeddingParams& p, hipStream_t stream);
 
 // Copy n int32 from pinned host memory (given by its device-side address) to
-// device memory, as a kernel on `stream`.
+// device memory, as a kernel on `stream`; src and dst 8-byte aligned.  When
+// done_dev_view is not null (host memory, by its device-side address),
+// done_value is written there once the source has been read in full.
 hipError_t launch_plan_copy(const int32_t* src_dev_view, int32_t* dst, int64_t n,
-                            hipStream_t stream);
+                            int32_t* done_dev_view, int32_t done_value, hipStream_t stream);
 
 }  // namespace sgg

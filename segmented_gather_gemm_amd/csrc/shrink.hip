@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256, 1) void shrink_kernel(ShrinkParams p) {
   __shared__ __attribute__((aligned(16))) char smem[detail::ShrinkShape<MF, NF>::SMEM];
   __shared__ int last_flag;
   int seg, item;
-  if (!detail::shrink_item_of(p, blockIdx.x, gridDim.x, &seg, &item)) return;
+  if (!detail::shrink_item_of(p, blockIdx.x, &seg, &item)) return;
   detail::shrink_tile<MF, NF>(p, seg, item, smem, &last_flag);
 }
 
@@ -128,14 +128,20 @@ ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments
     t.partial_bytes = round_up(static_cast<int64_t>(t.ksplit) * s * CR * 4, 256);
     return t;
   }
-  // No K split needed: the workgroup-shared GEMM tiles.  Tokens: 128 per
-  // tile for segments longer than 64, else 64; rank rows: the smallest of
-  // 32 / 64 / 128 covering c*R; then halve the rows, then the tokens, while
-  // the grid has fewer work items than CUs.  Measured: the GEMM kernel is
-  // 1.5x faster on prefill gate_up and skewed o_proj, slower on grids under
-  // one workgroup per CU.
-  int gm = chunk > 64 ? 128 : 64;
-  int gn = CR <= 32 ? 32 : (CR <= 64 ? 64 : 128);
+  // No K split needed: the workgroup-shared GEMM tiles.  Batches of long
+  // segments (mean work segment of 96 tokens or more, e.g. prefill) take
+  // 128 tokens per tile and rank rows the smallest of 32 / 64 / 128 covering
+  // c*R; batches of short segments (decode mixed in, many adapters, a long
+  // tail of one-request adapters) take 64 x 32 tiles, whose larger grid
+  // spreads the long segments over more CUs.  Then halve the rows, then the
+  // tokens, while the grid has fewer work items than CUs.  Measured: 64 x 32
+  // beats 128 x 32 by 10-20 % on the mixed and skewed batches (full-layer
+  // qkv 44 -> 39 us, skewed down_proj 202 -> 185 us), 128 x 128 beats every
+  // smaller tile by 25 % or more on prefill; the split-K kernel is faster on
+  // grids under one workgroup per CU.
+  const bool long_segments = num_segments > 0 && s >= 96 * static_cast<int64_t>(num_segments);
+  int gm = long_segments && chunk > 64 ? 128 : 64;
+  int gn = !long_segments ? 32 : (CR <= 32 ? 32 : (CR <= 64 ? 64 : 128));
   auto gemm_units = [&](int m, int n) {
     const int64_t mb = (chunk + m - 1) / m, nbk = (CR + n - 1) / n;
     const int64_t grid_units = static_cast<int64_t>(num_segments) * mb;

@@ -45,17 +45,8 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
   const int wm = wave % WM, wn = wave / WM;
 
   int seg, item;
-  {
-    const int per = p.mblocks * p.nblocks;
-    if (p.round_robin) {
-      segment_round_robin(blockIdx.x, per, &seg, &item);
-      if (seg >= p.num_segments) return;
-    } else {
-      const int L = xcd_contiguous(blockIdx.x, gridDim.x);
-      seg = L / per;
-      item = L % per;
-    }
-  }
+  segment_round_robin(blockIdx.x, p.mblocks * p.nblocks, &seg, &item);
+  if (seg >= p.num_segments) return;
   const int mb0 = item % p.mblocks;
   const int nb = item / p.mblocks;
   // segment bounds, clamped to [0, s) so a malformed plan stays in bounds
@@ -113,9 +104,10 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
       xrow[j] = p.x + static_cast<int64_t>((pr >= 0 && pr < p.s) ? pr : 0) * p.ldx + 8 * lcol;
     }
 
-    // DEPTH register sets: with two, step t+2 is requested while step t is
-    // multiplied and step t+1 (requested one step earlier) waits to be
-    // staged; with one, step t+1 is requested while step t is multiplied.
+    // DEPTH register sets of prefetch: step t + DEPTH is requested while
+    // step t is multiplied from LDS stage t & 1 and step t + 1, requested
+    // DEPTH - 1 steps earlier, waits in its register set to be staged.  The
+    // loop is unrolled by DEPTH so that each register set is a fixed one.
     uint4 xl[DEPTH][XPER], al[DEPTH][APER];
     auto issue = [&](int kt, uint4 (&xs)[XPER], uint4 (&as)[APER]) {
       const int64_t k = static_cast<int64_t>(kt) * 64 + 8 * lcol;
@@ -166,32 +158,19 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
       for (int f = 0; f < FM; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     __syncthreads();  // the previous row block's tiles are no longer read
-    if constexpr (DEPTH == 2) {
-      issue(0, xl[0], al[0]);
-      if (nk > 1) issue(1, xl[DEPTH - 1], al[DEPTH - 1]);
-      stash(0, xl[0], al[0]);
-      __syncthreads();
-      // Step kt is in LDS stage kt & 1 and step kt + 1 in register set
-      // (kt + 1) & 1; unrolled by two so that the register sets are fixed.
-      for (int kt = 0; kt < nk; kt += 2) {
-        if (kt + 2 < nk) issue(kt + 2, xl[0], al[0]);
-        mma(0, acc);
-        if (kt + 1 >= nk) break;
-        stash(1, xl[DEPTH - 1], al[DEPTH - 1]);
-        __syncthreads();
-        if (kt + 3 < nk) issue(kt + 3, xl[DEPTH - 1], al[DEPTH - 1]);
-        mma(1, acc);
-        if (kt + 2 < nk) stash(0, xl[0], al[0]);
-        __syncthreads();
-      }
-    } else {
-      issue(0, xl[0], al[0]);
-      stash(0, xl[0], al[0]);
-      __syncthreads();
-      for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) issue(kt + 1, xl[0], al[0]);
-        mma(kt & 1, acc);
-        if (kt + 1 < nk) stash((kt + 1) & 1, xl[0], al[0]);
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u)
+      if (u < nk) issue(u, xl[u], al[u]);
+    stash(0, xl[0], al[0]);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += DEPTH) {
+#pragma unroll
+      for (int u = 0; u < DEPTH; ++u) {
+        const int k = kt + u;
+        if (k >= nk) break;
+        if (k + DEPTH < nk) issue(k + DEPTH, xl[u], al[u]);
+        mma(k & 1, acc);
+        if (k + 1 < nk) stash((k + 1) & 1, xl[(u + 1) % DEPTH], al[(u + 1) % DEPTH]);
         __syncthreads();
       }
     }

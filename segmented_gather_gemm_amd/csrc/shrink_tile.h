@@ -28,19 +28,11 @@ struct ShrinkShape {
   static constexpr int SMEM = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
 };
 
-// Work item of block b in a grid of G blocks: false for the padding blocks of
-// a round-robin grid.
-__device__ __forceinline__ bool shrink_item_of(const ShrinkParams& p, int b, int G, int* seg,
-                                               int* item) {
+// Work item of block b: false for the padding blocks of the grid.
+__device__ __forceinline__ bool shrink_item_of(const ShrinkParams& p, int b, int* seg, int* item) {
   const int per = p.mblocks * p.nblocks * p.ksplit;
-  if (p.round_robin) {
-    segment_round_robin(b, per, seg, item);
-    return *seg < p.num_segments;
-  }
-  const int L = xcd_contiguous(b, G);
-  *seg = L / per;
-  *item = L % per;
-  return true;
+  segment_round_robin(b, per, seg, item);
+  return *seg < p.num_segments;
 }
 
 // Tile `item` of segment `seg`; `smem` holds ShrinkShape<MF, NF>::SMEM bytes.

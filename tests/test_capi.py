@@ -344,3 +344,88 @@ def test_lm_head_planner_errors():
     with pytest.raises(sgg.SggError):
         sgg.lora_plan_lm_head([5, 5], [0, 1], 2, 128, seg_capacity=1)
 
+
+
+# ------------------------------------------------------ CPython call module
+
+def _header_signature(name):
+    """'p' / 'l' / 'i' per parameter of `name` as declared in the header."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    sig = ""
+    for param in m.group(1).split(","):
+        param = param.strip()
+        if "*" in param:
+            sig += "p"
+        elif param.startswith("int64_t"):
+            sig += "l"
+        elif param.startswith("int32_t"):
+            sig += "i"
+        else:
+            raise AssertionError(f"{name}: unexpected parameter {param!r}")
+    return sig
+
+
+def test_call_module_signatures_match_header():
+    C = _lib.calls()
+    assert set(C.SIGNATURES) == {"lora_plan_max_segments", "lora_plan_upload",
+                                 "lora_plan_lm_head_upload", "lora_shrink_workspace_bytes",
+                                 "lora_qkv_workspace_bytes", "lora_shrink", "lora_expand",
+                                 "lora_qkv", "lora_a_embedding"}
+    for name, sig in C.SIGNATURES.items():
+        assert sig == _header_signature(name), name
+        assert callable(getattr(C, name)), name
+        with pytest.raises(TypeError, match=f"takes {len(sig)} arguments"):
+            getattr(C, name)(*([0] * (len(sig) + 1)))
+
+
+def test_call_module_argument_checks():
+    C = _lib.calls()
+    assert C.lora_plan_max_segments(4096, 8, 16) == L.lora_plan_max_segments(4096, 8, 16)
+    assert C.lora_plan_max_segments(np.int64(4096), np.int32(8), 16) == \
+        L.lora_plan_max_segments(4096, 8, 16)
+    with pytest.raises(OverflowError):
+        C.lora_plan_max_segments(10, 1 << 31, 16)
+    with pytest.raises(TypeError):
+        C.lora_plan_max_segments(10.5, 8, 16)
+    with pytest.raises(TypeError):
+        C.lora_shrink_workspace_bytes(256, 4096, 3, 16, 8, "128")
+    for args in [(256, 4096, 3, 16, 8, 128), (33792, 4096, 2, 64, 300, 128), (0, 4096, 3, 16, 8, 128)]:
+        assert C.lora_shrink_workspace_bytes(*args) == L.lora_shrink_workspace_bytes(*args)
+        assert C.lora_qkv_workspace_bytes(*args) == L.lora_qkv_workspace_bytes(*args)
+
+
+def _as_int(v):
+    return v.value or 0 if isinstance(v, ctypes.c_void_p) else v
+
+
+@pytest.mark.parametrize("kw", [dict(x=NULL), dict(K=0), dict(ldh=4), dict(indptr=NULL),
+                                dict(x=ctypes.c_void_p(0x10008)), dict(s=0)])
+def test_call_module_shrink_same_status(kw):
+    """The call module passes every argument through unchanged: the library
+    returns the same status and message as through ctypes."""
+    a = dict(x=FAKE, ldx=256, A=FAKE, h=FAKE, ldh=8, s=16, K=256, L=2, c=1, R=8,
+             indptr=FAKE, slots=FAKE, nseg=2, perm=FAKE, ranks=FAKE, chunk=16, ws=NULL, wsb=0)
+    a.update(kw)
+    rc = _shrink(**kw)
+    msg = _err()
+    v = [_as_int(a[k]) for k in ("x", "ldx", "A", "h", "ldh", "s", "K", "L", "c", "R", "indptr",
+                                 "slots", "nseg", "perm", "ranks", "chunk", "ws", "wsb")]
+    assert _lib.calls().lora_shrink(*v, None) == rc
+    if rc:
+        assert _err() == msg
+
+
+def test_call_module_qkv_and_embedding_same_status():
+    C = _lib.calls()
+    offs = np.array([0, 4096, 5120, 6144], np.int32)
+    f = FAKE.value
+    args = [f, 4096, f, f, 6144, f, 6144, 256, 4096, 8, 16, offs.ctypes.data, 3, 4096,
+            f, f, 8, f, f, f, 128]
+    assert C.lora_qkv(*args, 0, 0, 0) == -1 and "workspace" in _err()
+    need = C.lora_qkv_workspace_bytes(256, 4096, 3, 16, 8, 128)
+    assert C.lora_qkv(*args, f, need - 1, 0) == -3 and "workspace" in _err()
+    emb = [f, f, 1000, f, 16, 4, 2, 16, 1000, f, f, 1, f, f]
+    assert C.lora_a_embedding(*emb, 1, None) == -2 and "extra" in _err()
+    assert C.lora_a_embedding(*emb[:8], 1001, *emb[9:], 0, None) == -1 and "vocab_size" in _err()

@@ -550,6 +550,44 @@ def test_embedding_edges():
         sgg.lora_a_embedding(ids.to(DEV), A_emb.to(DEV), be.batch_info, V, extra_embeddings=1)
 
 
+def test_staging_ring_reuse_while_gpu_lags():
+    """More batches than staging slots are planned while a delay kernel holds
+    the stream, so the host must wait for each slot's done flag before
+    reusing it; every batch's embedding gather (enqueued right after its
+    upload) must still see its own plan."""
+    rng = np.random.default_rng(44)
+    L, V, Re = 4, 300, 16
+    ranks = [16, 8, 0, 16]
+    A_emb = torch.randn(L, Re, V).to(torch.bfloat16)
+    A_dev = A_emb.to(DEV)
+    be = _sgg().ChunkedSgmvLoRA(L, 128, DEV)
+    cases = []
+    for i in range(30):
+        bs = int(rng.integers(1, 13))
+        lens = [int(v) for v in rng.integers(1, 41, bs)]
+        slots = [int(v) for v in rng.integers(0, L, bs)]
+        ids = torch.as_tensor(rng.integers(-5, V + 5, sum(lens)), dtype=torch.int64)
+        cases.append([lens, slots, ids, ids.to(DEV)])
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)   # tens of milliseconds: the host runs ahead
+    for case in cases:
+        be.prepare_lora_batch(case[0], case[1], ranks, [1.0] * L)
+        case[3] = be.run_lora_a_embedding(case[3], A_dev, V)
+    torch.cuda.synchronize()
+    stg = be._staging
+    assert list(stg.flag_view) == stg.seq   # every upload raised its flag
+    for lens, slots, ids, e in cases:
+        want = ol.embedding_a(ids.numpy(), to_f64(A_emb), lens, slots, ranks, V)
+        assert np.array_equal(to_f64(e), want)
+
+
+def test_staging_wait_gives_up_on_a_flag_never_raised():
+    """Host logic only: a slot whose upload never ran raises instead of spinning."""
+    stg = _sgg().ChunkedSgmvLoRA(2, 128, DEV)._staging
+    with pytest.raises(RuntimeError, match="has not run"):
+        stg._wait(0, 7, limit_s=0.05)
+
+
 def test_missing_base_gives_delta():
     b, proj, t = _small_case(40, [10, 6], [0, 1], 2, [8, 8], [2.0, 1.0], 256, [0, 256], 8)
     be = backend(b)
