@@ -60,6 +60,9 @@ class _Staging:
         self.host = [None] * slots
         self.dev = [None] * slots
         self.infos = [{} for _ in range(slots)]   # layout key -> LoRABatchInfo views
+        self.host_addr = [0] * slots               # staging / device addresses and bytes
+        self.dev_addr = [0] * slots
+        self.dev_bytes = [0] * slots
         self.flags = torch.zeros(slots, dtype=torch.int32, pin_memory=True)
         self.flag_view = self.flags.numpy()
         self.flag_addr = self.flags.data_ptr()
@@ -76,6 +79,9 @@ class _Staging:
             size = max(n, 4096)
             self.host[i] = torch.empty(size, dtype=torch.int32, pin_memory=True)
             self.dev[i] = torch.empty(size, dtype=torch.int32, device=self.device)
+            self.host_addr[i] = self.host[i].data_ptr()
+            self.dev_addr[i] = self.dev[i].data_ptr()
+            self.dev_bytes[i] = 4 * size
             self.infos[i] = {}
         return i
 
@@ -124,6 +130,9 @@ class ChunkedSgmvLoRA:
         self._layouts = {}
         self._info_arr = (ctypes.c_int32 * 6)()
         self._info_addr = ctypes.addressof(self._info_arr)
+        self._info_np = np.frombuffer(self._info_arr, dtype=np.int32)
+        self._seg_caps = {}
+        self._dev_index = self.device.index
 
     # ---------------------------------------------------------------- plan
     def _layout(self, s_cap, seg_cap, req_cap):
@@ -163,26 +172,32 @@ class ChunkedSgmvLoRA:
             s_cap, req_cap = max_tokens, max_bs
         else:
             min_chunk = chunk_size_override if chunk_size_override > 0 else MIN_CHUNK_SIZE
-            seg_cap = B.lora_plan_max_segments(s, L, min_chunk)
+            seg_cap = self._seg_caps.get((s, min_chunk))
+            if seg_cap is None:
+                seg_cap = B.lora_plan_max_segments(s, L, min_chunk)
+                if len(self._seg_caps) < 4096:
+                    self._seg_caps[(s, min_chunk)] = seg_cap
             s_cap, req_cap = s, bs
         key = (s_cap, seg_cap, req_cap)
         total, regions = self._layout(s_cap, seg_cap, req_cap)
         stg = self._staging
         ring = stg.take(total)
-        dev = self._graph_dev if use_cuda_graph else stg.dev[ring]
+        if use_cuda_graph:
+            dev = self._graph_dev
+            dev_addr, dev_bytes = dev.data_ptr(), 4 * dev.numel()
+        else:
+            dev, dev_addr, dev_bytes = stg.dev[ring], stg.dev_addr[ring], stg.dev_bytes[ring]
         ranks = np.ascontiguousarray(lora_ranks, dtype=np.int32)
         scal = np.ascontiguousarray(scalings, dtype=np.float32)
-        idx = self.device.index if self.device.index is not None else torch.cuda.current_device()
+        idx = self._dev_index if self._dev_index is not None else torch.cuda.current_device()
         stream = torch._C._cuda_getCurrentRawStream(idx)
-        info = self._info_arr
         flag, flag_value = stg.signal(ring)
         check(calls().lora_plan_upload(
-            None if lens is None else lens.ctypes.data, slots.ctypes.data, bs, ranks.ctypes.data,
-            scal.ctypes.data, L, 1 if is_decode else 0, self.max_chunk_size,
-            int(chunk_size_override), s_cap, seg_cap, req_cap, stg.host[ring].data_ptr(),
-            dev.data_ptr(), 4 * dev.numel(), self._info_addr, flag, flag_value, stream))
+            lens, slots, bs, ranks, scal, L, 1 if is_decode else 0, self.max_chunk_size,
+            int(chunk_size_override), s_cap, seg_cap, req_cap, stg.host_addr[ring], dev_addr,
+            dev_bytes, self._info_addr, flag, flag_value, stream))
         stg.done(ring)
-        n_seg, chunk, longest, n_work, longest_work = info[0], info[1], info[2], info[4], info[5]
+        n_seg, chunk, longest, _, n_work, longest_work = self._info_np.tolist()
         if use_cuda_graph:
             # fixed views and launch shape: capacity segments over capacity tokens
             batch = self.cuda_graph_batch_info

@@ -65,10 +65,10 @@ def _vp(t):
     return t.data_ptr() if t is not None else 0
 
 
-def _stream(device):
-    """Raw handle of torch's current stream on `device` (the launch stream)."""
-    idx = device.index if device.index is not None else torch.cuda.current_device()
-    return torch._C._cuda_getCurrentRawStream(idx)
+def _stream(t):
+    """Raw handle of torch's current stream on the device of tensor `t` (the
+    launch stream)."""
+    return torch._C._cuda_getCurrentRawStream(t.get_device())
 
 
 def _host_i32(values):
@@ -250,7 +250,7 @@ def lora_shrink(x, weights, batch_info: LoRABatchInfo, num_slices=1, out=None, w
     check(calls().lora_shrink(
         _vp(x), x.stride(0), _vp(weights), _vp(out), out.stride(0), s, K, L, num_slices, R,
         _vp(ind), _vp(sl), nseg, _vp(batch_info.permutation), _vp(batch_info.lora_ranks), hint,
-        _vp(ws), ws.numel() if ws is not None else 0, _stream(x.device)))
+        _vp(ws), ws.numel() if ws is not None else 0, _stream(x)))
     return out
 
 
@@ -278,7 +278,7 @@ def lora_expand(h, weights, batch_info: LoRABatchInfo, slice_offsets, max_slice_
     check(calls().lora_expand(
         _vp(h), h.stride(0), _vp(weights), N, _vp(base_output), base_output.stride(0), s, L, R,
         p_offs, c, int(max_slice_size), _vp(ind), _vp(sl), nseg, _vp(batch_info.permutation),
-        _vp(batch_info.lora_ranks), _vp(batch_info.scalings), hint, _stream(h.device)))
+        _vp(batch_info.lora_ranks), _vp(batch_info.scalings), hint, _stream(h)))
     return base_output
 
 
@@ -308,10 +308,10 @@ def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
         need = calls().lora_qkv_workspace_bytes(s, K, c, R, nseg, hint)
         ws = default_workspace(x.device, max(need, 1))
     check(calls().lora_qkv(
-        _vp(x), x.stride(0), _vp(A), _vp(B), N, _vp(base_output), base_output.stride(0), s, K,
-        L, R, p_offs, c, int(max_slice_size), _vp(ind), _vp(sl), nseg,
-        _vp(batch_info.permutation), _vp(batch_info.lora_ranks), _vp(batch_info.scalings), hint,
-        _vp(ws), ws.numel(), _stream(x.device)))
+        x.data_ptr(), x.stride(0), A.data_ptr(), B.data_ptr(), N, base_output.data_ptr(),
+        base_output.stride(0), s, K, L, R, p_offs, c, int(max_slice_size), ind.data_ptr(),
+        sl.data_ptr(), nseg, batch_info.permutation.data_ptr(), batch_info.lora_ranks.data_ptr(),
+        batch_info.scalings.data_ptr(), hint, ws.data_ptr(), ws.numel(), _stream(x)))
     return base_output
 
 
@@ -335,5 +335,5 @@ def lora_a_embedding(input_ids, weights, batch_info: LoRABatchInfo, vocab_size,
         int(vocab_size), _vp(batch_info.seg_indptr), _vp(batch_info.weight_indices),
         batch_info.num_segments, _vp(batch_info.permutation),
         _vp(batch_info.lora_ranks), 0 if extra_embeddings is None else 1,
-        _stream(weights.device)))
+        _stream(weights)))
     return out

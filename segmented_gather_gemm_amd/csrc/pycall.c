@@ -14,10 +14,26 @@
 
 #include "sgg_lora.h"
 
-/* Convert args[i] by sig[i]: 'p' address (int or None), 'l' int64, 'i' int32. */
+/* Host buffers exported by the arguments of one call (NumPy arrays passed
+ * for host pointers), held until the call returns. */
+#define MAX_HELD 8
+typedef struct {
+  Py_buffer view[MAX_HELD];
+  int n;
+} Held;
+
+static void release(Held* held) {
+  for (int i = 0; i < held->n; ++i) PyBuffer_Release(&held->view[i]);
+  held->n = 0;
+}
+
+/* Convert args[i] by sig[i]: 'p' pointer -- an integer address, None (NULL)
+ * or a C-contiguous buffer (its first byte, e.g. a NumPy array's data);
+ * 'l' int64; 'i' int32. */
 static int convert(const char* name, const char* sig, PyObject* const* args, Py_ssize_t nargs,
-                   int64_t* out) {
+                   int64_t* out, Held* held) {
   const Py_ssize_t want = (Py_ssize_t)strlen(sig);
+  held->n = 0;
   if (nargs != want) {
     PyErr_Format(PyExc_TypeError, "%s takes %zd arguments (%zd given)", name, want, nargs);
     return 0;
@@ -27,6 +43,20 @@ static int convert(const char* name, const char* sig, PyObject* const* args, Py_
     if (sig[k] == 'p') {
       if (a == Py_None) {
         out[k] = 0;
+        continue;
+      }
+      if (!PyLong_Check(a) && PyObject_CheckBuffer(a)) {
+        if (held->n == MAX_HELD) {
+          PyErr_Format(PyExc_TypeError, "%s: too many buffer arguments", name);
+          release(held);
+          return 0;
+        }
+        if (PyObject_GetBuffer(a, &held->view[held->n], PyBUF_C_CONTIGUOUS) < 0) {
+          release(held);
+          return 0;
+        }
+        out[k] = (int64_t)(uintptr_t)held->view[held->n].buf;
+        ++held->n;
         continue;
       }
       unsigned long long v;
@@ -45,6 +75,7 @@ static int convert(const char* name, const char* sig, PyObject* const* args, Py_
       if (v == -1 && PyErr_Occurred()) goto bad;
       if (sig[k] == 'i' && (v < INT32_MIN || v > INT32_MAX)) {
         PyErr_Format(PyExc_OverflowError, "%s: argument %zd does not fit in int32", name, k);
+        release(held);
         return 0;
       }
       out[k] = (int64_t)v;
@@ -53,7 +84,8 @@ static int convert(const char* name, const char* sig, PyObject* const* args, Py_
   bad:
     PyErr_Clear();
     PyErr_Format(PyExc_TypeError, "%s: argument %zd must be an integer%s", name, k,
-                 sig[k] == 'p' ? " address or None" : "");
+                 sig[k] == 'p' ? " address, a contiguous buffer or None" : "");
+    release(held);
     return 0;
   }
   return 1;
@@ -72,10 +104,18 @@ static int convert(const char* name, const char* sig, PyObject* const* args, Py_
 #define SIG_lora_qkv "plpplpllliipiippipppiplp"
 #define SIG_lora_a_embedding "pplplliilppippip"
 
-/* One int64 per argument, sized by the signature string. */
+/* One int64 per argument, sized by the signature string; CALL runs the
+ * entry point, then releases the held buffers. */
 #define CONVERT(fn)                   \
   int64_t v[sizeof(SIG_##fn) - 1];    \
-  if (!convert(#fn, SIG_##fn, args, n, v)) return NULL
+  Held held;                          \
+  if (!convert(#fn, SIG_##fn, args, n, v, &held)) return NULL
+#define RETURN_INT(expr)              \
+  do {                                \
+    const long long rc_ = (expr);     \
+    release(&held);                   \
+    return PyLong_FromLongLong(rc_);  \
+  } while (0)
 
 #define P(k) ((void*)(uintptr_t)v[k])
 #define I32P(k) ((int32_t*)(uintptr_t)v[k])
@@ -84,12 +124,12 @@ static int convert(const char* name, const char* sig, PyObject* const* args, Py_
 
 static PyObject* py_lora_plan_max_segments(PyObject* self, PyObject* const* args, Py_ssize_t n) {
   CONVERT(lora_plan_max_segments);
-  return PyLong_FromLongLong(lora_plan_max_segments(L(0), I(1), I(2)));
+  RETURN_INT(lora_plan_max_segments(L(0), I(1), I(2)));
 }
 
 static PyObject* py_lora_plan_upload(PyObject* self, PyObject* const* args, Py_ssize_t n) {
   CONVERT(lora_plan_upload);
-  return PyLong_FromLong(lora_plan_upload(
+  RETURN_INT(lora_plan_upload(
       I32P(0), I32P(1), I(2), I32P(3), (const float*)P(4), I(5), I(6), I(7), I(8), L(9), I(10),
       I(11), P(12), P(13), L(14), I32P(15), I32P(16), I(17), P(18)));
 }
@@ -97,7 +137,7 @@ static PyObject* py_lora_plan_upload(PyObject* self, PyObject* const* args, Py_s
 static PyObject* py_lora_plan_lm_head_upload(PyObject* self, PyObject* const* args,
                                              Py_ssize_t n) {
   CONVERT(lora_plan_lm_head_upload);
-  return PyLong_FromLong(lora_plan_lm_head_upload(
+  RETURN_INT(lora_plan_lm_head_upload(
       I32P(0), I32P(1), I(2), I32P(3), (const float*)P(4), I(5), I(6), I(7), L(8), I(9), I(10),
       P(11), P(12), L(13), I32P(14), I32P(15), I(16), P(17)));
 }
@@ -105,32 +145,32 @@ static PyObject* py_lora_plan_lm_head_upload(PyObject* self, PyObject* const* ar
 static PyObject* py_lora_shrink_workspace_bytes(PyObject* self, PyObject* const* args,
                                                 Py_ssize_t n) {
   CONVERT(lora_shrink_workspace_bytes);
-  return PyLong_FromLongLong(lora_shrink_workspace_bytes(L(0), L(1), I(2), I(3), I(4), I(5)));
+  RETURN_INT(lora_shrink_workspace_bytes(L(0), L(1), I(2), I(3), I(4), I(5)));
 }
 
 static PyObject* py_lora_qkv_workspace_bytes(PyObject* self, PyObject* const* args,
                                              Py_ssize_t n) {
   CONVERT(lora_qkv_workspace_bytes);
-  return PyLong_FromLongLong(lora_qkv_workspace_bytes(L(0), L(1), I(2), I(3), I(4), I(5)));
+  RETURN_INT(lora_qkv_workspace_bytes(L(0), L(1), I(2), I(3), I(4), I(5)));
 }
 
 static PyObject* py_lora_shrink(PyObject* self, PyObject* const* args, Py_ssize_t n) {
   CONVERT(lora_shrink);
-  return PyLong_FromLong(lora_shrink(P(0), L(1), P(2), P(3), L(4), L(5), L(6), I(7), I(8), I(9),
+  RETURN_INT(lora_shrink(P(0), L(1), P(2), P(3), L(4), L(5), L(6), I(7), I(8), I(9),
                                      I32P(10), I32P(11), I(12), I32P(13), I32P(14), I(15), P(16),
                                      L(17), P(18)));
 }
 
 static PyObject* py_lora_expand(PyObject* self, PyObject* const* args, Py_ssize_t n) {
   CONVERT(lora_expand);
-  return PyLong_FromLong(lora_expand(P(0), L(1), P(2), L(3), P(4), L(5), L(6), I(7), I(8),
+  RETURN_INT(lora_expand(P(0), L(1), P(2), L(3), P(4), L(5), L(6), I(7), I(8),
                                      I32P(9), I(10), I(11), I32P(12), I32P(13), I(14), I32P(15),
                                      I32P(16), (const float*)P(17), I(18), P(19)));
 }
 
 static PyObject* py_lora_qkv(PyObject* self, PyObject* const* args, Py_ssize_t n) {
   CONVERT(lora_qkv);
-  return PyLong_FromLong(lora_qkv(P(0), L(1), P(2), P(3), L(4), P(5), L(6), L(7), L(8), I(9),
+  RETURN_INT(lora_qkv(P(0), L(1), P(2), P(3), L(4), P(5), L(6), L(7), L(8), I(9),
                                   I(10), I32P(11), I(12), I(13), I32P(14), I32P(15), I(16),
                                   I32P(17), I32P(18), (const float*)P(19), I(20), P(21), L(22),
                                   P(23)));
@@ -138,7 +178,7 @@ static PyObject* py_lora_qkv(PyObject* self, PyObject* const* args, Py_ssize_t n
 
 static PyObject* py_lora_a_embedding(PyObject* self, PyObject* const* args, Py_ssize_t n) {
   CONVERT(lora_a_embedding);
-  return PyLong_FromLong(lora_a_embedding((const int64_t*)P(0), P(1), L(2), P(3), L(4), L(5),
+  RETURN_INT(lora_a_embedding((const int64_t*)P(0), P(1), L(2), P(3), L(4), L(5),
                                           I(6), I(7), L(8), I32P(9), I32P(10), I(11), I32P(12),
                                           I32P(13), I(14), P(15)));
 }

@@ -429,3 +429,24 @@ def test_call_module_qkv_and_embedding_same_status():
     emb = [f, f, 1000, f, 16, 4, 2, 16, 1000, f, f, 1, f, f]
     assert C.lora_a_embedding(*emb, 1, None) == -2 and "extra" in _err()
     assert C.lora_a_embedding(*emb[:8], 1001, *emb[9:], 0, None) == -1 and "vocab_size" in _err()
+
+
+def test_call_module_takes_contiguous_host_buffers():
+    """A NumPy array passed for a host pointer stands for its first byte; a
+    non-contiguous one is refused before the library is called."""
+    C = _lib.calls()
+    f = FAKE.value
+    offs = np.array([0, 4096, 5120, 6144], np.int32)
+    head = [f, 4096, f, f, 6144, f, 6144, 256, 4096, 8, 16]
+    tail = [3, 4096, f, f, 8, f, f, f, 128, 0, 0, 0]
+    assert C.lora_qkv(*head, offs, *tail) == -1 and "workspace" in _err()
+    bad = np.array([0, 4096, 4097, 5120, 5121, 6144, 6145, 6146], np.int32)[::2]
+    with pytest.raises((BufferError, ValueError, TypeError)):
+        C.lora_qkv(*head, bad, *tail)
+    # the library reads the offsets from the buffer (rejected before any launch)
+    exp = [f, 8, f, 256, f, 256, 16, 2, 8]
+    rest = [f, f, 2, f, f, f, 16, 0]
+    assert C.lora_expand(*exp, np.array([0, 200, 100], np.int32), 2, 256, *rest) == -1
+    assert "non-decreasing" in _err()
+    assert C.lora_expand(*exp, np.array([1, 256], np.int32), 1, 256, *rest) == -1
+    assert "slice_offsets[0]" in _err()
