@@ -14,11 +14,11 @@
 // bytes of one row.  The base rows of the next 16 tokens are in flight while
 // the current ones are computed and stored.
 //
-// Work order: each XCD takes a contiguous range of (segment, tile) items with
-// tiles fastest, so the workgroups resident on an XCD sweep whole rows of the
-// base tensor and share the segment's h rows and its adapter's B tiles in L2.
-// With few segments (e.g. a capacity-padded graph launch, whose trailing
-// segments are empty) segments are dealt round-robin to the XCDs instead.
+// Work order: segments are dealt round-robin to the XCDs (segment_round_robin)
+// with all column tiles of a segment on one XCD, tiles fastest, so the
+// workgroups resident on an XCD sweep whole rows of the base tensor and share
+// the segment's h rows in L2, while the chunks of a dominant adapter spread
+// over all XCDs.
 #include "sgg_device.h"
 #include "sgg_kernels.h"
 #include "expand_tile.h"
