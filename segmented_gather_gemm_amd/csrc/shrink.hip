@@ -128,7 +128,28 @@ ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments
     t.partial_bytes = round_up(static_cast<int64_t>(t.ksplit) * s * CR * 4, 256);
     return t;
   }
-  // No K split needed: the workgroup-shared GEMM tiles.  Batches of long
+  // No K split needed.  Batches of short segments that are small (at most
+  // 6144 tokens) or have a long K (8192 or more) keep this kernel, with one K
+  // range and tiles of 32 tokens (64 above 6144 tokens) by half of c*R: its
+  // four waves stream interleaved K chunks with no barrier between them,
+  // which beat the shared GEMM tiles by 8-25 % on the full-layer shapes
+  // (4288 tokens, 93 segments: gate_up 36.9 -> 29.2 us, down_proj 63 -> 55
+  // us) and on the skewed down_proj (K = 14336: 181 -> 140 us), while the
+  // GEMM tiles stay ahead for the skewed o_proj (8192 tokens, K = 4096).
+  const bool long_segments = num_segments > 0 && s >= 96 * static_cast<int64_t>(num_segments);
+  if (!long_segments && (s <= 6144 || K >= 8192)) {
+    t.mf = s > 6144 ? 4 : 2;
+    t.nf = 1;
+    for (int v : kNf)
+      if (16 * v <= CR / 2 && t.mf * v <= 32) t.nf = v;
+    t.nblocks = (CR + 16 * t.nf - 1) / (16 * t.nf);
+    t.mblocks = (chunk + 16 * t.mf - 1) / (16 * t.mf);
+    if (t.mblocks < 1) t.mblocks = 1;
+    t.gemm = 0;
+    t.grid = grid_for(num_segments, static_cast<int64_t>(t.nblocks) * t.mblocks);
+    return t;
+  }
+  // The workgroup-shared GEMM tiles.  Batches of long
   // segments (mean work segment of 96 tokens or more, e.g. prefill) take
   // 128 tokens per tile and rank rows the smallest of 32 / 64 / 128 covering
   // c*R; batches of short segments (decode mixed in, many adapters, a long
@@ -139,7 +160,6 @@ ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments
   // qkv 44 -> 39 us, skewed down_proj 202 -> 185 us), 128 x 128 beats every
   // smaller tile by 25 % or more on prefill; the split-K kernel is faster on
   // grids under one workgroup per CU.
-  const bool long_segments = num_segments > 0 && s >= 96 * static_cast<int64_t>(num_segments);
   int gm = long_segments && chunk > 64 ? 128 : 64;
   int gn = !long_segments ? 32 : (CR <= 32 ? 32 : (CR <= 64 ? 64 : 128));
   auto gemm_units = [&](int m, int n) {
