@@ -84,8 +84,11 @@ int check_expand(const void* h, int64_t ldh, const void* B, int64_t N, const voi
   return SGG_OK;
 }
 
-// Columns per workgroup: 128 * pairs; 256 when that still gives at least four
-// workgroups per CU, else 128 (measured: 512 is slower for prefill shapes).
+// Columns per workgroup: 128 * pairs; 256 when that still gives at least 16
+// workgroups per CU, else 128.  Measured: 256 wins on the 28672-wide gate_up
+// of prefill (1014 -> 825 us) and of the full-layer batch (192 -> 147 us);
+// 128 wins by 1-3 us on the 4096- and 6144-wide outputs of the full-layer and
+// skewed batches, whose grids are 5-10x smaller; 512 is slower everywhere.
 // Rank steps of 32.
 sgg::ExpandTiling choose_expand_tiling(const int32_t* offs, int c, int num_segments, int R,
                                        int32_t* tile_start, int32_t* total) {
@@ -95,7 +98,7 @@ sgg::ExpandTiling choose_expand_tiling(const int32_t* offs, int c, int num_segme
   for (int pairs : {2}) {
     int64_t tiles = 0;
     for (int k = 0; k < c; ++k) tiles += (offs[k + 1] - offs[k] + 128 * pairs - 1) / (128 * pairs);
-    if (tiles * num_segments >= 1024) {
+    if (tiles * num_segments >= 4096) {
       t.pairs = pairs;
       break;
     }
