@@ -16,8 +16,9 @@ Every run also times the prefill gate_up workload (chunk cap 128).
 Prints ONE JSON line.  `value` is tokens/s of whole steps (wall clock over
 the timed steps, inputs resident in HBM); kernel durations come from HIP
 events on the stream the kernels run on.  `--secondary` adds the prefill
-chunk sweep (16 / 32 / 64 / 128), the skewed batch (o_proj, down_proj) and
-the full Llama-3-8B-shaped layer sweep with the embedding gather.
+chunk sweep (16 / 32 / 64 / 128), the skewed batch (o_proj, down_proj), the
+full Llama-3-8B-shaped layer sweep with the embedding gather, and the pruned
+lm_head pass of the decode batch.
 """
 
 import argparse
@@ -45,8 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=48, help="rotated input sets")
     ap.add_argument("--secondary", action="store_true",
-                    help="also time the prefill chunk sweep, the skewed batch and the full "
-                         "layer sweep")
+                    help="also time the prefill chunk sweep, the skewed batch, the full "
+                         "layer sweep and the lm_head pass")
     ap.add_argument("--full-layers", type=int, default=8,
                     help="layers with distinct weights timed in the full layer sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -451,6 +452,57 @@ def run_full(device, layers, steps=5, warmup=1):
             "embedding_us": round(emb_us, 2)}
 
 
+def run_lm_head(device, steps=20, warmup=3):
+    """Pruned lm_head pass of the decode batch: each of the 256 requests sends
+    one token to the lm_head (4096 -> vocab 128256, r=16, 8 adapters).  The
+    lm_head plan keeps the tokens in original order (identity permutation), so
+    its segments are runs of consecutive same-slot requests -- about one token
+    each when the adapters are dealt uniformly.  The sorted plan of the same
+    tokens is timed beside it."""
+    import torch
+    import segmented_gather_gemm_amd as sgg
+    from synth import draw_batch, draw_projection
+    from synth.workloads import Projection
+    b = draw_batch("decode")
+    proj = Projection("lm_head", 4096, [0, 128256], 16)
+    t = _to(device, draw_projection(b, proj, proj_index=len(b.projections)))
+    cnt = algo_counts(b, proj, 16)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=device)
+    h = torch.empty((b.num_tokens, proj.rank), dtype=torch.bfloat16, device=device)
+    stream = torch.cuda.current_stream(device)
+    res = {"workload": "lm_head pass of the decode batch: 256 requests x 1 token, 8 adapters "
+                       "uniform, r=16, 4096 -> 128256"}
+    for mode in ("identity_plan", "sorted_plan"):
+        be = sgg.ChunkedSgmvLoRA(b.num_loras, b.max_chunk_size, device)
+        if mode == "identity_plan":
+            info = be.prepare_lm_head_batch([1] * len(b.req_slots), b.req_slots, b.lora_ranks,
+                                            b.scalings)
+        else:
+            info = be.prepare_lora_batch(None, b.req_slots, b.lora_ranks, b.scalings,
+                                         is_decode=True)
+        calls = {
+            "shrink": lambda: sgg.lora_shrink(t["x"], t["A"], info, 1, out=h, workspace=ws),
+            "expand": lambda: sgg.lora_expand(h, t["B"], info, proj.slice_offsets, proj.max_slice,
+                                              t["base"]),
+        }
+        out = {"segments": info.num_segments, "work_segments": info.num_work_segments}
+        for name, fn in calls.items():
+            for _ in range(warmup):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out[name] = _rates(cnt[name]["bytes"], cnt[name]["flops"],
+                               e0.elapsed_time(e1) * 1e3 / steps)
+        tot = out["shrink"]["avg_us"] + out["expand"]["avg_us"]
+        out["tokens_per_s"] = round(b.num_tokens / (tot * 1e-6), 1)
+        res[mode] = out
+    return res
+
+
 def copy_probe(device):
     import torch
     n = 1 << 30
@@ -556,6 +608,8 @@ def main():
         line["skewed"] = run_skewed(device)
         print("# full layer sweep", file=sys.stderr, flush=True)
         line["full"] = run_full(device, args.full_layers)
+        print("# lm_head pass", file=sys.stderr, flush=True)
+        line["lm_head"] = run_lm_head(device)
     if not args.no_cpu:
         print("# cpu baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

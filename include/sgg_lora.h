@@ -118,16 +118,22 @@ int64_t lora_plan_max_segments(int64_t num_tokens, int32_t max_loras, int32_t mi
  *   4 req_slots [req_capacity]         5 lora_ranks [max_loras]
  *   6 scalings [max_loras] (float32 bits)
  *   7 work_indptr [seg_capacity + 1]   8 work_slots [seg_capacity]
- * lora_plan_layout writes the 9 element offsets to offsets[0..8] and returns
+ *   9 work_permutation [token_capacity] (lm_head plans only)
+ * lora_plan_layout writes the 10 element offsets to offsets[0..9] and returns
  * the total element count (host only; -1 for negative sizes).
  */
-#define SGG_PLAN_REGIONS 9
+#define SGG_PLAN_REGIONS 10
 /* Work segments (regions 7, 8): the plan's segments with consecutive
  * segments of one slot merged while the merged length stays within
  * max(chunk_size, SGG_WORK_SEGMENT_TOKENS).  They partition the same sorted
- * positions, so any kernel call gives the same result with them as with the
- * plan's segments; with short chunks they let a workgroup reuse an adapter's
- * weights across more tokens. */
+ * positions, so any kernel call gives the same result with them (and the
+ * plan's permutation) as with the plan's segments; with short chunks they let
+ * a workgroup reuse an adapter's weights across more tokens.  For an lm_head
+ * plan they are built the same way from the pruned tokens sorted by slot (a
+ * stable sort), whose permutation is region 9: kernels given region 9 as the
+ * permutation and regions 7, 8 as the segments compute the same result as
+ * over the lm_head plan itself, without re-reading an adapter's weights for
+ * every short run of one adapter. */
 #define SGG_WORK_SEGMENT_TOKENS 128
 int64_t lora_plan_layout(int64_t token_capacity, int32_t seg_capacity, int32_t req_capacity,
                          int32_t max_loras, int64_t* offsets);
@@ -198,8 +204,10 @@ int lora_plan_lm_head(const int32_t* pruned_lens, const int32_t* req_slots, int3
 /*
  * lora_plan_lm_head_upload -- as lora_plan_upload, for the lm_head plan of
  * lora_plan_lm_head: the same buffer layout (req_seg_indptr holds the
- * boundaries of each request's pruned tokens), work segments, done flag and
- * single transfer on `stream`.
+ * boundaries of each request's pruned tokens), done flag and single transfer
+ * on `stream`; the work segments and the work permutation (regions 7-9) come
+ * from the pruned tokens sorted by slot.  lora_plan_upload leaves region 9
+ * alone and does not transfer it.
  */
 int lora_plan_lm_head_upload(const int32_t* pruned_lens, const int32_t* req_slots,
                              int32_t num_reqs, const int32_t* lora_ranks, const float* scalings,

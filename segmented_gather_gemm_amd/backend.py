@@ -108,7 +108,7 @@ class _Staging:
 
 
 _NAMES = ("permutation", "seg_indptr", "seg_slots", "req_seg_indptr", "req_slots", "ranks",
-          "scalings", "work_indptr", "work_slots")
+          "scalings", "work_indptr", "work_slots", "work_perm")
 
 
 class ChunkedSgmvLoRA:
@@ -143,7 +143,8 @@ class ChunkedSgmvLoRA:
             total = int(lib().lora_plan_layout(s_cap, seg_cap, req_cap, self.max_loras_per_batch,
                                                offs))
             sizes = (s_cap, seg_cap + 1, seg_cap, req_cap + 1, req_cap,
-                     self.max_loras_per_batch, self.max_loras_per_batch, seg_cap + 1, seg_cap)
+                     self.max_loras_per_batch, self.max_loras_per_batch, seg_cap + 1, seg_cap,
+                     s_cap)
             lay = (total, [(int(o), n) for o, n in zip(offs, sizes)])
             self._layouts[key] = lay
         return lay
@@ -285,7 +286,7 @@ class ChunkedSgmvLoRA:
             scalings=v["scalings"].view(torch.float32), req_seg_indptr=v["req_seg_indptr"],
             req_weight_indices=v["req_slots"], use_cuda_graph=False, max_seg_len=longest,
             work_indptr=v["work_indptr"], work_slots=v["work_slots"], num_work_segments=n_work,
-            max_work_len=longest_work)
+            max_work_len=longest_work, work_perm=v["work_perm"])
 
     def init_cuda_graph_batch_info(self, max_bs_in_cuda_graph, num_tokens_per_bs):
         """Preallocate fixed-capacity device plan arrays for graph capture.

@@ -39,13 +39,15 @@ class LoRABatchInfo:
     req_weight_indices: Optional[torch.Tensor] = None
     use_cuda_graph: bool = False
     max_seg_len: int = 0          # longest planned segment (0: unknown, use max_len)
-    # Work segments (optional): the same sorted positions with consecutive
-    # segments of one slot merged (lora_plan_upload); kernels run over them
-    # when present, with the same results.
+    # Work decomposition (optional): segments with consecutive segments of
+    # one slot merged, over `work_perm` (None: the plan's permutation; an
+    # lm_head plan's tokens sorted by slot); kernels run over it when present,
+    # with the same results (lora_plan_upload, lora_plan_lm_head_upload).
     work_indptr: Optional[torch.Tensor] = None
     work_slots: Optional[torch.Tensor] = None
     num_work_segments: int = 0
     max_work_len: int = 0
+    work_perm: Optional[torch.Tensor] = None
 
     @property
     def tile_hint(self):
@@ -53,11 +55,14 @@ class LoRABatchInfo:
         return self.max_seg_len if self.max_seg_len > 0 else self.max_len
 
     def kernel_segments(self):
-        """(indptr, slots, count, tile hint) of the segmentation the kernels run over."""
+        """(indptr, slots, count, tile hint, permutation) of the decomposition
+        the kernels run over."""
         if self.work_indptr is not None:
             hint = self.max_work_len if self.max_work_len > 0 else self.tile_hint
-            return self.work_indptr, self.work_slots, self.num_work_segments, hint
-        return self.seg_indptr, self.weight_indices, self.num_segments, self.tile_hint
+            perm = self.permutation if self.work_perm is None else self.work_perm
+            return self.work_indptr, self.work_slots, self.num_work_segments, hint, perm
+        return (self.seg_indptr, self.weight_indices, self.num_segments, self.tile_hint,
+                self.permutation)
 
 
 def _vp(t):
@@ -242,14 +247,14 @@ def lora_shrink(x, weights, batch_info: LoRABatchInfo, num_slices=1, out=None, w
     if out is None:
         out = torch.empty((s, CR), dtype=torch.bfloat16, device=x.device)
     _need_bf16("out", out, 2)
-    ind, sl, nseg, hint = batch_info.kernel_segments()
+    ind, sl, nseg, hint, perm = batch_info.kernel_segments()
     ws = workspace
     if ws is None:   # the library checks the size of a caller's workspace itself
         need = calls().lora_shrink_workspace_bytes(s, K, num_slices, R, nseg, hint)
         ws = default_workspace(x.device, need) if need else None
     check(calls().lora_shrink(
         _vp(x), x.stride(0), _vp(weights), _vp(out), out.stride(0), s, K, L, num_slices, R,
-        _vp(ind), _vp(sl), nseg, _vp(batch_info.permutation), _vp(batch_info.lora_ranks), hint,
+        _vp(ind), _vp(sl), nseg, _vp(perm), _vp(batch_info.lora_ranks), hint,
         _vp(ws), ws.numel() if ws is not None else 0, _stream(x)))
     return out
 
@@ -274,10 +279,10 @@ def lora_expand(h, weights, batch_info: LoRABatchInfo, slice_offsets, max_slice_
     _need_bf16("base_output", base_output, 2)
     if base_output.shape[0] != s:
         raise ValueError("base_output rows differ from h rows")
-    ind, sl, nseg, hint = batch_info.kernel_segments()
+    ind, sl, nseg, hint, perm = batch_info.kernel_segments()
     check(calls().lora_expand(
         _vp(h), h.stride(0), _vp(weights), N, _vp(base_output), base_output.stride(0), s, L, R,
-        p_offs, c, int(max_slice_size), _vp(ind), _vp(sl), nseg, _vp(batch_info.permutation),
+        p_offs, c, int(max_slice_size), _vp(ind), _vp(sl), nseg, _vp(perm),
         _vp(batch_info.lora_ranks), _vp(batch_info.scalings), hint, _stream(h)))
     return base_output
 
@@ -302,7 +307,7 @@ def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
     if base_output is None:
         base_output = torch.zeros((s, int(offs[-1])), dtype=torch.bfloat16, device=x.device)
     _need_bf16("base_output", base_output, 2)
-    ind, sl, nseg, hint = batch_info.kernel_segments()
+    ind, sl, nseg, hint, perm = batch_info.kernel_segments()
     ws = workspace
     if ws is None:   # the library checks the size of a caller's workspace itself
         need = calls().lora_qkv_workspace_bytes(s, K, c, R, nseg, hint)
@@ -310,7 +315,7 @@ def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
     check(calls().lora_qkv(
         x.data_ptr(), x.stride(0), A.data_ptr(), B.data_ptr(), N, base_output.data_ptr(),
         base_output.stride(0), s, K, L, R, p_offs, c, int(max_slice_size), ind.data_ptr(),
-        sl.data_ptr(), nseg, batch_info.permutation.data_ptr(), batch_info.lora_ranks.data_ptr(),
+        sl.data_ptr(), nseg, perm.data_ptr(), batch_info.lora_ranks.data_ptr(),
         batch_info.scalings.data_ptr(), hint, ws.data_ptr(), ws.numel(), _stream(x)))
     return base_output
 

@@ -2,6 +2,7 @@
 // is enqueued), tile choice and kernel launches.
 #include <cinttypes>
 #include <cstring>
+#include <vector>
 
 #include "sgg_internal.h"
 #include "sgg_kernels.h"
@@ -397,7 +398,7 @@ extern "C" int64_t lora_plan_layout(int64_t token_capacity, int32_t seg_capacity
   if (token_capacity < 0 || seg_capacity < 0 || req_capacity < 0 || max_loras < 0) return -1;
   const int64_t sizes[SGG_PLAN_REGIONS] = {token_capacity, seg_capacity + 1, seg_capacity,
                                            req_capacity + 1, req_capacity, max_loras, max_loras,
-                                           seg_capacity + 1, seg_capacity};
+                                           seg_capacity + 1, seg_capacity, token_capacity};
   int64_t pos = 0;
   for (int i = 0; i < SGG_PLAN_REGIONS; ++i) {
     if (offsets) offsets[i] = pos;
@@ -472,16 +473,37 @@ int plan_upload(bool lm_head, const int32_t* seq_lens, const int32_t* req_slots,
     longest = len > longest ? len : longest;
   }
   // Work segments: merge consecutive segments of one slot up to `cap` tokens.
+  // For the lm_head plan they come from the pruned tokens sorted by slot (a
+  // stable sort, whose permutation goes to region 9): its identity order
+  // leaves runs of about one token wherever adapters interleave, and every
+  // run would re-read its adapter's B tile across the whole vocabulary.
   const int32_t* sind = h + off[1];
   const int32_t* sslot = h + off[2];
+  int32_t n_src = n_seg;
+  if (lm_head) {
+    thread_local std::vector<int32_t> sorted;
+    sorted.resize(2 * static_cast<size_t>(seg_capacity) + static_cast<size_t>(num_reqs) + 2);
+    int32_t* tind = sorted.data();
+    int32_t* tslot = tind + seg_capacity + 1;
+    int32_t* treq = tslot + seg_capacity;
+    int32_t ts = 0, tchunk = 0;
+    int64_t ttok = 0;
+    rc = lora_plan_segments(seq_lens, req_slots, num_reqs, max_loras, 0, max_chunk_size,
+                            chunk_size_override, h + off[9], token_capacity, tind, tslot,
+                            seg_capacity, treq, &ts, &tchunk, &ttok);
+    if (rc) return rc;
+    sind = tind;
+    sslot = tslot;
+    n_src = ts;
+  }
   int32_t* wind = h + off[7];
   int32_t* wslot = h + off[8];
   const int32_t cap = chunk > SGG_WORK_SEGMENT_TOKENS ? chunk : SGG_WORK_SEGMENT_TOKENS;
   int32_t n_work = 0, longest_work = 0;
   wind[0] = 0;
-  for (int32_t i = 0; i < n_seg;) {
+  for (int32_t i = 0; i < n_src;) {
     int32_t j = i + 1;
-    while (j < n_seg && sslot[j] == sslot[i] && sind[j + 1] - sind[i] <= cap) ++j;
+    while (j < n_src && sslot[j] == sslot[i] && sind[j + 1] - sind[i] <= cap) ++j;
     wslot[n_work] = sslot[i];
     wind[n_work + 1] = sind[j];
     const int32_t len = sind[j] - sind[i];
@@ -493,17 +515,19 @@ int plan_upload(bool lm_head, const int32_t* seq_lens, const int32_t* req_slots,
     wslot[i] = 0;
     wind[i + 1] = wind[n_work];
   }
-  // One transfer: a copy kernel reading the pinned buffer through its device
-  // mapping (it also raises the done flag); a runtime copy only if the buffer
-  // has no device mapping, followed by an empty copy that raises the flag.
+  // One transfer (region 9 only for the lm_head plan): a copy kernel reading
+  // the pinned buffer through its device mapping (it also raises the done
+  // flag); a runtime copy only if the buffer has no device mapping, followed
+  // by an empty copy that raises the flag.
+  const int64_t n_copy = lm_head ? total : off[9];
   void* src = nullptr;
   hipError_t e = hipHostGetDevicePointer(&src, host_staging, 0);
   if (e == hipSuccess && src != nullptr) {
     e = sgg::launch_plan_copy(static_cast<const int32_t*>(src), static_cast<int32_t*>(device_plan),
-                              total, done_dev, done_value, static_cast<hipStream_t>(stream));
+                              n_copy, done_dev, done_value, static_cast<hipStream_t>(stream));
   } else {
     (void)hipGetLastError();  // clear the failed lookup
-    e = hipMemcpyAsync(device_plan, host_staging, static_cast<size_t>(total) * 4,
+    e = hipMemcpyAsync(device_plan, host_staging, static_cast<size_t>(n_copy) * 4,
                        hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
     if (e == hipSuccess && done_dev != nullptr)
       e = sgg::launch_plan_copy(nullptr, nullptr, 0, done_dev, done_value,

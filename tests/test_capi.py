@@ -287,12 +287,12 @@ def test_np_dtypes_roundtrip():
 
 
 def test_plan_layout_regions():
-    """lora_plan_layout: 9 regions (plan, routing, tables, work segments),
-    64-element aligned, in the documented order and sizes."""
+    """lora_plan_layout: 10 regions (plan, routing, tables, work segments,
+    work permutation), 64-element aligned, in the documented order and sizes."""
     lib = _lib.lib()
-    offs = (ctypes.c_int64 * 9)()
+    offs = (ctypes.c_int64 * 10)()
     total = lib.lora_plan_layout(300, 40, 20, 8, offs)
-    sizes = [300, 41, 40, 21, 20, 8, 8, 41, 40]
+    sizes = [300, 41, 40, 21, 20, 8, 8, 41, 40, 300]
     pos = 0
     for i, n in enumerate(sizes):
         assert offs[i] == pos, i

@@ -396,6 +396,11 @@ def test_lm_head_pruned_pass():
     assert info.permutation.cpu().tolist() == ref["permutation"]
     assert info.seg_indptr[:n + 1].cpu().tolist() == ref["seg_indptr"]
     assert info.weight_indices[:n].cpu().tolist() == ref["seg_slots"]
+    # the kernels run over the pruned tokens sorted by slot: the work
+    # permutation and segments are the chunked plan of the pruned tokens
+    sref = op.plan(lens, slots, False, 128)
+    assert info.work_perm.cpu().tolist() == sref["permutation"]
+    check_work_segments(info, sref)
     x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
     h = be.run_lora_a_sgemm(x, A, pruned_batch_info=info)
     y = be.run_lora_b_sgemm(h, Bw, base_output=base.clone(), pruned_batch_info=info)
@@ -412,6 +417,9 @@ def test_lm_head_pruned_pass():
         pn = pinfo.num_segments
         assert pinfo.seg_indptr[:pn + 1].cpu().tolist() == pref["seg_indptr"]
         assert pinfo.weight_indices[:pn].cpu().tolist() == pref["seg_slots"]
+        psref = op.plan(pl, wi, False, 128)
+        assert pinfo.work_perm.cpu().tolist() == psref["permutation"]
+        check_work_segments(pinfo, psref)
         rows = torch.arange(int(cum[a]), int(cum[z]), device=DEV)
         if rows.numel() == 0:
             continue
@@ -492,7 +500,7 @@ def test_out_of_range_slot_is_no_adapter():
     be = backend(b)
     info = plan_on(be, b)
     # slot outside [0, 2) in the segments the kernels run over: no adapter
-    _, slots, n, _ = info.kernel_segments()
+    _, slots, n, _, _ = info.kernel_segments()
     slots[:n] = 7
     info.weight_indices[:info.num_segments] = 7
     x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
