@@ -99,6 +99,12 @@ def _need_bf16(name, t, dims):
         raise ValueError(f"{name} must have unit stride in its last dimension")
 
 
+def _need_rows_cols(name, t, rows, cols):
+    """`t` holds at least `rows` x `cols` elements (the kernels write them)."""
+    if t.shape[0] != rows or t.shape[1] < cols:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, needs ({rows}, >= {cols})")
+
+
 def _need_dense(name, t):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -247,6 +253,7 @@ def lora_shrink(x, weights, batch_info: LoRABatchInfo, num_slices=1, out=None, w
     if out is None:
         out = torch.empty((s, CR), dtype=torch.bfloat16, device=x.device)
     _need_bf16("out", out, 2)
+    _need_rows_cols("out", out, s, CR)
     ind, sl, nseg, hint, perm = batch_info.kernel_segments()
     ws = workspace
     if ws is None:   # the library checks the size of a caller's workspace itself
@@ -274,11 +281,11 @@ def lora_expand(h, weights, batch_info: LoRABatchInfo, slice_offsets, max_slice_
     L, N, R = weights.shape
     if s != batch_info.num_tokens:
         raise ValueError(f"h has {s} rows, the plan has {batch_info.num_tokens} tokens")
+    _need_rows_cols("h", h, s, c * R)
     if base_output is None:
         base_output = torch.zeros((s, int(offs[-1])), dtype=torch.bfloat16, device=h.device)
     _need_bf16("base_output", base_output, 2)
-    if base_output.shape[0] != s:
-        raise ValueError("base_output rows differ from h rows")
+    _need_rows_cols("base_output", base_output, s, int(offs[-1]))
     ind, sl, nseg, hint, perm = batch_info.kernel_segments()
     check(calls().lora_expand(
         _vp(h), h.stride(0), _vp(weights), N, _vp(base_output), base_output.stride(0), s, L, R,
@@ -307,6 +314,7 @@ def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
     if base_output is None:
         base_output = torch.zeros((s, int(offs[-1])), dtype=torch.bfloat16, device=x.device)
     _need_bf16("base_output", base_output, 2)
+    _need_rows_cols("base_output", base_output, s, int(offs[-1]))
     ind, sl, nseg, hint, perm = batch_info.kernel_segments()
     ws = workspace
     if ws is None:   # the library checks the size of a caller's workspace itself
@@ -333,6 +341,8 @@ def lora_a_embedding(input_ids, weights, batch_info: LoRABatchInfo, vocab_size,
         raise ValueError(f"{s} ids, the plan has {batch_info.num_tokens} tokens")
     if out is None:
         out = torch.empty((s, R), dtype=torch.bfloat16, device=weights.device)
+    _need_bf16("out", out, 2)
+    _need_rows_cols("out", out, s, R)
     # the plan's own segments: the gather parallelises over segments, so the
     # finer partition is the faster one here
     check(calls().lora_a_embedding(

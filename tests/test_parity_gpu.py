@@ -596,6 +596,30 @@ def test_staging_wait_gives_up_on_a_flag_never_raised():
         stg._wait(0, 7, limit_s=0.05)
 
 
+def test_binding_rejects_outputs_too_small():
+    """Host-side checks: an output (or h) with too few rows or columns is
+    refused before anything is launched."""
+    sgg = _sgg()
+    b, proj, t = _small_case(41, [10, 6], [0, 1], 2, [8, 8], [2.0, 1.0], 256, [0, 256], 8)
+    be = backend(b)
+    info = plan_on(be, b)
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    h = torch.zeros((16, 8), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError, match="out has shape"):
+        sgg.lora_shrink(x, A, info, 1, out=torch.zeros((15, 8), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError, match="out has shape"):
+        sgg.lora_shrink(x, A, info, 1, out=torch.zeros((16, 4), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError, match="base_output has shape"):
+        sgg.lora_expand(h, Bw, info, [0, 256], 256, base[:, :200])
+    with pytest.raises(ValueError, match="h has shape"):
+        sgg.lora_expand(h[:, :4], Bw, info, [0, 256], 256, base.clone())
+    ids = torch.zeros(16, dtype=torch.int64, device=DEV)
+    A_emb = torch.zeros((2, 8, 100), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError, match="out has shape"):
+        sgg.lora_a_embedding(ids, A_emb, info, 100,
+                             out=torch.zeros((8, 8), dtype=torch.bfloat16, device=DEV))
+
+
 def test_missing_base_gives_delta():
     b, proj, t = _small_case(40, [10, 6], [0, 1], 2, [8, 8], [2.0, 1.0], 256, [0, 256], 8)
     be = backend(b)
