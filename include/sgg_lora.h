@@ -177,6 +177,40 @@ int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slots, int32_t 
                      int32_t* out_info, int32_t* done_flag, int32_t done_value, void* stream);
 
 /*
+ * lora_plan_device -- the batch plan computed on the GPU, as one kernel on
+ * `stream`, from request lengths and slots already in device memory.
+ * (chunked_backend.py page: the steps of lora_plan_upload -- chunk size,
+ *  permutation, segments, request boundaries, graph-capacity padding of the
+ *  CUDA-graph branch of prepare_lora_batch.)
+ *
+ * Writes regions 0-8 of the layout above into `device_plan` (bit for bit the
+ * plan lora_plan_upload writes for the same batch and capacities) and
+ * out_info's six values, then a status, to device_info[0..6].  Nothing goes
+ * through the host and nothing synchronises, so the launch can be captured
+ * in a graph with the kernels that read the plan; the caller updates the
+ * lengths and slots in device memory between replays.
+ *   seq_lens       device int32 [num_reqs]; ignored (one token each) when
+ *                  is_decode.
+ *   req_slots      device int32 [num_reqs]; lora_ranks, scalings: device
+ *                  arrays of max_loras entries.
+ *   device_info    device int32 [8].
+ * Host-side errors as lora_plan_upload; SGG_ERR_UNSUPPORTED above
+ * SGG_DEVICE_PLAN_MAX_REQS requests or SGG_DEVICE_PLAN_MAX_LORAS slots.  A
+ * batch that is invalid on the device (slot outside [0, max_loras), negative
+ * length, a decode request of other than one token, more tokens or segments
+ * than the capacities) is not planned: device_info[6] holds a non-zero
+ * status and every segment and work segment is written empty.
+ */
+#define SGG_DEVICE_PLAN_MAX_REQS 4096
+#define SGG_DEVICE_PLAN_MAX_LORAS 1024
+int lora_plan_device(const int32_t* seq_lens, const int32_t* req_slots, int32_t num_reqs,
+                     const int32_t* lora_ranks, const float* scalings, int32_t max_loras,
+                     int32_t is_decode, int32_t max_chunk_size, int32_t chunk_size_override,
+                     int64_t token_capacity, int32_t seg_capacity, int32_t req_capacity,
+                     void* device_plan, int64_t buffer_bytes, int32_t* device_info,
+                     void* stream);
+
+/*
  * lora_plan_lm_head -- plan of a pruned lm_head pass.
  * (chunked_backend.py page: _prepare_lm_head_batch_info and
  *  _build_lm_head_batch_info.)

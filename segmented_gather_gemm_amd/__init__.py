@@ -13,6 +13,7 @@ from .binding import (
     default_workspace,
     lora_a_embedding,
     lora_expand,
+    lora_plan_device,
     lora_plan_lm_head,
     lora_plan_max_segments,
     lora_plan_segments,
@@ -25,6 +26,6 @@ calls()
 
 __all__ = [
     "ChunkedSgmvLoRA", "LoRABatchInfo", "SggError", "default_workspace", "lora_a_embedding",
-    "lora_expand", "lora_plan_lm_head", "lora_plan_max_segments", "lora_plan_segments",
+    "lora_expand", "lora_plan_device", "lora_plan_lm_head", "lora_plan_max_segments", "lora_plan_segments",
     "lora_qkv", "lora_shrink",
 ]

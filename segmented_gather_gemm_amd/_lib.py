@@ -28,6 +28,9 @@ SIGNATURES = {
     "lora_plan_upload": (ctypes.c_int, [
         _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
         _i64, _i32, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _vp]),
+    "lora_plan_device": (ctypes.c_int, [
+        _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+        _i64, _i32, _i32, _vp, _i64, _vp, _vp]),
     "lora_plan_lm_head_upload": (ctypes.c_int, [
         _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
         _i64, _i32, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _vp]),

@@ -126,6 +126,8 @@ class ChunkedSgmvLoRA:
         self.cuda_graph_batch_info = None
         self._graph_dev = None
         self._graph_cap = None
+        self._graph_info_dev = None
+        self.cuda_graph_plan_info = None
         self._staging = _Staging(self.device)
         self._layouts = {}
         self._info_arr = (ctypes.c_int32 * 6)()
@@ -322,6 +324,29 @@ class ChunkedSgmvLoRA:
             req_weight_indices=v["req_slots"], use_cuda_graph=True, max_seg_len=hint,
             work_indptr=v["work_indptr"], work_slots=v["work_slots"], num_work_segments=cap,
             max_work_len=hint)
+        return self.cuda_graph_batch_info
+
+    def prepare_lora_batch_device(self, seq_lens, weight_indices, lora_ranks, scalings,
+                                  is_decode=False, chunk_size_override=0):
+        """Plan into the graph buffer on the GPU (lora_plan_device) from
+        device tensors: no host round trip, so a graph may capture this call
+        together with the kernels; update the tensors' contents between
+        replays.  Needs init_cuda_graph_batch_info; the batch size is
+        weight_indices.numel() (at most the graph's).  The plan's counts and
+        status are left in ``cuda_graph_plan_info`` (int32 [8], device)."""
+        if self._graph_cap is None:
+            raise RuntimeError("call init_cuda_graph_batch_info first")
+        max_bs, max_tokens, seg_cap = self._graph_cap
+        if weight_indices.numel() > max_bs:
+            raise ValueError("batch exceeds the graph capacity")
+        if self._graph_info_dev is None:
+            self._graph_info_dev = torch.zeros(8, dtype=torch.int32, device=self.device)
+        B.lora_plan_device(seq_lens, weight_indices, lora_ranks, scalings,
+                           self.max_loras_per_batch, is_decode, self.max_chunk_size,
+                           chunk_size_override, max_tokens, seg_cap, max_bs, self._graph_dev,
+                           self._graph_info_dev)
+        self.cuda_graph_plan_info = self._graph_info_dev
+        self.batch_info = self.cuda_graph_batch_info
         return self.cuda_graph_batch_info
 
     # -------------------------------------------------------------- kernels

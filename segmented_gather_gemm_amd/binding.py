@@ -190,6 +190,35 @@ def lora_plan_lm_head(pruned_lens, req_slots, max_loras, max_chunk_size, chunk_s
             "capacity": cap}
 
 
+def lora_plan_device(seq_lens, req_slots, lora_ranks, scalings, max_loras, is_decode,
+                     max_chunk_size, chunk_size_override, token_capacity, seg_capacity,
+                     req_capacity, device_plan, device_info):
+    """Plan a batch on the GPU into `device_plan` (int32 device tensor in the
+    lora_plan_layout layout) from device tensors: seq_lens (int32, ignored in
+    decode mode), req_slots (int32), lora_ranks (int32) and scalings
+    (float32).  The counts and a status go to device_info (int32 [8]) on the
+    device; nothing is copied to the host."""
+    def dev_i32(name, t, n):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.numel() < n:
+            raise ValueError(f"{name} must be a contiguous int32 device tensor of >= {n} entries")
+    bs = req_slots.numel()
+    dev_i32("req_slots", req_slots, bs)
+    if not is_decode:
+        dev_i32("seq_lens", seq_lens, bs)
+    dev_i32("lora_ranks", lora_ranks, max_loras)
+    dev_i32("device_plan", device_plan, 1)
+    dev_i32("device_info", device_info, 8)
+    if scalings.dtype != torch.float32 or not scalings.is_cuda or not scalings.is_contiguous() \
+            or scalings.numel() < max_loras:
+        raise ValueError("scalings must be a contiguous float32 device tensor")
+    check(calls().lora_plan_device(
+        None if is_decode else seq_lens.data_ptr(), req_slots.data_ptr(), bs,
+        lora_ranks.data_ptr(), scalings.data_ptr(), int(max_loras), 1 if is_decode else 0,
+        int(max_chunk_size), int(chunk_size_override), int(token_capacity), int(seg_capacity),
+        int(req_capacity), device_plan.data_ptr(), 4 * device_plan.numel(),
+        device_info.data_ptr(), _stream(device_plan)))
+
+
 # ----------------------------------------------------------------- workspace
 
 _workspaces = {}

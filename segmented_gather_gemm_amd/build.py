@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsgg_lora.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 CALLMOD = os.path.join(PKG, "_sggcall" + sysconfig.get_config_var("EXT_SUFFIX"))
-SOURCES = ["plan.cpp", "shrink.hip", "shrink_gemm.hip", "expand.hip", "lora_api.hip"]
+SOURCES = ["plan.cpp", "plan_device.hip", "shrink.hip", "shrink_gemm.hip", "expand.hip",
+           "lora_api.hip"]
 ARCH = os.environ.get("SGG_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -560,6 +560,44 @@ extern "C" int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slot
                      out_info, done_flag, done_value, stream);
 }
 
+extern "C" int lora_plan_device(const int32_t* seq_lens, const int32_t* req_slots,
+                                int32_t num_reqs, const int32_t* lora_ranks,
+                                const float* scalings, int32_t max_loras, int32_t is_decode,
+                                int32_t max_chunk_size, int32_t chunk_size_override,
+                                int64_t token_capacity, int32_t seg_capacity,
+                                int32_t req_capacity, void* device_plan, int64_t buffer_bytes,
+                                int32_t* device_info, void* stream) {
+  int64_t off[SGG_PLAN_REGIONS];
+  const int64_t total = lora_plan_layout(token_capacity, seg_capacity, req_capacity, max_loras, off);
+  SGG_CHECK(total >= 0, SGG_ERR_INVALID, "negative capacity");
+  SGG_CHECK(max_loras >= 1 && max_loras <= sgg::kDevicePlanMaxLoras, SGG_ERR_UNSUPPORTED,
+            "max_loras=%d outside [1, %d] for the device planner", max_loras,
+            sgg::kDevicePlanMaxLoras);
+  SGG_CHECK(num_reqs >= 0 && num_reqs <= sgg::kDevicePlanMaxReqs, SGG_ERR_UNSUPPORTED,
+            "num_reqs=%d outside [0, %d] for the device planner", num_reqs,
+            sgg::kDevicePlanMaxReqs);
+  SGG_CHECK(num_reqs <= req_capacity, SGG_ERR_CAPACITY, "%d requests > capacity %d", num_reqs,
+            req_capacity);
+  SGG_CHECK(token_capacity <= INT32_MAX, SGG_ERR_INVALID, "token_capacity above int32 indexing");
+  SGG_CHECK(num_reqs == 0 || req_slots != nullptr, SGG_ERR_INVALID, "req_slots is NULL");
+  SGG_CHECK(is_decode || num_reqs == 0 || seq_lens != nullptr, SGG_ERR_INVALID,
+            "seq_lens is NULL in extend mode");
+  SGG_CHECK(lora_ranks && scalings && device_plan && device_info, SGG_ERR_INVALID,
+            "lora_ranks, scalings, device_plan or device_info is NULL");
+  SGG_CHECK(chunk_size_override >= 0, SGG_ERR_INVALID, "chunk_size_override=%d is negative",
+            chunk_size_override);
+  SGG_CHECK((reinterpret_cast<uintptr_t>(device_plan) & 3) == 0, SGG_ERR_INVALID,
+            "device_plan must be 4-byte aligned");
+  SGG_CHECK(buffer_bytes >= off[9] * 4, SGG_ERR_CAPACITY,
+            "plan buffer of %" PRId64 " bytes, regions 0-8 need %" PRId64, buffer_bytes,
+            off[9] * 4);
+  const hipError_t e = sgg::launch_plan_device(
+      is_decode ? nullptr : seq_lens, req_slots, num_reqs, lora_ranks, scalings, max_loras,
+      is_decode, max_chunk_size, chunk_size_override, token_capacity, seg_capacity, off,
+      static_cast<int32_t*>(device_plan), device_info, static_cast<hipStream_t>(stream));
+  return launch_status(e, "plan_device");
+}
+
 extern "C" int lora_plan_lm_head_upload(const int32_t* pruned_lens, const int32_t* req_slots,
                                         int32_t num_reqs, const int32_t* lora_ranks,
                                         const float* scalings, int32_t max_loras,

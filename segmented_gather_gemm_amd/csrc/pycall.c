@@ -97,6 +97,7 @@ static int convert(const char* name, const char* sig, PyObject* const* args, Py_
 #define SIG_lora_plan_max_segments "lii"
 #define SIG_lora_plan_upload "ppippiiiiliipplppip"
 #define SIG_lora_plan_lm_head_upload "ppippiiiliipplppip"
+#define SIG_lora_plan_device "ppippiiiiliiplpp"
 #define SIG_lora_shrink_workspace_bytes "lliiii"
 #define SIG_lora_qkv_workspace_bytes "lliiii"
 #define SIG_lora_shrink "plppllliiippippiplp"
@@ -132,6 +133,12 @@ static PyObject* py_lora_plan_upload(PyObject* self, PyObject* const* args, Py_s
   RETURN_INT(lora_plan_upload(
       I32P(0), I32P(1), I(2), I32P(3), (const float*)P(4), I(5), I(6), I(7), I(8), L(9), I(10),
       I(11), P(12), P(13), L(14), I32P(15), I32P(16), I(17), P(18)));
+}
+
+static PyObject* py_lora_plan_device(PyObject* self, PyObject* const* args, Py_ssize_t n) {
+  CONVERT(lora_plan_device);
+  RETURN_INT(lora_plan_device(I32P(0), I32P(1), I(2), I32P(3), (const float*)P(4), I(5), I(6),
+                              I(7), I(8), L(9), I(10), I(11), P(12), L(13), I32P(14), P(15)));
 }
 
 static PyObject* py_lora_plan_lm_head_upload(PyObject* self, PyObject* const* args,
@@ -189,6 +196,7 @@ static PyMethodDef methods[] = {
     ENTRY(lora_plan_max_segments),
     ENTRY(lora_plan_upload),
     ENTRY(lora_plan_lm_head_upload),
+    ENTRY(lora_plan_device),
     ENTRY(lora_shrink_workspace_bytes),
     ENTRY(lora_qkv_workspace_bytes),
     ENTRY(lora_shrink),
@@ -207,7 +215,8 @@ PyMODINIT_FUNC PyInit__sggcall(void) {
   PyObject* m = PyModule_Create(&module);
   if (m == NULL) return NULL;
   PyObject* sigs = Py_BuildValue(
-      "{ssssssssssssssssss}", "lora_plan_max_segments", SIG_lora_plan_max_segments,
+      "{ssssssssssssssssssss}", "lora_plan_max_segments", SIG_lora_plan_max_segments,
+      "lora_plan_device", SIG_lora_plan_device,
       "lora_plan_upload", SIG_lora_plan_upload, "lora_plan_lm_head_upload",
       SIG_lora_plan_lm_head_upload, "lora_shrink_workspace_bytes",
       SIG_lora_shrink_workspace_bytes, "lora_qkv_workspace_bytes", SIG_lora_qkv_workspace_bytes,

@@ -97,6 +97,16 @@ hipError_t launch_shrink_gemm(const ShrinkParams& p, int bm, int bn, int64_t gri
 hipError_t launch_expand(const ExpandParams& p, const ExpandTiling& t, hipStream_t stream);
 hipError_t launch_embedding(const EmbeddingParams& p, hipStream_t stream);
 
+// The batch plan on the GPU (plan_device.hip): one workgroup; up to
+// kDevicePlanMaxReqs requests and kDevicePlanMaxLoras slots.
+constexpr int kDevicePlanMaxLoras = 1024;  // SGG_DEVICE_PLAN_MAX_LORAS
+constexpr int kDevicePlanMaxReqs = 4096;   // SGG_DEVICE_PLAN_MAX_REQS
+hipError_t launch_plan_device(const int32_t* seq_lens, const int32_t* req_slots, int32_t bs,
+                              const int32_t* ranks, const float* scalings, int32_t L,
+                              int32_t is_decode, int32_t max_chunk, int32_t chunk_override,
+                              int64_t token_capacity, int32_t seg_capacity, const int64_t* off,
+                              int32_t* plan, int32_t* info, hipStream_t stream);
+
 // Copy n int32 from pinned host memory (given by its device-side address) to
 // device memory, as a kernel on `stream`; src and dst 8-byte aligned.  When
 // done_dev_view is not null (host memory, by its device-side address),

@@ -369,7 +369,7 @@ def _header_signature(name):
 
 def test_call_module_signatures_match_header():
     C = _lib.calls()
-    assert set(C.SIGNATURES) == {"lora_plan_max_segments", "lora_plan_upload",
+    assert set(C.SIGNATURES) == {"lora_plan_max_segments", "lora_plan_upload", "lora_plan_device",
                                  "lora_plan_lm_head_upload", "lora_shrink_workspace_bytes",
                                  "lora_qkv_workspace_bytes", "lora_shrink", "lora_expand",
                                  "lora_qkv", "lora_a_embedding"}

@@ -7,6 +7,8 @@ first/last tokens and a seeded random sample), computed one by one by the
 oracle, in the launch configuration the benchmark times.
 """
 
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -691,3 +693,157 @@ def test_graph_mode_replays_match_oracle():
         assert np.array_equal(to_f64(e), want_e), f"graph replay {trial} embedding"
         # eager work between replays, on the default stream
         torch.mm(torch.randn(64, 64, device=DEV), torch.randn(64, 64, device=DEV))
+
+
+# ----------------------------------------------------------- device planner
+
+def _plan_regions(be, s, bs, cap):
+    """The meaningful contents of the graph plan buffer, region by region."""
+    v = be.cuda_graph_batch_info
+    return {"permutation": v.permutation[:s].cpu().tolist(),
+            "seg_indptr": v.seg_indptr[:cap + 1].cpu().tolist(),
+            "seg_slots": v.weight_indices[:cap].cpu().tolist(),
+            "req_seg_indptr": v.req_seg_indptr[:bs + 1].cpu().tolist(),
+            "req_slots": v.req_weight_indices[:bs].cpu().tolist(),
+            "ranks": v.lora_ranks.cpu().tolist(),
+            "scalings": v.scalings.cpu().tolist(),
+            "work_indptr": v.work_indptr[:cap + 1].cpu().tolist(),
+            "work_slots": v.work_slots[:cap].cpu().tolist()}
+
+
+DEVICE_PLAN_CASES = [
+    # (name, bs, max_bs, tokens_per_bs, L, lens (None: decode), max_chunk, override)
+    ("decode256", 256, 256, 1, 8, None, 128, 0),
+    ("decode3000_L700", 3000, 3000, 1, 700, None, 128, 0),
+    ("extend_zero_lens", 100, 128, 300, 37, (0, 300), 128, 0),
+    ("override3", 50, 64, 200, 5, (0, 20), 128, 3),
+    ("override48", 60, 64, 200, 4, (0, 200), 128, 48),
+    ("cap16", 40, 40, 100, 6, (1, 100), 16, 0),
+    ("L1024_bs4096", 4096, 4096, 3, 1024, (0, 3), 128, 0),
+]
+
+
+@pytest.mark.parametrize("case", DEVICE_PLAN_CASES, ids=[c[0] for c in DEVICE_PLAN_CASES])
+def test_device_plan_matches_host_plan(case):
+    """lora_plan_device writes, bit for bit, the plan the host planner uploads
+    for the same batch and capacities, and that plan is the oracle's."""
+    sgg = _sgg()
+    name, bs, max_bs, tpb, L, lens_rng, max_chunk, override = case
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    decode = lens_rng is None
+    lens = [1] * bs if decode else rng.integers(lens_rng[0], lens_rng[1] + 1, bs).tolist()
+    slots = rng.integers(0, L, bs).tolist()
+    ranks = rng.integers(0, 65, L).tolist()
+    scal = rng.uniform(0, 4, L).astype(np.float32).tolist()
+    hb = sgg.ChunkedSgmvLoRA(L, max_chunk, DEV)
+    db = sgg.ChunkedSgmvLoRA(L, max_chunk, DEV)
+    hb.init_cuda_graph_batch_info(max_bs, tpb)
+    db.init_cuda_graph_batch_info(max_bs, tpb)
+    _, max_tokens, cap = hb._graph_cap
+    hb.prepare_lora_batch(None if decode else lens, slots, ranks, scal, is_decode=decode,
+                          use_cuda_graph=True, chunk_size_override=override)
+    i32 = lambda v: torch.tensor(v, dtype=torch.int32, device=DEV)
+    db.prepare_lora_batch_device(None if decode else i32(lens), i32(slots), i32(ranks),
+                                 torch.tensor(scal, dtype=torch.float32, device=DEV),
+                                 is_decode=decode, chunk_size_override=override)
+    torch.cuda.synchronize()
+    s = sum(lens)
+    got, want = _plan_regions(db, s, bs, cap), _plan_regions(hb, s, bs, cap)
+    for k in want:
+        assert got[k] == want[k], k
+    ref = op.plan(None if decode else lens, slots, decode, max_chunk, override, capacity=cap)
+    assert got["permutation"] == ref["permutation"]
+    assert got["seg_indptr"] == ref["seg_indptr"] and got["seg_slots"] == ref["seg_slots"]
+    info = db.cuda_graph_plan_info.cpu().tolist()
+    assert info[6] == 0
+    assert info[0] == ref["num_segments"] and info[1] == ref["chunk_size"] and info[3] == s
+
+
+@pytest.mark.parametrize("bad", ["slot", "negative_len", "decode_bad_slot", "too_many_tokens"])
+def test_device_plan_invalid_batch_is_empty(bad):
+    """An invalid batch found on the device is not planned: a non-zero status
+    and every segment empty, so the kernels that follow do nothing."""
+    sgg = _sgg()
+    L, bs = 4, 16
+    be = sgg.ChunkedSgmvLoRA(L, 128, DEV)
+    be.init_cuda_graph_batch_info(bs, 8)
+    _, max_tokens, cap = be._graph_cap
+    lens, slots, decode = [3] * bs, [1] * bs, False
+    if bad == "slot":
+        slots[5] = L
+    elif bad == "negative_len":
+        lens[2] = -1
+    elif bad == "decode_bad_slot":
+        decode, lens = True, [1] * bs
+        slots[0] = -1
+    elif bad == "too_many_tokens":
+        lens[0] = max_tokens
+    i32 = lambda v: torch.tensor(v, dtype=torch.int32, device=DEV)
+    lens_d = i32(lens)
+    be.prepare_lora_batch_device(None if decode else lens_d, i32(slots), i32([8] * L),
+                                 torch.ones(L, dtype=torch.float32, device=DEV), is_decode=decode)
+    torch.cuda.synchronize()
+    v = be.cuda_graph_batch_info
+    assert be.cuda_graph_plan_info[6].item() != 0
+    assert v.seg_indptr[:cap + 1].cpu().tolist() == [0] * (cap + 1)
+    assert v.work_indptr[:cap + 1].cpu().tolist() == [0] * (cap + 1)
+
+
+def test_device_plan_captured_with_kernels():
+    """The device planner captured in one graph with the shrink and the
+    expand; the lengths and slots are rewritten in device memory before each
+    replay, and every replay is checked against the oracle."""
+    sgg = _sgg()
+    L, K, R, offs = 5, 512, 16, [0, 256, 320, 384]
+    max_bs, tpb = 24, 12
+    rng = np.random.default_rng(77)
+    ranks, scal = [16, 8, 0, 16, 12], [1.0, 0.5, 2.0, 1.5, 1.0]
+    proto = Batch("devgraph", 7777, [tpb] * max_bs, [0] * max_bs, False, L, ranks, scal, 128,
+                  [Projection("qkv", K, offs, R)])
+    proj = proto.projections[0]
+    t = draw_projection(proto, proj)
+    x, A, Bw = (t[k].to(DEV) for k in ("x", "A", "B"))
+    base0 = t["base"].to(DEV)
+    base = base0.clone()
+    h = torch.empty(max_bs * tpb, 3 * R, dtype=torch.bfloat16, device=DEV)
+    ws = torch.zeros(8 << 20, dtype=torch.uint8, device=DEV)
+    be = sgg.ChunkedSgmvLoRA(L, 128, DEV)
+    info = be.init_cuda_graph_batch_info(max_bs, tpb)
+    lens_d = torch.full((max_bs,), tpb, dtype=torch.int32, device=DEV)
+    slots_d = torch.zeros(max_bs, dtype=torch.int32, device=DEV)
+    ranks_d = torch.tensor(ranks, dtype=torch.int32, device=DEV)
+    scal_d = torch.tensor(scal, dtype=torch.float32, device=DEV)
+
+    def step():
+        be.prepare_lora_batch_device(lens_d, slots_d, ranks_d, scal_d)
+        sgg.lora_shrink(x, A, info, 3, out=h, workspace=ws)
+        sgg.lora_expand(h, Bw, info, offs, 256, base)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for trial in range(4):
+        lens = rng.integers(0, tpb + 1, max_bs).tolist()
+        slots = rng.integers(0, L, max_bs).tolist()
+        lens_d.copy_(torch.tensor(lens, dtype=torch.int32))
+        slots_d.copy_(torch.tensor(slots, dtype=torch.int32))
+        base.copy_(base0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert be.cuda_graph_plan_info[6].item() == 0
+        s = sum(lens)
+        b = Batch("g", 0, lens, slots, False, L, ranks, scal, 128, proto.projections)
+        ts = {"x": t["x"][:s], "A": t["A"], "B": t["B"], "base": t["base"][:s]}
+        want_h, want_y = oracle_forward(ts, b, proj)
+        assert_close(h[:s], want_h, f"device-planned replay {trial} h")
+        assert_close(base[:s], want_y, f"device-planned replay {trial} y")
+        # rows past the batch's tokens are not touched
+        assert torch.equal(base[s:].view(torch.int16), base0[s:].view(torch.int16))
