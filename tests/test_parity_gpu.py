@@ -7,6 +7,7 @@ first/last tokens and a seeded random sample), computed one by one by the
 oracle, in the launch configuration the benchmark times.
 """
 
+import ctypes
 import zlib
 
 import numpy as np
@@ -847,3 +848,35 @@ def test_device_plan_captured_with_kernels():
         assert_close(base[:s], want_y, f"device-planned replay {trial} y")
         # rows past the batch's tokens are not touched
         assert torch.equal(base[s:].view(torch.int16), base0[s:].view(torch.int16))
+
+
+def test_plan_upload_from_pageable_staging():
+    """lora_plan_upload with a staging buffer that has no device mapping
+    (pageable memory) takes the runtime-copy path and still raises the done
+    flag; the uploaded plan is the oracle's."""
+    from segmented_gather_gemm_amd import _lib
+    lens, slots, L = [3, 0, 5, 2, 7], [2, 1, 0, 2, 1], 3
+    ranks = np.array([8, 16, 4], np.int32)
+    scal = np.array([1.0, 0.5, 2.0], np.float32)
+    s, bs = sum(lens), len(lens)
+    cap = int(_lib.lib().lora_plan_max_segments(s, L, 16))
+    offs = (ctypes.c_int64 * 10)()
+    total = int(_lib.lib().lora_plan_layout(s, cap, bs, L, offs))
+    staging = np.zeros(total, np.int32)            # pageable host memory
+    dev = torch.zeros(total, dtype=torch.int32, device=DEV)
+    flag = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+    info = np.zeros(6, np.int32)
+    rc = _lib.calls().lora_plan_upload(
+        np.array(lens, np.int32), np.array(slots, np.int32), bs, ranks, scal, L, 0, 128, 0, s,
+        cap, bs, staging, dev.data_ptr(), 4 * total, info, flag.data_ptr(), 7,
+        torch._C._cuda_getCurrentRawStream(0))
+    assert rc == 0, _lib.lib().lora_last_error()
+    torch.cuda.synchronize()
+    assert flag.item() == 7
+    ref = op.plan(lens, slots, False, 128, capacity=cap)
+    got = dev.cpu().numpy()
+    assert got[offs[0]:offs[0] + s].tolist() == ref["permutation"]
+    assert got[offs[1]:offs[1] + cap + 1].tolist() == ref["seg_indptr"]
+    assert got[offs[2]:offs[2] + cap].tolist() == ref["seg_slots"]
+    assert got[offs[5]:offs[5] + L].tolist() == ranks.tolist()
+    assert info[0] == ref["num_segments"] and info[1] == ref["chunk_size"] and info[3] == s
