@@ -99,9 +99,16 @@ def _need_bf16(name, t, dims):
         raise ValueError(f"{name} must have unit stride in its last dimension")
 
 
+def _need_bf16_dense(name, t, dims):
+    """A dense bf16 device tensor of `dims` dimensions (weights)."""
+    if t.dtype is not torch.bfloat16 or not t.is_cuda or t.dim() != dims or not t.is_contiguous():
+        _need_bf16(name, t, dims)
+        _need_dense(name, t)
+
+
 def _need_rows_cols(name, t, rows, cols):
     """`t` holds at least `rows` x `cols` elements (the kernels write them)."""
-    if t.shape[0] != rows or t.shape[1] < cols:
+    if t.size(0) != rows or t.size(1) < cols:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, needs ({rows}, >= {cols})")
 
 
@@ -268,8 +275,7 @@ def _offsets(slice_offsets):
 def lora_shrink(x, weights, batch_info: LoRABatchInfo, num_slices=1, out=None, workspace=None):
     """LoRA-A: x (s, K), weights (L, c*R, K) -> h (s, c*R), original token order."""
     _need_bf16("x", x, 2)
-    _need_bf16("weights", weights, 3)
-    _need_dense("weights", weights)
+    _need_bf16_dense("weights", weights, 3)
     s, K = x.shape
     L, CR, K2 = weights.shape
     if K2 != K:
@@ -302,8 +308,7 @@ def lora_expand(h, weights, batch_info: LoRABatchInfo, slice_offsets, max_slice_
     ``base_output=None`` gives a zero-filled output (the update alone).
     """
     _need_bf16("h", h, 2)
-    _need_bf16("weights", weights, 3)
-    _need_dense("weights", weights)
+    _need_bf16_dense("weights", weights, 3)
     offs, p_offs = _offsets(slice_offsets)
     c = len(offs) - 1
     s = h.shape[0]
@@ -327,10 +332,8 @@ def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
              base_output=None, workspace=None):
     """Stacked shrink + expand with one plan (qkv: 3 slices, gate_up: 2)."""
     _need_bf16("x", x, 2)
-    _need_bf16("A", A, 3)
-    _need_bf16("B", B, 3)
-    _need_dense("A", A)
-    _need_dense("B", B)
+    _need_bf16_dense("A", A, 3)
+    _need_bf16_dense("B", B, 3)
     offs, p_offs = _offsets(slice_offsets)
     c = len(offs) - 1
     s, K = x.shape
@@ -360,10 +363,9 @@ def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
 def lora_a_embedding(input_ids, weights, batch_info: LoRABatchInfo, vocab_size,
                      extra_embeddings=None, out=None):
     """LoRA-A embedding lookup: ids (s,), weights (L, R, V) -> (s, R)."""
-    if input_ids.dtype != torch.int64 or input_ids.device.type != "cuda":
+    if input_ids.dtype is not torch.int64 or not input_ids.is_cuda:
         raise TypeError("input_ids must be an int64 tensor on a ROCm device")
-    _need_bf16("weights", weights, 3)
-    _need_dense("weights", weights)
+    _need_bf16_dense("weights", weights, 3)
     s = input_ids.shape[0]
     L, R, V = weights.shape
     if s != batch_info.num_tokens:
@@ -375,9 +377,9 @@ def lora_a_embedding(input_ids, weights, batch_info: LoRABatchInfo, vocab_size,
     # the plan's own segments: the gather parallelises over segments, so the
     # finer partition is the faster one here
     check(calls().lora_a_embedding(
-        _vp(input_ids.contiguous()), _vp(weights), V, _vp(out), out.stride(0), s, L, R,
-        int(vocab_size), _vp(batch_info.seg_indptr), _vp(batch_info.weight_indices),
-        batch_info.num_segments, _vp(batch_info.permutation),
-        _vp(batch_info.lora_ranks), 0 if extra_embeddings is None else 1,
-        _stream(weights)))
+        input_ids.contiguous().data_ptr(), weights.data_ptr(), V, out.data_ptr(), out.stride(0),
+        s, L, R, int(vocab_size), batch_info.seg_indptr.data_ptr(),
+        batch_info.weight_indices.data_ptr(), batch_info.num_segments,
+        batch_info.permutation.data_ptr(), batch_info.lora_ranks.data_ptr(),
+        0 if extra_embeddings is None else 1, _stream(weights)))
     return out
