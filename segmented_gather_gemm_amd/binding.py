@@ -84,7 +84,8 @@ def _host_i32(values):
 def _cpu_i32_ptr(t):
     if t is None:
         return ctypes.cast(0, _P32)
-    assert t.dtype == torch.int32 and t.device.type == "cpu" and t.is_contiguous()
+    if t.dtype != torch.int32 or t.device.type != "cpu" or not t.is_contiguous():
+        raise ValueError("plan output arrays must be contiguous int32 CPU tensors")
     return ctypes.cast(t.data_ptr(), _P32)
 
 
