@@ -17,8 +17,8 @@ Prints ONE JSON line.  `value` is tokens/s of whole steps (wall clock over
 the timed steps, inputs resident in HBM); kernel durations come from HIP
 events on the stream the kernels run on.  `--secondary` adds the prefill
 chunk sweep (16 / 32 / 64 / 128), the skewed batch (o_proj, down_proj), the
-full Llama-3-8B-shaped layer sweep with the embedding gather, and the pruned
-lm_head pass of the decode batch.
+full Llama-3-8B-shaped layer sweep with the embedding gather, the pruned
+lm_head pass of the decode batch, and the device-side planner.
 """
 
 import argparse
@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--sets", type=int, default=48, help="rotated input sets")
     ap.add_argument("--secondary", action="store_true",
                     help="also time the prefill chunk sweep, the skewed batch, the full "
-                         "layer sweep and the lm_head pass")
+                         "layer sweep, the lm_head pass and the device-side planner")
     ap.add_argument("--full-layers", type=int, default=8,
                     help="layers with distinct weights timed in the full layer sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -503,6 +503,53 @@ def run_lm_head(device, steps=20, warmup=3):
     return res
 
 
+def run_device_plan(device, steps=200):
+    """The device-side planner (lora_plan_device) on the decode batch and on
+    the prefill batch, one launch per step back to back behind a delay
+    kernel; the host planner with its upload timed the same way beside it."""
+    import torch
+    import segmented_gather_gemm_amd as sgg
+    from synth import draw_batch
+    stream = torch.cuda.current_stream(device)
+    res = {}
+    for name, b in (("decode", draw_batch("decode")), ("prefill", draw_batch("prefill"))):
+        decode = b.is_decode
+        max_bs = len(b.req_slots)
+        tpb = 1 if decode else max(b.seq_lens)
+        be = sgg.ChunkedSgmvLoRA(b.num_loras, b.max_chunk_size, device)
+        be.init_cuda_graph_batch_info(max_bs, tpb)
+        i32 = lambda v: torch.tensor(v, dtype=torch.int32, device=device)
+        lens_d = i32(b.seq_lens)
+        slots_d, ranks_d = i32(b.req_slots), i32(b.lora_ranks)
+        scal_d = torch.tensor(b.scalings, dtype=torch.float32, device=device)
+        slots, ranks = np.asarray(b.req_slots, np.int32), np.asarray(b.lora_ranks, np.int32)
+        scal = np.asarray(b.scalings, np.float32)
+        lens = None if decode else np.asarray(b.seq_lens, np.int32)
+        calls = {
+            "device_planner_us": lambda: be.prepare_lora_batch_device(
+                lens_d, slots_d, ranks_d, scal_d, is_decode=decode),
+            "host_planner_and_upload_us": lambda: be.prepare_lora_batch(
+                lens, slots, ranks, scal, is_decode=decode, use_cuda_graph=True),
+        }
+        out = {"tokens": b.num_tokens, "requests": max_bs}
+        for key, fn in calls.items():
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            held = hold_stream(stream, 5.0 + 0.05 * steps)
+            e0.record(stream)
+            for _ in range(steps):
+                fn()
+            e1.record(stream)
+            b2b = not held.query()
+            torch.cuda.synchronize()
+            out[key] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
+            out[key.replace("_us", "_back_to_back")] = b2b
+        res[name] = out
+    return res
+
+
 def copy_probe(device):
     import torch
     n = 1 << 30
@@ -610,6 +657,8 @@ def main():
         line["full"] = run_full(device, args.full_layers)
         print("# lm_head pass", file=sys.stderr, flush=True)
         line["lm_head"] = run_lm_head(device)
+        print("# device planner", file=sys.stderr, flush=True)
+        line["device_plan"] = run_device_plan(device)
     if not args.no_cpu:
         print("# cpu baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -12,14 +12,15 @@
 //   2. tokens per slot (LDS histogram), the chunk size, each slot's first
 //      sorted position and first segment (scans over the slots);
 //   3. each request's first sorted position: the stable counting sort.  One
-//      wave walks the requests 64 at a time; a lane adds the lengths of
-//      earlier lanes of its slot and the slot's running total, and the
-//      slot's first lane in the group then advances that total;
-//   4. the permutation: every thread takes tokens, finds each token's
-//      request by binary search and writes its sorted position;
-//   5. segments (full chunks, remainder last), work segments (consecutive
-//      segments of one slot merged greedily within max(chunk, 128) tokens),
-//      capacity padding (slot 0, zero length) and the rank / scaling tables.
+//      wave walks the requests 64 at a time; for each slot among them (by
+//      ballot) its lanes add the lengths of its earlier lanes to the slot's
+//      running position, which the slot's first lane then advances;
+//   4. the permutation: one wave per request writes its tokens' sorted
+//      positions;
+//   5. segments (full chunks, remainder last) and work segments
+//      (consecutive segments of one slot merged greedily within
+//      max(chunk, 128) tokens, in closed form), one per thread; capacity
+//      padding (slot 0, zero length) and the rank / scaling tables.
 // An invalid batch (a slot outside [0, L), a negative length, a decode
 // request of other than one token, more tokens or segments than the
 // capacities) is not planned: the status goes to info[6] and every segment
@@ -53,32 +54,98 @@ __device__ __forceinline__ int chunk_for(int64_t n, int max_chunk) {
   return wanted < max_chunk ? wanted : max_chunk;
 }
 
-// Exclusive scan of v over the workgroup; returns the prefix and writes the
-// total to *total.  Every thread must call it.
-__device__ int64_t block_exclusive_scan(int64_t v, int64_t* wave_sums, int64_t* total) {
+// Exclusive scans of two values over the workgroup: *pa, *pb get the
+// prefixes and *ta, *tb the totals.  Every thread must call it.
+__device__ void block_exclusive_scan2(int64_t a, int64_t b, int64_t (*wave_sums)[2], int64_t* pa,
+                                      int64_t* pb, int64_t* ta, int64_t* tb) {
+  constexpr int kWaves = kPlanThreads / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int64_t x = v;
+  int64_t x = a, y = b;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int64_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) wave_sums[wave] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t acc = 0;
-    for (int w = 0; w < kPlanThreads / 64; ++w) {
-      const int64_t t = wave_sums[w];
-      wave_sums[w] = acc;
-      acc += t;
+    const int64_t u = __shfl_up(x, d, 64);
+    const int64_t v = __shfl_up(y, d, 64);
+    if (lane >= d) {
+      x += u;
+      y += v;
     }
-    wave_sums[kPlanThreads / 64] = acc;
+  }
+  if (lane == 63) {
+    wave_sums[wave][0] = x;
+    wave_sums[wave][1] = y;
   }
   __syncthreads();
-  const int64_t prefix = wave_sums[wave] + x - v;
-  *total = wave_sums[kPlanThreads / 64];
+  if (wave == 0) {  // exclusive scan of the wave sums in the first wave
+    int64_t sx = lane < kWaves ? wave_sums[lane][0] : 0;
+    int64_t sy = lane < kWaves ? wave_sums[lane][1] : 0;
+    const int64_t ox = sx, oy = sy;
+#pragma unroll
+    for (int d = 1; d < kWaves; d <<= 1) {
+      const int64_t u = __shfl_up(sx, d, 64);
+      const int64_t v = __shfl_up(sy, d, 64);
+      if (lane >= d) {
+        sx += u;
+        sy += v;
+      }
+    }
+    if (lane < kWaves) {
+      wave_sums[lane][0] = sx - ox;
+      wave_sums[lane][1] = sy - oy;
+    }
+    if (lane == kWaves - 1) {
+      wave_sums[kWaves][0] = sx;
+      wave_sums[kWaves][1] = sy;
+    }
+  }
   __syncthreads();
-  return prefix;
+  *pa = wave_sums[wave][0] + x - a;
+  *pb = wave_sums[wave][1] + y - b;
+  *ta = wave_sums[kWaves][0];
+  *tb = wave_sums[kWaves][1];
+  __syncthreads();  // the sums are read before a later call overwrites them
+}
+
+// The work segments of one slot of n tokens: its segments are full chunks
+// and a remainder r = n % chunk (if any); merging consecutive segments
+// greedily within `cap` tokens gives groups of m = cap / chunk full chunks,
+// and the remainder joins the last group when it still fits.
+struct SlotWork {
+  int nf, r, m, full_groups, merged, groups, longest;
+};
+
+__device__ __forceinline__ SlotWork slot_work(int n, int chunk, int cap) {
+  SlotWork w;
+  w.nf = n / chunk;
+  w.r = n - w.nf * chunk;
+  w.m = cap / chunk > 0 ? cap / chunk : 1;
+  w.full_groups = (w.nf + w.m - 1) / w.m;
+  const int last_full = w.nf == 0 ? 0 : (w.nf % w.m == 0 ? w.m : w.nf % w.m);
+  w.merged = w.r > 0 && w.nf > 0 && last_full * chunk + w.r <= cap;
+  w.groups = w.full_groups + (w.r > 0 && !w.merged ? 1 : 0);
+  int lw = (w.nf >= w.m ? w.m : w.nf) * chunk;  // a full group
+  const int tail = last_full * chunk + (w.merged ? w.r : 0);
+  if (tail > lw) lw = tail;
+  if (w.r > 0 && !w.merged && w.r > lw) lw = w.r;
+  w.longest = n == 0 ? 0 : lw;
+  return w;
+}
+
+// Token offset (within its slot) where work segment g of the slot ends.
+__device__ __forceinline__ int slot_work_end(const SlotWork& w, int g, int n, int chunk) {
+  if (g < w.full_groups - 1) return (g + 1) * w.m * chunk;
+  if (g == w.full_groups - 1) return w.merged ? n : w.nf * chunk;
+  return n;  // the remainder on its own
+}
+
+// Largest index a < n with v[a] <= x (v non-decreasing, v[0] <= x).
+__device__ __forceinline__ int last_at_most(const int32_t* v, int n, int x) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (v[mid] <= x) lo = mid;
+    else hi = mid;
+  }
+  return lo;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanParams p) {
@@ -89,7 +156,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
   __shared__ int32_t first_work[kDevicePlanMaxLoras]; // first work segment per slot
   __shared__ int32_t req_ptr[kDevicePlanMaxReqs + 1]; // request token boundaries
   __shared__ int32_t req_pos[kDevicePlanMaxReqs];     // first sorted position per request
-  __shared__ int64_t wave_sums[kPlanThreads / 64 + 1];
+  __shared__ int64_t wave_sums[kPlanThreads / 64 + 1][2];
   __shared__ int32_t status, longest, longest_work;
 
   const int tid = threadIdx.x;
@@ -124,9 +191,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
       if (a < 0 || a >= L) atomicOr(&status, 2);
       else if (len > 0) atomicAdd(&count[a], len);
       req_slots_out[r] = a;
+      req_pos[r] = a;  // the slot, until step 3 replaces it with the position
     }
-    int64_t chunk_total;
-    const int64_t pre = block_exclusive_scan(len > 0 ? len : 0, wave_sums, &chunk_total);
+    int64_t pre, unused, chunk_total, unused_total;
+    block_exclusive_scan2(len > 0 ? len : 0, 0, wave_sums, &pre, &unused, &chunk_total,
+                          &unused_total);
     if (r < bs) {
       const int64_t end = carry + pre + (len > 0 ? len : 0);
       if (end > INT32_MAX) atomicOr(&status, 4);
@@ -152,22 +221,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
   const int cap = chunk > SGG_WORK_SEGMENT_TOKENS ? chunk : SGG_WORK_SEGMENT_TOKENS;
   const int n_slot = tid < L ? count[tid] : 0;
   const int segs = (n_slot + chunk - 1) / chunk;
-  int works = 0;  // work segments: the slot's segments merged greedily within `cap`
-  for (int q = 0; q < segs;) {
-    int tok = 0, q1 = q;
-    while (q1 < segs) {
-      const int len = q1 < segs - 1 ? chunk : n_slot - (segs - 1) * chunk;
-      if (q1 > q && tok + len > cap) break;
-      tok += len;
-      ++q1;
-    }
-    ++works;
-    q = q1;
+  const SlotWork sw = slot_work(n_slot > 0 ? n_slot : 0, chunk, cap);
+  const int works = n_slot > 0 ? sw.groups : 0;
+  if (n_slot > 0) {
+    atomicMax(&longest, n_slot < chunk ? n_slot : chunk);
+    atomicMax(&longest_work, sw.longest);
   }
-  int64_t tot_tok, n_seg, n_work;
-  const int64_t pos = block_exclusive_scan(n_slot, wave_sums, &tot_tok);
-  const int64_t sg = block_exclusive_scan(segs, wave_sums, &n_seg);
-  const int64_t wk = block_exclusive_scan(works, wave_sums, &n_work);
+  // one scan of the token counts, one of the segment and work-segment
+  // counts packed in one word (each total stays below 2^31)
+  int64_t pos, packed, tot_tok, tot_packed;
+  block_exclusive_scan2(n_slot, (static_cast<int64_t>(segs) << 32) | works, wave_sums, &pos,
+                        &packed, &tot_tok, &tot_packed);
+  const int64_t sg = packed >> 32, wk = packed & 0xffffffffll;
+  const int64_t n_seg = tot_packed >> 32, n_work = tot_packed & 0xffffffffll;
   if (tid < L) {
     first_pos[tid] = static_cast<int32_t>(pos);
     first_seg[tid] = static_cast<int32_t>(sg);
@@ -203,76 +269,76 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
   for (int a = tid; a < L; a += kPlanThreads) running[a] = first_pos[a];
   __syncthreads();
   if (tid < 64) {
+    // One wave, 64 requests at a time.  For each slot present among them
+    // (in order of first appearance): its lanes' positions are the slot's
+    // running position plus the lengths of its earlier lanes.
     const int lane = tid;
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
     for (int r0 = 0; r0 < bs; r0 += 64) {
       const int r = r0 + lane;
-      const int a = r < bs ? p.req_slots[r] : -1;
-      const int len = r < bs ? req_ptr[r + 1] - req_ptr[r] : 0;
-      int before = 0, group = 0;
-      bool first = true;
-      for (int j = 0; j < 64; ++j) {
-        const int aj = __shfl(a, j, 64);
-        const int lj = __shfl(len, j, 64);
-        if (aj == a) {
-          group += lj;
-          if (j < lane) {
-            before += lj;
-            first = false;
+      const bool valid = r < bs;
+      const int a = valid ? req_pos[r] : -1;
+      const int len = valid ? req_ptr[r + 1] - req_ptr[r] : 0;
+      const bool unit = __ballot(valid && len != 1) == 0;  // every length is one
+      uint64_t todo = __ballot(valid);
+      while (todo != 0) {
+        const int leader = __builtin_ctzll(todo);
+        const int slot = __builtin_amdgcn_readlane(a, leader);
+        const uint64_t m = __ballot(a == slot);
+        int before, total;
+        if (unit) {
+          before = __popcll(m & below);
+          total = __popcll(m);
+        } else {  // exclusive scan of the members' lengths
+          int v = (a == slot) ? len : 0;
+          const int own = v;
+#pragma unroll
+          for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(v, d, 64);
+            if (lane >= d) v += u;
           }
+          before = v - own;
+          total = __shfl(v, 63, 64);
         }
+        const int base = running[slot];
+        if (a == slot) req_pos[r] = base + before;
+        __builtin_amdgcn_wave_barrier();
+        if (lane == leader) running[slot] = base + total;
+        __builtin_amdgcn_wave_barrier();
+        todo &= ~m;
       }
-      const int base = r < bs ? running[a] : 0;
-      if (r < bs) req_pos[r] = base + before;
-      // every lane has read its slot's total before the first lanes advance it
-      __builtin_amdgcn_wave_barrier();
-      if (r < bs && first) running[a] = base + group;
-      __builtin_amdgcn_wave_barrier();
     }
   }
   __syncthreads();
 
-  // 4. Permutation: sorted position -> token.
-  for (int64_t t0 = 0; t0 < s; t0 += kPlanThreads) {
-    const int t = static_cast<int>(t0) + tid;
-    if (t < s) {
-      int lo = 0, hi = bs;  // request r with req_ptr[r] <= t < req_ptr[r + 1]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (req_ptr[mid] <= t) lo = mid;
-        else hi = mid;
-      }
-      perm[req_pos[lo] + (t - req_ptr[lo])] = t;
+  // 4. Permutation: sorted position -> token; one wave per request, its
+  // lanes writing consecutive positions.
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int r = wave; r < bs; r += kPlanThreads / 64) {
+      const int start = req_ptr[r];
+      const int len = req_ptr[r + 1] - start;
+      const int pos = req_pos[r];
+      for (int k = lane; k < len; k += 64) perm[pos + k] = start + k;
     }
   }
 
-  // 5. Segments and work segments of each slot, padding, tables.
-  for (int a = tid; a < L; a += kPlanThreads) {
+  // 5. Segments and work segments (one per thread, each finding its slot by
+  // binary search over the slots' first indices), padding, tables.
+  for (int i = tid; i < n_seg; i += kPlanThreads) {
+    const int a = last_at_most(first_seg, L, i);
+    const int q = i - first_seg[a];
     const int n = count[a];
-    if (n == 0) continue;
-    const int segs = (n + chunk - 1) / chunk;
-    const int pos0 = first_pos[a];
-    int i = first_seg[a];
-    for (int q = 0; q < segs; ++q, ++i) {
-      const int end = q < segs - 1 ? (q + 1) * chunk : n;
-      seg_slots[i] = a;
-      seg_indptr[i + 1] = pos0 + end;
-    }
-    atomicMax(&longest, n < chunk ? n : chunk);
-    int w = first_work[a];
-    for (int q = 0; q < segs; ++w) {
-      int tok = 0;
-      int q1 = q;
-      while (q1 < segs) {
-        const int len = q1 < segs - 1 ? chunk : n - (segs - 1) * chunk;
-        if (q1 > q && tok + len > cap) break;
-        tok += len;
-        ++q1;
-      }
-      work_slots[w] = a;
-      work_indptr[w + 1] = pos0 + (q1 < segs ? q1 * chunk : n);
-      atomicMax(&longest_work, tok);
-      q = q1;
-    }
+    const int end = (q + 1) * chunk < n ? (q + 1) * chunk : n;
+    seg_slots[i] = a;
+    seg_indptr[i + 1] = first_pos[a] + end;
+  }
+  for (int w = tid; w < n_work; w += kPlanThreads) {
+    const int a = last_at_most(first_work, L, w);
+    const int n = count[a];
+    const SlotWork sa = slot_work(n, chunk, cap);
+    work_slots[w] = a;
+    work_indptr[w + 1] = first_pos[a] + slot_work_end(sa, w - first_work[a], n, chunk);
   }
   for (int64_t i = n_seg + tid; i < p.seg_capacity; i += kPlanThreads) {
     seg_slots[i] = 0;
