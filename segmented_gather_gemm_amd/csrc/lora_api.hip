@@ -116,6 +116,13 @@ sgg::ExpandTiling choose_expand_tiling(const int32_t* offs, int c, int num_segme
   return t;
 }
 
+// The GEMM shrink tiles address x and each slot's A block through buffer
+// resources with 32-bit byte offsets.
+bool gemm_addressable(int64_t s, int64_t ldx, int64_t K, int64_t CR) {
+  const int64_t lim = int64_t{1} << 32;
+  return ((s - 1) * ldx + K) * 2 < lim && CR * K * 2 < lim;
+}
+
 int launch_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(SGG_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
   return SGG_OK;
@@ -159,7 +166,8 @@ int do_shrink(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh, i
               const int32_t* seg_slots, int32_t num_segments, const int32_t* permutation,
               const int32_t* lora_ranks, int32_t chunk_size, int32_t* counters,
               void* partial, int64_t partial_avail, hipStream_t stream) {
-  const sgg::ShrinkTiling t = sgg::choose_shrink_tiling(s, K, c * R, num_segments, chunk_size);
+  const sgg::ShrinkTiling t = sgg::choose_shrink_tiling(
+      s, K, c * R, num_segments, chunk_size, gemm_addressable(s, ldx, K, static_cast<int64_t>(c) * R));
   if (t.ksplit > 1) {
     SGG_CHECK(counters != nullptr && partial != nullptr && partial_avail >= t.partial_bytes,
               SGG_ERR_CAPACITY, "shrink workspace too small: %" PRId64
@@ -327,8 +335,8 @@ extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B
   void* h = ws + sgg::kCounterBytes;
   float* part = reinterpret_cast<float*>(ws + sgg::kCounterBytes + hbytes);
   const int64_t CR = static_cast<int64_t>(num_slices) * R;
-  const sgg::ShrinkTiling ts = sgg::choose_shrink_tiling(s, in_dim, num_slices * R,
-                                                         num_segments, chunk_size);
+  const sgg::ShrinkTiling ts = sgg::choose_shrink_tiling(
+      s, in_dim, num_slices * R, num_segments, chunk_size, gemm_addressable(s, ldx, in_dim, CR));
   SGG_CHECK(ts.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "shrink grid too large");
   if (slice_offsets[num_slices] == 0) return sgg::ok();  // no output columns: nothing changes
   const bool split = ts.ksplit > 1;

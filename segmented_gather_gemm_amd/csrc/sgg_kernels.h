@@ -84,7 +84,10 @@ struct ShrinkTiling {
   int64_t partial_bytes;     // f32 partial tiles (0 unless ksplit > 1)
   int64_t grid;
 };
-ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk);
+// gemm_ok: the GEMM tiles may be chosen (their buffer loads address x and
+// each slot's A block with 32-bit byte offsets).
+ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk,
+                                  bool gemm_ok = true);
 
 struct ExpandTiling {
   int pairs, ks;     // 32-column fragment pairs per wave, 32-deep rank steps

@@ -79,7 +79,8 @@ hipError_t launch_m(const ShrinkParams& p, int nf, int64_t grid, hipStream_t str
 // across workgroups, into at most 4 ranges (each extra range costs a partial
 // tile round trip).  Measured on decode shapes: small tiles with 4 K ranges
 // beat both one big tile and 16-32 K ranges.
-ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk) {
+ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk,
+                                  bool gemm_ok) {
   ShrinkTiling t{};
   static const int kNf[] = {1, 2, 3, 4, 6, 8};
   static const int kMf[] = {1, 2, 4, 8};
@@ -173,6 +174,7 @@ ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments
   // Too few workgroups for whole-K tiles (each workgroup has one K step of
   // loads in flight): the split-K kernel's finer tiles keep more CUs busy.
   if (gemm_units(gm, gn) < 256) return t;
+  if (!gemm_ok) return t;  // x or an A block beyond 32-bit offsets: one K range here
   t.gemm = 1;
   t.bm = gm;
   t.bn = gn;

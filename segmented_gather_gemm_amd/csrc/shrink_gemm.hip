@@ -17,6 +17,22 @@
 // slot's rank (or beyond c*R) only feeds its own output column, which is
 // stored as zero.  Only a ragged K tail (K % 64 != 0) zeroes the chunks past
 // K, in its last step.
+//
+// x and the slot's A block are read with buffer loads: a per-lane 32-bit row
+// offset fixed for the workgroup plus the step's K offset in a scalar
+// register, so the K loop spends no vector registers or instructions on
+// addresses, and a read past the end of the buffer returns zero instead of
+// faulting.  The host takes this kernel only when x and every slot's A block
+// fit in 4 GiB of offsets.
+//
+// With two or more register sets, every step requests the loads of step
+// t + DEPTH unconditionally (the last step again once past the end) and the
+// ragged-K zeroing happens while staging: a load issued under a branch makes
+// the compiler's wait before staging step t + 1 count conservatively and
+// drain the newer sets too (s_waitcnt vmcnt(0)), which serialises the
+// pipeline.  Measured on the skewed o_proj batch (64 x 32 tiles): 42 -> 35
+// us.  With one register set the branchy form is faster (prefill 128 x 128
+// tiles: 97 us against 122 us).
 #include "sgg_device.h"
 #include "sgg_kernels.h"
 
@@ -26,6 +42,16 @@ namespace {
 
 // Byte offset of 16-byte chunk c (0..7) of row r in a swizzled 128-byte-row tile.
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
+
+// Fourth word of a raw buffer resource on gfx9 (32-bit data format).
+constexpr int kRsrcWord3 = 0x00020000;
+
+// 16 bytes at byte offset voff + soff of a buffer (soff uniform).
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                               int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       rsrc, static_cast<int>(voff), soff, 0));
+}
 
 template <int BM, int BN, int WM, int DEPTH>
 __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
@@ -63,12 +89,18 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
   const int lcol = tid & 7;
   // A rows of this thread's loads (tile rows BM + lrow + 32*j): fixed for the
   // workgroup (in-bounds stand-in row 0 beyond c*R).
-  const uint16_t* arow[APER];
+  // raw buffer resources (loads at or past the end of the range return zero)
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.A + static_cast<int64_t>(slot_ok ? slot : 0) * p.CR * p.K),
+      static_cast<short>(0), static_cast<int>(static_cast<uint32_t>(p.CR * p.K * 2)), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.x), static_cast<short>(0),
+      static_cast<int>(static_cast<uint32_t>(((p.s - 1) * p.ldx + p.K) * 2)), kRsrcWord3);
+  uint32_t aoff[APER];
 #pragma unroll
   for (int j = 0; j < APER; ++j) {
     const int n = nb * BN + lrow + 32 * j;
-    arow[j] = p.A + (static_cast<int64_t>(slot_ok ? slot : 0) * p.CR + (n < p.CR ? n : 0)) * p.K +
-              8 * lcol;
+    aoff[j] = static_cast<uint32_t>((n < p.CR ? n : 0) * p.K * 2 + 16 * lcol);
   }
   const int nk = static_cast<int>((p.K + 63) / 64);
   const bool ktail = (p.K & 63) != 0;
@@ -96,12 +128,13 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
 
     // x rows of this thread's loads (tile rows lrow + 32*j; a stand-in row
     // for tokens outside the segment)
-    const uint16_t* xrow[XPER];
+    uint32_t xoff[XPER];
 #pragma unroll
     for (int j = 0; j < XPER; ++j) {
       const int r = lrow + 32 * j;
       const int pr = r < mcount ? p.perm[m0 + r] : p.perm[m0];
-      xrow[j] = p.x + static_cast<int64_t>((pr >= 0 && pr < p.s) ? pr : 0) * p.ldx + 8 * lcol;
+      xoff[j] = static_cast<uint32_t>(static_cast<int64_t>((pr >= 0 && pr < p.s) ? pr : 0) *
+                                      p.ldx * 2 + 16 * lcol);
     }
 
     // DEPTH register sets of prefetch: step t + DEPTH is requested while
@@ -109,28 +142,36 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
     // DEPTH - 1 steps earlier, waits in its register set to be staged.  The
     // loop is unrolled by DEPTH so that each register set is a fixed one.
     uint4 xl[DEPTH][XPER], al[DEPTH][APER];
+    // chunk lcol of step kt lies past a ragged end of K: it contributes zero
+    auto past_k = [&](int kt) {
+      return ktail && kt == nk - 1 && static_cast<int64_t>(kt) * 64 + 8 * lcol >= p.K;
+    };
     auto issue = [&](int kt, uint4 (&xs)[XPER], uint4 (&as)[APER]) {
-      const int64_t k = static_cast<int64_t>(kt) * 64 + 8 * lcol;
-      const int64_t koff = (k <= p.K - 8 ? k : p.K - 8) - 8 * lcol;
+      const int soff = kt * 128;
 #pragma unroll
-      for (int j = 0; j < XPER; ++j) xs[j] = load16(xrow[j] + koff);
+      for (int j = 0; j < XPER; ++j) xs[j] = buffer_load16(xrsrc, xoff[j], soff);
 #pragma unroll
-      for (int j = 0; j < APER; ++j) as[j] = load16(arow[j] + koff);
-      if (ktail && kt == nk - 1 && k >= p.K) {  // chunks past K contribute zero
+      for (int j = 0; j < APER; ++j) as[j] = buffer_load16(arsrc, aoff[j], soff);
+      if constexpr (DEPTH == 1) {
+        if (past_k(kt)) {
 #pragma unroll
-        for (int j = 0; j < XPER; ++j) xs[j] = make_uint4(0, 0, 0, 0);
+          for (int j = 0; j < XPER; ++j) xs[j] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < APER; ++j) as[j] = make_uint4(0, 0, 0, 0);
+          for (int j = 0; j < APER; ++j) as[j] = make_uint4(0, 0, 0, 0);
+        }
       }
     };
-    auto stash = [&](int buf, const uint4 (&xs)[XPER], const uint4 (&as)[APER]) {
+    auto stash = [&](int buf, int kt, const uint4 (&xs)[XPER], const uint4 (&as)[APER]) {
       char* st = smem + buf * STAGE;
+      const bool kill = DEPTH > 1 && past_k(kt);
 #pragma unroll
       for (int j = 0; j < XPER; ++j)
-        *reinterpret_cast<uint4*>(st + swz(lrow + 32 * j, lcol)) = xs[j];
+        *reinterpret_cast<uint4*>(st + swz(lrow + 32 * j, lcol)) =
+            kill ? make_uint4(0, 0, 0, 0) : xs[j];
 #pragma unroll
       for (int j = 0; j < APER; ++j)
-        *reinterpret_cast<uint4*>(st + swz(BM + lrow + 32 * j, lcol)) = as[j];
+        *reinterpret_cast<uint4*>(st + swz(BM + lrow + 32 * j, lcol)) =
+            kill ? make_uint4(0, 0, 0, 0) : as[j];
     };
     auto mma = [&](int buf, f32x4 (&acc)[FN][FM]) {
       const char* st = smem + buf * STAGE;
@@ -159,18 +200,27 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
 
     __syncthreads();  // the previous row block's tiles are no longer read
 #pragma unroll
-    for (int u = 0; u < DEPTH; ++u)
-      if (u < nk) issue(u, xl[u], al[u]);
-    stash(0, xl[0], al[0]);
+    for (int u = 0; u < DEPTH; ++u) {
+      if constexpr (DEPTH == 1) {
+        if (u < nk) issue(u, xl[u], al[u]);
+      } else {
+        issue(u < nk ? u : nk - 1, xl[u], al[u]);
+      }
+    }
+    stash(0, 0, xl[0], al[0]);
     __syncthreads();
     for (int kt = 0; kt < nk; kt += DEPTH) {
 #pragma unroll
       for (int u = 0; u < DEPTH; ++u) {
         const int k = kt + u;
         if (k >= nk) break;
-        if (k + DEPTH < nk) issue(k + DEPTH, xl[u], al[u]);
+        if constexpr (DEPTH == 1) {
+          if (k + 1 < nk) issue(k + 1, xl[0], al[0]);
+        } else {
+          issue(k + DEPTH < nk ? k + DEPTH : nk - 1, xl[u], al[u]);
+        }
         mma(k & 1, acc);
-        if (k + 1 < nk) stash((k + 1) & 1, xl[(u + 1) % DEPTH], al[(u + 1) % DEPTH]);
+        if (k + 1 < nk) stash((k + 1) & 1, k + 1, xl[(u + 1) % DEPTH], al[(u + 1) % DEPTH]);
         __syncthreads();
       }
     }

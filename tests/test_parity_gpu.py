@@ -170,6 +170,9 @@ def test_decode_full():
     (63, 64, 4, 2, 32, 4096),
     (64, 96, 16, 1, 64, 4096),
     (65, 24, 2, 4, 16, 1024),
+    (66, 64, 4, 1, 16, 14336),
+    (67, 48, 3, 2, 32, 10240),
+    (68, 20, 2, 3, 16, 8192),
 ])
 def test_stacked_call_matches_separate_calls(case):
     """lora_qkv on small batches (split K: the expand sums the shrink's
