@@ -129,16 +129,18 @@ ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments
     t.partial_bytes = round_up(static_cast<int64_t>(t.ksplit) * s * CR * 4, 256);
     return t;
   }
-  // No K split needed.  Batches of short segments that are small (at most
-  // 6144 tokens) or have a long K (8192 or more) keep this kernel, with one K
-  // range and tiles of 32 tokens (64 above 6144 tokens) by half of c*R: its
-  // four waves stream interleaved K chunks with no barrier between them,
-  // which beat the shared GEMM tiles by 8-25 % on the full-layer shapes
-  // (4288 tokens, 93 segments: gate_up 36.9 -> 29.2 us, down_proj 63 -> 55
-  // us) and on the skewed down_proj (K = 14336: 181 -> 140 us), while the
-  // GEMM tiles stay ahead for the skewed o_proj (8192 tokens, K = 4096).
+  // No K split needed.  Batches of short segments whose stacked rank rows
+  // are few (c*R <= 32) and that are small (at most 6144 tokens) or have a
+  // long K (8192 or more) keep this kernel, with one K range and tiles of 32
+  // tokens (64 above 6144 tokens) by half of c*R: its four waves stream
+  // interleaved K chunks with no barrier between them.  Measured against the
+  // 64 x 32 GEMM tiles (buffer loads, two register sets) on the full-layer
+  // batch (4288 tokens, 93 segments, 64 adapters, r = 32): o_proj 22.7 vs
+  // 25.6 us, down_proj 57.7 vs 65.2 us here; with c*R = 64 or more the GEMM
+  // tiles win (qkv 39.1 -> 36.0 us, gate_up 33.2 -> 29.1 us, skewed
+  // down_proj with r = 64: 149 -> 134 us).
   const bool long_segments = num_segments > 0 && s >= 96 * static_cast<int64_t>(num_segments);
-  if (!long_segments && (s <= 6144 || K >= 8192)) {
+  if (!long_segments && CR <= 32 && (s <= 6144 || K >= 8192)) {
     t.mf = s > 6144 ? 4 : 2;
     t.nf = 1;
     for (int v : kNf)
