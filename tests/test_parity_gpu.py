@@ -335,6 +335,25 @@ def test_large_batch_ragged_k():
     assert_close(y, want_y, "ragged-K GEMM y")
 
 
+def test_long_segment_gemm_ragged_k():
+    """Long segments (mean work segment >= 96 tokens, chunk 128) and c*R =
+    128 over about 33k tokens take the 128 x 128 GEMM shrink tiles with one
+    register set, whose ragged-K tail (K = 1064: 17 K steps, the last partly
+    past K) is zeroed at the load; NaN rank padding and mixed ranks; every
+    element against the oracle."""
+    rng = np.random.default_rng(93)
+    lens = rng.integers(900, 1200, size=32).tolist()
+    slots = rng.integers(0, 8, size=32).tolist()
+    ranks = [64, 48, 64, 32, 64, 64, 16, 64]
+    b, proj, t = _small_case(93, lens, slots, 8, ranks, rng.uniform(0.5, 2, 8).tolist(), 1064,
+                             [0, 256, 512], 64, nan_pad=True)
+    assert b.num_tokens > 32768
+    h, y = _gpu_forward(b, proj, t)
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, "long-segment ragged-K GEMM h")
+    assert_close(y, want_y, "long-segment ragged-K GEMM y")
+
+
 def test_long_k_small_grid():
     """Long K (129 K steps, the last partly past K) on a small grid, NaN rank
     padding, a rank-0 slot: the standalone shrink and the stacked call
