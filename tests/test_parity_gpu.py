@@ -354,6 +354,47 @@ def test_long_segment_gemm_ragged_k():
     assert_close(y, want_y, "long-segment ragged-K GEMM y")
 
 
+@pytest.mark.parametrize("case", ["gemm", "split", "one_range"])
+def test_strided_x(case):
+    """x as a column view of a wider tensor (row stride K + 64): the buffer
+    loads of the GEMM tiles (64 x 32 here), the decode split-K shrink and the
+    one-range split-K kernel (short segments, c*R = 32) read the right rows;
+    stacked and separate calls against the oracle on every element."""
+    sgg = _sgg()
+    rng = np.random.default_rng({"gemm": 97, "split": 98, "one_range": 99}[case])
+    if case == "gemm":
+        lens = rng.integers(40, 300, size=48).tolist()
+        slots = rng.integers(0, 40, size=48).tolist()
+        L, R, K, offs = 40, 32, 1024, [0, 768, 1536]
+    elif case == "split":
+        lens = [1] * 256
+        slots = rng.integers(0, 8, size=256).tolist()
+        L, R, K, offs = 8, 16, 2048, [0, 512, 768, 1024]
+    else:
+        lens = [1] * 192 + [512] * 4
+        slots = rng.integers(0, 32, size=196).tolist()
+        L, R, K, offs = 32, 32, 2048, [0, 1024]
+    b, proj, t = _small_case(97, lens, slots, L, [R] * L, rng.uniform(0.5, 2, L).tolist(), K,
+                             offs, R)
+    be = backend(b)
+    info = plan_on(be, b)
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    wide = torch.full((x.shape[0], K + 64), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wide[:, :K] = x
+    xs = wide[:, :K]
+    assert xs.stride(0) == K + 64
+    c = len(offs) - 1
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    h = sgg.lora_shrink(xs, A, info, c, workspace=ws)
+    y_sep = sgg.lora_expand(h, Bw, info, offs, max(np.diff(offs)), base.clone())
+    y = sgg.lora_qkv(xs, A, Bw, info, offs, max(np.diff(offs)), base.clone(), workspace=ws)
+    torch.cuda.synchronize()
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, f"strided x ({case}) h")
+    assert_close(y_sep, want_y, f"strided x ({case}) y")
+    assert torch.equal(y, y_sep)
+
+
 def test_long_k_small_grid():
     """Long K (129 K steps, the last partly past K) on a small grid, NaN rank
     padding, a rank-0 slot: the standalone shrink and the stacked call
