@@ -90,7 +90,10 @@ def _cpu_i32_ptr(t):
 
 
 def _need_bf16(name, t, dims):
-    if t.dtype is not torch.bfloat16 or not t.is_cuda or t.dim() != dims or t.stride(-1) != 1:
+    """A bf16 device tensor of `dims` dimensions with unit stride in its last
+    one; returns its strides (one query: each stride(i) call costs as much)."""
+    st = t.stride()
+    if t.dtype is not torch.bfloat16 or not t.is_cuda or len(st) != dims or st[-1] != 1:
         if t.dtype != torch.bfloat16:
             raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
         if not t.is_cuda:
@@ -98,6 +101,7 @@ def _need_bf16(name, t, dims):
         if t.dim() != dims:
             raise ValueError(f"{name} must have {dims} dimensions, got shape {tuple(t.shape)}")
         raise ValueError(f"{name} must have unit stride in its last dimension")
+    return st
 
 
 def _need_bf16_dense(name, t, dims):
@@ -109,7 +113,8 @@ def _need_bf16_dense(name, t, dims):
 
 def _need_rows_cols(name, t, rows, cols):
     """`t` holds at least `rows` x `cols` elements (the kernels write them)."""
-    if t.size(0) != rows or t.size(1) < cols:
+    shape = t.shape
+    if shape[0] != rows or shape[1] < cols:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, needs ({rows}, >= {cols})")
 
 
@@ -275,7 +280,7 @@ def _offsets(slice_offsets):
 
 def lora_shrink(x, weights, batch_info: LoRABatchInfo, num_slices=1, out=None, workspace=None):
     """LoRA-A: x (s, K), weights (L, c*R, K) -> h (s, c*R), original token order."""
-    _need_bf16("x", x, 2)
+    xst = _need_bf16("x", x, 2)
     _need_bf16_dense("weights", weights, 3)
     s, K = x.shape
     L, CR, K2 = weights.shape
@@ -288,7 +293,7 @@ def lora_shrink(x, weights, batch_info: LoRABatchInfo, num_slices=1, out=None, w
     R = CR // num_slices
     if out is None:
         out = torch.empty((s, CR), dtype=torch.bfloat16, device=x.device)
-    _need_bf16("out", out, 2)
+    ost = _need_bf16("out", out, 2)
     _need_rows_cols("out", out, s, CR)
     ind, sl, nseg, hint, perm = batch_info.kernel_segments()
     ws = workspace
@@ -296,7 +301,7 @@ def lora_shrink(x, weights, batch_info: LoRABatchInfo, num_slices=1, out=None, w
         need = calls().lora_shrink_workspace_bytes(s, K, num_slices, R, nseg, hint)
         ws = default_workspace(x.device, need) if need else None
     check(calls().lora_shrink(
-        _vp(x), x.stride(0), _vp(weights), _vp(out), out.stride(0), s, K, L, num_slices, R,
+        _vp(x), xst[0], _vp(weights), _vp(out), ost[0], s, K, L, num_slices, R,
         _vp(ind), _vp(sl), nseg, _vp(perm), _vp(batch_info.lora_ranks), hint,
         _vp(ws), ws.numel() if ws is not None else 0, _stream(x)))
     return out
@@ -308,7 +313,7 @@ def lora_expand(h, weights, batch_info: LoRABatchInfo, slice_offsets, max_slice_
 
     ``base_output=None`` gives a zero-filled output (the update alone).
     """
-    _need_bf16("h", h, 2)
+    hst = _need_bf16("h", h, 2)
     _need_bf16_dense("weights", weights, 3)
     offs, p_offs = _offsets(slice_offsets)
     c = len(offs) - 1
@@ -319,11 +324,11 @@ def lora_expand(h, weights, batch_info: LoRABatchInfo, slice_offsets, max_slice_
     _need_rows_cols("h", h, s, c * R)
     if base_output is None:
         base_output = torch.zeros((s, int(offs[-1])), dtype=torch.bfloat16, device=h.device)
-    _need_bf16("base_output", base_output, 2)
+    bst = _need_bf16("base_output", base_output, 2)
     _need_rows_cols("base_output", base_output, s, int(offs[-1]))
     ind, sl, nseg, hint, perm = batch_info.kernel_segments()
     check(calls().lora_expand(
-        _vp(h), h.stride(0), _vp(weights), N, _vp(base_output), base_output.stride(0), s, L, R,
+        _vp(h), hst[0], _vp(weights), N, _vp(base_output), bst[0], s, L, R,
         p_offs, c, int(max_slice_size), _vp(ind), _vp(sl), nseg, _vp(perm),
         _vp(batch_info.lora_ranks), _vp(batch_info.scalings), hint, _stream(h)))
     return base_output
@@ -332,7 +337,7 @@ def lora_expand(h, weights, batch_info: LoRABatchInfo, slice_offsets, max_slice_
 def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
              base_output=None, workspace=None):
     """Stacked shrink + expand with one plan (qkv: 3 slices, gate_up: 2)."""
-    _need_bf16("x", x, 2)
+    xst = _need_bf16("x", x, 2)
     _need_bf16_dense("A", A, 3)
     _need_bf16_dense("B", B, 3)
     offs, p_offs = _offsets(slice_offsets)
@@ -346,7 +351,7 @@ def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
         raise ValueError(f"x has {s} rows, the plan has {batch_info.num_tokens} tokens")
     if base_output is None:
         base_output = torch.zeros((s, int(offs[-1])), dtype=torch.bfloat16, device=x.device)
-    _need_bf16("base_output", base_output, 2)
+    bst = _need_bf16("base_output", base_output, 2)
     _need_rows_cols("base_output", base_output, s, int(offs[-1]))
     ind, sl, nseg, hint, perm = batch_info.kernel_segments()
     ws = workspace
@@ -354,8 +359,8 @@ def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
         need = calls().lora_qkv_workspace_bytes(s, K, c, R, nseg, hint)
         ws = default_workspace(x.device, max(need, 1))
     check(calls().lora_qkv(
-        x.data_ptr(), x.stride(0), A.data_ptr(), B.data_ptr(), N, base_output.data_ptr(),
-        base_output.stride(0), s, K, L, R, p_offs, c, int(max_slice_size), ind.data_ptr(),
+        x.data_ptr(), xst[0], A.data_ptr(), B.data_ptr(), N, base_output.data_ptr(),
+        bst[0], s, K, L, R, p_offs, c, int(max_slice_size), ind.data_ptr(),
         sl.data_ptr(), nseg, perm.data_ptr(), batch_info.lora_ranks.data_ptr(),
         batch_info.scalings.data_ptr(), hint, ws.data_ptr(), ws.numel(), _stream(x)))
     return base_output
@@ -373,12 +378,12 @@ def lora_a_embedding(input_ids, weights, batch_info: LoRABatchInfo, vocab_size,
         raise ValueError(f"{s} ids, the plan has {batch_info.num_tokens} tokens")
     if out is None:
         out = torch.empty((s, R), dtype=torch.bfloat16, device=weights.device)
-    _need_bf16("out", out, 2)
+    ost = _need_bf16("out", out, 2)
     _need_rows_cols("out", out, s, R)
     # the plan's own segments: the gather parallelises over segments, so the
     # finer partition is the faster one here
     check(calls().lora_a_embedding(
-        input_ids.contiguous().data_ptr(), weights.data_ptr(), V, out.data_ptr(), out.stride(0),
+        input_ids.contiguous().data_ptr(), weights.data_ptr(), V, out.data_ptr(), ost[0],
         s, L, R, int(vocab_size), batch_info.seg_indptr.data_ptr(),
         batch_info.weight_indices.data_ptr(), batch_info.num_segments,
         batch_info.permutation.data_ptr(), batch_info.lora_ranks.data_ptr(),
