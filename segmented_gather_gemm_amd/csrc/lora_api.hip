@@ -117,9 +117,11 @@ sgg::ExpandTiling choose_expand_tiling(const int32_t* offs, int c, int num_segme
 }
 
 // The GEMM shrink tiles address x and each slot's A block through buffer
-// resources with 32-bit byte offsets.
+// resources with 32-bit byte offsets; the last K step of a ragged K reads up
+// to 127 bytes past a row, so the ranges keep a margin below 2^32 (the
+// hardware adds the offsets in 32 bits).
 bool gemm_addressable(int64_t s, int64_t ldx, int64_t K, int64_t CR) {
-  const int64_t lim = int64_t{1} << 32;
+  const int64_t lim = (int64_t{1} << 32) - 256;
   return ((s - 1) * ldx + K) * 2 < lim && CR * K * 2 < lim;
 }
 
