@@ -394,8 +394,14 @@ extern "C" int lora_a_embedding(const int64_t* input_ids, const void* A_emb, int
   p.L = num_loras;
   p.R = R;
   p.num_segments = num_segments;
+  // Parts per segment: about 64 (token, j) pairs per workgroup.  Every pair
+  // is its own cache line (A_emb columns are V apart) and one CU keeps only
+  // so many line requests in flight, so the gather is spread over many CUs.
+  // Measured on the decode batch (256 tokens, 8 segments, R = 16): 4.4 us
+  // with about 1024 pairs per workgroup, 3.0 us with 64 or 128; the
+  // full-layer batch (4288 tokens) 9.1 -> 8.9 us.
   const int64_t avg = (s + num_segments - 1) / num_segments;
-  int64_t parts = (avg * R + 1023) / 1024;
+  int64_t parts = (avg * R + 63) / 64;
   p.parts = static_cast<int32_t>(parts < 1 ? 1 : (parts > 64 ? 64 : parts));
   rc = launch_status(sgg::launch_embedding(p, static_cast<hipStream_t>(stream)), "embedding");
   return rc ? rc : sgg::ok();
