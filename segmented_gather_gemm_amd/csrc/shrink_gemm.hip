@@ -14,9 +14,11 @@
 // No operand is masked inside the K loop: a token row outside the segment
 // (or with an invalid permutation entry) reads an in-bounds stand-in row and
 // only feeds its own output row, which is never stored; an A row beyond the
-// slot's rank (or beyond c*R) only feeds its own output column, which is
-// stored as zero.  Only a ragged K tail (K % 64 != 0) zeroes the chunks past
-// K, in its last step.
+// slot's rank (or beyond c*R) reads the slot's row 0 instead of its padding
+// and only feeds its own output column, which is stored as zero.  A tile
+// whose rank rows all lie past the slot's rank writes zeros and skips the K
+// loop.  Only a ragged K tail (K % 64 != 0) zeroes the chunks past K, in its
+// last step.
 //
 // x and the slot's A block are read with buffer loads: a per-lane 32-bit row
 // offset fixed for the workgroup plus the step's K offset in a scalar
@@ -96,11 +98,23 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.x), static_cast<short>(0),
       static_cast<int>(static_cast<uint32_t>(((p.s - 1) * p.ldx + p.K) * 2)), kRsrcWord3);
+  // A rows past c*R or past the slot's rank (padding, possibly NaN) read row
+  // 0 of the slot instead, a live row that stays in L1: their products only
+  // reach output rows stored as zero, and the L1 fill is spent on live rows.
   uint32_t aoff[APER];
 #pragma unroll
   for (int j = 0; j < APER; ++j) {
     const int n = nb * BN + lrow + 32 * j;
-    aoff[j] = static_cast<uint32_t>((n < p.CR ? n : 0) * p.K * 2 + 16 * lcol);
+    const bool live = n < p.CR && (n % p.R) < rho;
+    aoff[j] = static_cast<uint32_t>((live ? n : 0) * p.K * 2 + 16 * lcol);
+  }
+  // Whether any rank row of this tile lies within the slot's rank (uniform):
+  // a tile of padding rows only writes zeros and reads nothing.
+  bool tile_live = false;
+  {
+    const int n0 = nb * BN, n1 = min(n0 + BN, p.CR);
+    for (int k = n0 / p.R; k * p.R < n1 && !tile_live; ++k)
+      tile_live = max(n0, k * p.R) - k * p.R < rho;
   }
   const int nk = static_cast<int>((p.K + 63) / 64);
   const bool ktail = (p.K & 63) != 0;
@@ -115,7 +129,7 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
     const int m0 = lo + mb * BM;
     const int mcount = hi - m0 < BM ? hi - m0 : BM;
 
-    if (rho == 0) {  // base model slot: zero rows of h
+    if (rho == 0 || !tile_live) {  // base model slot or padding rows: zero rows of h
       for (int q = tid; q < mcount * (BN / 4); q += 256) {
         const int mm = q / (BN / 4);
         const int n = nb * BN + 4 * (q % (BN / 4));

@@ -68,7 +68,17 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int seg, int 
   int rho = (slot >= 0 && slot < p.L) ? p.ranks[slot] : 0;
   rho = rho < 0 ? 0 : (rho > p.R ? p.R : rho);
   const int a = rho > 0 ? slot : 0;
-  if (rho == 0 && split != 0) return;  // split 0 alone writes the zero rows
+  // A tile whose rank rows all lie past the slot's rank (padding) is handled
+  // like a rank-0 slot: nothing is read, split 0 alone writes the zero rows
+  // (the expand masks h columns past the rank, so no partials are needed).
+  bool tile_live = false;
+  {
+    const int n0 = nb * NB, n1 = min(n0 + NB, p.CR);
+    for (int k = n0 / p.R; k * p.R < n1 && !tile_live; ++k)
+      tile_live = max(n0, k * p.R) - k * p.R < rho;
+  }
+  const bool dead = rho == 0 || !tile_live;
+  if (dead && split != 0) return;  // split 0 alone writes the zero rows
 
   const int64_t kb = static_cast<int64_t>(split) * p.kps;
   const int64_t ke = kb + p.kps < p.K ? kb + p.kps : p.K;
@@ -128,7 +138,7 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int seg, int 
 #pragma unroll
     for (int i = 0; i < NFR; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (rho > 0 && nchunks > 0) {
+    if (!dead && nchunks > 0) {
       // One register set of loads in flight: the CH chunks of stage t+1 are
       // requested as soon as stage t has been copied into the LDS tiles, and
       // arrive while stage t is multiplied.
@@ -186,7 +196,7 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int seg, int 
 
     // Sum the four waves' tiles through LDS, a few fragments per round, and
     // emit 4 consecutive outputs of one token per (fragment, lane) item.
-    const bool direct = p.ksplit == 1 || rho == 0;
+    const bool direct = p.ksplit == 1 || dead;
 #pragma unroll
     for (int rd = 0; rd < ROUNDS; ++rd) {
       __syncthreads();

@@ -395,6 +395,42 @@ def test_strided_x(case):
     assert torch.equal(y, y_sep)
 
 
+@pytest.mark.parametrize("case", ["split", "one_range"])
+def test_tiles_past_the_rank(case):
+    """Ranks well below the padded R (NaN padding): split-K shrink tiles
+    whose rank rows all lie past the slot's rank read nothing and write zero
+    rows, on the K-split path (standalone last-arriver sum and the stacked
+    call's partials) and on the one-range path; every element against the
+    oracle, stacked and separate calls bit for bit."""
+    sgg = _sgg()
+    rng = np.random.default_rng({"split": 101, "one_range": 102}[case])
+    if case == "split":
+        lens = [1] * 96
+        slots = rng.integers(0, 6, size=96).tolist()
+        L, R, ranks, K, offs = 6, 64, [8, 16, 0, 64, 12, 32], 2048, [0, 512, 1024]
+    else:
+        lens = [1] * 2000 + [300] * 2
+        slots = rng.integers(0, 40, size=2002).tolist()
+        L, R, K, offs = 40, 32, 1024, [0, 768]
+        ranks = [(8, 16, 0, 32, 12)[a % 5] for a in range(L)]
+    b, proj, t = _small_case(101, lens, slots, L, ranks, rng.uniform(0.5, 2, L).tolist(), K,
+                             offs, R, nan_pad=True)
+    be = backend(b)
+    info = plan_on(be, b)
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    c = len(offs) - 1
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    h = sgg.lora_shrink(x, A, info, c, workspace=ws)
+    y_sep = sgg.lora_expand(h, Bw, info, offs, max(np.diff(offs)), base.clone())
+    y = sgg.lora_qkv(x, A, Bw, info, offs, max(np.diff(offs)), base.clone(), workspace=ws)
+    torch.cuda.synchronize()
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, f"past-rank tiles ({case}) h")
+    assert_close(y_sep, want_y, f"past-rank tiles ({case}) y")
+    assert torch.equal(y, y_sep)
+    assert not ws[:32768].any()
+
+
 def test_long_k_small_grid():
     """Long K (129 K steps, the last partly past K) on a small grid, NaN rank
     padding, a rank-0 slot: the standalone shrink and the stacked call
