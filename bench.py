@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_prefill_kernels_hbm_traffic.txt")
 
 
 def parse():
