@@ -89,18 +89,19 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
   // Loading role: row (tid/8 + 32*j) of the step's tile, 16-byte chunk tid%8.
   const int lrow = tid >> 3;
   const int lcol = tid & 7;
-  // A rows of this thread's loads (tile rows BM + lrow + 32*j): fixed for the
-  // workgroup (in-bounds stand-in row 0 beyond c*R).
-  // raw buffer resources (loads at or past the end of the range return zero)
+  // Raw buffer resources over the slot's A block and over x (loads at or past
+  // the end of a range return zero).
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.A + static_cast<int64_t>(slot_ok ? slot : 0) * p.CR * p.K),
       static_cast<short>(0), static_cast<int>(static_cast<uint32_t>(p.CR * p.K * 2)), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.x), static_cast<short>(0),
       static_cast<int>(static_cast<uint32_t>(((p.s - 1) * p.ldx + p.K) * 2)), kRsrcWord3);
-  // A rows past c*R or past the slot's rank (padding, possibly NaN) read row
-  // 0 of the slot instead, a live row that stays in L1: their products only
-  // reach output rows stored as zero, and the L1 fill is spent on live rows.
+  // A rows of this thread's loads (tile rows BM + lrow + 32*j), fixed for the
+  // workgroup.  Rows past c*R or past the slot's rank (padding, possibly NaN)
+  // read row 0 of the slot instead, a live row that stays in L1: their
+  // products only reach output rows stored as zero, and the L1 fill is spent
+  // on live rows.
   uint32_t aoff[APER];
 #pragma unroll
   for (int j = 0; j < APER; ++j) {
