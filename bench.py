@@ -4,21 +4,20 @@ A step is one pass of the whole path over one batch: host plan (native
 planner) -> one async upload of the plan -> LoRA-A shrink -> LoRA-B expand
 (scaling, stacked slice offsets, in place into base) -> LoRA-A embedding
 gather.  The timed steps are eager: one native call plans and uploads, one
-call runs the embedding gather and one runs lora_qkv (shrink then expand).
-Graph mode (the three launches captured once per input set over a
-fixed-capacity plan, replayed after each upload) is timed too and reported
-beside it.  The headline workload is the decode batch: 256 one-token requests on
-8 adapters drawn uniformly, rank 16, stacked qkv 4096 -> [4096, 1024, 1024],
-bf16; the embedding gather uses vocab 128256 and rank 16.  Inputs rotate over
-48 independent sets (> the 256 MB MALL) so kernels read HBM, not cache.
-Every run also times the prefill gate_up workload (chunk cap 128).
+call runs the embedding gather and one runs lora_qkv (the stacked shrink and
+expand).  Graph mode is timed too and reported beside it.  The headline
+workload is the decode batch: 256 one-token requests on 8 adapters drawn
+uniformly, rank 16, stacked qkv 4096 -> [4096, 1024, 1024], bf16; the
+embedding gather uses vocab 128256 and rank 16.  Inputs rotate over 48
+independent sets (> the 256 MB MALL) so kernels read HBM, not cache.
 
 Prints ONE JSON line.  `value` is tokens/s of whole steps (wall clock over
 the timed steps, inputs resident in HBM); kernel durations come from HIP
-events on the stream the kernels run on.  `--secondary` adds the prefill
-chunk sweep (16 / 32 / 64 / 128), the skewed batch (o_proj, down_proj), the
-full Llama-3-8B-shaped layer sweep with the embedding gather, the pruned
-lm_head pass of the decode batch, and the device-side planner.
+events on the stream the kernels run on.  Every run also times the other
+workloads, each under its own key: the prefill chunk sweep (16 / 32 / 64 /
+128), the skewed batch (o_proj, down_proj), the Llama-3-8B-shaped layer
+sweep with the embedding gather, the pruned lm_head pass of the decode batch
+and the device-side planner; `--quick` skips them.
 """
 
 import argparse
@@ -45,11 +44,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=48, help="rotated input sets")
-    ap.add_argument("--secondary", action="store_true",
-                    help="also time the prefill chunk sweep, the skewed batch, the full "
-                         "layer sweep, the lm_head pass and the device-side planner")
-    ap.add_argument("--full-layers", type=int, default=8,
-                    help="layers with distinct weights timed in the full layer sweep")
+    ap.add_argument("--quick", action="store_true",
+                    help="time the decode step only (skip the prefill chunk sweep, the skewed "
+                         "batch, the full layer sweep, the lm_head pass and the device planner)")
+    ap.add_argument("--full-layers", type=int, default=4,
+                    help="resident layers with distinct weights in the full layer sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -155,6 +154,56 @@ def hold_stream(stream, ms):
 _SLEEP_CYCLES_PER_MS = None
 
 
+def own_plan(info):
+    """A copy of a batch plan whose device arrays belong to it alone."""
+    import dataclasses
+    import torch
+    return dataclasses.replace(info, **{
+        f.name: getattr(info, f.name).clone() for f in dataclasses.fields(info)
+        if isinstance(getattr(info, f.name), torch.Tensor)})
+
+
+def seg_histogram(info):
+    """Plan segment lengths in power-of-two bins: {"1": n, "2-3": n, ..., "128+": n}."""
+    n = info.num_segments
+    lens = np.diff(info.seg_indptr[:n + 1].cpu().numpy().astype(np.int64))
+    edges = [1, 2, 4, 8, 16, 32, 64, 128]
+    out = {}
+    for i, lo in enumerate(edges):
+        hi = edges[i + 1] if i + 1 < len(edges) else None
+        key = str(lo) if hi == lo + 1 else (f"{lo}-{hi - 1}" if hi else f"{lo}+")
+        out[key] = int(((lens >= lo) & (lens < hi)).sum() if hi else (lens >= lo).sum())
+    return out
+
+
+def host_plan_us(be, b, max_chunk=None, n=50):
+    """Host time of one plan + upload call (prepare_lora_batch), averaged."""
+    import torch
+    lens = None if b.is_decode else np.asarray(b.seq_lens, np.int32)
+    slots = np.asarray(b.req_slots, np.int32)
+    ranks, scal = np.asarray(b.lora_ranks, np.int32), np.asarray(b.scalings, np.float32)
+    for _ in range(3):
+        be.prepare_lora_batch(lens, slots, ranks, scal, is_decode=b.is_decode)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        be.prepare_lora_batch(lens, slots, ranks, scal, is_decode=b.is_decode)
+    us = (time.perf_counter() - t0) / n * 1e6
+    torch.cuda.synchronize()
+    return round(us, 2)
+
+
+def rotated(t, n):
+    """n input sets for one projection: the drawn set, then copies whose
+    values are rolled along K (x, A) or N (B, base) on the GPU, so every set
+    is its own memory; rank padding rows and columns keep their places."""
+    sets = [t]
+    for i in range(1, n):
+        sets.append({"x": t["x"].roll(8 * i, dims=1), "A": t["A"].roll(8 * i, dims=2),
+                     "B": t["B"].roll(8 * i, dims=1), "base": t["base"].roll(8 * i, dims=1)})
+    return sets
+
+
 def run_decode(args, device):
     """Decode steps.  Headline (eager): host plan + one upload, then the
     embedding gather and the stacked shrink + expand (lora_qkv), one C call
@@ -204,11 +253,14 @@ def run_decode(args, device):
     # delay kernel holds the stream while one launch per step is queued
     # between two events, so the launches run back to back and the average
     # launch duration is the interval over the number of launches.
+    # Every timed launch gets its own copy of its plan: the backend's ring
+    # holds 8 live plans, and launch i must read set i's plan, not the plan
+    # of a later batch that reused its ring slot.
     infos = []
     for i in range(args.steps):
         st = sets[i % len(sets)]
-        infos.append(be.prepare_lora_batch(None, st["slots"], st["ranks"], st["scal"],
-                                           is_decode=True))
+        infos.append(own_plan(be.prepare_lora_batch(None, st["slots"], st["ranks"], st["scal"],
+                                                    is_decode=True)))
     torch.cuda.synchronize()
 
     def one(n, i):
@@ -293,6 +345,9 @@ def run_decode(args, device):
     plan_us = (time.perf_counter() - t1) / 50 * 1e6
     torch.cuda.synchronize()
 
+    hist = seg_histogram(be.prepare_lora_batch(None, sets[0]["slots"], sets[0]["ranks"],
+                                               sets[0]["scal"], is_decode=True))
+    torch.cuda.synchronize()
     counts = [algo_counts(st["b"], st["proj"], st["A_emb"].shape[1]) for st in sets]
     per = {}
     for n in names:
@@ -308,11 +363,50 @@ def run_decode(args, device):
     return {
         "wall_s": eager_wall, "graph_wall_s": graph_wall, "tokens": b0.num_tokens,
         "kernels": per, "prepare_host_us": round(plan_us, 2), "back_to_back": back_to_back,
+        "segment_lengths": hist,
         "shrink_expand": {"us": round(se_us, 3),
                           "gbs": round(se_bytes / (se_us * 1e-6) / 1e9, 1),
                           "hbm_frac": round(se_bytes / (se_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                           "tokens_per_s_kernels": round(b0.num_tokens / (se_us * 1e-6), 1)},
     }
+
+
+def run_floor(device, steps=100, sets=48):
+    """What the decode kernels' sizes allow on this stack: an empty kernel and
+    device-to-device copies whose read + write bytes equal the decode
+    shrink's and the stacked call's algorithmic bytes, each launched once per
+    step back to back behind a delay kernel (the decode kernels' timing
+    protocol), over `sets` rotated buffers so the copies read HBM."""
+    import torch
+    stream = torch.cuda.current_stream(device)
+    out = {}
+
+    def timed(fn):
+        for i in range(10):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        held = hold_stream(stream, 5.0 + 0.05 * steps)
+        e0.record(stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(stream)
+        b2b = not held.query()
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) * 1e3 / steps, 3), b2b
+
+    out["empty_kernel_us"], out["empty_back_to_back"] = timed(lambda i: torch.cuda._sleep(0))
+    for name, moved in (("shrink", 5268480), ("shrink_expand", 5268480 + 7889920)):
+        n = moved // 2
+        src = [torch.empty(n, dtype=torch.uint8, device=device) for _ in range(sets)]
+        dst = [torch.empty(n, dtype=torch.uint8, device=device) for _ in range(sets)]
+        us, b2b = timed(lambda i: dst[i % sets].copy_(src[i % sets]))
+        out[f"copy_{name}_bytes"] = moved
+        out[f"copy_{name}_us"] = us
+        out[f"copy_{name}_gbs"] = round(moved / (us * 1e-6) / 1e9, 1)
+        out[f"copy_{name}_back_to_back"] = b2b
+        del src, dst
+    return out
 
 
 def _rates(n_bytes, flops, us):
@@ -327,44 +421,51 @@ def _rates(n_bytes, flops, us):
             "fraction_of_attainable": round(roof / t, 4)}
 
 
-def measure_projection(device, b, proj, t, max_chunk, steps, warmup, emb_rank=16):
+def measure_projection(device, b, proj, sets, max_chunk, steps, warmup, emb_rank=16):
     """Events around each call, `steps` times after `warmup`: the shrink, the
     expand and (stacked projections) the stacked call, on one planned batch.
-    Inputs: `t` = device tensors x, A, B, base of the projection."""
+    Call i reads input set i mod len(sets) (`sets`: dicts of device tensors
+    x, A, B, base), so repeated calls do not find their inputs in the MALL.
+    Also reports the plan's segment-length histogram and the host time of
+    the plan + upload call."""
     import torch
     import segmented_gather_gemm_amd as sgg
 
     be = sgg.ChunkedSgmvLoRA(b.num_loras, max_chunk, device)
+    plan_us = host_plan_us(be, b)
     info = be.prepare_lora_batch(None if b.is_decode else b.seq_lens, b.req_slots,
                                  b.lora_ranks, b.scalings, is_decode=b.is_decode)
     c = proj.num_slices
-    h = torch.empty((b.num_tokens, t["A"].shape[1]), dtype=torch.bfloat16, device=device)
+    h = torch.empty((b.num_tokens, sets[0]["A"].shape[1]), dtype=torch.bfloat16, device=device)
     ws = torch.zeros(256 << 20, dtype=torch.uint8, device=device)
     stream = torch.cuda.current_stream(device)
     calls = {
-        "shrink": lambda: sgg.lora_shrink(t["x"], t["A"], info, c, out=h, workspace=ws),
-        "expand": lambda: sgg.lora_expand(h, t["B"], info, proj.slice_offsets, proj.max_slice,
-                                          t["base"]),
+        "shrink": lambda t: sgg.lora_shrink(t["x"], t["A"], info, c, out=h, workspace=ws),
+        "expand": lambda t: sgg.lora_expand(h, t["B"], info, proj.slice_offsets, proj.max_slice,
+                                            t["base"]),
     }
     if c > 1:
-        calls["stacked"] = lambda: sgg.lora_qkv(t["x"], t["A"], t["B"], info,
-                                                proj.slice_offsets, proj.max_slice, t["base"],
-                                                workspace=ws)
+        calls["stacked"] = lambda t: sgg.lora_qkv(t["x"], t["A"], t["B"], info,
+                                                  proj.slice_offsets, proj.max_slice, t["base"],
+                                                  workspace=ws)
     cnt = algo_counts(b, proj, emb_rank)
     cnt["stacked"] = {k: cnt["shrink"][k] + cnt["expand"][k] for k in ("bytes", "flops")}
-    out = {"tokens": b.num_tokens, "segments": info.num_segments, "chunk": info.max_len}
+    out = {"tokens": b.num_tokens, "segments": info.num_segments,
+           "work_segments": info.num_work_segments, "chunk": info.max_len,
+           "input_sets": len(sets), "segment_lengths": seg_histogram(info),
+           "plan_host_us": plan_us}
     for name, fn in calls.items():
-        for _ in range(warmup):
-            fn()
+        for i in range(warmup):
+            fn(sets[i % len(sets)])
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         ev[0].record(stream)
         for i in range(steps):
-            fn()
+            fn(sets[i % len(sets)])
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
         us = float(np.mean([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]))
         out[name] = _rates(cnt[name]["bytes"], cnt[name]["flops"], us)
-    tot = out["shrink"]["avg_us"] + out["expand"]["avg_us"]
+    tot = out["stacked"]["avg_us"] if c > 1 else out["shrink"]["avg_us"] + out["expand"]["avg_us"]
     out["tokens_per_s"] = round(b.num_tokens / (tot * 1e-6), 1)
     return out
 
@@ -373,9 +474,10 @@ def _to(device, d):
     return {k: v.to(device) for k, v in d.items()}
 
 
-def run_prefill(device, chunks=(128,), steps=20, warmup=3):
+def run_prefill(device, chunks=(16, 32, 64, 128), steps=20, warmup=3):
     """Prefill gate_up (32 requests of 64..2048 tokens, 32 adapters Zipf(1.1),
-    r=64, 4096 -> 2 x 14336), one entry per server chunk cap."""
+    r=64, 4096 -> 2 x 14336), one entry per server chunk cap.  One call moves
+    4.3 GB, far more than the MALL, so one input set suffices."""
     from synth import draw_batch, draw_projection
     res = {}
     t = None
@@ -384,72 +486,132 @@ def run_prefill(device, chunks=(128,), steps=20, warmup=3):
         proj = b.projections[0]
         if t is None:
             t = _to(device, draw_projection(b, proj))
-        res[f"chunk{mc}"] = measure_projection(device, b, proj, t, mc, steps, warmup)
+        res[f"chunk{mc}"] = measure_projection(device, b, proj, [t], mc, steps, warmup)
     res["workload"] = ("prefill gate_up, 32 requests (s=%d), 32 adapters Zipf(1.1), r=64, "
                        "4096 -> 2x14336" % b.num_tokens)
     return res
 
 
-def run_skewed(device, steps=20, warmup=3):
+def run_skewed(device, steps=20, warmup=4, n_sets=4):
     """Skewed mixed batch: 8192 tokens, 90 % on one adapter, ranks 8..64 padded
-    to 64 (NaN padding), o_proj 4096 -> 4096 and down_proj 14336 -> 4096."""
+    to 64 (NaN padding), o_proj 4096 -> 4096 and down_proj 14336 -> 4096;
+    `n_sets` rotated input sets (>= 1 GB) so repeated calls read HBM."""
+    import torch
     from synth import draw_batch, draw_projection
     b = draw_batch("skewed")
     res = {"workload": "skewed: s=8192, 128 adapters, 90 % on one, ranks {8,16,32,64} "
                        "padded to 64"}
     for pi, proj in enumerate(b.projections):
-        t = _to(device, draw_projection(b, proj, proj_index=pi))
-        res[proj.name] = measure_projection(device, b, proj, t, b.max_chunk_size, steps, warmup)
-        del t
+        sets = rotated(_to(device, draw_projection(b, proj, proj_index=pi)), n_sets)
+        res[proj.name] = measure_projection(device, b, proj, sets, b.max_chunk_size, steps,
+                                            warmup)
+        del sets
+        torch.cuda.empty_cache()
     return res
 
 
 def run_full(device, layers, steps=5, warmup=1):
     """Full layer sweep, Llama-3-8B shapes: per layer qkv, o, gate_up, down
-    over 4288 tokens (192 decode + 8 x 512), 64 adapters r=32.  `layers`
-    layers with distinct weights are timed; the per-layer figure is their
-    mean and the 32-layer figure is 32 x that mean."""
+    over 4288 tokens (192 decode + 8 x 512), 64 adapters r=32, one plan.
+    `layers` layers with distinct weights and activations (~0.9 GB each) are
+    resident and run in sequence, as a forward pass does, so no call finds its
+    inputs in the MALL; each call is timed with events around it.  Stacked
+    projections run as the stacked call (their standalone shrink and expand
+    are timed in a second sweep); the per-layer figure is the mean over layers
+    and passes, and the 32-layer figure is 32 x that."""
     import torch
     from synth import draw_batch, draw_embedding, draw_projection
     import segmented_gather_gemm_amd as sgg
     b = draw_batch("full")
-    per = {p.name: [] for p in b.projections}
-    parts = {p.name: {"shrink": [], "expand": []} for p in b.projections}
-    for layer in range(layers):
-        for pi, proj in enumerate(b.projections):
-            t = _to(device, draw_projection(b, proj, layer=layer, proj_index=pi))
-            m = measure_projection(device, b, proj, t, b.max_chunk_size, steps, warmup)
-            per[proj.name].append(m["stacked"]["avg_us"] if proj.num_slices > 1 else
-                                  m["shrink"]["avg_us"] + m["expand"]["avg_us"])
-            for n in ("shrink", "expand"):
-                parts[proj.name][n].append(m[n]["avg_us"])
-            del t
-    layer_us = float(sum(np.mean(v) for v in per.values()))
-    cnts = [algo_counts(b, p, 16) for p in b.projections]
+    be = sgg.ChunkedSgmvLoRA(b.num_loras, b.max_chunk_size, device)
+    plan_us = host_plan_us(be, b)
+    info = be.prepare_lora_batch(b.seq_lens, b.req_slots, b.lora_ranks, b.scalings)
+    hist = seg_histogram(info)
+    projs = b.projections
+    data = [[_to(device, draw_projection(b, p, layer=layer, proj_index=pi))
+             for pi, p in enumerate(projs)] for layer in range(layers)]
+    hs = [torch.empty((b.num_tokens, t["A"].shape[1]), dtype=torch.bfloat16, device=device)
+          for t in data[0]]
+    ws = torch.zeros(256 << 20, dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream(device)
+
+    def call(kind, pi, t):
+        p = projs[pi]
+        if kind == "stacked":
+            sgg.lora_qkv(t["x"], t["A"], t["B"], info, p.slice_offsets, p.max_slice, t["base"],
+                         workspace=ws)
+        elif kind == "shrink":
+            sgg.lora_shrink(t["x"], t["A"], info, p.num_slices, out=hs[pi], workspace=ws)
+        else:
+            sgg.lora_expand(hs[pi], t["B"], info, p.slice_offsets, p.max_slice, t["base"])
+
+    def sweep(kinds_of):
+        """Events around every call of `warmup + steps` passes over the layers;
+        mean microseconds per (projection, kind) over the timed passes."""
+        times = {}
+        for rep in range(warmup + steps):
+            evs = []
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            for layer in range(layers):
+                for pi in range(len(projs)):
+                    for kind in kinds_of(pi):
+                        call(kind, pi, data[layer][pi])
+                        e2 = torch.cuda.Event(enable_timing=True)
+                        e2.record(stream)
+                        evs.append((pi, kind, e, e2))
+                        e = e2
+            torch.cuda.synchronize()
+            if rep >= warmup:
+                for pi, kind, a, z in evs:
+                    times.setdefault((pi, kind), []).append(a.elapsed_time(z) * 1e3)
+        return {k: float(np.mean(v)) for k, v in times.items()}
+
+    main = sweep(lambda pi: ("stacked",) if projs[pi].num_slices > 1 else ("shrink", "expand"))
+    parts = sweep(lambda pi: ("shrink", "expand"))
+    per = {}
+    per_kernels = {}
+    for pi, p in enumerate(projs):
+        per[p.name] = (main[(pi, "stacked")] if p.num_slices > 1 else
+                       main[(pi, "shrink")] + main[(pi, "expand")])
+        per_kernels[p.name] = {k: round(parts[(pi, k)], 2) for k in ("shrink", "expand")}
+    layer_us = float(sum(per.values()))
+    cnts = [algo_counts(b, p, 16) for p in projs]
     layer_bytes = sum(c["shrink"]["bytes"] + c["expand"]["bytes"] for c in cnts)
     layer_flops = sum(c["shrink"]["flops"] + c["expand"]["flops"] for c in cnts)
-    # embedding gather over the same plan
+    per_proj = {}
+    for pi, p in enumerate(projs):
+        cb = cnts[pi]["shrink"]["bytes"] + cnts[pi]["expand"]["bytes"]
+        cf = cnts[pi]["shrink"]["flops"] + cnts[pi]["expand"]["flops"]
+        per_proj[p.name] = _rates(cb, cf, per[p.name])
+    del data
+    torch.cuda.empty_cache()
+    # embedding gather over the same plan (A_emb is 263 MB, above the MALL)
     ids, A_emb = draw_embedding(b)
     ids, A_emb = ids.to(device), A_emb.to(device)
-    be = sgg.ChunkedSgmvLoRA(b.num_loras, b.max_chunk_size, device)
-    info = be.prepare_lora_batch(b.seq_lens, b.req_slots, b.lora_ranks, b.scalings)
+    e_out = torch.empty((b.num_tokens, A_emb.shape[1]), dtype=torch.bfloat16, device=device)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    sgg.lora_a_embedding(ids, A_emb, info, b.vocab_size)
-    e0.record()
+    sgg.lora_a_embedding(ids, A_emb, info, b.vocab_size, out=e_out)
+    e0.record(stream)
     for _ in range(20):
-        sgg.lora_a_embedding(ids, A_emb, info, b.vocab_size)
-    e1.record()
+        sgg.lora_a_embedding(ids, A_emb, info, b.vocab_size, out=e_out)
+    e1.record(stream)
     torch.cuda.synchronize()
     emb_us = e0.elapsed_time(e1) * 1e3 / 20
+    emb_bytes = algo_counts(b, projs[0], A_emb.shape[1])["embedding"]["bytes"]
     return {"workload": "full layer sweep: Llama-3-8B shapes, 4288 tokens, 64 adapters r=32; "
-                        f"{layers} layers with distinct weights timed",
-            "per_layer_us": {k: round(float(np.mean(v)), 2) for k, v in per.items()},
-            "per_layer_kernels_us": {k: {n: round(float(np.mean(v)), 2) for n, v in d.items()}
-                                     for k, d in parts.items()},
+                        f"{layers} resident layers with distinct weights and activations, "
+                        f"{steps} timed passes",
+            "segments": info.num_segments, "work_segments": info.num_work_segments,
+            "segment_lengths": hist, "plan_host_us": plan_us,
+            "per_layer_us": {k: round(v, 2) for k, v in per.items()},
+            "per_projection": per_proj,
+            "per_layer_kernels_us": per_kernels,
             "layer": _rates(layer_bytes, layer_flops, layer_us),
             "layers32_ms": round(32 * layer_us / 1e3, 3),
             "tokens_per_s_32_layers": round(b.num_tokens / (32 * layer_us * 1e-6), 1),
-            "embedding_us": round(emb_us, 2)}
+            "embedding": {"avg_us": round(emb_us, 2), "algo_bytes": int(emb_bytes),
+                          "gbs": round(emb_bytes / (emb_us * 1e-6) / 1e9, 2)}}
 
 
 def run_lm_head(device, steps=20, warmup=3):
@@ -465,7 +627,8 @@ def run_lm_head(device, steps=20, warmup=3):
     from synth.workloads import Projection
     b = draw_batch("decode")
     proj = Projection("lm_head", 4096, [0, 128256], 16)
-    t = _to(device, draw_projection(b, proj, proj_index=len(b.projections)))
+    # about 100 MB per call: 4 rotated input sets keep repeated calls off the MALL
+    sets = rotated(_to(device, draw_projection(b, proj, proj_index=len(b.projections))), 4)
     cnt = algo_counts(b, proj, 16)
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device=device)
     h = torch.empty((b.num_tokens, proj.rank), dtype=torch.bfloat16, device=device)
@@ -481,18 +644,19 @@ def run_lm_head(device, steps=20, warmup=3):
             info = be.prepare_lora_batch(None, b.req_slots, b.lora_ranks, b.scalings,
                                          is_decode=True)
         calls = {
-            "shrink": lambda: sgg.lora_shrink(t["x"], t["A"], info, 1, out=h, workspace=ws),
-            "expand": lambda: sgg.lora_expand(h, t["B"], info, proj.slice_offsets, proj.max_slice,
-                                              t["base"]),
+            "shrink": lambda t: sgg.lora_shrink(t["x"], t["A"], info, 1, out=h, workspace=ws),
+            "expand": lambda t: sgg.lora_expand(h, t["B"], info, proj.slice_offsets,
+                                                proj.max_slice, t["base"]),
         }
-        out = {"segments": info.num_segments, "work_segments": info.num_work_segments}
+        out = {"segments": info.num_segments, "work_segments": info.num_work_segments,
+               "segment_lengths": seg_histogram(info)}
         for name, fn in calls.items():
-            for _ in range(warmup):
-                fn()
+            for i in range(warmup):
+                fn(sets[i % len(sets)])
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for _ in range(steps):
-                fn()
+            for i in range(steps):
+                fn(sets[i % len(sets)])
             e1.record(stream)
             torch.cuda.synchronize()
             out[name] = _rates(cnt[name]["bytes"], cnt[name]["flops"],
@@ -563,15 +727,28 @@ def copy_probe(device):
 
 # ----------------------------------------------------------------- CPU leg
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(seconds):
     """The oracle (plan oracle + fp64 math oracle) on the decode workload's
-    rotated batches, single-threaded BLAS, until `seconds` have elapsed."""
+    rotated batches until `seconds` have elapsed, with BLAS allowed every core
+    this process may run on."""
     from threadpoolctl import threadpool_limits
     from oracle import lora as ol
     from oracle import plan as op
     from synth import draw_batch, draw_embedding, draw_projection, to_f64
     from synth.workloads import rotation_batch
 
+    cores = len(os.sched_getaffinity(0))
     base_b = draw_batch("decode")
     prepared = []
     for i in range(2):
@@ -583,7 +760,7 @@ def cpu_baseline(seconds):
                          to_f64(A_emb)))
     done = 0
     tokens = 0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         while True:
             b, proj, t, ids, A_emb = prepared[done % len(prepared)]
@@ -596,9 +773,11 @@ def cpu_baseline(seconds):
             el = time.perf_counter() - t0
             if el >= seconds:
                 break
-    return {"value": round(tokens / el, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": round(tokens / el, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{done} full decode steps (256 tokens each: plan + qkv shrink/expand + "
-                      f"embedding gather, fp64 NumPy), {el:.1f} s, BLAS limited to 1 thread"}
+                      f"embedding gather, fp64 NumPy), {el:.1f} s, BLAS threads = {cores} "
+                      f"(the process's CPU affinity)"}
 
 
 def main():
@@ -647,10 +826,19 @@ def main():
                                             " (WARNING: delay ended before enqueueing did)")),
         "shrink_expand": res["shrink_expand"],
         "prepare_host_us": res["prepare_host_us"],
+        "segment_lengths": res["segment_lengths"],
     }
-    print("# prefill", file=sys.stderr, flush=True)
-    line["prefill"] = run_prefill(device, (16, 32, 64, 128) if args.secondary else (128,))
-    if args.secondary:
+    print("# floor", file=sys.stderr, flush=True)
+    floor = run_floor(device)
+    line["floor"] = floor
+    # fraction of what the sizes allow: the same bytes moved by a device copy
+    line["kernels"]["shrink"]["fraction_of_copy_floor"] = round(
+        floor["copy_shrink_us"] / k["shrink"]["avg_us"], 4)
+    line["shrink_expand"]["fraction_of_copy_floor"] = round(
+        floor["copy_shrink_expand_us"] / res["shrink_expand"]["us"], 4)
+    if not args.quick:
+        print("# prefill chunk sweep", file=sys.stderr, flush=True)
+        line["prefill"] = run_prefill(device)
         print("# skewed", file=sys.stderr, flush=True)
         line["skewed"] = run_skewed(device)
         print("# full layer sweep", file=sys.stderr, flush=True)

@@ -39,9 +39,41 @@ def _align(n, m=64):
     return (n + m - 1) // m * m
 
 
+def batch_arrays(seq_lens, weight_indices, lora_ranks, scalings, max_loras):
+    """Host arrays of one batch, checked before the native planner reads them:
+    (lens or None, slots, ranks, scalings, tokens).
+
+    ``seq_lens`` None means decode mode (one token per request); otherwise it
+    needs one entry per entry of ``weight_indices`` -- the planner reads
+    ``seq_lens[r]`` for every request r.  ``lora_ranks`` and ``scalings`` need
+    ``max_loras`` entries each.
+    """
+    if len(lora_ranks) != max_loras or len(scalings) != max_loras:
+        raise ValueError(f"lora_ranks and scalings need {max_loras} entries")
+    slots = np.ascontiguousarray(weight_indices, dtype=np.int32)
+    if slots.ndim != 1:
+        raise ValueError("weight_indices must be one-dimensional")
+    if seq_lens is None:
+        lens, s = None, len(slots)
+    else:
+        lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        if lens.shape != slots.shape:
+            raise ValueError(f"seq_lens has {lens.size} entries, weight_indices {slots.size}")
+        s = int(lens.sum(dtype=np.int64))
+    ranks = np.ascontiguousarray(lora_ranks, dtype=np.int32)
+    scal = np.ascontiguousarray(scalings, dtype=np.float32)
+    return lens, slots, ranks, scal, s
+
+
 class _Staging:
     """Ring of plan buffers: pinned host staging plus a device plan buffer per
     slot.
+
+    Every slot is allocated when the ring is made, and a larger plan grows all
+    slots at once, so after the first batch of a given size no batch
+    allocates (a pinned allocation costs hundreds of microseconds).  The
+    per-slot ``LoRABatchInfo`` views of a plan layout are likewise built for
+    all slots the first time that layout is seen.
 
     A slot's staging buffer is reused only after the upload that last read it
     has done so: the upload's copy kernel writes the slot's sequence number
@@ -52,37 +84,54 @@ class _Staging:
     slot's device buffer is then rewritten by an upload enqueued after every
     kernel launched before it on the same stream, so the kernels of a batch
     read its plan intact as long as they run on the stream the batch was
-    prepared on.
+    prepared on.  Buffers outgrown by a larger plan are kept alive, never
+    freed: kernels already enqueued may still read them.
     """
 
-    def __init__(self, device, slots=8):
+    def __init__(self, device, slots=8, words=16384):
         self.device = device
+        self.n = slots
         self.host = [None] * slots
         self.dev = [None] * slots
         self.infos = [{} for _ in range(slots)]   # layout key -> LoRABatchInfo views
         self.host_addr = [0] * slots               # staging / device addresses and bytes
         self.dev_addr = [0] * slots
         self.dev_bytes = [0] * slots
+        self.retired = []
         self.flags = torch.zeros(slots, dtype=torch.int32, pin_memory=True)
         self.flag_view = self.flags.numpy()
         self.flag_addr = self.flags.data_ptr()
         self.seq = [0] * slots
+        self.words = 0
         self.i = 0
+        self._grow(words)
 
-    def take(self, n):
-        i = self.i
-        self.i = (i + 1) % len(self.host)
-        want, flags = self.seq[i], self.flag_view
-        if flags[i] != want:
-            self._wait(i, want)
-        if self.host[i] is None or self.host[i].numel() < n:
-            size = max(n, 4096)
+    def _grow(self, n):
+        """Give every slot a buffer of at least n words (waits for every
+        enqueued upload to have read its staging buffer first)."""
+        size = max(int(n), 2 * self.words, 4096)
+        for i in range(self.n):
+            if self.flag_view[i] != self.seq[i]:
+                self._wait(i, self.seq[i])
+        for i in range(self.n):
+            if self.host[i] is not None:
+                self.retired.append((self.host[i], self.dev[i]))
             self.host[i] = torch.empty(size, dtype=torch.int32, pin_memory=True)
             self.dev[i] = torch.empty(size, dtype=torch.int32, device=self.device)
             self.host_addr[i] = self.host[i].data_ptr()
             self.dev_addr[i] = self.dev[i].data_ptr()
             self.dev_bytes[i] = 4 * size
             self.infos[i] = {}
+        self.words = size
+
+    def take(self, n):
+        if n > self.words:
+            self._grow(n)
+        i = self.i
+        self.i = (i + 1) % self.n
+        want = self.seq[i]
+        if self.flag_view[i] != want:
+            self._wait(i, want)
         return i
 
     def _wait(self, i, want, limit_s=30.0):
@@ -160,12 +209,9 @@ class ChunkedSgmvLoRA:
         (``max_loras_per_batch`` entries, rank 0 = no adapter).
         """
         L = self.max_loras_per_batch
-        if len(lora_ranks) != L or len(scalings) != L:
-            raise ValueError(f"lora_ranks and scalings need {L} entries")
-        slots = np.ascontiguousarray(weight_indices, dtype=np.int32)
+        lens, slots, ranks, scal, s = batch_arrays(seq_lens, weight_indices, lora_ranks,
+                                                   scalings, L)
         bs = len(slots)
-        lens = None if seq_lens is None else np.ascontiguousarray(seq_lens, dtype=np.int32)
-        s = bs if lens is None else int(lens.sum(dtype=np.int64))
         if use_cuda_graph:
             if self._graph_cap is None:
                 raise RuntimeError("call init_cuda_graph_batch_info first")
@@ -190,8 +236,6 @@ class ChunkedSgmvLoRA:
             dev_addr, dev_bytes = dev.data_ptr(), 4 * dev.numel()
         else:
             dev, dev_addr, dev_bytes = stg.dev[ring], stg.dev_addr[ring], stg.dev_bytes[ring]
-        ranks = np.ascontiguousarray(lora_ranks, dtype=np.int32)
-        scal = np.ascontiguousarray(scalings, dtype=np.float32)
         idx = self._dev_index if self._dev_index is not None else torch.cuda.current_device()
         stream = torch._C._cuda_getCurrentRawStream(idx)
         flag, flag_value = stg.signal(ring)
@@ -208,19 +252,23 @@ class ChunkedSgmvLoRA:
             batch.planned_tokens = s
             self.batch_info = batch
             return batch
-        # eager: the slot's views for this layout are built once and reused
+        # eager: the views of a layout are built once, for every slot of the
+        # ring at the same time, and reused
         batch = stg.infos[ring].get(key)
         if batch is None:
-            v = {name: dev[o:o + n] for name, (o, n) in zip(_NAMES, regions)}
-            batch = LoRABatchInfo(
-                bs=bs, num_tokens=s, num_segments=n_seg, max_len=chunk,
-                seg_indptr=v["seg_indptr"], weight_indices=v["seg_slots"],
-                permutation=v["permutation"], lora_ranks=v["ranks"],
-                scalings=v["scalings"].view(torch.float32),
-                req_seg_indptr=v["req_seg_indptr"], req_weight_indices=v["req_slots"],
-                use_cuda_graph=False, max_seg_len=longest, work_indptr=v["work_indptr"],
-                work_slots=v["work_slots"], num_work_segments=n_work, max_work_len=longest_work)
-            stg.infos[ring][key] = batch
+            for i in range(stg.n):
+                d = stg.dev[i]
+                v = {name: d[o:o + n] for name, (o, n) in zip(_NAMES, regions)}
+                stg.infos[i][key] = LoRABatchInfo(
+                    bs=bs, num_tokens=s, num_segments=0, max_len=chunk,
+                    seg_indptr=v["seg_indptr"], weight_indices=v["seg_slots"],
+                    permutation=v["permutation"], lora_ranks=v["ranks"],
+                    scalings=v["scalings"].view(torch.float32),
+                    req_seg_indptr=v["req_seg_indptr"], req_weight_indices=v["req_slots"],
+                    use_cuda_graph=False, work_indptr=v["work_indptr"],
+                    work_slots=v["work_slots"])
+            batch = stg.infos[ring][key]
+        batch.bs = bs
         batch.num_segments, batch.max_len, batch.max_seg_len = n_seg, chunk, longest
         batch.num_work_segments, batch.max_work_len = n_work, longest_work
         batch.planned_segments = n_seg
@@ -252,14 +300,11 @@ class ChunkedSgmvLoRA:
 
     def _lm_head_plan(self, pruned_lens, weight_indices, lora_ranks, scalings, override):
         L = self.max_loras_per_batch
-        if len(lora_ranks) != L or len(scalings) != L:
-            raise ValueError(f"lora_ranks and scalings need {L} entries")
-        slots = np.ascontiguousarray(weight_indices, dtype=np.int32)
-        lens = np.ascontiguousarray(pruned_lens, dtype=np.int32)
-        if len(lens) != len(slots):
-            raise ValueError("pruned_lens and weight_indices differ in length")
+        if pruned_lens is None:
+            raise ValueError("pruned_lens is required")
+        lens, slots, ranks, scal, s = batch_arrays(pruned_lens, weight_indices, lora_ranks,
+                                                   scalings, L)
         bs = len(slots)
-        s = int(lens.sum(dtype=np.int64))
         min_chunk = override if override > 0 else MIN_CHUNK_SIZE
         # runs of consecutive requests are not bounded by the slot count
         seg_cap = B.lora_plan_max_segments(s, max(bs, 1), min_chunk)
@@ -267,8 +312,6 @@ class ChunkedSgmvLoRA:
         stg = self._staging
         ring = stg.take(total)
         dev = stg.dev[ring]
-        ranks = np.ascontiguousarray(lora_ranks, dtype=np.int32)
-        scal = np.ascontiguousarray(scalings, dtype=np.float32)
         idx = self.device.index if self.device.index is not None else torch.cuda.current_device()
         stream = torch._C._cuda_getCurrentRawStream(idx)
         info = self._info_arr

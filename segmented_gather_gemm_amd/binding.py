@@ -235,11 +235,16 @@ def lora_plan_device(seq_lens, req_slots, lora_ranks, scalings, max_loras, is_de
 # ----------------------------------------------------------------- workspace
 
 _workspaces = {}
+_outgrown = []
 
 
 def default_workspace(device, nbytes):
     """A zero-initialised, grow-only scratch buffer per device.
 
+    A workspace that a larger call outgrows is kept alive, never freed: a
+    graph captured with it keeps its address and would otherwise write its
+    split-K counters, partials and h into memory another tensor may own.
+    Growth doubles, so all of them together take at most twice the largest.
     Calls that use the same workspace must not overlap: use it from one
     stream, or pass a separate workspace per stream.
     """
@@ -250,6 +255,7 @@ def default_workspace(device, nbytes):
         size = max(int(nbytes), 1 << 20)
         if ws is not None:
             size = max(size, 2 * ws.numel())
+            _outgrown.append(ws)
         ws = torch.zeros(size, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws

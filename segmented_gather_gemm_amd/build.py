@@ -11,12 +11,12 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsgg_lora.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 CALLMOD = os.path.join(PKG, "_sggcall" + sysconfig.get_config_var("EXT_SUFFIX"))
-SOURCES = ["plan.cpp", "plan_device.hip", "shrink.hip", "shrink_gemm.hip", "expand.hip",
-           "lora_api.hip"]
+SOURCES = ["plan.cpp", "tiling.cpp", "plan_device.hip", "shrink.hip", "shrink_gemm.hip",
+           "expand.hip", "lora_api.hip"]
 ARCH = os.environ.get("SGG_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
@@ -40,10 +40,23 @@ def _run(cmd, verbose, what):
 
 def build(verbose=False):
     """Build the shared library and the CPython call module; always
-    recompiles.  Returns the library's path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    recompiles (one hipcc per source, in parallel, then one link).  Returns
+    the library's path."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, s + ".o") for s in SOURCES]
+
+    def compile_one(i):
+        _run([hipcc()] + HIPCC_FLAGS + ["-c", os.path.join(CSRC, SOURCES[i]), "-o", objs[i]],
+             verbose, f"hipcc {SOURCES[i]}")
+
+    workers = max(1, min(len(SOURCES), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(workers) as pool:
+        list(pool.map(compile_one, range(len(SOURCES))))
     tmp = LIB + ".tmp"
-    _run([hipcc()] + HIPCC_FLAGS + srcs + ["-o", tmp], verbose, "hipcc")
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose,
+         "hipcc link")
     os.replace(tmp, LIB)
     # integer-argument entry points for the hot calls, linked to the library
     tmp = CALLMOD + ".tmp"

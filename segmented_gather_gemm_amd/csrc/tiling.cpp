@@ -1,0 +1,127 @@
+// Host-side tile choice for the LoRA-A shrink (the kernels are in shrink.hip
+// and shrink_gemm.hip).  Plain host code: the launch code and the workspace
+// size queries both call it, and the sanitizer build of the host code covers
+// it without any device code.
+#include "sgg_internal.h"
+#include "sgg_kernels.h"
+
+namespace sgg {
+
+// Tile choice.  Batches that fill the GPU with whole-K tiles use the
+// workgroup-shared GEMM kernel (shrink_gemm.hip); the rest use this kernel
+// with K split.  For this kernel: start from the largest tile (NF covering c*R up to 8
+// fragments, MF covering the longest segment up to 8, at most 32 accumulator
+// fragments per wave).  While the grid has fewer work items than CUs, split
+// columns (NF), then rows (MF), down to single fragments; only then split K
+// across workgroups, into at most 4 ranges (each extra range costs a partial
+// tile round trip).  Measured on decode shapes: small tiles with 4 K ranges
+// beat both one big tile and 16-32 K ranges.
+ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk,
+                                  bool gemm_ok) {
+  ShrinkTiling t{};
+  static const int kNf[] = {1, 2, 3, 4, 6, 8};
+  static const int kMf[] = {1, 2, 4, 8};
+  const int need_n = (CR + 15) / 16;
+  const int need_m = (chunk < 16 ? 16 : chunk + 15) / 16;
+  // column fragments: values that tile c*R exactly (no partly empty block)
+  auto nf_ok = [&](int v) { return v <= need_n ? need_n % v == 0 : v == kNf[0] || kNf[0] >= need_n; };
+  int ni = 5, mi = 3;
+  while (ni > 0 && (kNf[ni] > need_n && kNf[ni - 1] >= need_n)) --ni;  // smallest NF covering c*R
+  while (ni > 0 && !(kNf[ni] >= need_n || need_n % kNf[ni] == 0)) --ni;
+  while (mi > 0 && kMf[mi - 1] >= need_m) --mi;   // smallest MF covering the chunk (or 8)
+  while (kMf[mi] * kNf[ni] > 32) --mi;
+  auto units_for = [&](int nf, int mf) {
+    const int bm = 16 * mf;
+    const int64_t mblocks = (chunk + bm - 1) / bm;
+    const int64_t grid_units = static_cast<int64_t>(num_segments) * mblocks;
+    const int64_t real_units = (s + bm - 1) / bm + num_segments;
+    const int64_t nblocks = (CR + 16 * nf - 1) / (16 * nf);
+    return (grid_units < real_units ? grid_units : real_units) * nblocks;
+  };
+  while (units_for(kNf[ni], kMf[mi]) < 256 && ni > 0) {
+    --ni;
+    while (ni > 0 && !nf_ok(kNf[ni])) --ni;
+  }
+  while (units_for(kNf[ni], kMf[mi]) < 256 && mi > 0) --mi;
+  t.nf = kNf[ni];
+  t.mf = kMf[mi];
+  t.nblocks = (CR + 16 * t.nf - 1) / (16 * t.nf);
+  const int bm = 16 * t.mf;
+  t.mblocks = (chunk + bm - 1) / bm;
+  if (t.mblocks < 1) t.mblocks = 1;
+  const int64_t units = units_for(t.nf, t.mf);
+  const int64_t kgroups = (K + 255) / 256;   // 256-deep groups: one 64-deep chunk per wave
+  int64_t ksplit = 1;
+  const int64_t counters = (s / bm + num_segments + 1) * t.nblocks;
+  if (units > 0 && units < 256 && counters <= kCounterCap) {
+    ksplit = (256 + units - 1) / units;
+    if (ksplit > 4) ksplit = 4;
+    if (ksplit > kgroups) ksplit = kgroups;
+  }
+  t.kps = (kgroups + ksplit - 1) / ksplit * 256;
+  t.ksplit = static_cast<int>((K + t.kps - 1) / t.kps);
+  if (t.ksplit < 1) t.ksplit = 1;
+  t.grid = grid_for(num_segments, static_cast<int64_t>(t.ksplit) * t.nblocks * t.mblocks);
+  if (t.ksplit > 1) {
+    t.partial_bytes = round_up(static_cast<int64_t>(t.ksplit) * s * CR * 4, 256);
+    return t;
+  }
+  // No K split needed.  Batches of short segments whose stacked rank rows
+  // are few (c*R <= 32) and that are small (at most 6144 tokens) or have a
+  // long K (8192 or more) keep this kernel, with one K range and tiles of 32
+  // tokens (64 above 6144 tokens) by half of c*R: its four waves stream
+  // interleaved K chunks with no barrier between them.  Measured against the
+  // 64 x 32 GEMM tiles (buffer loads, two register sets) on the full-layer
+  // batch (4288 tokens, 93 segments, 64 adapters, r = 32): o_proj 22.7 vs
+  // 25.6 us, down_proj 57.7 vs 65.2 us here; with c*R = 64 or more the GEMM
+  // tiles win (qkv 39.1 -> 36.0 us, gate_up 33.2 -> 29.1 us, skewed
+  // down_proj with r = 64: 149 -> 134 us).
+  const bool long_segments = num_segments > 0 && s >= 96 * static_cast<int64_t>(num_segments);
+  if (!long_segments && CR <= 32 && (s <= 6144 || K >= 8192)) {
+    t.mf = s > 6144 ? 4 : 2;
+    t.nf = 1;
+    for (int v : kNf)
+      if (16 * v <= CR / 2 && t.mf * v <= 32) t.nf = v;
+    t.nblocks = (CR + 16 * t.nf - 1) / (16 * t.nf);
+    t.mblocks = (chunk + 16 * t.mf - 1) / (16 * t.mf);
+    if (t.mblocks < 1) t.mblocks = 1;
+    t.gemm = 0;
+    t.grid = grid_for(num_segments, static_cast<int64_t>(t.nblocks) * t.mblocks);
+    return t;
+  }
+  // The workgroup-shared GEMM tiles.  Batches of long
+  // segments (mean work segment of 96 tokens or more, e.g. prefill) take
+  // 128 tokens per tile and rank rows the smallest of 32 / 64 / 128 covering
+  // c*R; batches of short segments (decode mixed in, many adapters, a long
+  // tail of one-request adapters) take 64 x 32 tiles, whose larger grid
+  // spreads the long segments over more CUs.  Then halve the rows, then the
+  // tokens, while the grid has fewer work items than CUs.  Measured: 64 x 32
+  // beats 128 x 32 by 10-20 % on the mixed and skewed batches (full-layer
+  // qkv 44 -> 39 us, skewed down_proj 202 -> 185 us), 128 x 128 beats every
+  // smaller tile by 25 % or more on prefill; the split-K kernel is faster on
+  // grids under one workgroup per CU.
+  int gm = long_segments && chunk > 64 ? 128 : 64;
+  int gn = !long_segments ? 32 : (CR <= 32 ? 32 : (CR <= 64 ? 64 : 128));
+  auto gemm_units = [&](int m, int n) {
+    const int64_t mb = (chunk + m - 1) / m, nbk = (CR + n - 1) / n;
+    const int64_t grid_units = static_cast<int64_t>(num_segments) * mb;
+    const int64_t real_units = (s + m - 1) / m + num_segments;
+    return (grid_units < real_units ? grid_units : real_units) * nbk;
+  };
+  while (gemm_units(gm, gn) < 256 && gn > 32) gn /= 2;
+  while (gemm_units(gm, gn) < 256 && gm > 64) gm /= 2;
+  // Too few workgroups for whole-K tiles (each workgroup has one K step of
+  // loads in flight): the split-K kernel's finer tiles keep more CUs busy.
+  if (gemm_units(gm, gn) < 256) return t;
+  if (!gemm_ok) return t;  // x or an A block beyond 32-bit offsets: one K range here
+  t.gemm = 1;
+  t.bm = gm;
+  t.bn = gn;
+  t.mblocks = (chunk + gm - 1) / gm;
+  if (t.mblocks < 1) t.mblocks = 1;
+  t.nblocks = (CR + gn - 1) / gn;
+  t.grid = grid_for(num_segments, static_cast<int64_t>(t.nblocks) * t.mblocks);
+  return t;
+}
+
+}  // namespace sgg

@@ -450,3 +450,23 @@ def test_call_module_takes_contiguous_host_buffers():
     assert "non-decreasing" in _err()
     assert C.lora_expand(*exp, np.array([1, 256], np.int32), 1, 256, *rest) == -1
     assert "slice_offsets[0]" in _err()
+
+
+def test_batch_arrays_rejects_mismatched_lengths():
+    """prepare_lora_batch's host arrays are checked before the native planner
+    reads seq_lens[r] for every request r: a shorter seq_lens would be a host
+    over-read, a longer one would drop tokens from the plan."""
+    from segmented_gather_gemm_amd.backend import batch_arrays
+    ranks, scal = [8] * 4, [1.0] * 4
+    with pytest.raises(ValueError):
+        batch_arrays([1, 2], [0, 1, 2], ranks, scal, 4)
+    with pytest.raises(ValueError):
+        batch_arrays([1, 2, 3, 4], [0, 1, 2], ranks, scal, 4)
+    with pytest.raises(ValueError):
+        batch_arrays(None, [0], [8] * 3, scal, 4)
+    with pytest.raises(ValueError):
+        batch_arrays([[1, 2]], [[0, 1]], ranks, scal, 4)
+    lens, slots, r, sc, s = batch_arrays([1, 2, 3], [0, 1, 2], ranks, scal, 4)
+    assert s == 6 and lens.dtype == np.int32 and sc.dtype == np.float32
+    lens, slots, r, sc, s = batch_arrays(None, [3, 1], ranks, scal, 4)
+    assert lens is None and s == 2
