@@ -333,6 +333,29 @@ int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B, int64_t N
              int64_t workspace_bytes, void* stream);
 
 /*
+ * lora_qkv_noalloc -- lora_qkv without a caller workspace, for callers that
+ * cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments and results as
+ * lora_qkv (bit for bit), minus the workspace: the library uses a device
+ * array of SGG_NOALLOC_SCRATCH_BYTES bytes that each device holds from the
+ * first call on it until the process ends.  It calls no allocating routine.
+ *
+ * Errors: SGG_ERR_CAPACITY when lora_qkv_workspace_bytes() of the call
+ * exceeds SGG_NOALLOC_SCRATCH_BYTES (use lora_qkv with a workspace);
+ * SGG_ERR_HIP when the array's device address cannot be found; otherwise as
+ * lora_qkv.  All calls on one device share the array: calls that overlap in
+ * time (other streams, other host threads) race and must not be issued.
+ */
+#define SGG_NOALLOC_SCRATCH_BYTES (16LL << 20)
+int lora_qkv_noalloc(const void* x, int64_t ldx, const void* A, const void* B, int64_t N,
+                     void* base_output, int64_t ldo, int64_t s, int64_t in_dim,
+                     int32_t num_loras, int32_t R, const int32_t* slice_offsets,
+                     int32_t num_slices, int32_t max_slice_size, const int32_t* seg_indptr,
+                     const int32_t* seg_slots, int32_t num_segments,
+                     const int32_t* permutation, const int32_t* lora_ranks,
+                     const float* scalings, int32_t chunk_size, void* stream);
+
+/*
  * lora_a_embedding -- LoRA-A embedding lookup.
  * (chunked_backend.py page: run_lora_a_embedding; base_backend.py page:
  *  run_lora_a_embedding shape contract.)

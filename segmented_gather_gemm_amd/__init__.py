@@ -18,6 +18,7 @@ from .binding import (
     lora_plan_max_segments,
     lora_plan_segments,
     lora_qkv,
+    lora_qkv_noalloc,
     lora_shrink,
 )
 
@@ -27,5 +28,5 @@ calls()
 __all__ = [
     "ChunkedSgmvLoRA", "LoRABatchInfo", "SggError", "default_workspace", "lora_a_embedding",
     "lora_expand", "lora_plan_device", "lora_plan_lm_head", "lora_plan_max_segments", "lora_plan_segments",
-    "lora_qkv", "lora_shrink",
+    "lora_qkv", "lora_qkv_noalloc", "lora_shrink",
 ]

@@ -45,6 +45,9 @@ SIGNATURES = {
     "lora_qkv": (ctypes.c_int, [
         _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _pi32, _i32, _i32,
         _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i64, _vp]),
+    "lora_qkv_noalloc": (ctypes.c_int, [
+        _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _pi32, _i32, _i32,
+        _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp]),
     "lora_a_embedding": (ctypes.c_int, [
         _vp, _vp, _i64, _vp, _i64, _i64, _i32, _i32, _i64, _vp, _vp, _i32, _vp, _vp, _i32, _vp]),
 }

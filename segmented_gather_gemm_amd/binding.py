@@ -372,6 +372,34 @@ def lora_qkv(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
     return base_output
 
 
+def lora_qkv_noalloc(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slice_size,
+                     base_output):
+    """lora_qkv with the library's own device scratch instead of a workspace
+    (no allocation anywhere; base_output is required).  Calls on one device
+    share that scratch and must not overlap in time."""
+    xst = _need_bf16("x", x, 2)
+    _need_bf16_dense("A", A, 3)
+    _need_bf16_dense("B", B, 3)
+    offs, p_offs = _offsets(slice_offsets)
+    c = len(offs) - 1
+    s, K = x.shape
+    L, CR, K2 = A.shape
+    _, N, R = B.shape
+    if K2 != K or CR != c * R:
+        raise ValueError(f"A shape {tuple(A.shape)} does not match x ({K}) and c*R ({c}*{R})")
+    if s != batch_info.num_tokens:
+        raise ValueError(f"x has {s} rows, the plan has {batch_info.num_tokens} tokens")
+    bst = _need_bf16("base_output", base_output, 2)
+    _need_rows_cols("base_output", base_output, s, int(offs[-1]))
+    ind, sl, nseg, hint, perm = batch_info.kernel_segments()
+    check(lib().lora_qkv_noalloc(
+        x.data_ptr(), xst[0], A.data_ptr(), B.data_ptr(), N, base_output.data_ptr(), bst[0], s,
+        K, L, R, ctypes.cast(p_offs, _P32), c, int(max_slice_size), ind.data_ptr(),
+        sl.data_ptr(), nseg, perm.data_ptr(), batch_info.lora_ranks.data_ptr(),
+        batch_info.scalings.data_ptr(), hint, _stream(x)))
+    return base_output
+
+
 def lora_a_embedding(input_ids, weights, batch_info: LoRABatchInfo, vocab_size,
                      extra_embeddings=None, out=None):
     """LoRA-A embedding lookup: ids (s,), weights (L, R, V) -> (s, R)."""

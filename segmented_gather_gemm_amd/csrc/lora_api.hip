@@ -2,6 +2,7 @@
 // is enqueued), tile choice and kernel launches.
 #include <cinttypes>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "sgg_internal.h"
@@ -355,6 +356,73 @@ extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B
   if (rc) return rc;
   rc = launch_status(sgg::launch_expand(pe, te, st), "expand");
   return rc ? rc : sgg::ok();
+}
+
+// ------------------------------------------------------- no-allocation qkv
+// lora_qkv for callers that cannot allocate device memory (code under graph
+// capture, tight serving loops): the workspace is this file-scope device
+// array.  Each device holds its own copy, at its own address, for the life
+// of the process; host code uses that address (looked up once per device with
+// the device current), never the array's name, which on the host is only a
+// stand-in.  The array is zero when the module loads, and every lora_qkv call
+// leaves its counter region at zero again, which is all a call needs to find
+// at its start; h and the partials are written before they are read.  Calls
+// on one device share the array: calls that overlap in time race.
+
+namespace {
+
+static __device__ __align__(256) char scratch[SGG_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up once per
+// device); nullptr with the error recorded on failure.
+void* scratch_for_current_device(int* rc) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *rc = fail(SGG_ERR_HIP, "no current device for the scratch array (%s)",
+               e != hipSuccess ? hipGetErrorString(e) : "device index out of range");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *rc = fail(SGG_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                 hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int lora_qkv_noalloc(const void* x, int64_t ldx, const void* A, const void* B,
+                                int64_t N, void* base_output, int64_t ldo, int64_t s,
+                                int64_t in_dim, int32_t num_loras, int32_t R,
+                                const int32_t* slice_offsets, int32_t num_slices,
+                                int32_t max_slice_size, const int32_t* seg_indptr,
+                                const int32_t* seg_slots, int32_t num_segments,
+                                const int32_t* permutation, const int32_t* lora_ranks,
+                                const float* scalings, int32_t chunk_size, void* stream) {
+  const int64_t need =
+      lora_qkv_workspace_bytes(s, in_dim, num_slices, R, num_segments, chunk_size);
+  SGG_CHECK(need <= SGG_NOALLOC_SCRATCH_BYTES, SGG_ERR_CAPACITY,
+            "lora_qkv_noalloc needs %" PRId64 " bytes of scratch, its maximum is %lld; "
+            "call lora_qkv with a workspace instead",
+            need, static_cast<long long>(SGG_NOALLOC_SCRATCH_BYTES));
+  int rc = SGG_OK;
+  void* ws = scratch_for_current_device(&rc);
+  if (ws == nullptr) return rc;
+  return lora_qkv(x, ldx, A, B, N, base_output, ldo, s, in_dim, num_loras, R, slice_offsets,
+                  num_slices, max_slice_size, seg_indptr, seg_slots, num_segments, permutation,
+                  lora_ranks, scalings, chunk_size, ws, SGG_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 extern "C" int lora_a_embedding(const int64_t* input_ids, const void* A_emb, int64_t V, void* out,
