@@ -321,9 +321,24 @@ int lora_expand(const void* h, int64_t ldh, const void* B, int64_t N, void* base
  *   lora_shrink / lora_expand.  The intermediate h (bf16, s x c*R) lives in
  *   `workspace`, which must hold lora_qkv_workspace_bytes() bytes, zero-
  *   filled on first use, and is not shared by overlapping calls.
+ *
+ * The call makes two launches, and its result equals lora_shrink followed
+ * by lora_expand bit for bit.  A one-launch form exists for small batches
+ * (those whose shrink splits K across workgroups, e.g. decode) with
+ * c*R <= 48: the expand's workgroups wait for the shrink's workgroups of
+ * their segment inside one grid (bounded waits), taken when asked for with
+ * lora_set_option("fused_stacked", 1) and when the grid fits on the device at
+ * once.  It splits K its own way, so it agrees with the two-launch form to
+ * rounding, not bit for bit.  Measured on MI355X it is slower on the decode
+ * batch, and it is off by default.
  */
 int64_t lora_qkv_workspace_bytes(int64_t s, int64_t in_dim, int32_t num_slices, int32_t R,
                                  int32_t num_segments, int32_t chunk_size);
+/* Byte offset, in a lora_qkv workspace, of a 32-bit status word: bit 0 is set
+ * (and stays set) once a one-launch stacked call had to give up waiting for
+ * its shrink tiles and computed them again itself (the result is the same;
+ * see lora_set_option "spin_limit"). */
+#define SGG_WORKSPACE_STATUS_OFFSET 65532
 int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B, int64_t N,
              void* base_output, int64_t ldo, int64_t s, int64_t in_dim, int32_t num_loras,
              int32_t R, const int32_t* slice_offsets, int32_t num_slices,
@@ -331,6 +346,21 @@ int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B, int64_t N
              int32_t num_segments, const int32_t* permutation, const int32_t* lora_ranks,
              const float* scalings, int32_t chunk_size, void* workspace,
              int64_t workspace_bytes, void* stream);
+
+/*
+ * lora_set_option -- process-wide settings of the device calls; returns the
+ * previous value, or -1 for an unknown name.  Not needed for normal use.
+ *   "fused_stacked"  0 (default): lora_qkv makes two launches;
+ *                    1: one launch where it can (see lora_qkv).
+ *   "spin_limit"     polls (about 128 cycles apart) before a one-launch
+ *                    stacked call's wait gives up and recomputes (default
+ *                    2^20; 0 gives up at once, which tests use to exercise
+ *                    that path).
+ *   "fused_ksplit"   K ranges of the one-launch call's shrink tiles (0, the
+ *                    default: the most that fit; 2..16 forces that many when
+ *                    they fit).
+ */
+int64_t lora_set_option(const char* name, int64_t value);
 
 /*
  * lora_qkv_noalloc -- lora_qkv without a caller workspace, for callers that

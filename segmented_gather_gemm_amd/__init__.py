@@ -19,6 +19,7 @@ from .binding import (
     lora_plan_segments,
     lora_qkv,
     lora_qkv_noalloc,
+    lora_set_option,
     lora_shrink,
 )
 
@@ -28,5 +29,5 @@ calls()
 __all__ = [
     "ChunkedSgmvLoRA", "LoRABatchInfo", "SggError", "default_workspace", "lora_a_embedding",
     "lora_expand", "lora_plan_device", "lora_plan_lm_head", "lora_plan_max_segments", "lora_plan_segments",
-    "lora_qkv", "lora_qkv_noalloc", "lora_shrink",
+    "lora_qkv", "lora_qkv_noalloc", "lora_set_option", "lora_shrink",
 ]

@@ -232,6 +232,15 @@ def lora_plan_device(seq_lens, req_slots, lora_ranks, scalings, max_loras, is_de
         device_info.data_ptr(), _stream(device_plan)))
 
 
+def lora_set_option(name, value):
+    """Process-wide setting of the device calls ("fused_stacked": 1/0,
+    "spin_limit": polls); returns the previous value."""
+    old = lib().lora_set_option(name.encode(), int(value))
+    if old < 0:
+        raise ValueError(f"unknown option {name!r}")
+    return old
+
+
 # ----------------------------------------------------------------- workspace
 
 _workspaces = {}

@@ -8,7 +8,7 @@
 namespace sgg {
 namespace detail {
 
-template <int P, int KS>
+template <int P, int KS, bool FUSED = false>
 struct ExpandShape {
   static constexpr int TNW = 32 * P;                  // columns per wave
   static constexpr int CPR = 4 * KS;                  // 16-byte chunks per LDS h row (R <= 32*KS)
@@ -20,7 +20,15 @@ struct ExpandShape {
   static constexpr int HTILE_BYTES = 128 * CPR * 16;
   static constexpr int PROW_BYTES = 128 * 4;
   static constexpr int ACCT_BYTES = 4 * 16 * APAD * 4;
-  static constexpr int SMEM = HTILE_BYTES + PROW_BYTES + ACCT_BYTES;
+  // split-K partials of a pass of h rows, staged before they are summed
+  static constexpr int PSTAGE_BYTES = FUSED ? 32768 : 16384;
+  static constexpr int PSTAGE_OFF = HTILE_BYTES + PROW_BYTES + ACCT_BYTES;
+  static constexpr int SMEM = PSTAGE_OFF + PSTAGE_BYTES;
+};
+
+// No hand-off: h (or the partials) was written by an earlier launch.
+struct NoWait {
+  __device__ __forceinline__ bool operator()() const { return false; }
 };
 
 // Work item of block b: false for the padding blocks of the grid.
@@ -29,11 +37,16 @@ __device__ __forceinline__ bool expand_item_of(const ExpandParams& p, int b, int
   return *seg < p.num_segments;
 }
 
-// Column tile `tile` of segment `seg`; `smem` holds ExpandShape<P, KS>::SMEM
-// bytes (16-byte aligned).
-template <int P, int KS>
-__device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int tile, char* smem) {
-  using S = ExpandShape<P, KS>;
+// Column tile `tile` of segment `seg`; `smem` holds ExpandShape<P, KS, FUSED>::SMEM
+// bytes (16-byte aligned).  `wait()` runs once, by the whole workgroup, after
+// the B fragments are requested and before h is staged (the fused launch
+// waits there for its segment's partials; it may use `smem`).  It returns
+// true when it did other work meanwhile, and the B fragments are then
+// requested again rather than held across it.
+template <int P, int KS, bool FUSED = false, class Wait = NoWait>
+__device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int tile, char* smem,
+                                            const Wait& wait = Wait()) {
+  using S = ExpandShape<P, KS, FUSED>;
   constexpr int TNW = S::TNW;
   constexpr int CPR = S::CPR;
   constexpr int RPS = S::RPS;
@@ -69,32 +82,57 @@ __device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int 
   // Requested before the slot's rank arrives (every column j < R is in
   // bounds); columns at or beyond the rank are zeroed once it is known.
   uint4 bw[2 * P][KS];
+  const auto load_b = [&]() {
 #pragma unroll
-  for (int g = 0; g < 2 * P; ++g) {
-    const int n = colw + 16 * g + m;
-    const uint16_t* brow =
-        p.B + (static_cast<int64_t>(slot_ok ? slot : 0) * p.N + (n < colend ? n : 0)) * p.R;
+    for (int g = 0; g < 2 * P; ++g) {
+      const int n = colw + 16 * g + m;
+      const uint16_t* brow =
+          p.B + (static_cast<int64_t>(slot_ok ? slot : 0) * p.N + (n < colend ? n : 0)) * p.R;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int j = 32 * ks + 8 * q;
-      bw[g][ks] = make_uint4(0, 0, 0, 0);
-      if (active && n < colend && j < p.R) bw[g][ks] = load16(brow + j);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int j = 32 * ks + 8 * q;
+        bw[g][ks] = make_uint4(0, 0, 0, 0);
+        if (active && n < colend && j < p.R) bw[g][ks] = load16(brow + j);
+      }
     }
-  }
+  };
+  load_b();
   int rho = slot_ok ? p.ranks[slot] : 0;
   rho = rho < 0 ? 0 : (rho > p.R ? p.R : rho);
   if (rho == 0) return;  // base model: output rows stay untouched
   const float sigma = p.scalings[slot];
-#pragma unroll
-  for (int g = 0; g < 2 * P; ++g)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bw[g][ks] = keep_first(bw[g][ks], rho - (32 * ks + 8 * q));
-
   // Base-row role of this lane: row (RPL*i + lane/LPR) of a 16-token group,
   // columns colw + 8*(lane%LPR) .. +7.
   const int brw = lane / LPR;
   const int bc = colw + 8 * (lane % LPR);
   const bool bvec = p.vec8 && bc + 8 <= colend;
+  // FUSED: the base rows of the first two 16-token groups are requested
+  // before the wait, so they arrive while the shrink tiles run.
+  uint4 pre[2][BLD];
+  const auto prefetch = [&]() {
+    const int ntok0 = hi - lo < 128 ? hi - lo : 128;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int i = 0; i < BLD; ++i) {
+        const int rr = 16 * f + RPL * i + brw;
+        int r = rr < ntok0 ? p.perm[lo + rr] : -1;
+        r = (r >= 0 && r < p.s) ? r : -1;
+        pre[f][i] = make_uint4(0, 0, 0, 0);
+        if (r >= 0 && bvec && active)
+          pre[f][i] = *reinterpret_cast<const uint4*>(p.out + static_cast<int64_t>(r) * p.ldo + bc);
+      }
+  };
+  if constexpr (FUSED) prefetch();
+  if (wait()) {  // fragments and rows are in flight during a plain wait
+    load_b();
+    if constexpr (FUSED) prefetch();
+  }
+#pragma unroll
+  for (int g = 0; g < 2 * P; ++g)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bw[g][ks] = keep_first(bw[g][ks], rho - (32 * ks + 8 * q));
+
   const int hch = p.R >> 3;  // 16-byte chunks of one h row slice
   float* at = acct[wave];
 
@@ -106,22 +144,56 @@ __device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int 
       prow[tid] = (r >= 0 && r < p.s) ? r : -1;
     }
     if (p.hpart) {
-      // split-K partials, indexed by sorted position: no gather needed
-      for (int piece = tid; piece < ntok * hch; piece += 256) {
-        const int row = piece / hch, c = piece % hch;
-        const float* src = p.hpart + static_cast<int64_t>(c0 + row) * p.ldp + k * p.R + 8 * c;
-        f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-        for (int sp = 0; sp < p.hsplit; ++sp) {
-          const float* q = src + static_cast<int64_t>(sp) * p.s * p.ldp;
-          s0 += *reinterpret_cast<const f32x4*>(q);
-          s1 += *reinterpret_cast<const f32x4*>(q + 4);
+      // Split-K partials, indexed by sorted position (no gather), in passes
+      // of rows: every thread requests up to four 16-byte pieces (any row,
+      // column chunk, split) before storing them in the staging area, so a
+      // pass costs one round trip; then each (row, 8-column chunk) is summed
+      // in split order and rounded to bf16 into the h tile.
+      f32x4* pst = reinterpret_cast<f32x4*>(smem + S::PSTAGE_OFF);
+      const __amdgpu_buffer_rsrc_t prsrc = buffer_rsrc(p.hpart, p.hpart_bytes);
+      const int per_row = hch * 2 * p.hsplit;      // 16-byte pieces of one row
+      int rows_pp = (S::PSTAGE_BYTES / 16) / per_row;
+      rows_pp = rows_pp < 1 ? 1 : rows_pp;
+      for (int r0 = 0; r0 < ntok; r0 += rows_pp) {
+        const int rows = ntok - r0 < rows_pp ? ntok - r0 : rows_pp;
+        const int items = rows * per_row;
+        // item = ((sp * rows + row) * hch + c) * 2 + half
+        for (int q0 = tid; q0 < items; q0 += 4 * 256) {
+          f32x4 v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int qq = q0 + 256 * u;
+            const int q = qq < items ? qq : q0;
+            const int half = q & 1;
+            const int c = (q >> 1) % hch;
+            const int rs = (q >> 1) / hch;
+            const int row = rs % rows, sp = rs / rows;
+            const int64_t idx = (static_cast<int64_t>(sp) * p.s + (c0 + r0 + row)) * p.ldp +
+                                k * p.R + 8 * c + 4 * half;
+            v[u] = load_coherent16(prsrc, static_cast<uint32_t>(idx * 4));
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (q0 + 256 * u < items) pst[q0 + 256 * u] = v[u];
         }
-        uint4 v;
-        v.x = f32_to_bf16(s0[0]) | (f32_to_bf16(s0[1]) << 16);
-        v.y = f32_to_bf16(s0[2]) | (f32_to_bf16(s0[3]) << 16);
-        v.z = f32_to_bf16(s1[0]) | (f32_to_bf16(s1[1]) << 16);
-        v.w = f32_to_bf16(s1[2]) | (f32_to_bf16(s1[3]) << 16);
-        htile[row * CPR + (c ^ ((row / RPS) % CPR))] = v;
+        __syncthreads();
+        for (int piece = tid; piece < rows * hch; piece += 256) {
+          const int row = piece / hch, c = piece % hch;
+          f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+          for (int sp = 0; sp < p.hsplit; ++sp) {
+            const int q = ((sp * rows + row) * hch + c) * 2;
+            s0 += pst[q];
+            s1 += pst[q + 1];
+          }
+          uint4 v;
+          v.x = f32_to_bf16(s0[0]) | (f32_to_bf16(s0[1]) << 16);
+          v.y = f32_to_bf16(s0[2]) | (f32_to_bf16(s0[3]) << 16);
+          v.z = f32_to_bf16(s1[0]) | (f32_to_bf16(s1[1]) << 16);
+          v.w = f32_to_bf16(s1[2]) | (f32_to_bf16(s1[3]) << 16);
+          const int hr = r0 + row;
+          htile[hr * CPR + (c ^ ((hr / RPS) % CPR))] = v;
+        }
+        __syncthreads();
       }
     } else {
       for (int piece = tid; piece < ntok * hch; piece += 256) {
@@ -201,9 +273,22 @@ __device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int 
         }
       }
     };
-    fetch(0, bv0);
+    const bool use_pre = FUSED && c0 == lo;
+    if (use_pre) {
+#pragma unroll
+      for (int i = 0; i < BLD; ++i) bv0[i] = pre[0][i];
+    } else {
+      fetch(0, bv0);
+    }
     for (int f = 0; f < nf; f += 2) {
-      if (f + 1 < nf) fetch(f + 1, bv1);
+      if (f + 1 < nf) {
+        if (use_pre && f == 0) {
+#pragma unroll
+          for (int i = 0; i < BLD; ++i) bv1[i] = pre[1][i];
+        } else {
+          fetch(f + 1, bv1);
+        }
+      }
       step(f, bv0);
       if (f + 1 < nf) {
         if (f + 2 < nf) fetch(f + 2, bv0);

@@ -1,5 +1,6 @@
 // C-ABI device entry points: argument validation (host only, before anything
 // is enqueued), tile choice and kernel launches.
+#include <atomic>
 #include <cinttypes>
 #include <cstring>
 #include <mutex>
@@ -12,6 +13,11 @@
 using sgg::fail;
 
 namespace {
+
+// lora_set_option values.
+std::atomic<int64_t> g_fused_stacked{0};
+std::atomic<int64_t> g_fused_ksplit{0};
+std::atomic<int64_t> g_spin_limit{int64_t{1} << 20};
 
 #define SGG_CHECK(cond, code, ...) \
   do {                             \
@@ -92,19 +98,21 @@ int check_expand(const void* h, int64_t ldh, const void* B, int64_t N, const voi
 // 128 wins by 1-3 us on the 4096- and 6144-wide outputs of the full-layer and
 // skewed batches, whose grids are 5-10x smaller; 512 is slower everywhere.
 // Rank steps of 32.
+// `pairs` > 0 forces the column tile (128 * pairs).
 sgg::ExpandTiling choose_expand_tiling(const int32_t* offs, int c, int num_segments, int R,
-                                       int32_t* tile_start, int32_t* total) {
+                                       int32_t* tile_start, int32_t* total, int pairs = 0) {
   sgg::ExpandTiling t{};
   t.ks = R <= 32 ? 1 : (R <= 64 ? 2 : 4);
   t.pairs = 1;
-  for (int pairs : {2}) {
+  for (int cand : {2}) {
     int64_t tiles = 0;
-    for (int k = 0; k < c; ++k) tiles += (offs[k + 1] - offs[k] + 128 * pairs - 1) / (128 * pairs);
+    for (int k = 0; k < c; ++k) tiles += (offs[k + 1] - offs[k] + 128 * cand - 1) / (128 * cand);
     if (tiles * num_segments >= 4096) {
-      t.pairs = pairs;
+      t.pairs = cand;
       break;
     }
   }
+  if (pairs > 0) t.pairs = pairs;
   const int tn = 128 * t.pairs;
   int32_t acc = 0;
   for (int k = 0; k < c; ++k) {
@@ -161,6 +169,8 @@ sgg::ShrinkParams shrink_params(const void* x, int64_t ldx, const void* A, void*
   p.nblocks = t.nblocks;
   p.ksplit = t.ksplit;
   p.partials_only = partials_only && t.ksplit > 1 ? 1 : 0;
+  p.partial_bytes = static_cast<uint32_t>(t.partial_bytes < (int64_t{1} << 32) - 256
+                                              ? t.partial_bytes : 0);
   return p;
 }
 
@@ -176,6 +186,8 @@ int do_shrink(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh, i
               SGG_ERR_CAPACITY, "shrink workspace too small: %" PRId64
               " partial bytes needed, %" PRId64 " available", t.partial_bytes,
               partial ? partial_avail : 0);
+    SGG_CHECK(t.partial_bytes < (int64_t{1} << 32) - 256, SGG_ERR_UNSUPPORTED,
+              "split-K partials of %" PRId64 " bytes exceed 32-bit offsets", t.partial_bytes);
   }
   SGG_CHECK(t.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "shrink grid too large");
   const sgg::ShrinkParams p =
@@ -192,9 +204,9 @@ sgg::ExpandParams expand_params(const void* h, int64_t ldh, const void* B, int64
                                 const int32_t* seg_slots, int32_t num_segments,
                                 const int32_t* permutation, const int32_t* lora_ranks,
                                 const float* scalings, const float* hpart, int32_t hsplit,
-                                sgg::ExpandTiling* tiling) {
+                                sgg::ExpandTiling* tiling, int pairs = 0) {
   sgg::ExpandParams p{};
-  *tiling = choose_expand_tiling(offs, c, num_segments, R, p.tile_start, &p.total_tiles);
+  *tiling = choose_expand_tiling(offs, c, num_segments, R, p.tile_start, &p.total_tiles, pairs);
   bool vec8 = sgg::aligned16(out) && ldo % 8 == 0;
   for (int k = 0; k <= c; ++k) {
     p.offs[k] = offs[k];
@@ -204,6 +216,10 @@ sgg::ExpandParams expand_params(const void* h, int64_t ldh, const void* B, int64
   p.hpart = hpart;
   p.hsplit = hpart ? hsplit : 0;
   p.ldp = static_cast<int64_t>(c) * R;
+  {
+    const int64_t hb = static_cast<int64_t>(p.hsplit) * s * p.ldp * 4;
+    p.hpart_bytes = static_cast<uint32_t>(hb < (int64_t{1} << 32) - 256 ? hb : 0);
+  }
   p.B = static_cast<const uint16_t*>(B);
   p.out = static_cast<uint16_t*>(out);
   p.seg_indptr = seg_indptr;
@@ -252,10 +268,18 @@ extern "C" int64_t lora_qkv_workspace_bytes(int64_t s, int64_t in_dim, int32_t n
                                             int32_t R, int32_t num_segments, int32_t chunk_size) {
   if (s <= 0 || num_slices <= 0 || R <= 0) return 0;
   int64_t partial = 0;
-  if (in_dim > 0 && num_segments > 0 && chunk_size > 0)
-    partial = sgg::choose_shrink_tiling(s, in_dim, num_slices * R, num_segments, chunk_size)
-                  .partial_bytes;
-  return sgg::kCounterBytes + sgg::round_up(s * num_slices * R * 2, 256) + partial;
+  const int64_t CR = static_cast<int64_t>(num_slices) * R;
+  if (in_dim > 0 && num_segments > 0 && chunk_size > 0) {
+    const sgg::ShrinkTiling t =
+        sgg::choose_shrink_tiling(s, in_dim, static_cast<int>(CR), num_segments, chunk_size);
+    partial = t.partial_bytes;
+    // room for the one-launch form's partials (up to kFusedMaxSplit K ranges)
+    if (t.ksplit > 1 && CR <= 48) {
+      const int64_t fused = sgg::round_up(sgg::kFusedMaxSplit * s * CR * 4, 256);
+      partial = fused > partial ? fused : partial;
+    }
+  }
+  return sgg::kCounterBytes + sgg::round_up(s * CR * 2, 256) + partial;
 }
 
 extern "C" int lora_shrink(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh,
@@ -341,6 +365,8 @@ extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B
   const sgg::ShrinkTiling ts = sgg::choose_shrink_tiling(
       s, in_dim, num_slices * R, num_segments, chunk_size, gemm_addressable(s, ldx, in_dim, CR));
   SGG_CHECK(ts.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "shrink grid too large");
+  SGG_CHECK(ts.partial_bytes < (int64_t{1} << 32) - 256, SGG_ERR_UNSUPPORTED,
+            "split-K partials of %" PRId64 " bytes exceed 32-bit offsets", ts.partial_bytes);
   if (slice_offsets[num_slices] == 0) return sgg::ok();  // no output columns: nothing changes
   const bool split = ts.ksplit > 1;
   const sgg::ShrinkParams ps =
@@ -352,10 +378,62 @@ extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B
                     seg_indptr, seg_slots, num_segments, permutation, lora_ranks, scalings,
                     split ? part : nullptr, ts.ksplit, &te);
   SGG_CHECK(te.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "expand grid too large");
+  // The one-launch form (fused.hip), when asked for: a small batch whose
+  // shrink splits K (e.g. decode) and whose stacked rank rows fit one
+  // producer tile (c*R <= 48), if its grid -- producer tiles of its own
+  // tiling plus 128-column consumers -- fits on the device at once.  Its K
+  // split differs from the two-launch form's, so its bits can differ from
+  // it in rounding.  Measured on the decode batch it is slower than the two
+  // launches (a longer chain of dependent device-wide memory round trips), so
+  // it is off by default.
+  if (g_fused_stacked.load(std::memory_order_relaxed) != 0 && split && CR <= 48 &&
+      num_segments <= sgg::kFusedMaxSegments) {
+    sgg::ExpandTiling tf{};
+    sgg::ExpandParams pf =
+        expand_params(h, CR, B, N, base_output, ldo, s, num_loras, R, slice_offsets, num_slices,
+                      seg_indptr, seg_slots, num_segments, permutation, lora_ranks, scalings,
+                      part, 0, &tf, 1);
+    const sgg::ShrinkTiling tp = tf.ks <= 2
+        ? sgg::choose_fused_tiling(s, in_dim, static_cast<int>(CR), num_segments, chunk_size,
+                                   tf.grid, tf.ks, -1,
+                                   static_cast<int>(g_fused_ksplit.load(std::memory_order_relaxed)))
+        : sgg::ShrinkTiling{};
+    const int64_t per_seg = static_cast<int64_t>(tp.mblocks) * tp.nblocks * tp.ksplit;
+    const int64_t avail = workspace_bytes - sgg::kCounterBytes - hbytes;
+    if (tp.grid > 0 && per_seg < 65536 && per_seg + pf.total_tiles < 32768 &&
+        tp.grid + tf.grid < (int64_t{1} << 31) && tp.partial_bytes <= avail &&
+        tp.partial_bytes < (int64_t{1} << 32) - 256) {
+      const sgg::ShrinkParams pp =
+          shrink_params(x, ldx, A, h, CR, s, in_dim, num_loras, num_slices, R, seg_indptr,
+                        seg_slots, num_segments, permutation, lora_ranks, counters, part, true,
+                        tp);
+      pf.hsplit = tp.ksplit;
+      pf.hpart_bytes = static_cast<uint32_t>(tp.partial_bytes);
+      sgg::FusedSync fs{};
+      fs.ready = counters + sgg::kFusedReady;
+      fs.status = counters + sgg::kFusedStatus;
+      fs.producer_blocks = static_cast<int32_t>(tp.grid);
+      fs.producers_per_seg = static_cast<int32_t>(per_seg);
+      fs.consumers_per_seg = pf.total_tiles;
+      fs.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+      rc = launch_status(sgg::launch_fused(pp, tp, pf, tf, fs, st), "fused stacked call");
+      return rc ? rc : sgg::ok();
+    }
+  }
   rc = launch_status(sgg::launch_shrink(ps, ts, st), "shrink");
   if (rc) return rc;
   rc = launch_status(sgg::launch_expand(pe, te, st), "expand");
   return rc ? rc : sgg::ok();
+}
+
+extern "C" int64_t lora_set_option(const char* name, int64_t value) {
+  if (name == nullptr) return -1;
+  if (std::strcmp(name, "fused_stacked") == 0) return g_fused_stacked.exchange(value != 0);
+  if (std::strcmp(name, "spin_limit") == 0)
+    return g_spin_limit.exchange(value < 0 ? 0 : value);
+  if (std::strcmp(name, "fused_ksplit") == 0)
+    return g_fused_ksplit.exchange(value < 0 ? 0 : value);
+  return -1;
 }
 
 // ------------------------------------------------------- no-allocation qkv

@@ -54,6 +54,41 @@ __device__ __forceinline__ f32x4 mfma16x16x32(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (32-bit data format):
+// loads at or past the end return zero and stores there are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// 16 bytes at byte offset `off` of a buffer, with device-scope coherence
+// (the sc1 cache policy: the access sees, and is seen by, the other
+// workgroups of the device -- what an agent-scope atomic access does, 16
+// bytes at a time and without waiting for each access).
+constexpr int kDeviceScopePolicy = 16;
+__device__ __forceinline__ f32x4 load_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       r, static_cast<int>(off), 0, kDeviceScopePolicy));
+}
+__device__ __forceinline__ void store_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                 f32x4 v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r,
+                                         static_cast<int>(off), 0, kDeviceScopePolicy);
+}
+
+// Wait until this wave's outstanding vector memory operations have completed
+// (also a compiler memory barrier).  Cross-workgroup hand-offs publish data
+// with device-coherent stores (store_coherent16), which write through to the
+// point of coherence of the whole device; once every wave of the workgroup
+// has waited for its own stores, a barrier and one counter RMW make the data
+// safe to read with device-coherent loads from any XCD.  No L2 write-back (release) or
+// invalidate (acquire) is needed for data moved that way, and both are
+// costly here: a write-back per wave doubled the decode shrink's time.
+__device__ __forceinline__ void wave_stores_done() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // Blocks are handed to the XCDs round-robin (block b runs on XCD b % 8).
 // Segments are dealt round-robin to the XCDs the same way: block b takes
 // segment (b % 8) + 8 * ((b / 8) / per) and item (b / 8) % per of it, so the

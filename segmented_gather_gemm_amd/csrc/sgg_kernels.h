@@ -7,11 +7,17 @@
 namespace sgg {
 
 constexpr int kMaxSlices = 8;
-// Split-K arrival counters sit in a fixed region at the start of every
-// workspace, so a counter location never holds anything but a counter (each
-// call leaves its counters at zero) whatever the shapes of earlier calls.
-constexpr int64_t kCounterBytes = 32768;
-constexpr int kCounterCap = static_cast<int>(kCounterBytes / 4);
+// Counters sit in a fixed region at the start of every workspace, so a
+// counter location never holds anything but a counter (each call leaves its
+// counters at zero) whatever the shapes of earlier calls.  Words [0, 8192):
+// split-K arrival counters; [8192, 16383): the fused stacked call's
+// per-segment hand-off words; word 16383: its give-up status (sticky; byte
+// offset SGG_WORKSPACE_STATUS_OFFSET).
+constexpr int64_t kCounterBytes = 65536;
+constexpr int kCounterCap = 8192;
+constexpr int kFusedReady = 8192;
+constexpr int kFusedStatus = 16383;
+constexpr int kFusedMaxSegments = kFusedStatus - kFusedReady;
 
 // LoRA-A shrink over the segments of a plan.
 struct ShrinkParams {
@@ -31,6 +37,7 @@ struct ShrinkParams {
   int32_t ksplit;             // K ranges (one workgroup each)
   int32_t counter_cap;        // entries in `counters`
   int32_t partials_only;      // ksplit > 1: leave the partials for the expand, write no h
+  uint32_t partial_bytes;     // size of `partial` (below 2^32)
 };
 
 // LoRA-B expand (scale, add into base) over the segments of a plan.
@@ -49,6 +56,7 @@ struct ExpandParams {
   const float* hpart;
   int64_t ldp;
   int32_t hsplit;
+  uint32_t hpart_bytes;       // size of the partials (below 2^32)
   int64_t ldh, ldo, s, N;
   int32_t L, R, c, num_segments;
   int32_t vec8;               // 16-byte base access is aligned for every group of 8 columns
@@ -56,6 +64,24 @@ struct ExpandParams {
   int32_t tile_start[kMaxSlices + 1];  // first column tile of each slice
   int32_t total_tiles;
 };
+// Cross-workgroup hand-off of the fused stacked call (fused.hip): producer
+// blocks [0, producer_blocks) run the split-K shrink tiles and count
+// themselves in bits 0-15 of their segment's word ready[seg] once their
+// partials are published; consumer blocks run the expand tiles and wait for
+// that count to reach producers_per_seg before staging h.  Every block of a
+// segment also counts itself in bits 16-30; the last of the
+// producers_per_seg + consumers_per_seg resets the word to zero.  A wait
+// gives up after spin_limit polls: the consumer then computes its segment's
+// partials itself (the same bits) and sets bit 0 of *status.
+struct FusedSync {
+  int32_t* ready;
+  int32_t* status;
+  int32_t producer_blocks;
+  int32_t producers_per_seg;
+  int32_t consumers_per_seg;
+  int64_t spin_limit;
+};
+
 // Grid of a segment_round_robin launch: whole rounds of 8 segments.
 inline int64_t grid_for(int num_segments, int64_t per_segment) {
   return static_cast<int64_t>((num_segments + 7) / 8) * 8 * per_segment;
@@ -99,6 +125,24 @@ hipError_t launch_shrink_gemm(const ShrinkParams& p, int bm, int bn, int64_t gri
                               hipStream_t stream);
 hipError_t launch_expand(const ExpandParams& p, const ExpandTiling& t, hipStream_t stream);
 hipError_t launch_embedding(const EmbeddingParams& p, hipStream_t stream);
+
+// The stacked shrink + expand in one launch (fused.hip): producer tiles of
+// 16*mf tokens x 16*nf rank rows (mf <= 2, nf <= 3; partials only), consumer
+// tiles of 128 columns (pairs = 1, ks <= 2), at most kFusedMaxSegments
+// segments.  fused_resident_blocks() is how many blocks of that launch the
+// device keeps resident at once (0 if unknown or no such instance); the host
+// takes the fused launch only when the whole grid fits.
+int64_t fused_resident_blocks(int mf, int nf, int ks);
+// Producer tiling of the fused launch for a batch whose shrink splits K:
+// 16*mf tokens x all c*R rank rows per tile, and the largest K split (at
+// most kFusedMaxSplit ranges of at least 256, or `force_ksplit` if > 0)
+// whose grid, with `consumers` expand blocks, fits `resident` blocks
+// (resident < 0: query fused_resident_blocks).  grid == 0: no fused launch.
+constexpr int kFusedMaxSplit = 16;
+ShrinkTiling choose_fused_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk,
+                                 int64_t consumers, int ks, int64_t resident, int force_ksplit);
+hipError_t launch_fused(const ShrinkParams& ps, const ShrinkTiling& ts, const ExpandParams& pe,
+                        const ExpandTiling& te, const FusedSync& fs, hipStream_t stream);
 
 // The batch plan on the GPU (plan_device.hip): one workgroup; up to
 // kDevicePlanMaxReqs requests and kDevicePlanMaxLoras slots.

@@ -225,21 +225,20 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int seg, int 
           o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
           *reinterpret_cast<uint2*>(p.h + static_cast<int64_t>(r) * p.ldh + n) = o;
         } else {
-          // written through to the agent's coherence point (no dirty L2 lines)
-          float* dst = p.partial + (static_cast<int64_t>(split) * p.s + (m0 + mm)) * p.CR + n;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            __hip_atomic_store(dst + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          // written through to the device's coherence point (no dirty L2 lines)
+          const int64_t idx = (static_cast<int64_t>(split) * p.s + (m0 + mm)) * p.CR + n;
+          store_coherent16(buffer_rsrc(p.partial, p.partial_bytes),
+                           static_cast<uint32_t>(idx * 4), v);
         }
       }
     }
     if (direct || p.partials_only) continue;
 
     // Split-K: publish this partial, count arrivals, the last one reduces.
-    // One release (thread 0, after the barrier that orders the whole
-    // workgroup's partial stores before it) per workgroup, and one acquire
-    // in the last arriver only: agent-scope fences write back / invalidate
-    // the XCD's L2, so they are kept off every other path.
+    // The partials went out as agent-scope atomic stores: every wave waits
+    // for its own, then the barrier, then one counter RMW (see
+    // wave_stores_done); the last arriver reads them with agent-scope loads.
+    wave_stores_done();
     __syncthreads();
     // (lo / BM + seg + mb) is distinct for every (segment, row block) of a
     // CSR plan, so every tile has its own counter; the clamp only keeps a
@@ -247,11 +246,9 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int seg, int 
     int64_t cidx = (static_cast<int64_t>(lo / BM) + seg + mb) * p.nblocks + nb;
     if (cidx >= p.counter_cap) cidx = p.counter_cap - 1;
     if (tid == 0) {
-      const int old = __hip_atomic_fetch_add(p.counters + cidx, 1, __ATOMIC_RELEASE,
+      const int old = __hip_atomic_fetch_add(p.counters + cidx, 1, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = old == p.ksplit - 1;
-      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      last_flag = last;
+      last_flag = old == p.ksplit - 1;
     }
     __syncthreads();
     if (!last_flag) continue;
@@ -262,12 +259,21 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int seg, int 
       if (n >= p.CR) continue;
       const int r = p.perm[m0 + mm];
       if (r < 0 || r >= p.s) continue;
+      // Four splits' loads in flight at a time, summed in split order (the
+      // order in which the stacked call's expand sums them too).
+      const __amdgpu_buffer_rsrc_t prsrc = buffer_rsrc(p.partial, p.partial_bytes);
       f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int sp = 0; sp < p.ksplit; ++sp) {
-        const float* src = p.partial + (static_cast<int64_t>(sp) * p.s + (m0 + mm)) * p.CR + n;
+      for (int sp0 = 0; sp0 < p.ksplit; sp0 += 4) {
+        f32x4 w[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          v[i] += __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int u = 0; u < 4; ++u) {
+          const int sp = sp0 + u < p.ksplit ? sp0 + u : sp0;
+          const int64_t idx = (static_cast<int64_t>(sp) * p.s + (m0 + mm)) * p.CR + n;
+          w[u] = load_coherent16(prsrc, static_cast<uint32_t>(idx * 4));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (sp0 + u < p.ksplit) v += w[u];
       }
       uint2 o;
       o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);

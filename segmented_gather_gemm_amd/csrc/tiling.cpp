@@ -124,4 +124,43 @@ ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments
   return t;
 }
 
+// Producer tiling of the one-launch stacked call.  A decode batch's shrink is
+// a chain of dependent memory round trips (plan, operands, partials) more
+// than a stream of bytes, so the producers cover all c*R rank rows and up to
+// 64 tokens each (x read once per K range, no cross-tile re-reads of A), and
+// K is split as finely as the device can hold alongside the consumers: more
+// ranges shorten each producer's load, at the price of more partials for the
+// consumers to sum.
+ShrinkTiling choose_fused_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk,
+                                 int64_t consumers, int ks, int64_t resident, int force_ksplit) {
+  ShrinkTiling t{};
+  const int nf = (CR + 15) / 16;
+  if (nf > 3 || num_segments <= 0 || s <= 0 || K <= 0) return t;
+  const int64_t kgroups = (K + 255) / 256;
+  // tallest tile that covers the longest segment first (no empty producers),
+  // then shorter ones if its grid does not fit
+  for (int mf : {4, 2, 1}) {
+    if (mf > 1 && chunk <= 8 * mf) continue;   // a half-empty tile: take the next one
+    const int64_t res = resident >= 0 ? resident : fused_resident_blocks(mf, nf, ks);
+    const int64_t mblocks = (chunk + 16 * mf - 1) / (16 * mf);
+    for (int want = kFusedMaxSplit; want >= 2; want /= 2) {   // partials need a split
+      if (force_ksplit > 0 && want != force_ksplit) continue;
+      const int64_t kps = (kgroups + want - 1) / want * 256;
+      const int64_t ksplit = (K + kps - 1) / kps;
+      const int64_t grid = grid_for(num_segments, mblocks * ksplit);
+      if (ksplit < 2 || grid + consumers > res) continue;
+      t.mf = mf;
+      t.nf = nf;
+      t.mblocks = static_cast<int>(mblocks < 1 ? 1 : mblocks);
+      t.nblocks = 1;
+      t.ksplit = static_cast<int>(ksplit);
+      t.kps = kps;
+      t.partial_bytes = round_up(ksplit * s * CR * 4, 256);
+      t.grid = grid;
+      return t;
+    }
+  }
+  return t;
+}
+
 }  // namespace sgg

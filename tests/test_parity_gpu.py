@@ -21,6 +21,7 @@ from synth import Batch, Projection, draw_batch, draw_embedding, draw_projection
 pytestmark = pytest.mark.gpu
 
 ATOL = RTOL = 1e-2
+COUNTER_BYTES = 65536   # workspace counter region (and the fused call's status word)
 
 
 def _sgg():
@@ -95,6 +96,39 @@ def sample_rows(ref, s, n_random=768, seed=0):
     rng = np.random.default_rng(seed)
     rows.update(rng.integers(0, s, size=min(n_random, s)).tolist())
     return np.array(sorted(rows), dtype=np.int64)
+
+
+class fused_stacked:
+    """Context: lora_qkv in its one-launch form (lora_set_option
+    "fused_stacked" = 1) inside, the default two-launch form after."""
+
+    def __enter__(self):
+        self.old = _sgg().lora_set_option("fused_stacked", 1)
+
+    def __exit__(self, *exc):
+        _sgg().lora_set_option("fused_stacked", self.old)
+
+
+def stacked_both_forms(x, A, Bw, info, offs, wide, base, ws):
+    """lora_qkv in its default two-launch form and in its one-launch form;
+    returns both results (the one-launch form twice, asserted identical)."""
+    sgg = _sgg()
+    y = sgg.lora_qkv(x, A, Bw, info, offs, wide, base.clone(), workspace=ws)
+    with fused_stacked():
+        yf = sgg.lora_qkv(x, A, Bw, info, offs, wide, base.clone(), workspace=ws)
+        yf2 = sgg.lora_qkv(x, A, Bw, info, offs, wide, base.clone(), workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(yf, yf2)
+    return y, yf
+
+
+def own_plan(info):
+    """A copy of a plan whose device arrays belong to it alone (the backend's
+    ring keeps 8 live plans)."""
+    import dataclasses
+    return dataclasses.replace(info, **{
+        f.name: getattr(info, f.name).clone() for f in dataclasses.fields(info)
+        if isinstance(getattr(info, f.name), torch.Tensor)})
 
 
 def backend(b, max_chunk=None):
@@ -176,9 +210,10 @@ def test_decode_full():
 ])
 def test_stacked_call_matches_separate_calls(case):
     """lora_qkv on small batches (split K: the expand sums the shrink's
-    partials itself) gives the same bits as lora_shrink (whose last
-    arriving workgroup sums them) followed by lora_expand, matches the
-    oracle, and leaves the workspace counter region at zero."""
+    partials itself) gives the same bits as lora_shrink (whose last arriving
+    workgroup sums them) followed by lora_expand, call after call, and matches
+    the oracle; its one-launch form matches the oracle and repeats bit for
+    bit; the workspace counter region is left at zero."""
     sgg = _sgg()
     seed, s, L, c, R, K = case
     rng = np.random.default_rng(seed)
@@ -199,7 +234,126 @@ def test_stacked_call_matches_separate_calls(case):
         y = sgg.lora_qkv(x, A, Bw, info, offs, max(width), base.clone(), workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(y, y_sep), (seed, rep)
-        assert not ws[:32768].any(), (seed, rep)
+        assert not ws[:COUNTER_BYTES].any(), (seed, rep)
+    _, yf = stacked_both_forms(x, A, Bw, info, offs, max(width), base, ws)
+    assert_close(yf, want_y, f"case {seed} one launch")
+    assert not ws[:COUNTER_BYTES].any(), seed
+
+
+def _decode_case(seed, s=256, L=8, c=3, R=16, K=4096):
+    rng = np.random.default_rng(seed)
+    slots = rng.integers(0, L, size=s).tolist()
+    width = [4096, 1024, 1024][:c] if K == 4096 else [512] * c
+    offs = np.concatenate([[0], np.cumsum(width)]).tolist()
+    b, proj, t = _small_case(seed, [1] * s, slots, L, [R] * L,
+                             rng.uniform(0.5, 2.0, size=L).tolist(), K, offs, R)
+    return b, proj, t, offs, max(width)
+
+
+def test_fused_stacked_call_over_changing_plans():
+    """One-launch stacked calls on decode batches whose plans change from call
+    to call (segment counts 5..16, different token counts), back to back on
+    one workspace: every call matches the oracle and repeats bit for bit,
+    and the hand-off words and the status word end at zero."""
+    sgg = _sgg()
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    cases = [(71, 256, 8), (72, 100, 5), (73, 256, 16), (74, 37, 3), (75, 512, 12)]
+    outs = []
+    for seed, s, L in cases:
+        b, proj, t, offs, wide = _decode_case(seed, s=s, L=L)
+        be = backend(b)
+        info = own_plan(plan_on(be, b))
+        x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+        with fused_stacked():
+            y = sgg.lora_qkv(x, A, Bw, info, offs, wide, base.clone(), workspace=ws)
+            y2 = sgg.lora_qkv(x, A, Bw, info, offs, wide, base.clone(), workspace=ws)
+        outs.append((b, proj, t, y, y2))
+    torch.cuda.synchronize()
+    for b, proj, t, y, y2 in outs:
+        assert torch.equal(y, y2), b.seed
+        _, want_y = oracle_forward(t, b, proj)
+        assert_close(y, want_y, f"fused {b.seed}")
+    assert not ws[:COUNTER_BYTES].any()
+
+
+def test_fused_wait_gives_up_and_recomputes():
+    """With a spin limit of 0 the one-launch call's consumers give up on a
+    producer that has not published yet (the shrink tiles take microseconds;
+    a limit of 0 polls once), compute their segment's partials themselves and
+    set the status word: the result is still bit-identical to the one-launch
+    call that waited, and the hand-off words still end at zero."""
+    sgg = _sgg()
+    b, proj, t, offs, wide = _decode_case(76)
+    be = backend(b)
+    info = plan_on(be, b)
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    with fused_stacked():
+        y_ref = sgg.lora_qkv(x, A, Bw, info, offs, wide, base.clone(), workspace=ws)
+        torch.cuda.synchronize()
+        assert not ws[:COUNTER_BYTES].any()
+        old = sgg.lora_set_option("spin_limit", 0)
+        try:
+            y = sgg.lora_qkv(x, A, Bw, info, offs, wide, base.clone(), workspace=ws)
+        finally:
+            sgg.lora_set_option("spin_limit", old)
+        torch.cuda.synchronize()
+        status = int(ws[COUNTER_BYTES - 4:COUNTER_BYTES].view(torch.int32).item())
+        assert status == 1, status
+        assert torch.equal(y, y_ref)
+        assert not ws[:COUNTER_BYTES - 4].any()
+        ws.zero_()
+        y = sgg.lora_qkv(x, A, Bw, info, offs, wide, base.clone(), workspace=ws)
+        torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    assert not ws[:COUNTER_BYTES].any()
+    _, want_y = oracle_forward(t, b, proj)
+    assert_close(y, want_y, "one launch after give-up")
+
+
+def test_fused_stacked_call_in_a_graph():
+    """The one-launch stacked call captured in a graph over a capacity plan
+    (trailing segments empty): replays with new plans, eager work and
+    synchronisations between them, each checked against the oracle, and the
+    hand-off words back at zero after every replay."""
+    sgg = _sgg()
+    L, R, max_bs = 8, 16, 256
+    b0, proj, t, offs, wide = _decode_case(77, s=max_bs, L=L)
+    x, A, Bw = (t[k].to(DEV) for k in ("x", "A", "B"))
+    base0 = t["base"].to(DEV)
+    base = base0.clone()
+    ws = torch.zeros(16 << 20, dtype=torch.uint8, device=DEV)
+    be = sgg.ChunkedSgmvLoRA(L, 128, DEV)
+    info = be.init_cuda_graph_batch_info(max_bs, 1)
+    be.prepare_lora_batch(None, b0.req_slots, b0.lora_ranks, b0.scalings, is_decode=True,
+                          use_cuda_graph=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with fused_stacked():
+        with torch.cuda.stream(side):
+            sgg.lora_qkv(x, A, Bw, info, offs, wide, base, workspace=ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sgg.lora_qkv(x, A, Bw, info, offs, wide, base, workspace=ws)
+        torch.cuda.synchronize()
+    rng = np.random.default_rng(78)
+    for trial in range(4):
+        active = rng.integers(1, L + 1)
+        slots = rng.integers(0, active, size=max_bs).tolist()
+        be.prepare_lora_batch(None, slots, b0.lora_ranks, b0.scalings, is_decode=True,
+                              use_cuda_graph=True)
+        base.copy_(base0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert not ws[:COUNTER_BYTES].any(), trial
+        b = Batch("g", 0, [1] * max_bs, slots, True, L, b0.lora_ranks, b0.scalings, 128,
+                  b0.projections)
+        _, want_y = oracle_forward(t, b, proj)
+        assert_close(base, want_y, f"fused graph replay {trial}")
+        torch.mm(torch.randn(64, 64, device=DEV), torch.randn(64, 64, device=DEV))
 
 
 @pytest.fixture(scope="module")
@@ -416,11 +570,11 @@ def test_strided_x(case):
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
     h = sgg.lora_shrink(xs, A, info, c, workspace=ws)
     y_sep = sgg.lora_expand(h, Bw, info, offs, max(np.diff(offs)), base.clone())
-    y = sgg.lora_qkv(xs, A, Bw, info, offs, max(np.diff(offs)), base.clone(), workspace=ws)
-    torch.cuda.synchronize()
+    y, yf = stacked_both_forms(xs, A, Bw, info, offs, max(np.diff(offs)), base, ws)
     want_h, want_y = oracle_forward(t, b, proj)
     assert_close(h, want_h, f"strided x ({case}) h")
     assert_close(y_sep, want_y, f"strided x ({case}) y")
+    assert_close(yf, want_y, f"strided x ({case}) one-launch y")
     assert torch.equal(y, y_sep)
 
 
@@ -451,13 +605,13 @@ def test_tiles_past_the_rank(case):
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
     h = sgg.lora_shrink(x, A, info, c, workspace=ws)
     y_sep = sgg.lora_expand(h, Bw, info, offs, max(np.diff(offs)), base.clone())
-    y = sgg.lora_qkv(x, A, Bw, info, offs, max(np.diff(offs)), base.clone(), workspace=ws)
-    torch.cuda.synchronize()
+    y, yf = stacked_both_forms(x, A, Bw, info, offs, max(np.diff(offs)), base, ws)
     want_h, want_y = oracle_forward(t, b, proj)
     assert_close(h, want_h, f"past-rank tiles ({case}) h")
     assert_close(y_sep, want_y, f"past-rank tiles ({case}) y")
+    assert_close(yf, want_y, f"past-rank tiles ({case}) one-launch y")
     assert torch.equal(y, y_sep)
-    assert not ws[:32768].any()
+    assert not ws[:COUNTER_BYTES].any()
 
 
 def test_long_k_small_grid():
@@ -479,14 +633,13 @@ def test_long_k_small_grid():
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
     h = sgg.lora_shrink(x, A, info, 2, workspace=ws)
     y_sep = sgg.lora_expand(h, Bw, info, proj.slice_offsets, proj.max_slice, base.clone())
-    y = sgg.lora_qkv(x, A, Bw, info, proj.slice_offsets, proj.max_slice, base.clone(),
-                     workspace=ws)
-    torch.cuda.synchronize()
+    y, yf = stacked_both_forms(x, A, Bw, info, proj.slice_offsets, proj.max_slice, base, ws)
     want_h, want_y = oracle_forward(t, b, proj)
     assert_close(h, want_h, "long-K h")
     assert_close(y_sep, want_y, "long-K y (separate)")
+    assert_close(yf, want_y, "long-K y (one launch)")
     assert torch.equal(y, y_sep)
-    assert not ws[:32768].any()
+    assert not ws[:COUNTER_BYTES].any()
 
 
 def test_short_segments_in_groups():
