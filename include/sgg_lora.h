@@ -359,6 +359,9 @@ int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B, int64_t N
  *   "fused_ksplit"   K ranges of the one-launch call's shrink tiles (0, the
  *                    default: the most that fit; 2..16 forces that many when
  *                    they fit).
+ *   "expand_deal_tiles"  1 (default): the expand deals column tiles to the
+ *                    XCDs (an adapter's B columns stay in each L2 across its
+ *                    segments); 0: it deals segments.  Same results.
  */
 int64_t lora_set_option(const char* name, int64_t value);
 

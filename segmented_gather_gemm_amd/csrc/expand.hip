@@ -27,24 +27,29 @@ namespace sgg {
 
 namespace {
 
-template <int P, int KS>
+template <int P, int KS, bool HPART>
 __global__ __launch_bounds__(256) void expand_kernel(ExpandParams p) {
   __shared__ __attribute__((aligned(16))) char smem[detail::ExpandShape<P, KS>::SMEM];
   int seg, tile;
   if (!detail::expand_item_of(p, blockIdx.x, &seg, &tile)) return;
-  detail::expand_tile<P, KS>(p, seg, tile, smem);
+  detail::expand_tile<P, KS, HPART>(p, seg, tile, smem);
+}
+
+template <int P, bool HPART>
+hipError_t launch_ph(const ExpandParams& p, int ks, int64_t grid, hipStream_t stream) {
+  const dim3 g(static_cast<unsigned>(grid)), b(256);
+  switch (ks) {
+    case 1: hipLaunchKernelGGL((expand_kernel<P, 1, HPART>), g, b, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((expand_kernel<P, 2, HPART>), g, b, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((expand_kernel<P, 4, HPART>), g, b, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <int P>
 hipError_t launch_p(const ExpandParams& p, int ks, int64_t grid, hipStream_t stream) {
-  const dim3 g(static_cast<unsigned>(grid)), b(256);
-  switch (ks) {
-    case 1: hipLaunchKernelGGL((expand_kernel<P, 1>), g, b, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((expand_kernel<P, 2>), g, b, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((expand_kernel<P, 4>), g, b, 0, stream, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return p.hpart ? launch_ph<P, true>(p, ks, grid, stream) : launch_ph<P, false>(p, ks, grid, stream);
 }
 
 }  // namespace

@@ -20,10 +20,13 @@ struct ExpandShape {
   static constexpr int HTILE_BYTES = 128 * CPR * 16;
   static constexpr int PROW_BYTES = 128 * 4;
   static constexpr int ACCT_BYTES = 4 * 16 * APAD * 4;
-  // split-K partials of a pass of h rows, staged before they are summed
-  static constexpr int PSTAGE_BYTES = FUSED ? 32768 : 16384;
-  static constexpr int PSTAGE_OFF = HTILE_BYTES + PROW_BYTES + ACCT_BYTES;
-  static constexpr int SMEM = PSTAGE_OFF + PSTAGE_BYTES;
+  // Split-K partials of a pass of h rows, staged before they are summed.
+  // The area is the transpose tile's, which is idle while h is staged (the
+  // one-launch form, whose LDS is sized by its shrink tiles anyway, gets a
+  // larger one): an expand that reads h keeps its occupancy.
+  static constexpr int PSTAGE_BYTES = FUSED ? 32768 : ACCT_BYTES;
+  static constexpr int PSTAGE_OFF = HTILE_BYTES + PROW_BYTES;
+  static constexpr int SMEM = PSTAGE_OFF + (ACCT_BYTES > PSTAGE_BYTES ? ACCT_BYTES : PSTAGE_BYTES);
 };
 
 // No hand-off: h (or the partials) was written by an earlier launch.
@@ -32,7 +35,23 @@ struct NoWait {
 };
 
 // Work item of block b: false for the padding blocks of the grid.
+//
+// Column tiles dealt to the XCDs (tiles_per_xcd > 0): block b runs on XCD
+// x = b % 8 and takes tile x + 8*j of segment seg, walking its share of the
+// tiles of segment 0, then of segment 1, and so on.  Each XCD thus needs only
+// one eighth of an adapter's B columns, and reuses them from its L2 across
+// the adapter's consecutive segments while they are hot; every XCD gets an
+// equal share of every segment, however the tokens fall on the adapters; the
+// h rows of a segment are read by all eight XCDs (they are a small fraction
+// of the bytes).  Otherwise segments are dealt to the XCDs
+// (segment_round_robin): all tiles of a segment on one XCD.
 __device__ __forceinline__ bool expand_item_of(const ExpandParams& p, int b, int* seg, int* tile) {
+  if (p.tiles_per_xcd > 0) {
+    const int x = b % kXcds, l = b / kXcds;
+    *seg = l / p.tiles_per_xcd;
+    *tile = (l % p.tiles_per_xcd) * kXcds + x;
+    return *seg < p.num_segments && *tile < p.total_tiles;
+  }
   segment_round_robin(b, p.total_tiles, seg, tile);
   return *seg < p.num_segments;
 }
@@ -43,7 +62,10 @@ __device__ __forceinline__ bool expand_item_of(const ExpandParams& p, int b, int
 // waits there for its segment's partials; it may use `smem`).  It returns
 // true when it did other work meanwhile, and the B fragments are then
 // requested again rather than held across it.
-template <int P, int KS, bool FUSED = false, class Wait = NoWait>
+// HPART: h comes as split-K partials (p.hpart), else as bf16 rows (p.h); a
+// template flag, so an instance carries only the staging code it runs (the
+// other path's loads otherwise cost the main loop its wait counts).
+template <int P, int KS, bool HPART, bool FUSED = false, class Wait = NoWait>
 __device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int tile, char* smem,
                                             const Wait& wait = Wait()) {
   using S = ExpandShape<P, KS, FUSED>;
@@ -143,7 +165,7 @@ __device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int 
       const int r = p.perm[c0 + tid];
       prow[tid] = (r >= 0 && r < p.s) ? r : -1;
     }
-    if (p.hpart) {
+    if constexpr (HPART) {
       // Split-K partials, indexed by sorted position (no gather), in passes
       // of rows: every thread requests up to four 16-byte pieces (any row,
       // column chunk, split) before storing them in the staging area, so a

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void fused_kernel(ShrinkParams ps, ExpandParam
     __syncthreads();
     return true;
   };
-  detail::expand_tile<1, KS, true>(pe, seg, tile, smem, wait);
+  detail::expand_tile<1, KS, true, true>(pe, seg, tile, smem, wait);
   __syncthreads();
   if (threadIdx.x == 0) arrive(fs, seg, kDoneUnit);
 }

@@ -17,6 +17,7 @@ namespace {
 // lora_set_option values.
 std::atomic<int64_t> g_fused_stacked{0};
 std::atomic<int64_t> g_fused_ksplit{0};
+std::atomic<int64_t> g_expand_deal_tiles{1};
 std::atomic<int64_t> g_spin_limit{int64_t{1} << 20};
 
 #define SGG_CHECK(cond, code, ...) \
@@ -98,9 +99,13 @@ int check_expand(const void* h, int64_t ldh, const void* B, int64_t N, const voi
 // 128 wins by 1-3 us on the 4096- and 6144-wide outputs of the full-layer and
 // skewed batches, whose grids are 5-10x smaller; 512 is slower everywhere.
 // Rank steps of 32.
-// `pairs` > 0 forces the column tile (128 * pairs).
+// `pairs` > 0 forces the column tile (128 * pairs).  `deal_tiles`: column
+// tiles dealt to the XCDs (expand_item_of); *tiles_per_xcd gets their count
+// per XCD (0: segments dealt instead).
 sgg::ExpandTiling choose_expand_tiling(const int32_t* offs, int c, int num_segments, int R,
-                                       int32_t* tile_start, int32_t* total, int pairs = 0) {
+                                       int32_t* tile_start, int32_t* total,
+                                       int32_t* tiles_per_xcd, int pairs = 0,
+                                       bool deal_tiles = false) {
   sgg::ExpandTiling t{};
   t.ks = R <= 32 ? 1 : (R <= 64 ? 2 : 4);
   t.pairs = 1;
@@ -121,7 +126,13 @@ sgg::ExpandTiling choose_expand_tiling(const int32_t* offs, int c, int num_segme
   }
   tile_start[c] = acc;
   *total = acc;
-  t.grid = sgg::grid_for(num_segments, acc);
+  if (deal_tiles) {
+    *tiles_per_xcd = (acc + sgg::kXcdCount - 1) / sgg::kXcdCount;
+    t.grid = static_cast<int64_t>(sgg::kXcdCount) * num_segments * *tiles_per_xcd;
+  } else {
+    *tiles_per_xcd = 0;
+    t.grid = sgg::grid_for(num_segments, acc);
+  }
   return t;
 }
 
@@ -204,9 +215,12 @@ sgg::ExpandParams expand_params(const void* h, int64_t ldh, const void* B, int64
                                 const int32_t* seg_slots, int32_t num_segments,
                                 const int32_t* permutation, const int32_t* lora_ranks,
                                 const float* scalings, const float* hpart, int32_t hsplit,
-                                sgg::ExpandTiling* tiling, int pairs = 0) {
+                                sgg::ExpandTiling* tiling, int pairs = 0,
+                                bool segment_dealing = false) {
   sgg::ExpandParams p{};
-  *tiling = choose_expand_tiling(offs, c, num_segments, R, p.tile_start, &p.total_tiles, pairs);
+  const bool deal = !segment_dealing && g_expand_deal_tiles.load(std::memory_order_relaxed) != 0;
+  *tiling = choose_expand_tiling(offs, c, num_segments, R, p.tile_start, &p.total_tiles,
+                                 &p.tiles_per_xcd, pairs, deal);
   bool vec8 = sgg::aligned16(out) && ldo % 8 == 0;
   for (int k = 0; k <= c; ++k) {
     p.offs[k] = offs[k];
@@ -392,7 +406,7 @@ extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B
     sgg::ExpandParams pf =
         expand_params(h, CR, B, N, base_output, ldo, s, num_loras, R, slice_offsets, num_slices,
                       seg_indptr, seg_slots, num_segments, permutation, lora_ranks, scalings,
-                      part, 0, &tf, 1);
+                      part, 0, &tf, 1, true);
     const sgg::ShrinkTiling tp = tf.ks <= 2
         ? sgg::choose_fused_tiling(s, in_dim, static_cast<int>(CR), num_segments, chunk_size,
                                    tf.grid, tf.ks, -1,
@@ -433,6 +447,8 @@ extern "C" int64_t lora_set_option(const char* name, int64_t value) {
     return g_spin_limit.exchange(value < 0 ? 0 : value);
   if (std::strcmp(name, "fused_ksplit") == 0)
     return g_fused_ksplit.exchange(value < 0 ? 0 : value);
+  if (std::strcmp(name, "expand_deal_tiles") == 0)
+    return g_expand_deal_tiles.exchange(value != 0);
   return -1;
 }
 

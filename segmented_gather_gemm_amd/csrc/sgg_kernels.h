@@ -7,6 +7,7 @@
 namespace sgg {
 
 constexpr int kMaxSlices = 8;
+constexpr int kXcdCount = 8;  // MI355X: XCDs, each with its own L2 (blocks dealt b % 8)
 // Counters sit in a fixed region at the start of every workspace, so a
 // counter location never holds anything but a counter (each call leaves its
 // counters at zero) whatever the shapes of earlier calls.  Words [0, 8192):
@@ -63,6 +64,7 @@ struct ExpandParams {
   int32_t offs[kMaxSlices + 1];
   int32_t tile_start[kMaxSlices + 1];  // first column tile of each slice
   int32_t total_tiles;
+  int32_t tiles_per_xcd;      // > 0: column tiles dealt to the XCDs (expand_item_of)
 };
 // Cross-workgroup hand-off of the fused stacked call (fused.hip): producer
 // blocks [0, producer_blocks) run the split-K shrink tiles and count
