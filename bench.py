@@ -492,6 +492,26 @@ def measure_projection(device, b, proj, sets, max_chunk, steps, warmup, emb_rank
     return out
 
 
+def copy_floor_us(device, moved, reps=5):
+    """Microseconds of a device-to-device copy moving `moved` bytes (half
+    read, half written): what a pure stream of the same bytes takes here."""
+    import torch
+    n = moved // 2
+    src = torch.empty(n, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        dst.copy_(src)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    us = float(np.median([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)]))
+    del src, dst
+    torch.cuda.empty_cache()
+    return us
+
+
 def _to(device, d):
     return {k: v.to(device) for k, v in d.items()}
 
@@ -511,6 +531,15 @@ def run_prefill(device, chunks=(16, 32, 64, 128), steps=20, warmup=3):
         res[f"chunk{mc}"] = measure_projection(device, b, proj, [t], mc, steps, warmup)
     res["workload"] = ("prefill gate_up, 32 requests (s=%d), 32 adapters Zipf(1.1), r=64, "
                        "4096 -> 2x14336" % b.num_tokens)
+    # the expand next to a device copy of its algorithmic bytes
+    exp_bytes = algo_counts(b, proj, 16)["expand"]["bytes"]
+    del t
+    floor = copy_floor_us(device, exp_bytes)
+    res["expand_copy_floor"] = {"bytes": int(exp_bytes), "copy_us": round(floor, 1),
+                                "copy_gbs": round(exp_bytes / (floor * 1e-6) / 1e9, 1)}
+    for mc in chunks:
+        r = res[f"chunk{mc}"]["expand"]
+        r["fraction_of_copy_floor"] = round(floor / r["avg_us"], 4)
     return res
 
 

@@ -150,10 +150,9 @@ __device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int 
     load_b();
     if constexpr (FUSED) prefetch();
   }
-#pragma unroll
-  for (int g = 0; g < 2 * P; ++g)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bw[g][ks] = keep_first(bw[g][ks], rho - (32 * ks + 8 * q));
+  // The B fragments are masked to the rank just before their first use, so
+  // their loads stay in flight while h is staged.
+  bool b_masked = false;
 
   const int hch = p.R >> 3;  // 16-byte chunks of one h row slice
   float* at = acct[wave];
@@ -295,6 +294,13 @@ __device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int 
         }
       }
     };
+    if (!b_masked) {
+#pragma unroll
+      for (int g = 0; g < 2 * P; ++g)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bw[g][ks] = keep_first(bw[g][ks], rho - (32 * ks + 8 * q));
+      b_masked = true;
+    }
     const bool use_pre = FUSED && c0 == lo;
     if (use_pre) {
 #pragma unroll
