@@ -8,7 +8,7 @@
 namespace sgg {
 namespace detail {
 
-template <int P, int KS, bool FUSED = false>
+template <int P, int KS>
 struct ExpandShape {
   static constexpr int TNW = 32 * P;                  // columns per wave
   static constexpr int CPR = 4 * KS;                  // 16-byte chunks per LDS h row (R <= 32*KS)
@@ -20,13 +20,7 @@ struct ExpandShape {
   static constexpr int HTILE_BYTES = 128 * CPR * 16;
   static constexpr int PROW_BYTES = 128 * 4;
   static constexpr int ACCT_BYTES = 4 * 16 * APAD * 4;
-  // Split-K partials of a pass of h rows, staged before they are summed.
-  // The area is the transpose tile's, which is idle while h is staged (the
-  // one-launch form, whose LDS is sized by its shrink tiles anyway, gets a
-  // larger one): an expand that reads h keeps its occupancy.
-  static constexpr int PSTAGE_BYTES = FUSED ? 32768 : ACCT_BYTES;
-  static constexpr int PSTAGE_OFF = HTILE_BYTES + PROW_BYTES;
-  static constexpr int SMEM = PSTAGE_OFF + (ACCT_BYTES > PSTAGE_BYTES ? ACCT_BYTES : PSTAGE_BYTES);
+  static constexpr int SMEM = HTILE_BYTES + PROW_BYTES + ACCT_BYTES;
 };
 
 // No hand-off: h (or the partials) was written by an earlier launch.
@@ -56,7 +50,7 @@ __device__ __forceinline__ bool expand_item_of(const ExpandParams& p, int b, int
   return *seg < p.num_segments;
 }
 
-// Column tile `tile` of segment `seg`; `smem` holds ExpandShape<P, KS, FUSED>::SMEM
+// Column tile `tile` of segment `seg`; `smem` holds ExpandShape<P, KS>::SMEM
 // bytes (16-byte aligned).  `wait()` runs once, by the whole workgroup, after
 // the B fragments are requested and before h is staged (the fused launch
 // waits there for its segment's partials; it may use `smem`).  It returns
@@ -68,7 +62,7 @@ __device__ __forceinline__ bool expand_item_of(const ExpandParams& p, int b, int
 template <int P, int KS, bool HPART, bool FUSED = false, class Wait = NoWait>
 __device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int tile, char* smem,
                                             const Wait& wait = Wait()) {
-  using S = ExpandShape<P, KS, FUSED>;
+  using S = ExpandShape<P, KS>;
   constexpr int TNW = S::TNW;
   constexpr int CPR = S::CPR;
   constexpr int RPS = S::RPS;
@@ -165,56 +159,46 @@ __device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int 
       prow[tid] = (r >= 0 && r < p.s) ? r : -1;
     }
     if constexpr (HPART) {
-      // Split-K partials, indexed by sorted position (no gather), in passes
-      // of rows: every thread requests up to four 16-byte pieces (any row,
-      // column chunk, split) before storing them in the staging area, so a
-      // pass costs one round trip; then each (row, 8-column chunk) is summed
-      // in split order and rounded to bf16 into the h tile.
-      f32x4* pst = reinterpret_cast<f32x4*>(smem + S::PSTAGE_OFF);
+      // Split-K partials, indexed by sorted position (no gather): each
+      // (row, 8-column chunk) sums its splits in split order, with the loads
+      // of four splits in flight at a time, and rounds the sum to bf16 into
+      // the h tile.  Partials written by an earlier launch are read through
+      // the caches; in the one-launch form they come from other workgroups of
+      // the same launch, so they are read device-coherently.
       const __amdgpu_buffer_rsrc_t prsrc = buffer_rsrc(p.hpart, p.hpart_bytes);
-      const int per_row = hch * 2 * p.hsplit;      // 16-byte pieces of one row
-      int rows_pp = (S::PSTAGE_BYTES / 16) / per_row;
-      rows_pp = rows_pp < 1 ? 1 : rows_pp;
-      for (int r0 = 0; r0 < ntok; r0 += rows_pp) {
-        const int rows = ntok - r0 < rows_pp ? ntok - r0 : rows_pp;
-        const int items = rows * per_row;
-        // item = ((sp * rows + row) * hch + c) * 2 + half
-        for (int q0 = tid; q0 < items; q0 += 4 * 256) {
-          f32x4 v[4];
+      const auto part16 = [&](int64_t idx) {
+        if constexpr (FUSED) return load_coherent16(prsrc, static_cast<uint32_t>(idx * 4));
+        else return *reinterpret_cast<const f32x4*>(p.hpart + idx);
+      };
+      const int64_t split_stride = p.s * p.ldp;
+      for (int piece = tid; piece < ntok * hch; piece += 256) {
+        const int row = piece / hch, c = piece % hch;
+        const int64_t src = static_cast<int64_t>(c0 + row) * p.ldp + k * p.R + 8 * c;
+        f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+        int sp = 0;
+        for (; sp + 4 <= p.hsplit; sp += 4) {
+          f32x4 lo4[4], hi4[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const int qq = q0 + 256 * u;
-            const int q = qq < items ? qq : q0;
-            const int half = q & 1;
-            const int c = (q >> 1) % hch;
-            const int rs = (q >> 1) / hch;
-            const int row = rs % rows, sp = rs / rows;
-            const int64_t idx = (static_cast<int64_t>(sp) * p.s + (c0 + r0 + row)) * p.ldp +
-                                k * p.R + 8 * c + 4 * half;
-            v[u] = load_coherent16(prsrc, static_cast<uint32_t>(idx * 4));
+            lo4[u] = part16(src + (sp + u) * split_stride);
+            hi4[u] = part16(src + (sp + u) * split_stride + 4);
           }
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (q0 + 256 * u < items) pst[q0 + 256 * u] = v[u];
-        }
-        __syncthreads();
-        for (int piece = tid; piece < rows * hch; piece += 256) {
-          const int row = piece / hch, c = piece % hch;
-          f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-          for (int sp = 0; sp < p.hsplit; ++sp) {
-            const int q = ((sp * rows + row) * hch + c) * 2;
-            s0 += pst[q];
-            s1 += pst[q + 1];
+          for (int u = 0; u < 4; ++u) {
+            s0 += lo4[u];
+            s1 += hi4[u];
           }
-          uint4 v;
-          v.x = f32_to_bf16(s0[0]) | (f32_to_bf16(s0[1]) << 16);
-          v.y = f32_to_bf16(s0[2]) | (f32_to_bf16(s0[3]) << 16);
-          v.z = f32_to_bf16(s1[0]) | (f32_to_bf16(s1[1]) << 16);
-          v.w = f32_to_bf16(s1[2]) | (f32_to_bf16(s1[3]) << 16);
-          const int hr = r0 + row;
-          htile[hr * CPR + (c ^ ((hr / RPS) % CPR))] = v;
         }
-        __syncthreads();
+        for (; sp < p.hsplit; ++sp) {
+          s0 += part16(src + sp * split_stride);
+          s1 += part16(src + sp * split_stride + 4);
+        }
+        uint4 v;
+        v.x = f32_to_bf16(s0[0]) | (f32_to_bf16(s0[1]) << 16);
+        v.y = f32_to_bf16(s0[2]) | (f32_to_bf16(s0[3]) << 16);
+        v.z = f32_to_bf16(s1[0]) | (f32_to_bf16(s1[1]) << 16);
+        v.w = f32_to_bf16(s1[2]) | (f32_to_bf16(s1[3]) << 16);
+        htile[row * CPR + (c ^ ((row / RPS) % CPR))] = v;
       }
     } else {
       for (int piece = tid; piece < ntok * hch; piece += 256) {

@@ -57,7 +57,7 @@ __device__ __forceinline__ void arrive(const FusedSync& fs, int seg, int add) {
 template <int MF, int NF, int KS>
 struct FusedShape {
   static constexpr int A = detail::ShrinkShape<MF, NF>::SMEM;
-  static constexpr int B = detail::ExpandShape<1, KS, true>::SMEM;
+  static constexpr int B = detail::ExpandShape<1, KS>::SMEM;
   static constexpr int SMEM = A > B ? A : B;
 };
 
