@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_prefill_kernels_hbm_traffic.txt")
+LEGS = ("prefill", "skewed", "full", "lm_head", "device_plan")
 
 
 def parse():
@@ -47,6 +48,9 @@ def parse():
     ap.add_argument("--quick", action="store_true",
                     help="time the decode step only (skip the prefill chunk sweep, the skewed "
                          "batch, the full layer sweep, the lm_head pass and the device planner)")
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help="comma list of the workloads timed after the decode step "
+                         "(prefill, skewed, full, lm_head, device_plan; empty for none)")
     ap.add_argument("--full-layers", type=int, default=4,
                     help="resident layers with distinct weights in the full layer sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -354,6 +358,69 @@ def run_decode(args, device):
     torch.cuda.synchronize()
     graph_wall = time.perf_counter() - t0
 
+    # ---- graph mode with the device planner (secondary): per step, the
+    # batch's slot array is copied from pinned host memory into the device
+    # buffer the graph reads, then one replay plans on the GPU
+    # (lora_plan_device) and runs the embedding gather and the stacked call.
+    bd = sgg.ChunkedSgmvLoRA(b0.num_loras, b0.max_chunk_size, device)
+    dinfo = bd.init_cuda_graph_batch_info(b0.num_tokens, 1)
+    lens_d = torch.ones(b0.num_tokens, dtype=torch.int32, device=device)
+    slots_d = torch.zeros(b0.num_tokens, dtype=torch.int32, device=device)
+    slots_host = torch.empty((len(sets), b0.num_tokens), dtype=torch.int32, pin_memory=True)
+    ws_d = torch.zeros(64 << 20, dtype=torch.uint8, device=device)
+    for j, st in enumerate(sets):
+        slots_host[j] = torch.from_numpy(st["slots"])
+        st["ranks_d"] = torch.from_numpy(st["ranks"]).to(device)
+        st["scal_d"] = torch.from_numpy(st["scal"]).to(device)
+
+    def launch_d(st):
+        proj = st["proj"]
+        bd.prepare_lora_batch_device(lens_d, slots_d, st["ranks_d"], st["scal_d"],
+                                     is_decode=True)
+        sgg.lora_a_embedding(st["ids"], st["A_emb"], dinfo, vocab, out=st["e"])
+        sgg.lora_qkv(st["x"], st["A"], st["B"], dinfo, proj.slice_offsets, proj.max_slice,
+                     st["base"], workspace=ws_d)
+
+    slots_d.copy_(slots_host[0])
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        launch_d(sets[0])
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    dgraphs = []
+    for st in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            launch_d(st)
+        dgraphs.append(g)
+    torch.cuda.synchronize()
+
+    def dgraph_step(i):
+        j = i % len(sets)
+        slots_d.copy_(slots_host[j], non_blocking=True)
+        dgraphs[j].replay()
+
+    gc.collect()
+    for i in range(args.warmup):
+        dgraph_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        dgraph_step(i)
+    torch.cuda.synchronize()
+    dgraph_wall = time.perf_counter() - t0
+    # GPU time of the same steps, back to back behind a delay kernel
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    held = hold_stream(stream, 5.0 + 0.2 * args.steps)
+    e0.record(stream)
+    for i in range(args.steps):
+        dgraph_step(i)
+    e1.record(stream)
+    dgraph_b2b = not held.query()
+    torch.cuda.synchronize()
+    dgraph_gpu_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    del dgraphs
+
     # host planner alone (native plan into pinned staging + upload), for the record
     t1 = time.perf_counter()
     for i in range(50):
@@ -380,6 +447,12 @@ def run_decode(args, device):
     se_flops = per["shrink"]["algo_flops"] + per["expand"]["algo_flops"]
     return {
         "wall_s": eager_wall, "graph_wall_s": graph_wall, "tokens": b0.num_tokens,
+        "graph_device_plan": {
+            "ms_per_step": round(dgraph_wall / args.steps * 1e3, 4),
+            "tokens_per_s": round(b0.num_tokens * args.steps / dgraph_wall, 1),
+            "gpu_us_per_step": round(dgraph_gpu_us, 2), "gpu_back_to_back": dgraph_b2b,
+            "step": "slot array copied from pinned host memory, then one graph replay: "
+                    "lora_plan_device, embedding gather, lora_qkv (two launches)"},
         "priming": {"steps": primed, "ms": round(prime_ms, 1)},
         "kernels": per, "prepare_host_us": round(plan_us, 2), "back_to_back": back_to_back,
         "segment_lengths": hist,
@@ -418,6 +491,26 @@ def run_floor(device, steps=100, sets=48):
         return round(e0.elapsed_time(e1) * 1e3 / steps, 3), b2b
 
     out["empty_kernel_us"], out["empty_back_to_back"] = timed(lambda i: torch.cuda._sleep(0))
+    # host time of one replay of a captured graph holding one empty kernel
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(0)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        torch.cuda._sleep(0)
+    for _ in range(10):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    host = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    out["empty_graph_replay_host_us"] = round(host / steps * 1e6, 2)
+    del g
     for name, moved in (("shrink", 5268480), ("shrink_expand", 5268480 + 7889920)):
         n = moved // 2
         src = [torch.empty(n, dtype=torch.uint8, device=device) for _ in range(sets)]
@@ -837,6 +930,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
               f"single-GPU, with no sharding or collectives", file=sys.stderr)
         sys.exit(2)
+    bad = [x for x in args.legs.split(",") if x and x not in LEGS]
+    if bad:
+        print(f"unknown legs {bad}; known: {', '.join(LEGS)}", file=sys.stderr)
+        sys.exit(2)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
@@ -876,6 +973,7 @@ def main():
         "mode": "eager: host plan + one upload, embedding gather, lora_qkv (two launches)",
         "graph_tokens_per_s": round(graph, 1),
         "graph_ms_per_step": round(res["graph_wall_s"] / args.steps * 1e3, 4),
+        "graph_device_plan": res["graph_device_plan"],
         "kernels": k,
         "kernel_timing": ("HIP events on the launch stream around one launch per step, "
                           "back to back behind a delay kernel" + ("" if res["back_to_back"] else
@@ -893,17 +991,15 @@ def main():
         floor["copy_shrink_us"] / k["shrink"]["avg_us"], 4)
     line["shrink_expand"]["fraction_of_copy_floor"] = round(
         floor["copy_shrink_expand_us"] / res["shrink_expand"]["us"], 4)
-    if not args.quick:
-        print("# prefill chunk sweep", file=sys.stderr, flush=True)
-        line["prefill"] = run_prefill(device)
-        print("# skewed", file=sys.stderr, flush=True)
-        line["skewed"] = run_skewed(device)
-        print("# full layer sweep", file=sys.stderr, flush=True)
-        line["full"] = run_full(device, args.full_layers)
-        print("# lm_head pass", file=sys.stderr, flush=True)
-        line["lm_head"] = run_lm_head(device)
-        print("# device planner", file=sys.stderr, flush=True)
-        line["device_plan"] = run_device_plan(device)
+    legs = [] if args.quick else [x for x in args.legs.split(",") if x]
+    runners = {"prefill": ("prefill chunk sweep", lambda: run_prefill(device)),
+               "skewed": ("skewed", lambda: run_skewed(device)),
+               "full": ("full layer sweep", lambda: run_full(device, args.full_layers)),
+               "lm_head": ("lm_head pass", lambda: run_lm_head(device)),
+               "device_plan": ("device planner", lambda: run_device_plan(device))}
+    for leg in legs:
+        print(f"# {runners[leg][0]}", file=sys.stderr, flush=True)
+        line[leg] = runners[leg][1]()
     if not args.no_cpu:
         print("# cpu baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

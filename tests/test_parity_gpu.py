@@ -1071,10 +1071,12 @@ def test_device_plan_invalid_batch_is_empty(bad):
     assert v.work_indptr[:cap + 1].cpu().tolist() == [0] * (cap + 1)
 
 
-def test_device_plan_captured_with_kernels():
+@pytest.mark.parametrize("form", ["separate", "stacked"])
+def test_device_plan_captured_with_kernels(form):
     """The device planner captured in one graph with the shrink and the
-    expand; the lengths and slots are rewritten in device memory before each
-    replay, and every replay is checked against the oracle."""
+    expand (separate calls, or the stacked call as the decode step runs it);
+    the lengths and slots are rewritten in device memory before each replay,
+    and every replay is checked against the oracle."""
     sgg = _sgg()
     L, K, R, offs = 5, 512, 16, [0, 256, 320, 384]
     max_bs, tpb = 24, 12
@@ -1098,8 +1100,11 @@ def test_device_plan_captured_with_kernels():
 
     def step():
         be.prepare_lora_batch_device(lens_d, slots_d, ranks_d, scal_d)
-        sgg.lora_shrink(x, A, info, 3, out=h, workspace=ws)
-        sgg.lora_expand(h, Bw, info, offs, 256, base)
+        if form == "stacked":
+            sgg.lora_qkv(x, A, Bw, info, offs, 256, base, workspace=ws)
+        else:
+            sgg.lora_shrink(x, A, info, 3, out=h, workspace=ws)
+            sgg.lora_expand(h, Bw, info, offs, 256, base)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -1125,8 +1130,9 @@ def test_device_plan_captured_with_kernels():
         b = Batch("g", 0, lens, slots, False, L, ranks, scal, 128, proto.projections)
         ts = {"x": t["x"][:s], "A": t["A"], "B": t["B"], "base": t["base"][:s]}
         want_h, want_y = oracle_forward(ts, b, proj)
-        assert_close(h[:s], want_h, f"device-planned replay {trial} h")
-        assert_close(base[:s], want_y, f"device-planned replay {trial} y")
+        if form == "separate":
+            assert_close(h[:s], want_h, f"device-planned replay {trial} h")
+        assert_close(base[:s], want_y, f"device-planned replay {trial} y ({form})")
         # rows past the batch's tokens are not touched
         assert torch.equal(base[s:].view(torch.int16), base0[s:].view(torch.int16))
 
