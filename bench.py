@@ -55,6 +55,9 @@ def parse():
                     help="resident layers with distinct weights in the full layer sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--fused-timeline", action="store_true",
+                    help="only record the one-launch stacked call's per-workgroup timeline on "
+                         "the decode batch (the library's fused_trace option) and print it")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -858,6 +861,78 @@ def run_device_plan(device, steps=200):
     return res
 
 
+def fused_timeline(device, calls=40):
+    """Per-workgroup timeline of the one-launch stacked call on the decode
+    batch: each call runs alone (synchronised before and after) and its
+    workgroups' start, wait-done and end times are read back; the figures are
+    medians over the calls of each call's percentiles, in microseconds from
+    the call's first workgroup start."""
+    import torch
+    import segmented_gather_gemm_amd as sgg
+    sets = make_sets(8, device)
+    b0 = sets[0]["b"]
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=device)
+    be = sgg.ChunkedSgmvLoRA(b0.num_loras, b0.max_chunk_size, device)
+    infos = [own_plan(be.prepare_lora_batch(None, np.asarray(st["b"].req_slots, np.int32),
+                                            np.asarray(st["b"].lora_ranks, np.int32),
+                                            np.asarray(st["b"].scalings, np.float32),
+                                            is_decode=True)) for st in sets]
+    cap = 1 << 16
+    trace = torch.zeros(4 * cap, dtype=torch.int64, device=device)
+
+    def call(i):
+        st, info = sets[i % len(sets)], infos[i % len(sets)]
+        p = st["proj"]
+        sgg.lora_qkv(st["x"], st["A"], st["B"], info, p.slice_offsets, p.max_slice, st["base"],
+                     workspace=ws)
+
+    old = {"fused_stacked": sgg.lora_set_option("fused_stacked", 1)}
+    for i in range(10):
+        call(i)
+    torch.cuda.synchronize()
+    old["fused_trace_blocks"] = sgg.lora_set_option("fused_trace_blocks", cap)
+    old["fused_trace"] = sgg.lora_set_option("fused_trace", trace.data_ptr())
+    pct = (0, 10, 50, 90, 100)
+    rows = []
+    try:
+        for i in range(calls):
+            trace.zero_()
+            torch.cuda.synchronize()
+            call(i)
+            torch.cuda.synchronize()
+            t = trace.view(-1, 4).cpu().numpy().astype(np.int64)
+            t = t[t[:, 0] > 0]
+            base = t[:, 0].min()
+            us = lambda a: [round(float(np.percentile(a, q)) * 0.01, 2) for q in pct]
+            prod, cons = t[t[:, 3] == 0], t[t[:, 3] >= 1]
+            waited = cons[cons[:, 1] > 0]
+            rows.append({
+                "span": [round((t[:, 2].max() - base) * 0.01, 2)],
+                "shrink_tile_start": us(prod[:, 0] - base),
+                "shrink_tile_work_done": us(prod[:, 1] - base),
+                "shrink_tile_busy": us(prod[:, 1] - prod[:, 0]),
+                "expand_tile_start": us(cons[:, 0] - base),
+                "expand_tile_wait_done": us(waited[:, 1] - base),
+                "expand_tile_end": us(cons[:, 2] - base),
+                "expand_tile_after_wait": us(waited[:, 2] - waited[:, 1]),
+                "counts": [len(prod), len(cons), int((cons[:, 3] == 2).sum())]})
+    finally:
+        for k, v in old.items():
+            sgg.lora_set_option(k, v)
+    out = {"workload": "decode: 256 requests x 1 token, 8 adapters, r=16, stacked qkv "
+                       "4096 -> [4096,1024,1024]", "calls": calls,
+           "percentiles": list(pct), "unit": "us from the call's first workgroup start"}
+    for k in rows[0]:
+        if k == "counts":
+            continue
+        out[k] = [round(float(np.median([r[k][j] for r in rows])), 2)
+                  for j in range(len(rows[0][k]))]
+    c = rows[-1]["counts"]
+    out["workgroups"] = {"shrink_tiles": c[0], "expand_tiles": c[1],
+                         "gave_up_waiting": max(r["counts"][2] for r in rows)}
+    print(json.dumps(out), flush=True)
+
+
 def copy_probe(device):
     import torch
     n = 1 << 30
@@ -941,6 +1016,9 @@ def main():
     device = torch.device("cuda:0")
     if args.copy_probe:
         copy_probe(device)
+        return
+    if args.fused_timeline:
+        fused_timeline(device)
         return
     print(f"# decode: {args.sets} input sets, warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)

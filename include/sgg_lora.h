@@ -362,6 +362,18 @@ int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B, int64_t N
  *   "expand_deal_tiles"  1 (default): the expand deals column tiles to the
  *                    XCDs (an adapter's B columns stay in each L2 across its
  *                    segments); 0: it deals segments.  Same results.
+ *   "fused_trace"    a diagnostic: the device address (as an integer) of a
+ *                    zeroed buffer of 32 * "fused_trace_blocks" bytes, or 0
+ *                    (default, off).  While set, each one-launch stacked call
+ *                    writes, for each of its first "fused_trace_blocks"
+ *                    workgroups b, four 64-bit words at word 4b: start time,
+ *                    wait-done time (shrink tiles: work-done time; 0 for a
+ *                    workgroup with nothing to wait for), end time -- ticks
+ *                    of the device's 100 MHz real-time counter -- and its role
+ *                    (0 shrink tile, 1 expand tile, 2 expand tile that gave
+ *                    up waiting).  One buffer for the process: set it only
+ *                    while calls go to the device that holds it.
+ *   "fused_trace_blocks"  capacity of the "fused_trace" buffer, in workgroups.
  */
 int64_t lora_set_option(const char* name, int64_t value);
 

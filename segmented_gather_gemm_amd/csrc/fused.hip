@@ -63,12 +63,25 @@ struct FusedShape {
 
 // Producer tiles of 16*MF tokens x 16*NF rank rows; consumer tiles of 128
 // columns with rank steps KS.
+// Block timeline record (FusedSync::trace): lanes 0-3 of wave 0 each store
+// one word, with vector stores.
+__device__ __forceinline__ void trace_block(const FusedSync& fs, uint64_t t0, uint64_t t1,
+                                            int role) {
+  const int b = blockIdx.x;
+  if (fs.trace == nullptr || b >= fs.trace_blocks || threadIdx.x >= 4) return;
+  const uint64_t t2 = __builtin_amdgcn_s_memrealtime();
+  const int i = threadIdx.x;
+  const uint64_t v = i == 0 ? t0 : i == 1 ? t1 : i == 2 ? t2 : static_cast<uint64_t>(role);
+  fs.trace[4 * static_cast<int64_t>(b) + i] = v;
+}
+
 template <int MF, int NF, int KS>
 __global__ __launch_bounds__(256) void fused_kernel(ShrinkParams ps, ExpandParams pe,
                                                     FusedSync fs) {
   __shared__ __attribute__((aligned(16))) char smem[FusedShape<MF, NF, KS>::SMEM];
   __shared__ int unused_flag;
   __shared__ int published;
+  const uint64_t t_start = fs.trace ? __builtin_amdgcn_s_memrealtime() : 0;
   const int b = blockIdx.x;
   if (b < fs.producer_blocks) {
     int seg, item;
@@ -76,11 +89,15 @@ __global__ __launch_bounds__(256) void fused_kernel(ShrinkParams ps, ExpandParam
     detail::shrink_tile<MF, NF>(ps, seg, item, smem, &unused_flag);
     wave_stores_done();
     __syncthreads();
+    const uint64_t t_work = fs.trace ? __builtin_amdgcn_s_memrealtime() : 0;
     if (threadIdx.x == 0) arrive(fs, seg, 1 + kDoneUnit);
+    trace_block(fs, t_start, t_work, 0);
     return;
   }
   int seg, tile;
   if (!detail::expand_item_of(pe, b - fs.producer_blocks, &seg, &tile)) return;
+  uint64_t t_wait = 0;
+  int role = 1;
   const auto wait = [&]() {
     if (threadIdx.x == 0) {
       int ok = 0;
@@ -97,7 +114,9 @@ __global__ __launch_bounds__(256) void fused_kernel(ShrinkParams ps, ExpandParam
       published = ok;
     }
     __syncthreads();
+    if (fs.trace) t_wait = __builtin_amdgcn_s_memrealtime();
     if (published) return false;
+    role = 2;
     // Gave up: make this segment's partials here (the same values the
     // producers write), then read them as usual.
     if (threadIdx.x == 0)
@@ -113,6 +132,7 @@ __global__ __launch_bounds__(256) void fused_kernel(ShrinkParams ps, ExpandParam
   detail::expand_tile<1, KS, true, true>(pe, seg, tile, smem, wait);
   __syncthreads();
   if (threadIdx.x == 0) arrive(fs, seg, kDoneUnit);
+  trace_block(fs, t_start, t_wait, role);
 }
 
 #define SGG_FUSED_INSTANCES(X)                                                    \

@@ -17,6 +17,8 @@ namespace {
 // lora_set_option values.
 std::atomic<int64_t> g_fused_stacked{0};
 std::atomic<int64_t> g_fused_ksplit{0};
+std::atomic<int64_t> g_fused_trace{0};          // device address of a block timeline, or 0
+std::atomic<int64_t> g_fused_trace_blocks{0};
 std::atomic<int64_t> g_expand_deal_tiles{1};
 std::atomic<int64_t> g_spin_limit{int64_t{1} << 20};
 
@@ -430,6 +432,11 @@ extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B
       fs.producers_per_seg = static_cast<int32_t>(per_seg);
       fs.consumers_per_seg = pf.total_tiles;
       fs.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+      fs.trace = reinterpret_cast<uint64_t*>(g_fused_trace.load(std::memory_order_relaxed));
+      {
+        const int64_t tb = g_fused_trace_blocks.load(std::memory_order_relaxed);
+        fs.trace_blocks = fs.trace ? static_cast<int32_t>(tb < (int64_t{1} << 30) ? tb : 0) : 0;
+      }
       rc = launch_status(sgg::launch_fused(pp, tp, pf, tf, fs, st), "fused stacked call");
       return rc ? rc : sgg::ok();
     }
@@ -449,6 +456,9 @@ extern "C" int64_t lora_set_option(const char* name, int64_t value) {
     return g_fused_ksplit.exchange(value < 0 ? 0 : value);
   if (std::strcmp(name, "expand_deal_tiles") == 0)
     return g_expand_deal_tiles.exchange(value != 0);
+  if (std::strcmp(name, "fused_trace") == 0) return g_fused_trace.exchange(value);
+  if (std::strcmp(name, "fused_trace_blocks") == 0)
+    return g_fused_trace_blocks.exchange(value < 0 ? 0 : value);
   return -1;
 }
 

@@ -82,6 +82,12 @@ struct FusedSync {
   int32_t producers_per_seg;
   int32_t consumers_per_seg;
   int64_t spin_limit;
+  // Optional block timeline (null: off): block b < trace_blocks writes four
+  // 64-bit words at trace + 4b -- start, wait done (producers: work done),
+  // end, in ticks of the 100 MHz real-time counter, and its role (0 producer,
+  // 1 consumer, 2 consumer that gave up waiting).
+  uint64_t* trace;
+  int32_t trace_blocks;
 };
 
 // Grid of a segment_round_robin launch: whole rounds of 8 segments.

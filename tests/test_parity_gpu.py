@@ -311,6 +311,48 @@ def test_fused_wait_gives_up_and_recomputes():
     assert_close(y, want_y, "one launch after give-up")
 
 
+def test_fused_timeline_leaves_results_unchanged():
+    """The one-launch call's block timeline (lora_set_option "fused_trace"):
+    with it on, the result is bit-identical to the call without it; every
+    workgroup of the grid up to the capacity records start <= wait/work-done
+    <= end, the roles split into the shrink tiles first and the expand tiles
+    after them, and workgroups past the capacity write nothing."""
+    sgg = _sgg()
+    b, proj, t, offs, wide = _decode_case(79)
+    be = backend(b)
+    info = plan_on(be, b)
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    cap = 1 << 14
+    trace = torch.zeros(4 * (cap + 64), dtype=torch.int64, device=DEV)
+    with fused_stacked():
+        y_ref = sgg.lora_qkv(x, A, Bw, info, offs, wide, base.clone(), workspace=ws)
+        torch.cuda.synchronize()
+        old_b = sgg.lora_set_option("fused_trace_blocks", cap)
+        old_t = sgg.lora_set_option("fused_trace", trace.data_ptr())
+        try:
+            y = sgg.lora_qkv(x, A, Bw, info, offs, wide, base.clone(), workspace=ws)
+            torch.cuda.synchronize()
+        finally:
+            sgg.lora_set_option("fused_trace", old_t)
+            sgg.lora_set_option("fused_trace_blocks", old_b)
+    assert torch.equal(y, y_ref)
+    tr = trace.view(-1, 4).cpu().numpy()
+    assert not tr[cap:].any()
+    used = tr[:cap][tr[:cap, 0] > 0]
+    assert len(used) > 0
+    roles = used[:, 3]
+    assert set(roles.tolist()) <= {0, 1}
+    # shrink tiles (role 0) occupy the first workgroups of the grid
+    idx = np.nonzero(tr[:cap, 0] > 0)[0]
+    assert (np.diff((tr[idx, 3] > 0).astype(int)) >= 0).all()
+    waited = used[used[:, 1] > 0]
+    assert (waited[:, 0] <= waited[:, 1]).all() and (waited[:, 1] <= waited[:, 2]).all()
+    assert (used[:, 0] <= used[:, 2]).all()
+    _, want_y = oracle_forward(t, b, proj)
+    assert_close(y, want_y, "one launch with its timeline on")
+
+
 def test_fused_stacked_call_in_a_graph():
     """The one-launch stacked call captured in a graph over a capacity plan
     (trailing segments empty): replays with new plans, eager work and
