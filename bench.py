@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_prefill_kernels_hbm_traffic.txt")
-LEGS = ("prefill", "skewed", "full", "lm_head", "device_plan")
+LEGS = ("prefill", "skewed", "full", "lm_head", "device_plan", "short")
 
 
 def parse():
@@ -814,6 +814,42 @@ def run_lm_head(device, steps=20, warmup=3):
     return res
 
 
+def run_short_segments(device, steps=50, warmup=5, n_sets=8):
+    """The shrink's two arithmetic forms on batches of short segments: MFMA
+    tiles (default) and the VALU form (library option shrink_valu: 16-token
+    tiles, those with at most 4 tokens summed on the VALU with cross-lane
+    reductions).  Batches: 256 one-token decode requests over 128 adapters
+    (segments of ~2 tokens; stacked qkv, r=16) and the full-layer batch's
+    o_proj (192 one-token requests + 8 x 512 over 64 adapters, r=32)."""
+    import segmented_gather_gemm_amd as sgg
+    from synth import draw_batch, draw_projection
+    from synth.workloads import Batch, Projection
+    rng = np.random.default_rng(20261203)
+    many = Batch("decode_128_adapters", 20261203, [1] * 256,
+                 rng.integers(0, 128, 256).tolist(), True, 128, [16] * 128, [1.0] * 128, 128,
+                 [Projection("qkv", 4096, [0, 4096, 5120, 6144], 16)])
+    full = draw_batch("full")
+    o_proj = [p for p in full.projections if p.in_dim == 4096 and p.num_slices == 1][0]
+    res = {"workload": "short segments: decode 256 x 1 token over 128 adapters (qkv c=3, r=16); "
+                       "full-layer batch o_proj 4096 -> 4096 (r=32)"}
+    for name, b, proj in (("decode_128_adapters", many, many.projections[0]),
+                          ("full_o_proj", full, o_proj)):
+        sets = rotated(_to(device, draw_projection(b, proj)), n_sets)
+        out = {}
+        for form, flag in (("mfma", 0), ("valu", 1)):
+            old = sgg.lora_set_option("shrink_valu", flag)
+            try:
+                m = measure_projection(device, b, proj, sets, b.max_chunk_size, steps, warmup)
+            finally:
+                sgg.lora_set_option("shrink_valu", old)
+            out[form] = {k: m[k] for k in ("shrink", "stacked") if k in m}
+            out["segment_lengths"] = m["segment_lengths"]
+            out["segments"] = m["segments"]
+        res[name] = out
+        del sets
+    return res
+
+
 def run_device_plan(device, steps=200):
     """The device-side planner (lora_plan_device) on the decode batch and on
     the prefill batch, one launch per step back to back behind a delay
@@ -1074,7 +1110,8 @@ def main():
                "skewed": ("skewed", lambda: run_skewed(device)),
                "full": ("full layer sweep", lambda: run_full(device, args.full_layers)),
                "lm_head": ("lm_head pass", lambda: run_lm_head(device)),
-               "device_plan": ("device planner", lambda: run_device_plan(device))}
+               "device_plan": ("device planner", lambda: run_device_plan(device)),
+               "short": ("short segments: MFMA and VALU shrink", lambda: run_short_segments(device))}
     for leg in legs:
         print(f"# {runners[leg][0]}", file=sys.stderr, flush=True)
         line[leg] = runners[leg][1]()

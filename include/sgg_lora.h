@@ -362,6 +362,12 @@ int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B, int64_t N
  *   "expand_deal_tiles"  1 (default): the expand deals column tiles to the
  *                    XCDs (an adapter's B columns stay in each L2 across its
  *                    segments); 0: it deals segments.  Same results.
+ *   "shrink_valu"    0 (default): the shrink computes on the matrix cores;
+ *                    1: its split-K kernel takes 16-token tiles and sums the
+ *                    dot products of tiles with at most 4 tokens on the
+ *                    vector ALU (cross-lane reductions).  Same bytes read,
+ *                    results equal to rounding; measured slower, kept for
+ *                    comparison.
  *   "fused_trace"    a diagnostic: the device address (as an integer) of a
  *                    zeroed buffer of 32 * "fused_trace_blocks" bytes, or 0
  *                    (default, off).  While set, each one-launch stacked call

@@ -17,6 +17,7 @@ namespace {
 // lora_set_option values.
 std::atomic<int64_t> g_fused_stacked{0};
 std::atomic<int64_t> g_fused_ksplit{0};
+std::atomic<int64_t> g_shrink_valu{0};
 std::atomic<int64_t> g_fused_trace{0};          // device address of a block timeline, or 0
 std::atomic<int64_t> g_fused_trace_blocks{0};
 std::atomic<int64_t> g_expand_deal_tiles{1};
@@ -152,6 +153,16 @@ int launch_status(hipError_t e, const char* what) {
   return SGG_OK;
 }
 
+// The shrink tiling of a call: choose_shrink_tiling, re-tiled for the VALU
+// form when the "shrink_valu" option is on.
+sgg::ShrinkTiling shrink_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk,
+                                bool gemm_ok = true) {
+  sgg::ShrinkTiling t = sgg::choose_shrink_tiling(s, K, CR, num_segments, chunk, gemm_ok);
+  if (g_shrink_valu.load(std::memory_order_relaxed) != 0)
+    sgg::use_valu_tiles(&t, s, num_segments, chunk);
+  return t;
+}
+
 sgg::ShrinkParams shrink_params(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh,
                                 int64_t s, int64_t K, int32_t num_loras, int32_t c, int32_t R,
                                 const int32_t* seg_indptr, const int32_t* seg_slots,
@@ -192,7 +203,7 @@ int do_shrink(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh, i
               const int32_t* seg_slots, int32_t num_segments, const int32_t* permutation,
               const int32_t* lora_ranks, int32_t chunk_size, int32_t* counters,
               void* partial, int64_t partial_avail, hipStream_t stream) {
-  const sgg::ShrinkTiling t = sgg::choose_shrink_tiling(
+  const sgg::ShrinkTiling t = shrink_tiling(
       s, K, c * R, num_segments, chunk_size, gemm_addressable(s, ldx, K, static_cast<int64_t>(c) * R));
   if (t.ksplit > 1) {
     SGG_CHECK(counters != nullptr && partial != nullptr && partial_avail >= t.partial_bytes,
@@ -276,7 +287,7 @@ extern "C" int64_t lora_shrink_workspace_bytes(int64_t s, int64_t in_dim, int32_
   if (s <= 0 || in_dim <= 0 || num_slices <= 0 || R <= 0 || num_segments <= 0 || chunk_size <= 0)
     return 0;
   const sgg::ShrinkTiling t =
-      sgg::choose_shrink_tiling(s, in_dim, num_slices * R, num_segments, chunk_size);
+      shrink_tiling(s, in_dim, num_slices * R, num_segments, chunk_size);
   return t.ksplit > 1 ? sgg::kCounterBytes + t.partial_bytes : 0;
 }
 
@@ -287,7 +298,7 @@ extern "C" int64_t lora_qkv_workspace_bytes(int64_t s, int64_t in_dim, int32_t n
   const int64_t CR = static_cast<int64_t>(num_slices) * R;
   if (in_dim > 0 && num_segments > 0 && chunk_size > 0) {
     const sgg::ShrinkTiling t =
-        sgg::choose_shrink_tiling(s, in_dim, static_cast<int>(CR), num_segments, chunk_size);
+        shrink_tiling(s, in_dim, static_cast<int>(CR), num_segments, chunk_size);
     partial = t.partial_bytes;
     // room for the one-launch form's partials (up to kFusedMaxSplit K ranges)
     if (t.ksplit > 1 && CR <= 48) {
@@ -378,7 +389,7 @@ extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B
   void* h = ws + sgg::kCounterBytes;
   float* part = reinterpret_cast<float*>(ws + sgg::kCounterBytes + hbytes);
   const int64_t CR = static_cast<int64_t>(num_slices) * R;
-  const sgg::ShrinkTiling ts = sgg::choose_shrink_tiling(
+  const sgg::ShrinkTiling ts = shrink_tiling(
       s, in_dim, num_slices * R, num_segments, chunk_size, gemm_addressable(s, ldx, in_dim, CR));
   SGG_CHECK(ts.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "shrink grid too large");
   SGG_CHECK(ts.partial_bytes < (int64_t{1} << 32) - 256, SGG_ERR_UNSUPPORTED,
@@ -456,6 +467,7 @@ extern "C" int64_t lora_set_option(const char* name, int64_t value) {
     return g_fused_ksplit.exchange(value < 0 ? 0 : value);
   if (std::strcmp(name, "expand_deal_tiles") == 0)
     return g_expand_deal_tiles.exchange(value != 0);
+  if (std::strcmp(name, "shrink_valu") == 0) return g_shrink_valu.exchange(value != 0);
   if (std::strcmp(name, "fused_trace") == 0) return g_fused_trace.exchange(value);
   if (std::strcmp(name, "fused_trace_blocks") == 0)
     return g_fused_trace_blocks.exchange(value < 0 ? 0 : value);

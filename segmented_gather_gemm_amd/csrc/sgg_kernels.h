@@ -117,11 +117,17 @@ struct ShrinkTiling {
   int64_t kps;
   int64_t partial_bytes;     // f32 partial tiles (0 unless ksplit > 1)
   int64_t grid;
+  int valu;          // split-K kernel: tiles of at most 4 tokens on the VALU (mf 1, nf <= 3)
 };
 // gemm_ok: the GEMM tiles may be chosen (their buffer loads address x and
 // each slot's A block with 32-bit byte offsets).
 ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk,
                                   bool gemm_ok = true);
+// Re-tile a split-K kernel tiling to 16-token tiles whose short tiles (at
+// most 4 tokens) compute on the VALU; unchanged where that kernel form does
+// not apply (GEMM tiles, more than 48 rank rows per tile, too many arrival
+// counters).
+void use_valu_tiles(ShrinkTiling* t, int64_t s, int num_segments, int chunk);
 
 struct ExpandTiling {
   int pairs, ks;     // 32-column fragment pairs per wave, 32-deep rank steps

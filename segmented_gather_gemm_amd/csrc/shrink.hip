@@ -29,6 +29,12 @@
 // stacked shrink + expand the partials are instead left for the expand,
 // which sums them in the same order while staging h (no counters, no
 // cross-workgroup round trip here).
+//
+// Optionally (library option "shrink_valu") the kernel takes 16-token tiles
+// and computes the tiles of segments' short ends (at most 4 tokens, e.g. the
+// one-request segments of a many-adapter decode batch) on the VALU with
+// cross-lane reductions instead of MFMA (shrink_tile.h); it reads the same
+// bytes.  Measured, it is no faster, so it is off by default.
 #include "sgg_device.h"
 #include "sgg_internal.h"
 #include "sgg_kernels.h"
@@ -38,19 +44,19 @@ namespace sgg {
 
 namespace {
 
-template <int MF, int NF>
+template <int MF, int NF, bool VALU>
 __global__ __launch_bounds__(256, 1) void shrink_kernel(ShrinkParams p) {
   __shared__ __attribute__((aligned(16))) char smem[detail::ShrinkShape<MF, NF>::SMEM];
   __shared__ int last_flag;
   int seg, item;
   if (!detail::shrink_item_of(p, blockIdx.x, &seg, &item)) return;
-  detail::shrink_tile<MF, NF>(p, seg, item, smem, &last_flag);
+  detail::shrink_tile<MF, NF, VALU>(p, seg, item, smem, &last_flag);
 }
 
-template <int MF, int NF>
+template <int MF, int NF, bool VALU = false>
 hipError_t launch_mn(const ShrinkParams& p, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((shrink_kernel<MF, NF>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                     stream, p);
+  hipLaunchKernelGGL((shrink_kernel<MF, NF, VALU>), dim3(static_cast<unsigned>(grid)), dim3(256),
+                     0, stream, p);
   return hipGetLastError();
 }
 
@@ -73,6 +79,15 @@ hipError_t launch_m(const ShrinkParams& p, int nf, int64_t grid, hipStream_t str
 hipError_t launch_shrink(const ShrinkParams& p, const ShrinkTiling& t, hipStream_t stream) {
   if (t.grid <= 0) return hipSuccess;
   if (t.gemm) return launch_shrink_gemm(p, t.bm, t.bn, t.grid, stream);
+  if (t.valu) {
+    if (t.mf != 1) return hipErrorInvalidValue;
+    switch (t.nf) {
+      case 1: return launch_mn<1, 1, true>(p, t.grid, stream);
+      case 2: return launch_mn<1, 2, true>(p, t.grid, stream);
+      case 3: return launch_mn<1, 3, true>(p, t.grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (t.mf) {
     case 1: return launch_m<1>(p, t.nf, t.grid, stream);
     case 2: return launch_m<2>(p, t.nf, t.grid, stream);

@@ -9,6 +9,16 @@ namespace sgg {
 namespace detail {
 
 constexpr int kFragsPerRound = 8;  // accumulator fragments reduced per LDS round
+constexpr int kValuTokens = 4;     // tiles of at most this many tokens take the VALU form
+
+// a . b over 4 bf16 pairs (two 32-bit words each), accumulated in f32
+__device__ __forceinline__ float dot4_bf16(uint2 a, uint2 b, float acc) {
+  acc = fmaf(bf16_to_f32(a.x & 0xffffu), bf16_to_f32(b.x & 0xffffu), acc);
+  acc = fmaf(bf16_to_f32(a.x >> 16), bf16_to_f32(b.x >> 16), acc);
+  acc = fmaf(bf16_to_f32(a.y & 0xffffu), bf16_to_f32(b.y & 0xffffu), acc);
+  acc = fmaf(bf16_to_f32(a.y >> 16), bf16_to_f32(b.y >> 16), acc);
+  return acc;
+}
 
 // Byte offset of 16-byte chunk c (0..7) of row r in a swizzled 128-byte-row tile.
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
@@ -37,9 +47,19 @@ __device__ __forceinline__ bool shrink_item_of(const ShrinkParams& p, int b, int
 
 // Tile `item` of segment `seg`; `smem` holds ShrinkShape<MF, NF>::SMEM bytes.
 // Every early return is uniform over the workgroup.
-template <int MF, int NF>
+//
+// VALU (MF == 1 only): a tile with at most kValuTokens tokens computes its
+// dot products on the vector ALU instead of the matrix cores -- from the same
+// staged chunks, so it reads the same bytes.  Lane (q, kp) = (lane / 16,
+// lane % 16) takes 4 of each 64-deep chunk's k (4*kp .. 4*kp+3) for the rank
+// rows 16g + 4q + e of the tile and every token; at the end each row group
+// of 16 lanes sums its k parts by butterfly exchanges, so lane (q, kp) holds
+// token kp's sums for its rows: the layout an MFMA accumulator has, and the
+// four waves' tiles are summed and written as in the MFMA form.
+template <int MF, int NF, bool VALU = false>
 __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int seg, int item, char* smem,
                                             int* last_flag_ptr) {
+  static_assert(!VALU || (MF == 1 && NF <= 3), "VALU tiles: 16 tokens, at most 48 rank rows");
   using S = ShrinkShape<MF, NF>;
   constexpr int BM = S::BM;
   constexpr int NB = S::NB;
@@ -137,6 +157,28 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int seg, int 
     f32x4 acc[NFR];
 #pragma unroll
     for (int i = 0; i < NFR; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // VALU form: per-lane sums for token t, rank row 16g + 4q + e
+    const bool valu = VALU && mcount <= kValuTokens;
+    constexpr int VT = VALU ? kValuTokens : 1;
+    constexpr int VG = VALU ? NF : 1;
+    float vacc[VT][VG][4];
+    bool vtok[VT];
+    if constexpr (VALU) {
+#pragma unroll
+      for (int t = 0; t < VT; ++t) {
+        bool ok = t < mcount;
+        if (ok) {
+          const int r = p.perm[m0 + t];
+          ok = r >= 0 && r < p.s;
+        }
+        vtok[t] = ok;
+#pragma unroll
+        for (int g = 0; g < VG; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vacc[t][g][e] = 0.f;
+      }
+    }
+    const int vq = lane >> 4, vkp = lane & 15;
 
     if (!dead && nchunks > 0) {
       // One register set of loads in flight: the CH chunks of stage t+1 are
@@ -170,6 +212,31 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int seg, int 
           const int64_t k0 = kw + 256 * (CH * t + cc);
           if (k0 >= ke) break;  // wave-uniform
           const char* ct = tile + cc * ROWS * 128;
+          if constexpr (VALU) {
+            if (valu) {
+              // 8 bytes of 16-byte chunk vkp / 2 of each row
+              const int c = vkp >> 1, off = 8 * (vkp & 1);
+              const bool kv = k0 + 8 * c < ke;
+              uint2 xv[VT];
+#pragma unroll
+              for (int tt = 0; tt < VT; ++tt) {
+                const uint2 v = *reinterpret_cast<const uint2*>(ct + swz(tt, c) + off);
+                xv[tt] = (kv && vtok[tt]) ? v : make_uint2(0, 0);
+              }
+#pragma unroll
+              for (int g = 0; g < VG; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int nl = 16 * g + 4 * vq + e;
+                  const int n = nb * NB + nl;
+                  const uint2 v = *reinterpret_cast<const uint2*>(ct + swz(BM + nl, c) + off);
+                  const uint2 av = (kv && n < p.CR && (n % p.R) < rho) ? v : make_uint2(0, 0);
+#pragma unroll
+                  for (int tt = 0; tt < VT; ++tt) vacc[tt][g][e] = dot4_bf16(av, xv[tt], vacc[tt][g][e]);
+                }
+              continue;
+            }
+          }
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
             const int c = 4 * st + fgrp;
@@ -190,6 +257,34 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int seg, int 
 #pragma unroll
               for (int g = 0; g < NF; ++g) acc[f * NF + g] = mfma16x16x32(av[g], xv[f], acc[f * NF + g]);
           }
+        }
+      }
+    }
+
+    if constexpr (VALU) {
+      if (valu) {
+        // butterfly over the 16 k parts of each row group, then token vkp's
+        // sums into the accumulator layout (tokens past kValuTokens: zero)
+#pragma unroll
+        for (int tt = 0; tt < VT; ++tt)
+#pragma unroll
+          for (int g = 0; g < VG; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float v = vacc[tt][g][e];
+              v += __shfl_xor(v, 1, 64);
+              v += __shfl_xor(v, 2, 64);
+              v += __shfl_xor(v, 4, 64);
+              v += __shfl_xor(v, 8, 64);
+              vacc[tt][g][e] = v;
+            }
+#pragma unroll
+        for (int g = 0; g < VG; ++g) {
+          f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int tt = 0; tt < VT; ++tt)
+            if (vkp == tt) a = f32x4{vacc[tt][g][0], vacc[tt][g][1], vacc[tt][g][2], vacc[tt][g][3]};
+          acc[g] = a;
         }
       }
     }

@@ -124,6 +124,18 @@ ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments
   return t;
 }
 
+// The VALU form keeps the K split and the column tiles; only the token tiles
+// shrink to 16 (so that a short segment's tile holds just its tokens).
+void use_valu_tiles(ShrinkTiling* t, int64_t s, int num_segments, int chunk) {
+  if (t->gemm || t->nf > 3 || t->grid <= 0) return;
+  const int64_t counters = (s / 16 + num_segments + 1) * t->nblocks;
+  if (t->ksplit > 1 && counters > kCounterCap) return;
+  t->mf = 1;
+  t->mblocks = chunk > 16 ? (chunk + 15) / 16 : 1;
+  t->grid = grid_for(num_segments, static_cast<int64_t>(t->ksplit) * t->nblocks * t->mblocks);
+  t->valu = 1;
+}
+
 // Producer tiling of the one-launch stacked call.  A decode batch's shrink is
 // a chain of dependent memory round trips (plan, operands, partials) more
 // than a stream of bytes, so the producers cover all c*R rank rows and up to

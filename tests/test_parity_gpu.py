@@ -534,6 +534,58 @@ def _gpu_forward(b, proj, t, override=0, max_chunk=128):
     return h, y
 
 
+class shrink_valu:
+    """Context: the shrink's VALU form of short tiles (lora_set_option
+    "shrink_valu" = 1) inside, the default MFMA form after."""
+
+    def __enter__(self):
+        self.old = _sgg().lora_set_option("shrink_valu", 1)
+
+    def __exit__(self, *exc):
+        _sgg().lora_set_option("shrink_valu", self.old)
+
+
+def _valu_cases():
+    rng = np.random.default_rng(41)
+    one = ("one_token_segments", [1] * 256, rng.integers(0, 128, 256).tolist(), 128,
+           rng.choice([16, 8, 12, 0], 128).tolist(), 4096, [0, 512, 640, 768], 16, 0)
+    mixed = ("mixed", [1] * 40 + [3, 2, 4, 5, 37, 70], rng.integers(0, 32, 46).tolist(), 32,
+             [32] * 32, 1024, [0, 384], 32, 0)
+    ragged = ("ragged_k_chunk_1", [2, 1, 3, 9, 4, 1, 6], [0, 1, 2, 1, 0, 3, 2], 4,
+              [8, 5, 8, 3], 1000, [0, 100, 200], 8, 1)
+    return [one, mixed, ragged]
+
+
+@pytest.mark.parametrize("case", _valu_cases(), ids=lambda c: c[0])
+def test_shrink_valu_short_tiles(case):
+    """The shrink's VALU form (16-token tiles; those with at most 4 tokens
+    summed on the VALU with cross-lane reductions, the rest on MFMA): h and y
+    match the oracle on one-token segments of a many-adapter decode batch, a
+    mix of short and long segments, and a ragged K with chunk size 1; the
+    stacked call in this form matches the separate calls bit for bit."""
+    name, lens, slots, L, ranks, K, offs, R, override = case
+    sgg = _sgg()
+    scal = np.random.default_rng(42).uniform(0.5, 2.0, L).tolist()
+    b, proj, t = _small_case(43, lens, slots, L, ranks, scal, K, offs, R)
+    with shrink_valu():
+        h, y = _gpu_forward(b, proj, t, override)
+        want_h, want_y = oracle_forward(t, b, proj)
+        assert_close(h, want_h, f"{name} h (VALU tiles)")
+        assert_close(y, want_y, f"{name} y (VALU tiles)")
+        be = backend(b)
+        info = own_plan(plan_on(be, b, override))
+        x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+        ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+        wide = int(max(np.diff(offs)))
+        c = proj.num_slices
+        y_st = sgg.lora_qkv(x, A, Bw, info, offs, wide, base.clone(), workspace=ws)
+        h_sep = sgg.lora_shrink(x, A, info, c, workspace=ws)
+        y_sep = sgg.lora_expand(h_sep, Bw, info, offs, wide, base.clone())
+        torch.cuda.synchronize()
+    assert torch.equal(y_st, y_sep), name
+    assert_close(y_st, want_y, f"{name} stacked (VALU tiles)")
+
+
 @pytest.mark.parametrize("override", [1, 3, 16, 32, 64, 128, 0])
 def test_chunk_size_invariance(override):
     b, proj, t = _small_case(31, [5, 40, 1, 77, 130, 9], [2, 0, 2, 1, 0, 3], 4, [16] * 4,
