@@ -348,6 +348,67 @@ int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B, int64_t N
              int64_t workspace_bytes, void* stream);
 
 /*
+ * lora_moe_route -- the MoE LoRA add's routing (PR #24007 report page,
+ * implementation breakdown items 2-4: the MoE layer takes each token's adapter
+ * from the per-request fields req_seg_indptr / req_weight_indices, since the
+ * chunked segments are cut per adapter across requests; the MoE LoRA kernel
+ * combines adapter and expert into a "virtual expert").  The report names
+ * that kernel but does not give its body; this library's reading: copy j of
+ * token t goes to virtual expert a(t) * num_experts + topk_ids[t][j], where
+ * a(t) = req_weight_indices[r] for the request r with
+ * req_seg_indptr[r] <= t < req_seg_indptr[r + 1].
+ *   req_seg_indptr      device int32 [num_reqs + 1], non-decreasing.
+ *   req_weight_indices  device int32 [num_reqs] adapter slots.
+ *   topk_ids            device int32 [num_tokens][top_k] expert ids.
+ *   lora_ranks, scalings  device tables of the num_loras adapters.
+ *   virtual_slots       device int32 [num_tokens * top_k] out: the copies'
+ *                       virtual experts; num_loras * num_experts (a slot of
+ *                       rank 0) for a token outside every request, an adapter
+ *                       outside [0, num_loras) or an expert outside
+ *                       [0, num_experts).
+ *   virtual_ranks, virtual_scalings  device [num_loras * num_experts + 1] out:
+ *                       adapter a's rank / scaling at every a * E + e, rank 0
+ *                       and scaling 0 at the last entry.
+ * Plan the copies with lora_plan_device (decode mode: one-token requests,
+ * req_slots = virtual_slots, max_loras = num_loras * num_experts + 1) or with
+ * the host planner, then call lora_moe_add.  Async on `stream`; errors:
+ * SGG_ERR_INVALID (NULL pointers, non-positive counts), SGG_ERR_UNSUPPORTED
+ * (sizes beyond int32 indexing), SGG_ERR_HIP.
+ */
+int lora_moe_route(const int32_t* req_seg_indptr, const int32_t* req_weight_indices,
+                   int32_t num_reqs, const int32_t* topk_ids, int64_t num_tokens, int32_t top_k,
+                   int32_t num_experts, const int32_t* lora_ranks, const float* scalings,
+                   int32_t num_loras, int32_t* virtual_slots, int32_t* virtual_ranks,
+                   float* virtual_scalings, void* stream);
+
+/*
+ * lora_moe_add -- the MoE LoRA add on a fused-MoE intermediate (reading as in
+ * lora_moe_route): for every copy m = t * top_k + j of a plan over the
+ * num_tokens * top_k copies (segments by virtual expert v),
+ *     out[m, :N] += virtual_scalings[v] * B[v] (A[v] x[t])
+ * over the first virtual_ranks[v] rank rows; rows of virtual slots of rank 0
+ * (or at or past num_virtual) are unchanged.  It is lora_qkv with one slice
+ * and x row t read for the copies t * top_k + j (same kernels, same two
+ * launches, same workspace: lora_qkv_workspace_bytes(num_tokens * top_k,
+ * in_dim, 1, R, num_segments, chunk_size)).
+ *   x     device bf16 (num_tokens, in_dim), row stride ldx.
+ *   A     device bf16 (num_virtual, R, in_dim): adapter a's expert e at a*E+e.
+ *   B     device bf16 (num_virtual, N, R).
+ *   out   device bf16 (num_tokens * top_k, >= N), row stride ldo; read and
+ *         written in place.
+ *   plan arrays   the device plan of the copies (seg_indptr, seg_slots,
+ *         permutation over copies; virtual_ranks / virtual_scalings as
+ *         written by lora_moe_route).
+ * Errors as lora_qkv.
+ */
+int lora_moe_add(const void* x, int64_t ldx, int64_t num_tokens, int32_t top_k, const void* A,
+                 const void* B, int64_t N, void* out, int64_t ldo, int64_t in_dim,
+                 int32_t num_virtual, int32_t R, const int32_t* seg_indptr,
+                 const int32_t* seg_slots, int32_t num_segments, const int32_t* permutation,
+                 const int32_t* virtual_ranks, const float* virtual_scalings, int32_t chunk_size,
+                 void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * lora_set_option -- process-wide settings of the device calls; returns the
  * previous value, or -1 for an unknown name.  Not needed for normal use.
  *   "fused_stacked"  0 (default): lora_qkv makes two launches;

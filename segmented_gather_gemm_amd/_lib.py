@@ -49,6 +49,11 @@ SIGNATURES = {
         _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _pi32, _i32, _i32,
         _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp]),
     "lora_set_option": (_i64, [ctypes.c_char_p, _i64]),
+    "lora_moe_route": (ctypes.c_int, [
+        _vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp]),
+    "lora_moe_add": (ctypes.c_int, [
+        _vp, _i64, _i64, _i32, _vp, _vp, _i64, _vp, _i64, _i64, _i32, _i32,
+        _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i64, _vp]),
     "lora_a_embedding": (ctypes.c_int, [
         _vp, _vp, _i64, _vp, _i64, _i64, _i32, _i32, _i64, _vp, _vp, _i32, _vp, _vp, _i32, _vp]),
 }

@@ -184,6 +184,9 @@ class ChunkedSgmvLoRA:
         self._info_np = np.frombuffer(self._info_arr, dtype=np.int32)
         self._seg_caps = {}
         self._dev_index = self.device.index
+        self._moe = {}
+        self.moe_batch_info = None
+        self.moe_plan_info = None
 
     # ---------------------------------------------------------------- plan
     def _layout(self, s_cap, seg_cap, req_cap):
@@ -391,6 +394,77 @@ class ChunkedSgmvLoRA:
         self.cuda_graph_plan_info = self._graph_info_dev
         self.batch_info = self.cuda_graph_batch_info
         return self.cuda_graph_batch_info
+
+    def prepare_moe_lora_batch(self, topk_ids, num_experts, batch_info=None):
+        """The plan of a MoE LoRA add (PR #24007 report page: the MoE layer
+        reads each token's adapter from the per-request fields
+        req_seg_indptr / req_weight_indices and combines it with the
+        router's experts into "virtual experts").  On the GPU, with no host
+        round trip: lora_moe_route gives every top-k copy t*k + j of a token
+        its virtual expert a(t) * E + topk_ids[t, j], then lora_plan_device
+        plans the copies like a decode batch of one-token requests.
+        topk_ids: int32 (num_tokens, k) device tensor of the batch's tokens
+        (batch_info: the current plan unless given).  The result's arrays
+        are padded to a fixed capacity, so a graph may capture this call
+        with the kernels; the plan's counts and status are left in
+        ``moe_plan_info`` (int32 [8], device).  Capacity of the device
+        planner: num_tokens * k <= 4096 copies, L * E < 1024."""
+        info = self._info(batch_info)
+        if info.req_seg_indptr is None or info.req_weight_indices is None:
+            raise ValueError("the batch plan has no per-request routing fields")
+        if topk_ids.dim() != 2 or topk_ids.dtype != torch.int32 or not topk_ids.is_cuda:
+            raise TypeError("topk_ids must be an int32 (num_tokens, k) device tensor")
+        s, k = topk_ids.shape
+        if s != info.num_tokens:
+            raise ValueError(f"topk_ids has {s} rows, the batch has {info.num_tokens} tokens")
+        L, E = self.max_loras_per_batch, int(num_experts)
+        nv = L * E + 1
+        copies = s * k
+        seg_cap = B.lora_plan_max_segments(copies, nv, MIN_CHUNK_SIZE)
+        key = (copies, E)
+        bufs = self._moe.get(key)
+        if bufs is None:
+            offs = (ctypes.c_int64 * len(_NAMES))()
+            total = int(lib().lora_plan_layout(copies, seg_cap, copies, nv, offs))
+            sizes = (copies, seg_cap + 1, seg_cap, copies + 1, copies, nv, nv, seg_cap + 1,
+                     seg_cap, copies)
+            plan = torch.zeros(max(total, 1), dtype=torch.int32, device=self.device)
+            v = {name: plan[int(o):int(o) + n] for name, o, n in zip(_NAMES, offs, sizes)}
+            bufs = {"plan": plan, "v": v,
+                    "slots": torch.zeros(max(copies, 1), dtype=torch.int32, device=self.device),
+                    "vranks": torch.zeros(nv, dtype=torch.int32, device=self.device),
+                    "vscal": torch.zeros(nv, dtype=torch.float32, device=self.device),
+                    "info": torch.zeros(8, dtype=torch.int32, device=self.device)}
+            self._moe[key] = bufs
+        B.lora_moe_route(info.req_seg_indptr, info.req_weight_indices, info.bs, topk_ids, E,
+                         info.lora_ranks, info.scalings, L, bufs["slots"], bufs["vranks"],
+                         bufs["vscal"])
+        B.lora_plan_device(None, bufs["slots"][:copies], bufs["vranks"], bufs["vscal"], nv, True,
+                           self.max_chunk_size, 0, copies, seg_cap, copies, bufs["plan"],
+                           bufs["info"])
+        v = bufs["v"]
+        # typical segment length: copies per virtual expert, in whole 16-token
+        # tiles between 16 and 128 (longer segments are still covered)
+        per_expert = -(-copies // max(L * E, 1))
+        hint = max(MIN_CHUNK_SIZE, min(128, -(-per_expert // 16) * 16))
+        self.moe_plan_info = bufs["info"]
+        self.moe_batch_info = LoRABatchInfo(
+            bs=copies, num_tokens=copies, num_segments=seg_cap, max_len=hint,
+            seg_indptr=v["seg_indptr"], weight_indices=v["seg_slots"],
+            permutation=v["permutation"], lora_ranks=bufs["vranks"], scalings=bufs["vscal"],
+            use_cuda_graph=True, max_seg_len=hint, work_indptr=v["work_indptr"],
+            work_slots=v["work_slots"], num_work_segments=seg_cap, max_work_len=hint)
+        return self.moe_batch_info
+
+    def run_moe_lora_add(self, x, moe_lora_a, moe_lora_b, intermediate, top_k, moe_info=None,
+                         workspace=None):
+        """Add the LoRA deltas of a MoE layer into the fused-MoE intermediate
+        (num_tokens * top_k rows, row t*top_k + j for token t's j-th expert):
+        moe_lora_a (L, E, R, K), moe_lora_b (L, E, N, R)."""
+        info = moe_info if moe_info is not None else self.moe_batch_info
+        if info is None:
+            raise RuntimeError("prepare_moe_lora_batch has not been called")
+        return B.lora_moe_add(x, moe_lora_a, moe_lora_b, info, top_k, intermediate, workspace)
 
     # -------------------------------------------------------------- kernels
     def _info(self, pruned_batch_info=None):

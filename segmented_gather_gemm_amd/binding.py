@@ -409,6 +409,73 @@ def lora_qkv_noalloc(x, A, B, batch_info: LoRABatchInfo, slice_offsets, max_slic
     return base_output
 
 
+def lora_moe_route(req_seg_indptr, req_weight_indices, num_reqs, topk_ids, num_experts,
+                   lora_ranks, scalings, num_loras, virtual_slots, virtual_ranks,
+                   virtual_scalings):
+    """Virtual experts of the MoE LoRA add from the per-request routing fields
+    (all device tensors; see include/sgg_lora.h): virtual_slots (int32
+    [tokens * top_k]), virtual_ranks (int32) and virtual_scalings (float32)
+    [num_loras * num_experts + 1] are written on the stream."""
+    def dev(name, t, dtype, n):
+        if t.dtype != dtype or not t.is_cuda or not t.is_contiguous() or t.numel() < n:
+            raise ValueError(f"{name} must be a contiguous {dtype} device tensor of >= {n} "
+                             f"entries")
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be (num_tokens, top_k)")
+    s, k = topk_ids.shape
+    nv = num_loras * num_experts + 1
+    dev("req_seg_indptr", req_seg_indptr, torch.int32, num_reqs + 1)
+    if num_reqs:
+        dev("req_weight_indices", req_weight_indices, torch.int32, num_reqs)
+    dev("topk_ids", topk_ids, torch.int32, s * k)
+    dev("lora_ranks", lora_ranks, torch.int32, num_loras)
+    dev("scalings", scalings, torch.float32, num_loras)
+    dev("virtual_slots", virtual_slots, torch.int32, s * k)
+    dev("virtual_ranks", virtual_ranks, torch.int32, nv)
+    dev("virtual_scalings", virtual_scalings, torch.float32, nv)
+    check(lib().lora_moe_route(
+        req_seg_indptr.data_ptr(), req_weight_indices.data_ptr() if num_reqs else None,
+        int(num_reqs), topk_ids.data_ptr(), s, k, int(num_experts), lora_ranks.data_ptr(),
+        scalings.data_ptr(), int(num_loras), virtual_slots.data_ptr(),
+        virtual_ranks.data_ptr(), virtual_scalings.data_ptr(), _stream(topk_ids)))
+
+
+def lora_moe_add(x, A, B, moe_info: LoRABatchInfo, top_k, out, workspace=None):
+    """MoE LoRA add: out (tokens * top_k, N) += per copy t*top_k + j the LoRA
+    delta of its virtual expert (include/sgg_lora.h).  x (tokens, K);
+    A (num_virtual, R, K) or (L, E, R, K); B (num_virtual, N, R) or
+    (L, E, N, R); moe_info: the plan of the copies (ChunkedSgmvLoRA.
+    prepare_moe_lora_batch)."""
+    xst = _need_bf16("x", x, 2)
+    if A.dim() == 4:
+        A = A.reshape(A.shape[0] * A.shape[1], A.shape[2], A.shape[3])
+    if B.dim() == 4:
+        B = B.reshape(B.shape[0] * B.shape[1], B.shape[2], B.shape[3])
+    _need_bf16_dense("A", A, 3)
+    _need_bf16_dense("B", B, 3)
+    s, K = x.shape
+    nv, R, K2 = A.shape
+    _, N, R2 = B.shape
+    if K2 != K or R2 != R or B.shape[0] != nv:
+        raise ValueError(f"A {tuple(A.shape)} / B {tuple(B.shape)} do not match x ({K})")
+    if s * top_k != moe_info.num_tokens:
+        raise ValueError(f"x has {s} rows x top_k {top_k}, the plan has "
+                         f"{moe_info.num_tokens} copies")
+    ost = _need_bf16("out", out, 2)
+    _need_rows_cols("out", out, s * top_k, N)
+    ind, sl, nseg, hint, perm = moe_info.kernel_segments()
+    ws = workspace
+    if ws is None:
+        need = calls().lora_qkv_workspace_bytes(s * top_k, K, 1, R, nseg, hint)
+        ws = default_workspace(x.device, max(need, 1))
+    check(lib().lora_moe_add(
+        x.data_ptr(), xst[0], s, int(top_k), A.data_ptr(), B.data_ptr(), N, out.data_ptr(),
+        ost[0], K, nv, R, ind.data_ptr(), sl.data_ptr(), nseg, perm.data_ptr(),
+        moe_info.lora_ranks.data_ptr(), moe_info.scalings.data_ptr(), hint, ws.data_ptr(),
+        ws.numel(), _stream(x)))
+    return out
+
+
 def lora_a_embedding(input_ids, weights, batch_info: LoRABatchInfo, vocab_size,
                      extra_embeddings=None, out=None):
     """LoRA-A embedding lookup: ids (s,), weights (L, R, V) -> (s, R)."""

@@ -12,7 +12,7 @@ LIB = os.path.join(PKG, "libsgg_lora.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 CALLMOD = os.path.join(PKG, "_sggcall" + sysconfig.get_config_var("EXT_SUFFIX"))
 SOURCES = ["plan.cpp", "tiling.cpp", "plan_device.hip", "shrink.hip", "shrink_gemm.hip",
-           "expand.hip", "fused.hip", "lora_api.hip"]
+           "expand.hip", "fused.hip", "moe.hip", "lora_api.hip"]
 ARCH = os.environ.get("SGG_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -195,6 +195,8 @@ sgg::ShrinkParams shrink_params(const void* x, int64_t ldx, const void* A, void*
   p.partials_only = partials_only && t.ksplit > 1 ? 1 : 0;
   p.partial_bytes = static_cast<uint32_t>(t.partial_bytes < (int64_t{1} << 32) - 256
                                               ? t.partial_bytes : 0);
+  p.x_rows = s;
+  p.xdiv = 1;
   return p;
 }
 
@@ -353,14 +355,18 @@ extern "C" int lora_expand(const void* h, int64_t ldh, const void* B, int64_t N,
   return rc ? rc : sgg::ok();
 }
 
-extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B, int64_t N,
-                        void* base_output, int64_t ldo, int64_t s, int64_t in_dim,
-                        int32_t num_loras, int32_t R, const int32_t* slice_offsets,
-                        int32_t num_slices, int32_t max_slice_size, const int32_t* seg_indptr,
-                        const int32_t* seg_slots, int32_t num_segments,
-                        const int32_t* permutation, const int32_t* lora_ranks,
-                        const float* scalings, int32_t chunk_size, void* workspace,
-                        int64_t workspace_bytes, void* stream) {
+namespace {
+
+// The stacked shrink + expand of lora_qkv, over s output rows; output row r
+// reads x row r / xdiv (x has x_rows rows): 1 for lora_qkv, top_k for the
+// MoE LoRA add, whose output rows are a token's top-k copies.
+int stacked_call(const void* x, int64_t ldx, int64_t x_rows, int32_t xdiv, const void* A,
+                 const void* B, int64_t N, void* base_output, int64_t ldo, int64_t s,
+                 int64_t in_dim, int32_t num_loras, int32_t R, const int32_t* slice_offsets,
+                 int32_t num_slices, int32_t max_slice_size, const int32_t* seg_indptr,
+                 const int32_t* seg_slots, int32_t num_segments, const int32_t* permutation,
+                 const int32_t* lora_ranks, const float* scalings, int32_t chunk_size,
+                 void* workspace, int64_t workspace_bytes, void* stream) {
   int rc = check_plan(s, num_segments, seg_indptr, seg_slots, permutation, lora_ranks, num_loras,
                       chunk_size);
   if (rc) return rc;
@@ -390,15 +396,18 @@ extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B
   float* part = reinterpret_cast<float*>(ws + sgg::kCounterBytes + hbytes);
   const int64_t CR = static_cast<int64_t>(num_slices) * R;
   const sgg::ShrinkTiling ts = shrink_tiling(
-      s, in_dim, num_slices * R, num_segments, chunk_size, gemm_addressable(s, ldx, in_dim, CR));
+      s, in_dim, num_slices * R, num_segments, chunk_size,
+      gemm_addressable(x_rows, ldx, in_dim, CR));
   SGG_CHECK(ts.grid < (int64_t{1} << 31), SGG_ERR_UNSUPPORTED, "shrink grid too large");
   SGG_CHECK(ts.partial_bytes < (int64_t{1} << 32) - 256, SGG_ERR_UNSUPPORTED,
             "split-K partials of %" PRId64 " bytes exceed 32-bit offsets", ts.partial_bytes);
   if (slice_offsets[num_slices] == 0) return sgg::ok();  // no output columns: nothing changes
   const bool split = ts.ksplit > 1;
-  const sgg::ShrinkParams ps =
+  sgg::ShrinkParams ps =
       shrink_params(x, ldx, A, h, CR, s, in_dim, num_loras, num_slices, R, seg_indptr,
                     seg_slots, num_segments, permutation, lora_ranks, counters, part, true, ts);
+  ps.x_rows = x_rows;
+  ps.xdiv = xdiv;
   sgg::ExpandTiling te{};
   const sgg::ExpandParams pe =
       expand_params(h, CR, B, N, base_output, ldo, s, num_loras, R, slice_offsets, num_slices,
@@ -413,7 +422,7 @@ extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B
   // it in rounding.  Measured on the decode batch it is slower than the two
   // launches (a longer chain of dependent device-wide memory round trips), so
   // it is off by default.
-  if (g_fused_stacked.load(std::memory_order_relaxed) != 0 && split && CR <= 48 &&
+  if (g_fused_stacked.load(std::memory_order_relaxed) != 0 && split && CR <= 48 && xdiv == 1 &&
       num_segments <= sgg::kFusedMaxSegments) {
     sgg::ExpandTiling tf{};
     sgg::ExpandParams pf =
@@ -456,6 +465,81 @@ extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B
   if (rc) return rc;
   rc = launch_status(sgg::launch_expand(pe, te, st), "expand");
   return rc ? rc : sgg::ok();
+}
+
+}  // namespace
+
+extern "C" int lora_qkv(const void* x, int64_t ldx, const void* A, const void* B, int64_t N,
+                        void* base_output, int64_t ldo, int64_t s, int64_t in_dim,
+                        int32_t num_loras, int32_t R, const int32_t* slice_offsets,
+                        int32_t num_slices, int32_t max_slice_size, const int32_t* seg_indptr,
+                        const int32_t* seg_slots, int32_t num_segments,
+                        const int32_t* permutation, const int32_t* lora_ranks,
+                        const float* scalings, int32_t chunk_size, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
+  return stacked_call(x, ldx, s, 1, A, B, N, base_output, ldo, s, in_dim, num_loras, R,
+                      slice_offsets, num_slices, max_slice_size, seg_indptr, seg_slots,
+                      num_segments, permutation, lora_ranks, scalings, chunk_size, workspace,
+                      workspace_bytes, stream);
+}
+
+extern "C" int lora_moe_route(const int32_t* req_seg_indptr, const int32_t* req_weight_indices,
+                              int32_t num_reqs, const int32_t* topk_ids, int64_t num_tokens,
+                              int32_t top_k, int32_t num_experts, const int32_t* lora_ranks,
+                              const float* scalings, int32_t num_loras, int32_t* virtual_slots,
+                              int32_t* virtual_ranks, float* virtual_scalings, void* stream) {
+  SGG_CHECK(num_reqs >= 0 && num_tokens >= 0, SGG_ERR_INVALID,
+            "num_reqs=%d and num_tokens=%" PRId64 " must be non-negative", num_reqs, num_tokens);
+  SGG_CHECK(top_k >= 1 && num_experts >= 1 && num_loras >= 1, SGG_ERR_INVALID,
+            "top_k=%d, num_experts=%d and num_loras=%d must be positive", top_k, num_experts,
+            num_loras);
+  SGG_CHECK(num_tokens * top_k <= INT32_MAX, SGG_ERR_UNSUPPORTED,
+            "num_tokens * top_k above int32 indexing");
+  SGG_CHECK(static_cast<int64_t>(num_loras) * num_experts < INT32_MAX, SGG_ERR_UNSUPPORTED,
+            "num_loras * num_experts above int32 indexing");
+  SGG_CHECK(req_seg_indptr && lora_ranks && scalings && virtual_ranks && virtual_scalings,
+            SGG_ERR_INVALID, "req_seg_indptr, lora_ranks, scalings or a virtual table is NULL");
+  SGG_CHECK(req_weight_indices || num_reqs == 0, SGG_ERR_INVALID, "req_weight_indices is NULL");
+  SGG_CHECK((topk_ids && virtual_slots) || num_tokens == 0, SGG_ERR_INVALID,
+            "topk_ids or virtual_slots is NULL");
+  sgg::MoeRouteParams p{};
+  p.req_seg_indptr = req_seg_indptr;
+  p.req_weight_indices = req_weight_indices;
+  p.topk_ids = topk_ids;
+  p.ranks = lora_ranks;
+  p.scalings = scalings;
+  p.slots = virtual_slots;
+  p.vranks = virtual_ranks;
+  p.vscalings = virtual_scalings;
+  p.copies = num_tokens * top_k;
+  p.bs = num_reqs;
+  p.top_k = top_k;
+  p.E = num_experts;
+  p.L = num_loras;
+  const int rc = launch_status(sgg::launch_moe_route(p, static_cast<hipStream_t>(stream)),
+                               "MoE routing");
+  return rc ? rc : sgg::ok();
+}
+
+extern "C" int lora_moe_add(const void* x, int64_t ldx, int64_t num_tokens, int32_t top_k,
+                            const void* A, const void* B, int64_t N, void* out, int64_t ldo,
+                            int64_t in_dim, int32_t num_virtual, int32_t R,
+                            const int32_t* seg_indptr, const int32_t* seg_slots,
+                            int32_t num_segments, const int32_t* permutation,
+                            const int32_t* virtual_ranks, const float* virtual_scalings,
+                            int32_t chunk_size, void* workspace, int64_t workspace_bytes,
+                            void* stream) {
+  SGG_CHECK(num_tokens >= 0 && top_k >= 1, SGG_ERR_INVALID,
+            "num_tokens=%" PRId64 " and top_k=%d: need num_tokens >= 0 and top_k >= 1",
+            num_tokens, top_k);
+  SGG_CHECK(num_tokens * top_k <= INT32_MAX, SGG_ERR_UNSUPPORTED,
+            "num_tokens * top_k above int32 indexing");
+  SGG_CHECK(N <= INT32_MAX, SGG_ERR_UNSUPPORTED, "N above int32 offsets");
+  const int32_t offs[2] = {0, static_cast<int32_t>(N)};
+  return stacked_call(x, ldx, num_tokens, top_k, A, B, N, out, ldo, num_tokens * top_k, in_dim,
+                      num_virtual, R, offs, 1, static_cast<int32_t>(N), seg_indptr, seg_slots,
+                      num_segments, permutation, virtual_ranks, virtual_scalings, chunk_size,
+                      workspace, workspace_bytes, stream);
 }
 
 extern "C" int64_t lora_set_option(const char* name, int64_t value) {

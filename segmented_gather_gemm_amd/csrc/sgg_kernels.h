@@ -39,6 +39,10 @@ struct ShrinkParams {
   int32_t counter_cap;        // entries in `counters`
   int32_t partials_only;      // ksplit > 1: leave the partials for the expand, write no h
   uint32_t partial_bytes;     // size of `partial` (below 2^32)
+  // Row of x read for output row r: r / xdiv (1 normally; the MoE LoRA add
+  // has top_k output rows per token, x_rows = s / top_k rows of x).
+  int64_t x_rows;
+  int32_t xdiv;
 };
 
 // LoRA-B expand (scale, add into base) over the segments of a plan.
@@ -133,6 +137,24 @@ struct ExpandTiling {
   int pairs, ks;     // 32-column fragment pairs per wave, 32-deep rank steps
   int64_t grid;
 };
+
+// MoE routing: per top-k copy of every token, its virtual expert (adapter x
+// expert) from the per-request routing fields; and the virtual rank /
+// scaling tables (L*E entries plus one of rank 0 for copies without a valid
+// adapter or expert).
+struct MoeRouteParams {
+  const int32_t* req_seg_indptr;      // [bs + 1]
+  const int32_t* req_weight_indices;  // [bs]
+  const int32_t* topk_ids;            // [tokens][top_k]
+  const int32_t* ranks;               // [L]
+  const float* scalings;              // [L]
+  int32_t* slots;                     // [tokens * top_k] out
+  int32_t* vranks;                    // [L * E + 1] out
+  float* vscalings;                   // [L * E + 1] out
+  int64_t copies;                     // tokens * top_k
+  int32_t bs, top_k, E, L;
+};
+hipError_t launch_moe_route(const MoeRouteParams& p, hipStream_t stream);
 
 hipError_t launch_shrink(const ShrinkParams& p, const ShrinkTiling& t, hipStream_t stream);
 hipError_t launch_shrink_gemm(const ShrinkParams& p, int bm, int bn, int64_t grid,

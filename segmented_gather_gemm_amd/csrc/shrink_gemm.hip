@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
       static_cast<short>(0), static_cast<int>(static_cast<uint32_t>(p.CR * p.K * 2)), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.x), static_cast<short>(0),
-      static_cast<int>(static_cast<uint32_t>(((p.s - 1) * p.ldx + p.K) * 2)), kRsrcWord3);
+      static_cast<int>(static_cast<uint32_t>(((p.x_rows - 1) * p.ldx + p.K) * 2)), kRsrcWord3);
   // A rows of this thread's loads (tile rows BM + lrow + 32*j), fixed for the
   // workgroup.  Rows past c*R or past the slot's rank (padding, possibly NaN)
   // read row 0 of the slot instead, a live row that stays in L1: their
@@ -148,8 +148,8 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
     for (int j = 0; j < XPER; ++j) {
       const int r = lrow + 32 * j;
       const int pr = r < mcount ? p.perm[m0 + r] : p.perm[m0];
-      xoff[j] = static_cast<uint32_t>(static_cast<int64_t>((pr >= 0 && pr < p.s) ? pr : 0) *
-                                      p.ldx * 2 + 16 * lcol);
+      const int xr = (pr >= 0 && pr < p.s) ? (p.xdiv > 1 ? pr / p.xdiv : pr) : 0;
+      xoff[j] = static_cast<uint32_t>(static_cast<int64_t>(xr) * p.ldx * 2 + 16 * lcol);
     }
 
     // DEPTH register sets of prefetch: step t + DEPTH is requested while

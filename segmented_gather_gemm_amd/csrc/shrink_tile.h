@@ -140,7 +140,8 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int seg, int 
     for (int i = 0; i < XL; ++i) {
       const int mm = 8 * i + lrow;
       const int r = mm < mcount ? p.perm[m0 + mm] : 0;
-      xrow[i] = (r >= 0 && r < p.s) ? r : 0;  // in-bounds stand-in, zeroed at the fragment read
+      // in-bounds stand-in for an invalid row, zeroed at the fragment read
+      xrow[i] = (r >= 0 && r < p.s) ? (p.xdiv > 1 ? r / p.xdiv : r) : 0;
     }
     bool tvalid[MF];
 #pragma unroll

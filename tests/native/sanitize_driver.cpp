@@ -60,6 +60,10 @@ hipError_t launch_plan_copy(const int32_t*, int32_t*, int64_t, int32_t*, int32_t
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_moe_route(const MoeRouteParams&, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 int64_t fused_resident_blocks(int, int, int) { return int64_t{1} << 30; }
 hipError_t launch_fused(const ShrinkParams&, const ShrinkTiling&, const ExpandParams&,
                         const ExpandTiling&, const FusedSync&, hipStream_t) {

@@ -250,6 +250,41 @@ def test_qkv_rejects():
     assert L.lora_qkv(*args, FAKE, need - 1, NULL) == -3 and "workspace" in _err()
 
 
+def test_moe_route_rejects():
+    def route(**kw):
+        a = dict(indptr=FAKE, wi=FAKE, bs=4, topk=FAKE, s=8, k=2, E=8, ranks=FAKE, scal=FAKE,
+                 L=4, slots=FAKE, vr=FAKE, vs=FAKE)
+        a.update(kw)
+        return L.lora_moe_route(a["indptr"], a["wi"], a["bs"], a["topk"], a["s"], a["k"],
+                                a["E"], a["ranks"], a["scal"], a["L"], a["slots"], a["vr"],
+                                a["vs"], NULL)
+    assert route(k=0) == -1 and "top_k" in _err()
+    assert route(E=0) == -1 and "num_experts" in _err()
+    assert route(s=-1) == -1
+    assert route(indptr=NULL) == -1 and "req_seg_indptr" in _err()
+    assert route(wi=NULL) == -1 and "req_weight_indices" in _err()
+    assert route(topk=NULL) == -1 and "topk_ids" in _err()
+    assert route(s=1 << 30, k=4) == -2 and "int32" in _err()
+    assert route(L=1 << 20, E=1 << 12) == -2 and "int32" in _err()
+
+
+def test_moe_add_rejects():
+    def add(ws=NULL, wsb=0, **kw):
+        a = dict(x=FAKE, ldx=512, s=64, k=2, A=FAKE, B=FAKE, N=256, out=FAKE, ldo=256, K=512,
+                 nv=32, R=16, indptr=FAKE, slots=FAKE, nseg=8, perm=FAKE, ranks=FAKE,
+                 scal=FAKE, chunk=16)
+        a.update(kw)
+        return L.lora_moe_add(a["x"], a["ldx"], a["s"], a["k"], a["A"], a["B"], a["N"],
+                              a["out"], a["ldo"], a["K"], a["nv"], a["R"], a["indptr"],
+                              a["slots"], a["nseg"], a["perm"], a["ranks"], a["scal"],
+                              a["chunk"], ws, wsb, NULL)
+    assert add(k=0) == -1 and "top_k" in _err()
+    assert add(s=1 << 30, k=4) == -2 and "int32" in _err()
+    assert add() == -1 and "workspace" in _err()
+    assert add(ws=FAKE, wsb=1 << 30, ldo=128) == -1 and "ldo" in _err()
+    assert add(ws=FAKE, wsb=1 << 30, ldx=256) == -1 and "ldx" in _err()
+
+
 def test_workspace_sizes():
     # decode shapes split K across workgroups and need scratch; prefill shapes do not
     assert L.lora_shrink_workspace_bytes(256, 4096, 3, 16, 8, 128) > 0

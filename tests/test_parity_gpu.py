@@ -15,6 +15,7 @@ import pytest
 import torch
 
 from oracle import lora as ol
+from oracle import moe as om
 from oracle import plan as op
 from synth import Batch, Projection, draw_batch, draw_embedding, draw_projection, to_f64
 
@@ -1261,3 +1262,112 @@ def test_plan_upload_from_pageable_staging():
     assert got[offs[2]:offs[2] + cap].tolist() == ref["seg_slots"]
     assert got[offs[5]:offs[5] + L].tolist() == ranks.tolist()
     assert info[0] == ref["num_segments"] and info[1] == ref["chunk_size"] and info[3] == s
+
+
+# ------------------------------------------------------------- MoE LoRA add
+
+def _moe_case(seed, lens, L, ranks, E, k, K, N, R, bad_experts=0):
+    """A batch planned by the backend plus MoE routing and weights (bf16):
+    topk_ids (s, k) with `bad_experts` entries out of range."""
+    rng = np.random.default_rng(seed)
+    bs = len(lens)
+    slots = rng.integers(0, L, size=bs).tolist()
+    scal = rng.uniform(0.5, 2.0, size=L).tolist()
+    s = int(sum(lens))
+    topk = rng.integers(0, E, size=(s, k)).astype(np.int32)
+    for i in range(bad_experts):
+        topk[rng.integers(0, s), rng.integers(0, k)] = [-1, E, E + 7][i % 3]
+    bf = lambda a: torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16)
+    t = {"x": bf(rng.standard_normal((s, K))),
+         "A": bf(rng.standard_normal((L, E, R, K)) * 0.05),
+         "B": bf(rng.standard_normal((L, E, N, R)) * 0.05),
+         "out": bf(rng.standard_normal((s * k, N)))}
+    return slots, scal, topk, t
+
+
+def _moe_want(t, lens, slots, ranks, scal, topk, E):
+    """Oracle result; rows of out-of-range experts keep their values."""
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    ok = (topk >= 0) & (topk < E)
+    want = om.moe_lora_add(to_f64(t["x"]), to_f64(t["A"]), to_f64(t["B"]), to_f64(t["out"]),
+                           indptr, slots, np.where(ok, topk, 0), ranks, scal)
+    keep = ~ok.reshape(-1)
+    want[keep] = to_f64(t["out"])[keep]
+    return want, indptr
+
+
+@pytest.mark.parametrize("case", [
+    ("extend", [3, 1, 5, 2, 1, 4, 37, 60, 9, 128], 4, [16, 8, 0, 16], 8, 2, 512, 256, 16, 0),
+    ("decode", [1] * 300, 6, [16, 16, 12, 8, 16, 4], 8, 2, 1024, 384, 16, 0),
+    ("top4_bad_experts", [2, 7, 1, 30, 5], 3, [32, 0, 24], 4, 4, 256, 136, 32, 5),
+], ids=lambda c: c[0])
+def test_moe_lora_add_matches_oracle(case):
+    """Per-request routing to virtual experts (lora_moe_route, bit-exact
+    against the oracle), the copies planned on the GPU, and the MoE LoRA add
+    into the fused-MoE intermediate against the oracle; copies whose expert
+    id is out of range keep their rows bit for bit."""
+    name, lens, L, ranks, E, k, K, N, R, bad = case
+    sgg = _sgg()
+    slots, scal, topk, t = _moe_case(zlib.crc32(name.encode()) % 1000, lens, L, ranks, E, k, K, N, R,
+                                     bad_experts=bad)
+    be = sgg.ChunkedSgmvLoRA(L, 128, DEV)
+    decode = name == "decode"
+    be.prepare_lora_batch(None if decode else lens, slots, ranks, scal, is_decode=decode)
+    topk_d = torch.from_numpy(topk).to(DEV)
+    info = be.prepare_moe_lora_batch(topk_d, E)
+    out = t["out"].to(DEV)
+    be.run_moe_lora_add(t["x"].to(DEV), t["A"].to(DEV), t["B"].to(DEV), out, k)
+    torch.cuda.synchronize()
+    assert int(be.moe_plan_info[6].item()) == 0, "the copies' plan was rejected"
+    want, indptr = _moe_want(t, lens, slots, ranks, scal, topk, E)
+    ok = (topk >= 0) & (topk < E)
+    v_want = om.virtual_experts(indptr, slots, np.where(ok, topk, 0), E)
+    v_want[~ok.reshape(-1)] = L * E
+    got_v = be._moe[(len(topk) * k, E)]["slots"][:len(topk) * k].cpu().numpy()
+    assert np.array_equal(got_v, v_want)
+    keep = ~ok.reshape(-1)
+    assert torch.equal(out[torch.from_numpy(keep).to(DEV)].view(torch.int16),
+                       t["out"][torch.from_numpy(keep)].to(DEV).view(torch.int16))
+    assert_close(out, want, f"MoE LoRA add ({name})")
+
+
+def test_moe_lora_add_in_a_graph():
+    """Routing, the GPU plan of the copies and the add captured in one graph;
+    replays with new router choices written into the captured topk tensor,
+    eager work between them, each checked against the oracle."""
+    sgg = _sgg()
+    lens, L, ranks, E, k, K, N, R = [1] * 200, 4, [16, 8, 16, 0], 8, 2, 512, 256, 16
+    slots, scal, topk, t = _moe_case(5, lens, L, ranks, E, k, K, N, R)
+    be = sgg.ChunkedSgmvLoRA(L, 128, DEV)
+    be.prepare_lora_batch(None, slots, ranks, scal, is_decode=True)
+    topk_d = torch.from_numpy(topk).to(DEV)
+    x, A, Bw = t["x"].to(DEV), t["A"].to(DEV), t["B"].to(DEV)
+    out0 = t["out"].to(DEV)
+    out = out0.clone()
+    ws = torch.zeros(16 << 20, dtype=torch.uint8, device=DEV)
+
+    def step():
+        info = be.prepare_moe_lora_batch(topk_d, E)
+        sgg.lora_moe_add(x, A, Bw, info, k, out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    for trial in range(3):
+        topk = rng.integers(0, E, size=topk.shape).astype(np.int32)
+        topk_d.copy_(torch.from_numpy(topk))
+        out.copy_(out0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want, _ = _moe_want(t, lens, slots, ranks, scal, topk, E)
+        assert_close(out, want, f"MoE graph replay {trial}")
+        torch.mm(torch.randn(64, 64, device=DEV), torch.randn(64, 64, device=DEV))
