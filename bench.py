@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_prefill_kernels_hbm_traffic.txt")
-LEGS = ("prefill", "skewed", "full", "lm_head", "device_plan", "short")
+LEGS = ("prefill", "skewed", "full", "lm_head", "device_plan", "short", "moe")
 
 
 def parse():
@@ -627,6 +627,15 @@ def run_prefill(device, chunks=(16, 32, 64, 128), steps=20, warmup=3):
         res[f"chunk{mc}"] = measure_projection(device, b, proj, [t], mc, steps, warmup)
     res["workload"] = ("prefill gate_up, 32 requests (s=%d), 32 adapters Zipf(1.1), r=64, "
                        "4096 -> 2x14336" % b.num_tokens)
+    # the shrink's opt-in segment-pair tiles (256 tokens, K in two ranges), for the record
+    import segmented_gather_gemm_amd as sgg
+    old = sgg.lora_set_option("shrink_pair_tiles", 1)
+    try:
+        m = measure_projection(device, b, proj, [t], chunks[-1], steps, warmup)
+    finally:
+        sgg.lora_set_option("shrink_pair_tiles", old)
+    res["segment_pair_tiles"] = {"chunk": chunks[-1], "shrink": m["shrink"],
+                                 "stacked": m["stacked"]}
     # the expand next to a device copy of its algorithmic bytes
     exp_bytes = algo_counts(b, proj, 16)["expand"]["bytes"]
     del t
@@ -847,6 +856,76 @@ def run_short_segments(device, steps=50, warmup=5, n_sets=8):
             out["segments"] = m["segments"]
         res[name] = out
         del sets
+    return res
+
+
+def run_moe(device, steps=50, warmup=5, n_sets=8):
+    """MoE LoRA add on a decode batch (256 one-token requests, 8 adapters,
+    r=16) routed top-2 over 8 experts, LoRA on the experts' up projection
+    (4096 -> 14336): per step, lora_moe_route + lora_plan_device (the copies'
+    plan on the GPU) and lora_moe_add into the fused-MoE intermediate
+    (512 rows).  HIP events around each call, back to back."""
+    import torch
+    import segmented_gather_gemm_amd as sgg
+    rng = np.random.default_rng(20261204)
+    s, L, E, k, K, N, R = 256, 8, 8, 2, 4096, 14336, 16
+    slots = rng.integers(0, L, s).tolist()
+    ranks, scal = [R] * L, [1.0] * L
+    be = sgg.ChunkedSgmvLoRA(L, 128, device)
+    be.prepare_lora_batch(None, slots, ranks, scal, is_decode=True)
+    bf = lambda a: torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).to(device)
+    sets = []
+    for i in range(n_sets):
+        topk = np.stack([rng.permutation(E)[:k] for _ in range(s)]).astype(np.int32)
+        sets.append({"topk": torch.from_numpy(topk).to(device),
+                     "x": bf(rng.standard_normal((s, K))),
+                     "A": bf(rng.standard_normal((L, E, R, K)) * 0.02),
+                     "B": bf(rng.standard_normal((L, E, N, R)) * 0.02),
+                     "out": bf(rng.standard_normal((s * k, N)))})
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream(device)
+    infos = {}
+
+    def plan(i):
+        infos[i % n_sets] = be.prepare_moe_lora_batch(sets[i % n_sets]["topk"], E)
+
+    def add(i):
+        st = sets[i % n_sets]
+        sgg.lora_moe_add(st["x"], st["A"], st["B"], be.moe_batch_info, k, st["out"],
+                         workspace=ws)
+
+    res = {"workload": f"MoE LoRA add: decode {s} x 1 token, {L} adapters r={R}, top-{k} of "
+                       f"{E} experts, expert up projection {K} -> {N}; {s * k} copies over "
+                       f"{L * E} virtual experts", "input_sets": n_sets}
+    for name, fn in (("route_and_plan", plan), ("plan_then_add", None)):
+        if fn is None:
+            def fn(i):
+                plan(i)
+                add(i)
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        held = hold_stream(stream, 5.0 + 0.1 * steps)
+        e0.record(stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(stream)
+        b2b = not held.query()
+        torch.cuda.synchronize()
+        res[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
+        res[name + "_back_to_back"] = b2b
+    add_us = res["plan_then_add_us"] - res["route_and_plan_us"]
+    # algorithmic bytes of the add: x once, each active virtual expert's A and
+    # B once, the intermediate rows read and written once
+    act = len({(a, int(e)) for st in sets[:1] for a, row in zip(slots, st["topk"].cpu().numpy())
+               for e in row})
+    by = 2 * s * K + act * R * (K + N) * 2 + 2 * 2 * s * k * N
+    res["add_us"] = round(add_us, 2)
+    res["add_algo_bytes"] = int(by)
+    res["add_gbs"] = round(by / (add_us * 1e-6) / 1e9, 1)
+    res["add_hbm_frac"] = round(by / (add_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    res["tokens_per_s"] = round(s / (res["plan_then_add_us"] * 1e-6), 1)
     return res
 
 
@@ -1111,7 +1190,8 @@ def main():
                "full": ("full layer sweep", lambda: run_full(device, args.full_layers)),
                "lm_head": ("lm_head pass", lambda: run_lm_head(device)),
                "device_plan": ("device planner", lambda: run_device_plan(device)),
-               "short": ("short segments: MFMA and VALU shrink", lambda: run_short_segments(device))}
+               "short": ("short segments: MFMA and VALU shrink", lambda: run_short_segments(device)),
+               "moe": ("MoE LoRA add", lambda: run_moe(device))}
     for leg in legs:
         print(f"# {runners[leg][0]}", file=sys.stderr, flush=True)
         line[leg] = runners[leg][1]()

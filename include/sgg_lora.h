@@ -429,6 +429,12 @@ int lora_moe_add(const void* x, int64_t ldx, int64_t num_tokens, int32_t top_k, 
  *                    vector ALU (cross-lane reductions).  Same bytes read,
  *                    results equal to rounding; measured slower, kept for
  *                    comparison.
+ *   "shrink_pair_tiles"  0 (default); 1: long-segment batches with c*R
+ *                    above 64 (prefill) take shrink tiles of 256 tokens over
+ *                    pairs of consecutive same-slot work segments, with K
+ *                    split in two (the shrink then needs a split-K workspace,
+ *                    see lora_shrink_workspace_bytes).  Results equal to
+ *                    rounding; measured slower, kept for comparison.
  *   "fused_trace"    a diagnostic: the device address (as an integer) of a
  *                    zeroed buffer of 32 * "fused_trace_blocks" bytes, or 0
  *                    (default, off).  While set, each one-launch stacked call

@@ -18,6 +18,7 @@ namespace {
 std::atomic<int64_t> g_fused_stacked{0};
 std::atomic<int64_t> g_fused_ksplit{0};
 std::atomic<int64_t> g_shrink_valu{0};
+std::atomic<int64_t> g_shrink_pair_tiles{0};
 std::atomic<int64_t> g_fused_trace{0};          // device address of a block timeline, or 0
 std::atomic<int64_t> g_fused_trace_blocks{0};
 std::atomic<int64_t> g_expand_deal_tiles{1};
@@ -153,11 +154,14 @@ int launch_status(hipError_t e, const char* what) {
   return SGG_OK;
 }
 
-// The shrink tiling of a call: choose_shrink_tiling, re-tiled for the VALU
-// form when the "shrink_valu" option is on.
+// The shrink tiling of a call: choose_shrink_tiling (its segment-pair tiles
+// only with the "shrink_pair_tiles" option on), re-tiled for the VALU form
+// when the "shrink_valu" option is on.
 sgg::ShrinkTiling shrink_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk,
                                 bool gemm_ok = true) {
-  sgg::ShrinkTiling t = sgg::choose_shrink_tiling(s, K, CR, num_segments, chunk, gemm_ok);
+  const bool pair_ok = g_shrink_pair_tiles.load(std::memory_order_relaxed) != 0;
+  sgg::ShrinkTiling t =
+      sgg::choose_shrink_tiling(s, K, CR, num_segments, chunk, gemm_ok, pair_ok);
   if (g_shrink_valu.load(std::memory_order_relaxed) != 0)
     sgg::use_valu_tiles(&t, s, num_segments, chunk);
   return t;
@@ -552,6 +556,8 @@ extern "C" int64_t lora_set_option(const char* name, int64_t value) {
   if (std::strcmp(name, "expand_deal_tiles") == 0)
     return g_expand_deal_tiles.exchange(value != 0);
   if (std::strcmp(name, "shrink_valu") == 0) return g_shrink_valu.exchange(value != 0);
+  if (std::strcmp(name, "shrink_pair_tiles") == 0)
+    return g_shrink_pair_tiles.exchange(value != 0);
   if (std::strcmp(name, "fused_trace") == 0) return g_fused_trace.exchange(value);
   if (std::strcmp(name, "fused_trace_blocks") == 0)
     return g_fused_trace_blocks.exchange(value < 0 ? 0 : value);

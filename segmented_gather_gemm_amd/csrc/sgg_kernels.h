@@ -115,7 +115,7 @@ struct EmbeddingParams {
 // Tile choice for the shrink (also sizes its workspace).
 struct ShrinkTiling {
   int gemm;          // 1: shrink_gemm_kernel with bm x bn tiles; 0: split-K shrink_kernel
-  int bm, bn;        // gemm tile (tokens x stacked rank rows)
+  int bm, bn;        // gemm tile (tokens x stacked rank rows); bm = 256: segment pairs, K split
   int mf, nf;        // split-K kernel: row / column fragments of 16
   int mblocks, nblocks, ksplit;
   int64_t kps;
@@ -124,9 +124,11 @@ struct ShrinkTiling {
   int valu;          // split-K kernel: tiles of at most 4 tokens on the VALU (mf 1, nf <= 3)
 };
 // gemm_ok: the GEMM tiles may be chosen (their buffer loads address x and
-// each slot's A block with 32-bit byte offsets).
+// each slot's A block with 32-bit byte offsets).  pair_ok: the GEMM tiles
+// over segment pairs with K split (bm = 256) may be chosen; they need a
+// split-K workspace (partial_bytes) where the other GEMM tiles need none.
 ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk,
-                                  bool gemm_ok = true);
+                                  bool gemm_ok = true, bool pair_ok = false);
 // Re-tile a split-K kernel tiling to 16-token tiles whose short tiles (at
 // most 4 tokens) compute on the VALU; unchanged where that kernel form does
 // not apply (GEMM tiles, more than 48 rank rows per tile, too many arrival

@@ -37,6 +37,7 @@
 // tiles: 97 us against 122 us).
 #include "sgg_device.h"
 #include "sgg_kernels.h"
+#include "shrink_tile.h"
 
 namespace sgg {
 
@@ -55,8 +56,8 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint
                                        rsrc, static_cast<int>(voff), soff, 0));
 }
 
-template <int BM, int BN, int WM, int DEPTH>
-__global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
+template <int BM, int BN, int WM, int DEPTH, bool PAIR = false>
+__global__ __launch_bounds__(256, PAIR ? 1 : 2) void shrink_gemm_kernel(ShrinkParams p) {
   constexpr int WN = 4 / WM;
   constexpr int FM = BM / (16 * WM);        // token fragments per wave
   constexpr int FN = BN / (16 * WN);        // rank-row fragments per wave
@@ -66,6 +67,7 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
   constexpr int STAGE = ROWS * 128;         // bytes of one LDS stage
   static_assert(FM >= 1 && FN >= 1 && ROWS % 32 == 0, "tile shape");
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  __shared__ int last_flag;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -73,15 +75,30 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
   const int wm = wave % WM, wn = wave / WM;
 
   int seg, item;
-  segment_round_robin(blockIdx.x, p.mblocks * p.nblocks, &seg, &item);
+  segment_round_robin(blockIdx.x, p.mblocks * p.nblocks * (PAIR ? p.ksplit : 1), &seg, &item);
   if (seg >= p.num_segments) return;
+  int split = 0;
+  if constexpr (PAIR) {
+    split = item / (p.mblocks * p.nblocks);
+    item %= p.mblocks * p.nblocks;
+  }
   const int mb0 = item % p.mblocks;
   const int nb = item / p.mblocks;
+  const int slot = p.seg_slots[seg];
   // segment bounds, clamped to [0, s) so a malformed plan stays in bounds
   const int lo = max(p.seg_indptr[seg], 0);
-  const int hi = min(static_cast<int64_t>(p.seg_indptr[seg + 1]), p.s);
+  int64_t end = p.seg_indptr[seg + 1];
+  if constexpr (PAIR) {
+    // Tiles over pairs (2i, 2i+1) of consecutive segments of one slot (a
+    // contiguous range of sorted positions); the odd one of a pair exits.
+    if (seg & 1) {
+      if (p.seg_slots[seg - 1] == slot) return;
+    } else if (seg + 1 < p.num_segments && p.seg_slots[seg + 1] == slot) {
+      end = p.seg_indptr[seg + 2];
+    }
+  }
+  const int hi = min(end, p.s);
   if (hi <= lo) return;
-  const int slot = p.seg_slots[seg];
   const bool slot_ok = slot >= 0 && slot < p.L;
   int rho = slot_ok ? p.ranks[slot] : 0;
   rho = rho < 0 ? 0 : (rho > p.R ? p.R : rho);
@@ -117,8 +134,18 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
     for (int k = n0 / p.R; k * p.R < n1 && !tile_live; ++k)
       tile_live = max(n0, k * p.R) - k * p.R < rho;
   }
-  const int nk = static_cast<int>((p.K + 63) / 64);
+  // 64-deep K steps [kt0, kt0 + nk) of this workgroup (PAIR: split `split`
+  // of p.ksplit ranges of p.kps)
+  const int nk_all = static_cast<int>((p.K + 63) / 64);
+  int kt0 = 0, nk = nk_all;
+  if constexpr (PAIR) {
+    const int per = static_cast<int>(p.kps / 64);
+    kt0 = split * per;
+    nk = nk_all - kt0 < per ? nk_all - kt0 : per;
+  }
   const bool ktail = (p.K & 63) != 0;
+  const bool dead = rho == 0 || !tile_live;
+  if (PAIR && dead && split != 0) return;  // split 0 alone writes the zero rows
 
   // Fragment role: row (lane%16) of a fragment, k group (lane/16).
   const int frow = lane & 15;
@@ -130,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
     const int m0 = lo + mb * BM;
     const int mcount = hi - m0 < BM ? hi - m0 : BM;
 
-    if (rho == 0 || !tile_live) {  // base model slot or padding rows: zero rows of h
+    if (dead) {  // base model slot or padding rows: zero rows of h
       for (int q = tid; q < mcount * (BN / 4); q += 256) {
         const int mm = q / (BN / 4);
         const int n = nb * BN + 4 * (q % (BN / 4));
@@ -159,10 +186,11 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
     uint4 xl[DEPTH][XPER], al[DEPTH][APER];
     // chunk lcol of step kt lies past a ragged end of K: it contributes zero
     auto past_k = [&](int kt) {
-      return ktail && kt == nk - 1 && static_cast<int64_t>(kt) * 64 + 8 * lcol >= p.K;
+      return ktail && kt0 + kt == nk_all - 1 &&
+             static_cast<int64_t>(kt0 + kt) * 64 + 8 * lcol >= p.K;
     };
     auto issue = [&](int kt, uint4 (&xs)[XPER], uint4 (&as)[APER]) {
-      const int soff = kt * 128;
+      const int soff = (kt0 + kt) * 128;
 #pragma unroll
       for (int j = 0; j < XPER; ++j) xs[j] = buffer_load16(xrsrc, xoff[j], soff);
 #pragma unroll
@@ -240,6 +268,36 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
       }
     }
 
+    if (PAIR && p.ksplit > 1) {
+      // Split K: this range's f32 partial (rows past the rank as zero),
+      // written through to the device's coherence point, indexed by sorted
+      // position; then the arrival count and, unless the stacked call's
+      // expand sums the partials itself, the last arriver's reduction.
+      const __amdgpu_buffer_rsrc_t prsrc = buffer_rsrc(p.partial, p.partial_bytes);
+#pragma unroll
+      for (int f = 0; f < FM; ++f) {
+        const int mm = xr0 + 16 * f + frow;
+        if (mm >= mcount) continue;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          const int n = nb * BN + (ar0 - BM) + 16 * i + 4 * fgrp;
+          if (n >= p.CR) continue;
+          f32x4 v = acc[i][f];
+          const int j0 = n % p.R;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j0 + e >= rho) v[e] = 0.f;
+          const int64_t idx = (static_cast<int64_t>(split) * p.s + (m0 + mm)) * p.CR + n;
+          store_coherent16(prsrc, static_cast<uint32_t>(idx * 4), v);
+        }
+      }
+      if (p.partials_only) continue;
+      // (lo / BM + seg + mb) is distinct for every tile of a CSR plan
+      detail::finish_split_tile(p, (static_cast<int64_t>(lo / BM) + seg + mb) * p.nblocks + nb,
+                                m0, mcount, nb * BN, BN, &last_flag);
+      continue;
+    }
+
     // Epilogue: lane holds rank rows n .. n+3 of token column m for each
     // fragment; rows past the rank are stored as zero.
 #pragma unroll
@@ -264,10 +322,10 @@ __global__ __launch_bounds__(256, 2) void shrink_gemm_kernel(ShrinkParams p) {
   }
 }
 
-template <int BM, int BN, int WM, int DEPTH>
+template <int BM, int BN, int WM, int DEPTH, bool PAIR = false>
 hipError_t launch_g(const ShrinkParams& p, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((shrink_gemm_kernel<BM, BN, WM, DEPTH>), dim3(static_cast<unsigned>(grid)),
-                     dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((shrink_gemm_kernel<BM, BN, WM, DEPTH, PAIR>),
+                     dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -280,6 +338,7 @@ hipError_t launch_shrink_gemm(const ShrinkParams& p, int bm, int bn, int64_t gri
                               hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   switch (bm * 1000 + bn) {
+    case 256128: return launch_g<256, 128, 2, 1, true>(p, grid, stream);
     case 128128: return launch_g<128, 128, 2, 1>(p, grid, stream);
     case 128064: return launch_g<128, 64, 2, 2>(p, grid, stream);
     case 128032: return launch_g<128, 32, 4, 2>(p, grid, stream);

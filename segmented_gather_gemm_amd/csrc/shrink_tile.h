@@ -45,6 +45,57 @@ __device__ __forceinline__ bool shrink_item_of(const ShrinkParams& p, int b, int
   return *seg < p.num_segments;
 }
 
+// Split-K completion of one tile -- rows [m0, m0 + mcount) of the sorted
+// order by columns [n0, n0 + nb_cols) of c*R -- whose f32 partial went out
+// with device-coherent stores.  Every wave waits for its own stores, then the
+// barrier and one counter RMW (see wave_stores_done); the last of the
+// ksplit workgroups to arrive reads the partials with device-coherent loads,
+// sums them in split order (the order in which the stacked call's expand sums
+// them too), writes bf16 h and resets the counter.  Every thread calls it;
+// `cidx` is the tile's counter (clamped to the region).
+__device__ inline void finish_split_tile(const ShrinkParams& p, int64_t cidx, int m0, int mcount,
+                                         int n0, int nb_cols, int* last_flag) {
+  const int tid = threadIdx.x;
+  wave_stores_done();
+  __syncthreads();
+  if (cidx >= p.counter_cap) cidx = p.counter_cap - 1;
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(p.counters + cidx, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    *last_flag = old == p.ksplit - 1;
+  }
+  __syncthreads();
+  if (!*last_flag) return;
+  const __amdgpu_buffer_rsrc_t prsrc = buffer_rsrc(p.partial, p.partial_bytes);
+  const int items = mcount * (nb_cols / 4);
+  for (int q = tid; q < items; q += 256) {
+    const int mm = q / (nb_cols / 4);
+    const int n = n0 + 4 * (q % (nb_cols / 4));
+    if (n >= p.CR) continue;
+    const int r = p.perm[m0 + mm];
+    if (r < 0 || r >= p.s) continue;
+    // four splits' loads in flight at a time
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < p.ksplit; sp0 += 4) {
+      f32x4 w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sp = sp0 + u < p.ksplit ? sp0 + u : sp0;
+        const int64_t idx = (static_cast<int64_t>(sp) * p.s + (m0 + mm)) * p.CR + n;
+        w[u] = load_coherent16(prsrc, static_cast<uint32_t>(idx * 4));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (sp0 + u < p.ksplit) v += w[u];
+    }
+    uint2 o;
+    o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+    o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p.h + static_cast<int64_t>(r) * p.ldh + n) = o;
+  }
+  if (tid == 0) __hip_atomic_store(p.counters + cidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Tile `item` of segment `seg`; `smem` holds ShrinkShape<MF, NF>::SMEM bytes.
 // Every early return is uniform over the workgroup.
 //
@@ -331,52 +382,10 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int seg, int 
     if (direct || p.partials_only) continue;
 
     // Split-K: publish this partial, count arrivals, the last one reduces.
-    // The partials went out as agent-scope atomic stores: every wave waits
-    // for its own, then the barrier, then one counter RMW (see
-    // wave_stores_done); the last arriver reads them with agent-scope loads.
-    wave_stores_done();
-    __syncthreads();
     // (lo / BM + seg + mb) is distinct for every (segment, row block) of a
-    // CSR plan, so every tile has its own counter; the clamp only keeps a
-    // malformed plan in bounds.
-    int64_t cidx = (static_cast<int64_t>(lo / BM) + seg + mb) * p.nblocks + nb;
-    if (cidx >= p.counter_cap) cidx = p.counter_cap - 1;
-    if (tid == 0) {
-      const int old = __hip_atomic_fetch_add(p.counters + cidx, 1, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-      last_flag = old == p.ksplit - 1;
-    }
-    __syncthreads();
-    if (!last_flag) continue;
-    const int items = mcount * (NB / 4);
-    for (int q = tid; q < items; q += 256) {
-      const int mm = q / (NB / 4);
-      const int n = nb * NB + 4 * (q % (NB / 4));
-      if (n >= p.CR) continue;
-      const int r = p.perm[m0 + mm];
-      if (r < 0 || r >= p.s) continue;
-      // Four splits' loads in flight at a time, summed in split order (the
-      // order in which the stacked call's expand sums them too).
-      const __amdgpu_buffer_rsrc_t prsrc = buffer_rsrc(p.partial, p.partial_bytes);
-      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int sp0 = 0; sp0 < p.ksplit; sp0 += 4) {
-        f32x4 w[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int sp = sp0 + u < p.ksplit ? sp0 + u : sp0;
-          const int64_t idx = (static_cast<int64_t>(sp) * p.s + (m0 + mm)) * p.CR + n;
-          w[u] = load_coherent16(prsrc, static_cast<uint32_t>(idx * 4));
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (sp0 + u < p.ksplit) v += w[u];
-      }
-      uint2 o;
-      o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-      o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-      *reinterpret_cast<uint2*>(p.h + static_cast<int64_t>(r) * p.ldh + n) = o;
-    }
-    if (tid == 0) __hip_atomic_store(p.counters + cidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // CSR plan, so every tile has its own counter.
+    finish_split_tile(p, (static_cast<int64_t>(lo / BM) + seg + mb) * p.nblocks + nb, m0,
+                      mcount, nb * NB, NB, &last_flag);
   }
 }
 

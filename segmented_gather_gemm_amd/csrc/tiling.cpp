@@ -17,7 +17,7 @@ namespace sgg {
 // tile round trip).  Measured on decode shapes: small tiles with 4 K ranges
 // beat both one big tile and 16-32 K ranges.
 ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk,
-                                  bool gemm_ok) {
+                                  bool gemm_ok, bool pair_ok) {
   ShrinkTiling t{};
   static const int kNf[] = {1, 2, 3, 4, 6, 8};
   static const int kMf[] = {1, 2, 4, 8};
@@ -114,6 +114,35 @@ ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments
   // loads in flight): the split-K kernel's finer tiles keep more CUs busy.
   if (gemm_units(gm, gn) < 256) return t;
   if (!gemm_ok) return t;  // x or an A block beyond 32-bit offsets: one K range here
+  // Segment-pair tiles (only when asked for): for long segments with c*R
+  // above 64, tiles of 256 tokens over pairs of consecutive work segments of
+  // one slot, by 128 rank rows, with K split in two (f32 partials, summed in
+  // split order).  Twice the tokens per read of the slot's A block cut the
+  // L1 fill of the prefill gate_up shrink by a quarter (568 -> 433 MB), but
+  // measured it is slower, 216 us against 94 us: at 96 KB of LDS and 356
+  // registers a CU holds one such workgroup, the 284 workgroups run in two
+  // rounds, and each CU fills at ~14 GB/s against ~21 GB/s for the 128 x 128
+  // tiles.  (Splitting K of the 128 x 128 tiles alone, 544 workgroups,
+  // measured 94 us: the fill, not the workgroup count, sets the time.)
+  if (pair_ok && long_segments && gn == 128 && chunk <= 128 && kgroups >= 2) {
+    const int64_t kps = (kgroups + 1) / 2 * 256;
+    const int64_t ksplit = (K + kps - 1) / kps;
+    const int64_t nblocks = (CR + 127) / 128;
+    const int64_t counters = (s / 256 + num_segments + 1) * nblocks;
+    const int64_t partial = round_up(ksplit * s * CR * 4, 256);
+    if (ksplit >= 2 && counters <= kCounterCap && partial < (int64_t{1} << 32) - 256) {
+      t.gemm = 1;
+      t.bm = 256;
+      t.bn = 128;
+      t.kps = kps;
+      t.ksplit = static_cast<int>(ksplit);
+      t.mblocks = 1;
+      t.nblocks = static_cast<int>(nblocks);
+      t.partial_bytes = partial;
+      t.grid = grid_for(num_segments, ksplit * nblocks);
+      return t;
+    }
+  }
   t.gemm = 1;
   t.bm = gm;
   t.bn = gn;

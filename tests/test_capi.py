@@ -286,9 +286,16 @@ def test_moe_add_rejects():
 
 
 def test_workspace_sizes():
-    # decode shapes split K across workgroups and need scratch; prefill shapes do not
+    # decode shapes split K across workgroups and need scratch; prefill shapes
+    # do not, unless the segment-pair tiles (K in two ranges) are asked for
     assert L.lora_shrink_workspace_bytes(256, 4096, 3, 16, 8, 128) > 0
     assert L.lora_shrink_workspace_bytes(33792, 4096, 2, 64, 300, 128) == 0
+    old = L.lora_set_option(b"shrink_pair_tiles", 1)
+    try:
+        assert L.lora_shrink_workspace_bytes(33792, 4096, 2, 64, 300, 128) >= 2 * 33792 * 128 * 4
+        assert L.lora_shrink_workspace_bytes(33792, 4096, 2, 32, 300, 128) == 0
+    finally:
+        L.lora_set_option(b"shrink_pair_tiles", old)
     assert L.lora_shrink_workspace_bytes(0, 4096, 3, 16, 8, 128) == 0
 
 

@@ -423,6 +423,36 @@ def test_prefill_sampled(prefill_data, max_chunk):
     check_every_row_fp32(b, proj, dev, h, y)
 
 
+def test_prefill_segment_pair_tiles(prefill_data):
+    """The shrink's segment-pair tiles (lora_set_option "shrink_pair_tiles"
+    = 1: 256-token tiles over pairs of consecutive same-slot work segments,
+    K in two ranges) on the prefill batch: sampled rows against the oracle,
+    every row against float32 products, and the stacked call against the
+    separate calls bit for bit (both sum the two K ranges in split order)."""
+    sgg = _sgg()
+    b, proj, t, dev = prefill_data
+    old = sgg.lora_set_option("shrink_pair_tiles", 1)
+    try:
+        be = backend(b, 128)
+        info = plan_on(be, b)
+        ref = check_plan(info, b, 128)
+        rows = sample_rows(ref, b.num_tokens, seed=5)
+        h, y = run_forward(be, proj, dev["x"], dev["A"], dev["B"], dev["base"].clone())
+        ws = torch.zeros(256 << 20, dtype=torch.uint8, device=DEV)
+        h_sep = sgg.lora_shrink(dev["x"], dev["A"], info, proj.num_slices, workspace=ws)
+        y_sep = sgg.lora_expand(h_sep, dev["B"], info, proj.slice_offsets, proj.max_slice,
+                                dev["base"].clone())
+        torch.cuda.synchronize()
+    finally:
+        sgg.lora_set_option("shrink_pair_tiles", old)
+    assert torch.equal(y, y_sep)
+    want_h, want_y = oracle_forward(t, b, proj, rows)
+    rows_t = torch.as_tensor(rows, device=DEV)
+    assert_close(h.index_select(0, rows_t), want_h, "prefill pair tiles h")
+    assert_close(y.index_select(0, rows_t), want_y, "prefill pair tiles y")
+    check_every_row_fp32(b, proj, dev, h, y)
+
+
 def check_every_row_fp32(b, proj, dev, h, y):
     """Every row of a full-size result against plain float32 torch products on
     the GPU, adapter by adapter with tokens taken from the requests (no plan
