@@ -269,17 +269,36 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
   for (int a = tid; a < L; a += kPlanThreads) running[a] = first_pos[a];
   __syncthreads();
   if (tid < 64) {
-    // One wave, 64 requests at a time.  For each slot present among them
-    // (in order of first appearance): its lanes' positions are the slot's
-    // running position plus the lengths of its earlier lanes.
+    // One wave, 64 requests at a time: each lane's position is its slot's
+    // running position plus the lengths of the earlier lanes of its slot.
     const int lane = tid;
     const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int slot_bits = L > 1 ? 32 - __builtin_clz(static_cast<unsigned>(L - 1)) : 0;
     for (int r0 = 0; r0 < bs; r0 += 64) {
       const int r = r0 + lane;
       const bool valid = r < bs;
       const int a = valid ? req_pos[r] : -1;
       const int len = valid ? req_ptr[r + 1] - req_ptr[r] : 0;
       const bool unit = __ballot(valid && len != 1) == 0;  // every length is one
+      if (unit) {
+        // One-token requests (decode batches, MoE copies): the lanes of a
+        // lane's slot by matching the slot's bits with one ballot per bit,
+        // whatever the number of slots among the 64.
+        uint64_t same = __ballot(valid);
+        for (int b = 0; b < slot_bits; ++b) {
+          const bool bit = (a >> b) & 1;
+          const uint64_t ones = __ballot(valid && bit);
+          same &= bit ? ones : ~ones;
+        }
+        const int base = valid ? running[a] : 0;
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+          req_pos[r] = base + __popcll(same & below);
+          if ((same & below) == 0) running[a] = base + __popcll(same);  // the slot's first lane
+        }
+        __builtin_amdgcn_wave_barrier();
+        continue;
+      }
       uint64_t todo = __ballot(valid);
       while (todo != 0) {
         const int leader = __builtin_ctzll(todo);
