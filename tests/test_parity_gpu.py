@@ -354,6 +354,63 @@ def test_fused_timeline_leaves_results_unchanged():
     assert_close(y, want_y, "one launch with its timeline on")
 
 
+def test_graph_keeps_its_default_workspace():
+    """run_qkv_lora captured in a graph with the default workspace; then an
+    eager call large enough to grow that workspace, and new allocations that
+    would reuse freed memory; the replays still match the oracle, because an
+    outgrown workspace is kept alive, not freed."""
+    sgg = _sgg()
+    from segmented_gather_gemm_amd import binding
+    L, max_bs = 8, 256
+    b0, proj, t, offs, wide = _decode_case(81, s=max_bs, L=L)
+    x, A, Bw = (t[k].to(DEV) for k in ("x", "A", "B"))
+    base0 = t["base"].to(DEV)
+    base = base0.clone()
+    be = sgg.ChunkedSgmvLoRA(L, 128, DEV)
+    be.init_cuda_graph_batch_info(max_bs, 1)
+    be.prepare_lora_batch(None, b0.req_slots, b0.lora_ranks, b0.scalings, is_decode=True,
+                          use_cuda_graph=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        be.run_qkv_lora(x, A, Bw, offs, wide, base)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        be.run_qkv_lora(x, A, Bw, offs, wide, base)
+    torch.cuda.synchronize()
+    key = (DEV.type, DEV.index if DEV.index is not None else torch.cuda.current_device())
+    ws_captured = binding._workspaces[key]
+    # a call that needs a larger default workspace grows it (forced here: the
+    # size the previous tests left it at is not known), then an eager call
+    binding.default_workspace(DEV, ws_captured.numel() + 1)
+    bb, pb, tb, offs_b, wide_b = _decode_case(82, s=4096, L=L, K=512)
+    eb = sgg.ChunkedSgmvLoRA(L, 128, DEV)
+    plan_on(eb, bb)
+    yb = eb.run_qkv_lora(tb["x"].to(DEV), tb["A"].to(DEV), tb["B"].to(DEV), offs_b, wide_b,
+                         tb["base"].to(DEV))
+    torch.cuda.synchronize()
+    assert binding._workspaces[key].data_ptr() != ws_captured.data_ptr(), "workspace did not grow"
+    _, want_b = oracle_forward(tb, bb, pb)
+    assert_close(yb, want_b, "eager call after the capture")
+    filler = [torch.full((1 << 20,), -1, dtype=torch.int32, device=DEV) for _ in range(8)]
+    rng = np.random.default_rng(83)
+    for trial in range(3):
+        slots = rng.integers(0, L, size=max_bs).tolist()
+        be.prepare_lora_batch(None, slots, b0.lora_ranks, b0.scalings, is_decode=True,
+                              use_cuda_graph=True)
+        base.copy_(base0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        b = Batch("g", 0, [1] * max_bs, slots, True, L, b0.lora_ranks, b0.scalings, 128,
+                  b0.projections)
+        _, want_y = oracle_forward(t, b, proj)
+        assert_close(base, want_y, f"replay {trial} after the workspace grew")
+    del filler
+
+
 def test_fused_stacked_call_in_a_graph():
     """The one-launch stacked call captured in a graph over a capacity plan
     (trailing segments empty): replays with new plans, eager work and
