@@ -14,11 +14,19 @@
 // bytes of one row.  The base rows of the next 16 tokens are in flight while
 // the current ones are computed and stored.
 //
-// Work order: segments are dealt round-robin to the XCDs (segment_round_robin)
-// with all column tiles of a segment on one XCD, tiles fastest, so the
-// workgroups resident on an XCD sweep whole rows of the base tensor and share
-// the segment's h rows in L2, while the chunks of a dominant adapter spread
-// over all XCDs.
+// Work order: column tiles are dealt to the XCDs (expand_item_of): each XCD
+// takes every eighth tile of every segment, segment after segment, so it
+// needs only one eighth of an adapter's B columns and reuses them from its L2
+// across the adapter's consecutive segments, and every XCD gets an equal share
+// of every segment however the tokens fall on the adapters.  (Dealing whole
+// segments to the XCDs, the alternative kept behind the "expand_deal_tiles"
+// option, re-fetched B from HBM per segment: the prefill expand read 1.24x its
+// algorithmic bytes against 1.02x now.)
+//
+// With split-K partials (HPART, the stacked call) h is staged from them: each
+// (row, 8-column chunk) sums its splits in split order in registers and
+// rounds to bf16, the shrink's own reduction order, so the stacked call gives
+// the separate calls' bits.
 #include "sgg_device.h"
 #include "sgg_kernels.h"
 #include "expand_tile.h"

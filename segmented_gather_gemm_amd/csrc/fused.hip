@@ -22,13 +22,13 @@
 //
 // Hand-off word, one per segment: bits 0-15 count producers that have
 // published, bits 16-30 count blocks (producers and consumers) that are done
-// with the word.  The partials are agent-scope atomic stores; a producer adds
-// to both fields at once after every one of its waves has waited for its own
-// stores and the workgroup barrier (wave_stores_done).  A consumer polls bits
-// 0-15 and then reads the partials with agent-scope loads; when it is done it
-// adds to bits 16-30.  The block that completes the count resets the word to
-// zero for the next call.  All arrivals are RMWs on the one word, so the
-// reset comes after every other block's use of it.
+// with the word.  The partials go out as device-coherent stores; a producer
+// adds to both fields at once after every one of its waves has waited for its
+// own stores and the workgroup barrier (wave_stores_done).  A consumer polls
+// bits 0-15 and then reads the partials with device-coherent loads; when it
+// is done it adds to bits 16-30.  The block that completes the count resets
+// the word to zero for the next call.  All arrivals are RMWs on the one word,
+// so the reset comes after every other block's use of it.
 #include <mutex>
 
 #include "sgg_device.h"
