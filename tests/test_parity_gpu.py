@@ -1387,6 +1387,8 @@ def _moe_want(t, lens, slots, ranks, scal, topk, E):
     ("extend", [3, 1, 5, 2, 1, 4, 37, 60, 9, 128], 4, [16, 8, 0, 16], 8, 2, 512, 256, 16, 0),
     ("decode", [1] * 300, 6, [16, 16, 12, 8, 16, 4], 8, 2, 1024, 384, 16, 0),
     ("top4_bad_experts", [2, 7, 1, 30, 5], 3, [32, 0, 24], 4, 4, 256, 136, 32, 5),
+    # the shape bench.py times: 256 decode tokens, top-2 of 8 experts, 4096 -> 14336
+    ("bench_shape", [1] * 256, 8, [16] * 8, 8, 2, 4096, 14336, 16, 0),
 ], ids=lambda c: c[0])
 def test_moe_lora_add_matches_oracle(case):
     """Per-request routing to virtual experts (lora_moe_route, bit-exact
@@ -1395,10 +1397,10 @@ def test_moe_lora_add_matches_oracle(case):
     id is out of range keep their rows bit for bit."""
     name, lens, L, ranks, E, k, K, N, R, bad = case
     sgg = _sgg()
-    slots, scal, topk, t = _moe_case(zlib.crc32(name.encode()) % 1000, lens, L, ranks, E, k, K, N, R,
-                                     bad_experts=bad)
+    slots, scal, topk, t = _moe_case(zlib.crc32(name.encode()) % 1000, lens, L, ranks, E, k, K,
+                                     N, R, bad_experts=bad)
     be = sgg.ChunkedSgmvLoRA(L, 128, DEV)
-    decode = name == "decode"
+    decode = name in ("decode", "bench_shape")
     be.prepare_lora_batch(None if decode else lens, slots, ranks, scal, is_decode=decode)
     topk_d = torch.from_numpy(topk).to(DEV)
     info = be.prepare_moe_lora_batch(topk_d, E)
