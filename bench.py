@@ -16,8 +16,9 @@ the timed steps, inputs resident in HBM); kernel durations come from HIP
 events on the stream the kernels run on.  Every run also times the other
 workloads, each under its own key: the prefill chunk sweep (16 / 32 / 64 /
 128), the skewed batch (o_proj, down_proj), the Llama-3-8B-shaped layer
-sweep with the embedding gather, the pruned lm_head pass of the decode batch
-and the device-side planner; `--quick` skips them.
+sweep with the embedding gather, the pruned lm_head pass of the decode batch,
+the device-side planner, the shrink's MFMA and VALU forms on short segments
+and the MoE LoRA add; `--legs` picks some, `--quick` skips them all.
 """
 
 import argparse
@@ -1190,7 +1191,8 @@ def main():
                "full": ("full layer sweep", lambda: run_full(device, args.full_layers)),
                "lm_head": ("lm_head pass", lambda: run_lm_head(device)),
                "device_plan": ("device planner", lambda: run_device_plan(device)),
-               "short": ("short segments: MFMA and VALU shrink", lambda: run_short_segments(device)),
+               "short": ("short segments: MFMA and VALU shrink",
+                         lambda: run_short_segments(device)),
                "moe": ("MoE LoRA add", lambda: run_moe(device))}
     for leg in legs:
         print(f"# {runners[leg][0]}", file=sys.stderr, flush=True)
