@@ -1237,6 +1237,27 @@ DEVICE_PLAN_CASES = [
 ]
 
 
+def _random_device_plan_cases(n=10):
+    """Seeded random batches for the device planner: one-token requests
+    (decode mode, or extend mode with every length 1 -- the placement's
+    bit-matching path) and extend batches, slot counts 1..1024."""
+    rng = np.random.default_rng(4242)
+    out = []
+    for i in range(n):
+        L = int(rng.choice([1, 2, 3, 64, 65, 511, 512, 1023, 1024, int(rng.integers(1, 1025))]))
+        bs = int(rng.integers(1, 4097))
+        kind = i % 3
+        lens = None if kind == 0 else ((1, 1) if kind == 1 else (0, 5))
+        tpb = 1 if lens is None else lens[1]
+        cap = int(rng.choice([16, 32, 64, 128]))
+        override = int(rng.choice([0, 0, 16, 48]))   # the graph capacity assumes chunks >= 16
+        out.append((f"random{i}_L{L}_bs{bs}", bs, bs, tpb, L, lens, cap, override))
+    return out
+
+
+DEVICE_PLAN_CASES += _random_device_plan_cases()
+
+
 @pytest.mark.parametrize("case", DEVICE_PLAN_CASES, ids=[c[0] for c in DEVICE_PLAN_CASES])
 def test_device_plan_matches_host_plan(case):
     """lora_plan_device writes, bit for bit, the plan the host planner uploads
