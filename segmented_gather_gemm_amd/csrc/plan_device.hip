@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
   __shared__ int32_t req_ptr[kDevicePlanMaxReqs + 1]; // request token boundaries
   __shared__ int32_t req_pos[kDevicePlanMaxReqs];     // first sorted position per request
   __shared__ int64_t wave_sums[kPlanThreads / 64 + 1][2];
-  __shared__ int32_t status, longest, longest_work;
+  __shared__ int32_t status, longest, longest_work, all_unit;
 
   const int tid = threadIdx.x;
   const int bs = p.bs, L = p.L;
@@ -175,8 +175,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
     status = SGG_OK;
     longest = 0;
     longest_work = 0;
+    all_unit = 1;
   }
   if (tid < L) count[tid] = 0;
+  // the rank and scaling tables, requested now so that their round trip
+  // overlaps the planning (written out in step 5; L <= kPlanThreads)
+  int32_t rank_of_tid = 0, scal_of_tid = 0;
+  if (tid < L) {
+    rank_of_tid = p.ranks[tid];
+    scal_of_tid = __float_as_int(p.scalings[tid]);
+  }
   __syncthreads();
 
   // 1. Request boundaries and validation; tokens per slot.
@@ -190,6 +198,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
       if (len < 0 || (p.is_decode && len != 1)) atomicOr(&status, 1);
       if (a < 0 || a >= L) atomicOr(&status, 2);
       else if (len > 0) atomicAdd(&count[a], len);
+      if (len != 1) all_unit = 0;
       req_slots_out[r] = a;
       req_pos[r] = a;  // the slot, until step 3 replaces it with the position
     }
@@ -330,9 +339,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
   }
   __syncthreads();
 
-  // 4. Permutation: sorted position -> token; one wave per request, its
+  // 4. Permutation: sorted position -> token; one thread per request when
+  // every request has one token (decode), else one wave per request, its
   // lanes writing consecutive positions.
-  {
+  if (all_unit) {
+    for (int r = tid; r < bs; r += kPlanThreads) perm[req_pos[r]] = req_ptr[r];
+  } else {
     const int lane = tid & 63, wave = tid >> 6;
     for (int r = wave; r < bs; r += kPlanThreads / 64) {
       const int start = req_ptr[r];
@@ -367,9 +379,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
     work_slots[i] = 0;
     work_indptr[i + 1] = static_cast<int32_t>(s);
   }
-  for (int a = tid; a < L; a += kPlanThreads) {
-    ranks_out[a] = p.ranks[a];
-    scal_out[a] = __float_as_int(p.scalings[a]);
+  if (tid < L) {
+    ranks_out[tid] = rank_of_tid;
+    scal_out[tid] = scal_of_tid;
   }
   if (tid == 0) {
     seg_indptr[0] = 0;
