@@ -11,12 +11,14 @@
 //   1. request boundaries (a block-wide scan of the lengths), validation;
 //   2. tokens per slot (LDS histogram), the chunk size, each slot's first
 //      sorted position and first segment (scans over the slots);
-//   3. each request's first sorted position: the stable counting sort.  One
-//      wave walks the requests 64 at a time; for each slot among them (by
-//      ballot) its lanes add the lengths of its earlier lanes to the slot's
+//   3. each request's first sorted position: the stable counting sort.  For
+//      one-token requests every wave places 64 at once (slots matched by one
+//      ballot per slot bit, a per-wave count table for the offsets); else one
+//      wave walks the requests 64 at a time and, for each slot among them (by
+//      ballot), its lanes add the lengths of its earlier lanes to the slot's
 //      running position, which the slot's first lane then advances;
-//   4. the permutation: one wave per request writes its tokens' sorted
-//      positions;
+//   4. the permutation: one thread per request when every request has one
+//      token, else one wave per request writing its tokens' sorted positions;
 //   5. segments (full chunks, remainder last) and work segments
 //      (consecutive segments of one slot merged greedily within
 //      max(chunk, 128) tokens, in closed form), one per thread; capacity
@@ -35,6 +37,7 @@ namespace sgg {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
 
 struct DevicePlanParams {
   const int32_t* seq_lens;  // [bs], or null: one token per request (decode)
@@ -58,7 +61,7 @@ __device__ __forceinline__ int chunk_for(int64_t n, int max_chunk) {
 // prefixes and *ta, *tb the totals.  Every thread must call it.
 __device__ void block_exclusive_scan2(int64_t a, int64_t b, int64_t (*wave_sums)[2], int64_t* pa,
                                       int64_t* pb, int64_t* ta, int64_t* tb) {
-  constexpr int kWaves = kPlanThreads / 64;
+  constexpr int kWaves = kPlanWaves;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int64_t x = a, y = b;
 #pragma unroll
@@ -156,6 +159,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
   __shared__ int32_t first_work[kDevicePlanMaxLoras]; // first work segment per slot
   __shared__ int32_t req_ptr[kDevicePlanMaxReqs + 1]; // request token boundaries
   __shared__ int32_t req_pos[kDevicePlanMaxReqs];     // first sorted position per request
+  __shared__ uint16_t wave_count[kPlanWaves * kDevicePlanMaxLoras];  // step 3, one-token requests
   __shared__ int64_t wave_sums[kPlanThreads / 64 + 1][2];
   __shared__ int32_t status, longest, longest_work, all_unit;
 
@@ -277,57 +281,69 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
   // 3. First sorted position of each request (stable counting sort).
   for (int a = tid; a < L; a += kPlanThreads) running[a] = first_pos[a];
   __syncthreads();
-  if (tid < 64) {
-    // One wave, 64 requests at a time: each lane's position is its slot's
-    // running position plus the lengths of the earlier lanes of its slot.
-    const int lane = tid;
-    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    const int slot_bits = L > 1 ? 32 - __builtin_clz(static_cast<unsigned>(L - 1)) : 0;
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int slot_bits = L > 1 ? 32 - __builtin_clz(static_cast<unsigned>(L - 1)) : 0;
+  if (all_unit) {
+    // One-token requests (decode batches, MoE copies), kPlanThreads at a
+    // time, every wave at once.  A wave finds the lanes of each lane's slot
+    // by matching the slot's bits, one ballot per bit (whatever the number
+    // of slots among its 64); the slot's first lane records the wave's count
+    // in a per-wave table, and a lane's position is the slot's running
+    // position plus the counts of the earlier waves plus its rank in its
+    // wave.  Then one thread per slot advances the running position.
+    for (int r0 = 0; r0 < bs; r0 += kPlanThreads) {
+      for (int i = tid; i < kPlanWaves * L; i += kPlanThreads) wave_count[i] = 0;
+      __syncthreads();
+      const int r = r0 + tid;
+      const bool valid = r < bs;
+      const int a = valid ? req_pos[r] : -1;
+      uint64_t same = __ballot(valid);
+      for (int b = 0; b < slot_bits; ++b) {
+        const bool bit = (a >> b) & 1;
+        const uint64_t ones = __ballot(valid && bit);
+        same &= bit ? ones : ~ones;
+      }
+      const int rank = __popcll(same & below);
+      if (valid && rank == 0) wave_count[wave * L + a] = static_cast<uint16_t>(__popcll(same));
+      __syncthreads();
+      if (valid) {
+        int pos = running[a] + rank;
+        for (int w = 0; w < wave; ++w) pos += wave_count[w * L + a];
+        req_pos[r] = pos;
+      }
+      __syncthreads();
+      for (int a2 = tid; a2 < L; a2 += kPlanThreads) {
+        int t = 0;
+        for (int w = 0; w < kPlanWaves; ++w) t += wave_count[w * L + a2];
+        running[a2] += t;
+      }
+      __syncthreads();
+    }
+  } else if (tid < 64) {
+    // One wave, 64 requests at a time.  For each slot present among them
+    // (in order of first appearance): its lanes' positions are the slot's
+    // running position plus the lengths of its earlier lanes.
     for (int r0 = 0; r0 < bs; r0 += 64) {
       const int r = r0 + lane;
       const bool valid = r < bs;
       const int a = valid ? req_pos[r] : -1;
       const int len = valid ? req_ptr[r + 1] - req_ptr[r] : 0;
-      const bool unit = __ballot(valid && len != 1) == 0;  // every length is one
-      if (unit) {
-        // One-token requests (decode batches, MoE copies): the lanes of a
-        // lane's slot by matching the slot's bits with one ballot per bit,
-        // whatever the number of slots among the 64.
-        uint64_t same = __ballot(valid);
-        for (int b = 0; b < slot_bits; ++b) {
-          const bool bit = (a >> b) & 1;
-          const uint64_t ones = __ballot(valid && bit);
-          same &= bit ? ones : ~ones;
-        }
-        const int base = valid ? running[a] : 0;
-        __builtin_amdgcn_wave_barrier();
-        if (valid) {
-          req_pos[r] = base + __popcll(same & below);
-          if ((same & below) == 0) running[a] = base + __popcll(same);  // the slot's first lane
-        }
-        __builtin_amdgcn_wave_barrier();
-        continue;
-      }
       uint64_t todo = __ballot(valid);
       while (todo != 0) {
         const int leader = __builtin_ctzll(todo);
         const int slot = __builtin_amdgcn_readlane(a, leader);
         const uint64_t m = __ballot(a == slot);
-        int before, total;
-        if (unit) {
-          before = __popcll(m & below);
-          total = __popcll(m);
-        } else {  // exclusive scan of the members' lengths
-          int v = (a == slot) ? len : 0;
-          const int own = v;
+        // exclusive scan of the members' lengths
+        int v = (a == slot) ? len : 0;
+        const int own = v;
 #pragma unroll
-          for (int d = 1; d < 64; d <<= 1) {
-            const int u = __shfl_up(v, d, 64);
-            if (lane >= d) v += u;
-          }
-          before = v - own;
-          total = __shfl(v, 63, 64);
+        for (int d = 1; d < 64; d <<= 1) {
+          const int u = __shfl_up(v, d, 64);
+          if (lane >= d) v += u;
         }
+        const int before = v - own;
+        const int total = __shfl(v, 63, 64);
         const int base = running[slot];
         if (a == slot) req_pos[r] = base + before;
         __builtin_amdgcn_wave_barrier();
@@ -345,8 +361,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
   if (all_unit) {
     for (int r = tid; r < bs; r += kPlanThreads) perm[req_pos[r]] = req_ptr[r];
   } else {
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int r = wave; r < bs; r += kPlanThreads / 64) {
+    for (int r = wave; r < bs; r += kPlanWaves) {
       const int start = req_ptr[r];
       const int len = req_ptr[r + 1] - start;
       const int pos = req_pos[r];
