@@ -1234,6 +1234,8 @@ DEVICE_PLAN_CASES = [
     ("override48", 60, 64, 200, 4, (0, 200), 128, 48),
     ("cap16", 40, 40, 100, 6, (1, 100), 16, 0),
     ("L1024_bs4096", 4096, 4096, 3, 1024, (0, 3), 128, 0),
+    ("decode_L1024_bs4096", 4096, 4096, 1, 1024, None, 128, 0),
+    ("unit_L1024_bs4096", 4096, 4096, 1, 1024, (1, 1), 128, 0),
 ]
 
 
