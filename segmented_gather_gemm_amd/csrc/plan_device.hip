@@ -8,9 +8,11 @@
 // the kernels that read the plan.
 //
 // One workgroup of 1024 threads:
-//   1. request boundaries (a block-wide scan of the lengths), validation;
+//   1. request boundaries (a block-wide scan of the lengths; in decode mode
+//      the index itself), validation;
 //   2. tokens per slot (LDS histogram), the chunk size, each slot's first
-//      sorted position and first segment (scans over the slots);
+//      sorted position and first segment (scans over the slots: across the
+//      lanes of one wave when there are at most 64 slots);
 //   3. each request's first sorted position: the stable counting sort.  For
 //      one-token requests every wave places 64 at once (slots matched by one
 //      ballot per slot bit, a per-wave count table for the offsets); else one
@@ -108,6 +110,22 @@ __device__ void block_exclusive_scan2(int64_t a, int64_t b, int64_t (*wave_sums)
   __syncthreads();  // the sums are read before a later call overwrites them
 }
 
+// Inclusive scans of three values over one wave (32-bit, wrapping).
+__device__ __forceinline__ void wave_inclusive_scan3(uint32_t& x, uint32_t& y, uint32_t& z) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t u = __shfl_up(x, d, 64);
+    const uint32_t v = __shfl_up(y, d, 64);
+    const uint32_t w = __shfl_up(z, d, 64);
+    if (lane >= d) {
+      x += u;
+      y += v;
+      z += w;
+    }
+  }
+}
+
 // The work segments of one slot of n tokens: its segments are full chunks
 // and a remainder r = n % chunk (if any); merging consecutive segments
 // greedily within `cap` tokens gives groups of m = cap / chunk full chunks,
@@ -162,8 +180,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
   __shared__ uint16_t wave_count[kPlanWaves * kDevicePlanMaxLoras];  // step 3, one-token requests
   __shared__ int64_t wave_sums[kPlanThreads / 64 + 1][2];
   __shared__ int32_t status, longest, longest_work, all_unit;
+  __shared__ uint32_t slot_totals[2];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int bs = p.bs, L = p.L;
   int32_t* perm = p.plan + p.off[0];
   int32_t* seg_indptr = p.plan + p.off[1];
@@ -207,8 +227,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
       req_pos[r] = a;  // the slot, until step 3 replaces it with the position
     }
     int64_t pre, unused, chunk_total, unused_total;
-    block_exclusive_scan2(len > 0 ? len : 0, 0, wave_sums, &pre, &unused, &chunk_total,
-                          &unused_total);
+    if (p.seq_lens == nullptr) {  // one token per request: the prefix is the index
+      pre = r - r0;
+      chunk_total = bs - r0 < kPlanThreads ? bs - r0 : kPlanThreads;
+    } else {
+      block_exclusive_scan2(len > 0 ? len : 0, 0, wave_sums, &pre, &unused, &chunk_total,
+                            &unused_total);
+    }
     if (r < bs) {
       const int64_t end = carry + pre + (len > 0 ? len : 0);
       if (end > INT32_MAX) atomicOr(&status, 4);
@@ -240,20 +265,47 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
     atomicMax(&longest, n_slot < chunk ? n_slot : chunk);
     atomicMax(&longest_work, sw.longest);
   }
-  // one scan of the token counts, one of the segment and work-segment
-  // counts packed in one word (each total stays below 2^31)
-  int64_t pos, packed, tot_tok, tot_packed;
-  block_exclusive_scan2(n_slot, (static_cast<int64_t>(segs) << 32) | works, wave_sums, &pos,
-                        &packed, &tot_tok, &tot_packed);
-  const int64_t sg = packed >> 32, wk = packed & 0xffffffffll;
-  const int64_t n_seg = tot_packed >> 32, n_work = tot_packed & 0xffffffffll;
-  if (tid < L) {
-    first_pos[tid] = static_cast<int32_t>(pos);
-    first_seg[tid] = static_cast<int32_t>(sg);
-    first_work[tid] = static_cast<int32_t>(wk);
+  int64_t n_seg, n_work;
+  if (L <= 64) {
+    // The slots fit the first wave: 32-bit scans across its lanes, no
+    // block-level pass.  (The sums can wrap only for a batch of more than
+    // 2^31 tokens, which the status already rejects.)
+    if (wave == 0) {
+      uint32_t x = static_cast<uint32_t>(n_slot), y = static_cast<uint32_t>(segs);
+      uint32_t z = static_cast<uint32_t>(works);
+      wave_inclusive_scan3(x, y, z);
+      if (tid < L) {
+        first_pos[tid] = static_cast<int32_t>(x - static_cast<uint32_t>(n_slot));
+        first_seg[tid] = static_cast<int32_t>(y - static_cast<uint32_t>(segs));
+        first_work[tid] = static_cast<int32_t>(z - static_cast<uint32_t>(works));
+      }
+      const uint32_t ty = __shfl(y, 63, 64), tz = __shfl(z, 63, 64);
+      if (lane == 0) {
+        slot_totals[0] = ty;
+        slot_totals[1] = tz;
+        if (static_cast<int64_t>(ty) > p.seg_capacity) atomicOr(&status, 8);
+      }
+    }
+    __syncthreads();
+    n_seg = slot_totals[0];
+    n_work = slot_totals[1];
+  } else {
+    // one scan of the token counts, one of the segment and work-segment
+    // counts packed in one word (each total stays below 2^31)
+    int64_t pos, packed, tot_tok, tot_packed;
+    block_exclusive_scan2(n_slot, (static_cast<int64_t>(segs) << 32) | works, wave_sums, &pos,
+                          &packed, &tot_tok, &tot_packed);
+    const int64_t sg = packed >> 32, wk = packed & 0xffffffffll;
+    n_seg = tot_packed >> 32;
+    n_work = tot_packed & 0xffffffffll;
+    if (tid < L) {
+      first_pos[tid] = static_cast<int32_t>(pos);
+      first_seg[tid] = static_cast<int32_t>(sg);
+      first_work[tid] = static_cast<int32_t>(wk);
+    }
+    if (tid == 0 && n_seg > p.seg_capacity) atomicOr(&status, 8);
+    __syncthreads();
   }
-  if (tid == 0 && n_seg > p.seg_capacity) atomicOr(&status, 8);
-  __syncthreads();
   const int st = status;
 
   if (st != SGG_OK) {
@@ -281,7 +333,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
   // 3. First sorted position of each request (stable counting sort).
   for (int a = tid; a < L; a += kPlanThreads) running[a] = first_pos[a];
   __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6;
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   const int slot_bits = L > 1 ? 32 - __builtin_clz(static_cast<unsigned>(L - 1)) : 0;
   if (all_unit) {
