@@ -125,9 +125,62 @@ __global__ __launch_bounds__(256) void embedding_kernel(EmbeddingParams p) {
   }
 }
 
+// Position-major form, for plans of at most kEmbedPosSegments segments
+// (decode batches): one wave per 64 consecutive (sorted position, j) pairs.
+// Each lane requests its position's permutation entry and, at the same time,
+// one segment start (lane i: seg_indptr[i]); a ballot per position of the
+// wave's window then finds the segment holding it, so the token id and the
+// segment's slot come one round trip later and the table value one after
+// that -- three dependent loads where the segment-major form above needs
+// four.  The value is requested for every j < R and kept only below the
+// rank, so the rank's load runs beside it.
+constexpr int kEmbedPosSegments = 63;
+
+__global__ __launch_bounds__(64) void embedding_pos_kernel(EmbeddingParams p) {
+  const int lane = threadIdx.x;
+  const int64_t q0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int64_t q = q0 + lane;
+  const int64_t pos = q / p.R;
+  const int j = static_cast<int>(q - pos * p.R);
+  const int nseg = p.num_segments;
+  const int start = lane <= nseg ? p.seg_indptr[lane] : 0;
+  const int r = pos < p.s ? p.perm[pos] : -1;
+  // segment of this lane's position: the last segment starting at or before
+  // it, if the position lies before that segment's end
+  int seg = -1;
+  const int64_t p_first = q0 / p.R, p_last = (q0 + 63) / p.R;
+  for (int64_t k = p_first; k <= p_last; ++k) {
+    const uint64_t m = __ballot(lane < nseg && start <= k);
+    if (m == 0) continue;
+    const int sk = 63 - __builtin_clzll(m);
+    const int end = __builtin_amdgcn_readlane(start, sk + 1);
+    if (pos == k && k < end) seg = sk;
+  }
+  if (seg < 0 || r < 0 || r >= p.s || pos >= p.s) return;
+  const int slot = p.seg_slots[seg];
+  const int64_t id = p.ids[r];
+  const bool slot_ok = slot >= 0 && slot < p.L;
+  uint16_t v = 0;
+  int rho = 0;
+  if (slot_ok) {
+    rho = p.ranks[slot];
+    if (id >= 0 && id < p.vocab) v = p.A[(static_cast<int64_t>(slot) * p.R + j) * p.V + id];
+  }
+  rho = rho < 0 ? 0 : (rho > p.R ? p.R : rho);
+  p.out[static_cast<int64_t>(r) * p.ldo + j] = j < rho ? v : 0;
+}
+
 }  // namespace
 
 hipError_t launch_embedding(const EmbeddingParams& p, hipStream_t stream) {
+  const int64_t pos_grid = (p.s * p.R + 63) / 64;
+  if (p.num_segments <= kEmbedPosSegments && pos_grid < (int64_t{1} << 31)) {
+    const int64_t grid = pos_grid;
+    if (grid <= 0 || p.num_segments <= 0) return hipSuccess;
+    hipLaunchKernelGGL(embedding_pos_kernel, dim3(static_cast<unsigned>(grid)), dim3(64), 0,
+                       stream, p);
+    return hipGetLastError();
+  }
   const int64_t grid = static_cast<int64_t>(p.num_segments) * p.parts;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(embedding_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, p);

@@ -668,7 +668,9 @@ extern "C" int lora_a_embedding(const int64_t* input_ids, const void* A_emb, int
   p.L = num_loras;
   p.R = R;
   p.num_segments = num_segments;
-  // Parts per segment: about 64 (token, j) pairs per workgroup.  Every pair
+  // Plans of more segments than the position-major form takes (see
+  // launch_embedding) run segment-major, with parts per segment: about 64
+  // (token, j) pairs per workgroup.  Every pair
   // is its own cache line (A_emb columns are V apart) and one CU keeps only
   // so many line requests in flight, so the gather is spread over many CUs.
   // Measured on the decode batch (256 tokens, 8 segments, R = 16): 4.4 us

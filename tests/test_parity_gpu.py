@@ -1057,6 +1057,40 @@ def test_workspace_reuse_across_shapes():
     assert torch.equal(h1, h2)
 
 
+EMBED_CASES = [
+    # (name, R, seq_lens, slots, num_loras, ranks, override): plans of at most
+    # 63 segments take the position-major gather, larger ones the
+    # segment-major one; both must give the oracle's bits.
+    ("R8_zero_lengths", 8, [0, 5, 0, 3, 7, 0, 1], [2, 0, 1, 2, 4, 3, 0], 5, [8, 0, 3, 8, 5], 0),
+    ("R24_straddles_waves", 24, [9, 4, 11, 2], [1, 0, 1, 2], 3, [24, 7, 16], 0),
+    ("R128_token_over_two_waves", 128, [3, 2, 4], [0, 1, 0], 2, [128, 65], 0),
+    ("63_segments", 16, [4] * 63, list(range(63)), 63, [16] * 63, 0),
+    ("64_segments", 16, [4] * 64, list(range(64)), 64, [16] * 64, 0),
+    ("override3_many_short", 16, [7, 5, 9, 3], [0, 1, 0, 2], 3, [16, 9, 4], 3),
+]
+
+
+@pytest.mark.parametrize("case", EMBED_CASES, ids=[c[0] for c in EMBED_CASES])
+def test_embedding_plans(case):
+    """The LoRA-A embedding gather, bit for bit against the oracle, on both
+    of its forms: zero-length requests, partial and zero ranks, ranks whose
+    (token, j) pairs straddle or span waves, and plans of 63 and 64
+    segments."""
+    sgg = _sgg()
+    name, R, lens, slots, L, ranks, override = case
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    b = Batch(name, 0, lens, slots, False, L, ranks, [1.0] * L, 128)
+    V = 300
+    s = sum(lens)
+    ids = torch.tensor(rng.integers(-2, V + 3, s), dtype=torch.int64)
+    A_emb = torch.randn(L, R, V).to(torch.bfloat16)
+    be = backend(b)
+    plan_on(be, b, override)
+    e = be.run_lora_a_embedding(ids.to(DEV), A_emb.to(DEV), V)
+    want = ol.embedding_a(ids.numpy(), to_f64(A_emb), lens, slots, ranks, V)
+    assert np.array_equal(to_f64(e), want)
+
+
 def test_embedding_edges():
     sgg = _sgg()
     b = Batch("emb", 39, [3, 4, 2], [2, 0, 1], False, 3, [16, 0, 5], [1.0] * 3, 128)
