@@ -161,7 +161,7 @@ __device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int 
     if constexpr (HPART) {
       // Split-K partials, indexed by sorted position (no gather): each
       // (row, 8-column chunk) sums its splits in split order, with the loads
-      // of four splits in flight at a time, and rounds the sum to bf16 into
+      // of several splits in flight at a time, and rounds the sum to bf16 into
       // the h tile.  Partials written by an earlier launch are read through
       // the caches; in the one-launch form they come from other workgroups of
       // the same launch, so they are read device-coherently.
@@ -176,15 +176,20 @@ __device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int 
         const int64_t src = static_cast<int64_t>(c0 + row) * p.ldp + k * p.R + 8 * c;
         f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
         int sp = 0;
-        for (; sp + 4 <= p.hsplit; sp += 4) {
-          f32x4 lo4[4], hi4[4];
+        // Splits whose loads are in flight together: four, except in the
+        // 256-column tiles with one rank step, where two keep the kernel at
+        // 92 registers and five workgroups per CU instead of 108 and four
+        // (MoE add 33.9 -> 30.5 us; the sums keep the same order).
+        constexpr int SB = (P == 2 && KS == 1) ? 2 : 4;
+        for (; sp + SB <= p.hsplit; sp += SB) {
+          f32x4 lo4[SB], hi4[SB];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
+          for (int u = 0; u < SB; ++u) {
             lo4[u] = part16(src + (sp + u) * split_stride);
             hi4[u] = part16(src + (sp + u) * split_stride + 4);
           }
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
+          for (int u = 0; u < SB; ++u) {
             s0 += lo4[u];
             s1 += hi4[u];
           }
