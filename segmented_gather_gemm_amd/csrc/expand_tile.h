@@ -95,10 +95,14 @@ __device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int 
   const int q = lane >> 4;
 
   // B fragments: fragment g row m is column colw + 16*g + m; rank chunk 8q + 32ks.
-  // Requested before the slot's rank arrives (every column j < R is in
-  // bounds); columns at or beyond the rank are zeroed once it is known.
+  // With one rank step (R <= 32) they are requested before the slot's rank
+  // arrives (every column j < R is in bounds) and columns at or beyond the
+  // rank are zeroed once it is known.  With more rank steps only the chunks
+  // below the rank are requested, after it arrives: padded ranks then cost
+  // no B bytes (skewed batch, ranks 8-64 padded to 64: expands 55.5 ->
+  // 52.5 us; prefill unchanged).
   uint4 bw[2 * P][KS];
-  const auto load_b = [&]() {
+  const auto load_b = [&](int jmax) {
 #pragma unroll
     for (int g = 0; g < 2 * P; ++g) {
       const int n = colw + 16 * g + m;
@@ -108,14 +112,16 @@ __device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int 
       for (int ks = 0; ks < KS; ++ks) {
         const int j = 32 * ks + 8 * q;
         bw[g][ks] = make_uint4(0, 0, 0, 0);
-        if (active && n < colend && j < p.R) bw[g][ks] = load16(brow + j);
+        if (active && n < colend && j < jmax) bw[g][ks] = load16(brow + j);
       }
     }
   };
-  load_b();
+  constexpr bool kRankAwareB = KS >= 2 && !FUSED;
+  if constexpr (!kRankAwareB) load_b(p.R);
   int rho = slot_ok ? p.ranks[slot] : 0;
   rho = rho < 0 ? 0 : (rho > p.R ? p.R : rho);
   if (rho == 0) return;  // base model: output rows stay untouched
+  if constexpr (kRankAwareB) load_b(rho);
   const float sigma = p.scalings[slot];
   // Base-row role of this lane: row (RPL*i + lane/LPR) of a 16-token group,
   // columns colw + 8*(lane%LPR) .. +7.
@@ -141,7 +147,7 @@ __device__ __forceinline__ void expand_tile(const ExpandParams& p, int seg, int 
   };
   if constexpr (FUSED) prefetch();
   if (wait()) {  // fragments and rows are in flight during a plain wait
-    load_b();
+    load_b(p.R);
     if constexpr (FUSED) prefetch();
   }
   // The B fragments are masked to the rank just before their first use, so
