@@ -77,6 +77,34 @@ ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments
   // tiles win (qkv 39.1 -> 36.0 us, gate_up 33.2 -> 29.1 us, skewed
   // down_proj with r = 64: 149 -> 134 us).
   const bool long_segments = num_segments > 0 && s >= 96 * static_cast<int64_t>(num_segments);
+  // With a long K (8192 or more) such batches fill the CUs from fewer
+  // re-reads: tiles of 64 tokens by all of c*R (x read once, each A block
+  // once per 64 tokens) with K split in ranges of 7 groups (1792): full-layer
+  // down_proj (4288 tokens, 93 segments, K = 14336, r = 32) 77.7 -> 64.3 us,
+  // against 66.0 us with K in 4, 70.1 us in 14 and 72.3 us with 128-token
+  // tiles.  (On the skewed down_proj, c*R = 64, the GEMM tiles below stay
+  // faster: 119 us against 176-212 us for such tiles.)
+  if (!long_segments && CR <= 32 && K >= 8192) {
+    const int nf = (CR + 15) / 16;
+    const int64_t ks = (kgroups + 6) / 7;
+    const int64_t kps = (kgroups + ks - 1) / ks * 256;
+    const int64_t ksplit2 = (K + kps - 1) / kps;
+    const int64_t counters2 = (s / 64 + num_segments + 1);
+    const int64_t partial = round_up(ksplit2 * s * CR * 4, 256);
+    if (ksplit2 > 1 && counters2 <= kCounterCap && partial < (int64_t{1} << 32) - 256) {
+      t.mf = 4;
+      t.nf = nf;
+      t.nblocks = 1;
+      t.mblocks = (chunk + 63) / 64;
+      if (t.mblocks < 1) t.mblocks = 1;
+      t.kps = kps;
+      t.ksplit = static_cast<int>(ksplit2);
+      t.gemm = 0;
+      t.grid = grid_for(num_segments, static_cast<int64_t>(t.ksplit) * t.mblocks);
+      t.partial_bytes = partial;
+      return t;
+    }
+  }
   if (!long_segments && CR <= 32 && (s <= 6144 || K >= 8192)) {
     t.mf = s > 6144 ? 4 : 2;
     t.nf = 1;
