@@ -874,6 +874,55 @@ def test_long_k_small_grid():
     assert not ws[:COUNTER_BYTES].any()
 
 
+LONG_K_CASES = [
+    # (name, seed, K, slice offsets, R, ranks drawn from): batches of short
+    # segments with c*R <= 32 and K >= 8192 take 64-token tiles over all rank
+    # rows with K split (ranges of 1792), the last range ragged for K = 9000
+    ("c1_R32_K14336", 61, 14336, [0, 1024], 32, [32]),
+    ("c2_R16_K9000", 62, 9000, [0, 640, 1280], 16, [16, 16, 9, 0, 4]),
+    # c*R = 8: a grid this small takes the decode-sized K split instead (2 ranges)
+    ("c1_R8_K8192_small_grid", 63, 8192, [0, 512], 8, [8, 8, 3, 0]),
+]
+
+
+@pytest.mark.parametrize("case", LONG_K_CASES, ids=[c[0] for c in LONG_K_CASES])
+def test_long_k_short_segments(case):
+    """The long-K split-K tiles: the standalone shrink (split-K completion)
+    and expand against the oracle on every element, NaN rank padding, rank-0
+    and partial ranks; with two slices the stacked call bit for bit against
+    the separate calls; the workspace counters left at zero."""
+    sgg = _sgg()
+    from segmented_gather_gemm_amd._lib import calls
+    name, seed, K, offs, R, rank_pool = case
+    rng = np.random.default_rng(seed)
+    n_req, L = 150, 40
+    lens = rng.integers(1, 31, size=n_req).tolist()
+    slots = rng.integers(0, L, size=n_req).tolist()
+    ranks = [int(rng.choice(rank_pool)) for _ in range(L)]
+    b, proj, t = _small_case(seed, lens, slots, L, ranks, rng.uniform(0.5, 2, L).tolist(), K,
+                             offs, R, nan_pad=True)
+    be = backend(b)
+    info = plan_on(be, b)
+    check_plan(info, b, 128)
+    c = len(offs) - 1
+    ind, sl, nseg, hint, perm = info.kernel_segments()
+    assert calls().lora_shrink_workspace_bytes(b.num_tokens, K, c, R, nseg, hint) > COUNTER_BYTES
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    h = sgg.lora_shrink(x, A, info, c, workspace=ws)
+    y_sep = sgg.lora_expand(h, Bw, info, proj.slice_offsets, proj.max_slice, base.clone())
+    torch.cuda.synchronize()
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, f"{name} h")
+    assert_close(y_sep, want_y, f"{name} y")
+    if c > 1:
+        y = sgg.lora_qkv(x, A, Bw, info, proj.slice_offsets, proj.max_slice, base.clone(),
+                         workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_sep)
+    assert not ws[:COUNTER_BYTES].any()
+
+
 def test_short_segments_in_groups():
     """Many short segments (forced chunk 8) on few slots: the planner merges
     consecutive segments of one slot into work segments of up to
