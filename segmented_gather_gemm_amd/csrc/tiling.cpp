@@ -15,7 +15,9 @@ namespace sgg {
 // columns (NF), then rows (MF), down to single fragments; only then split K
 // across workgroups, into at most 4 ranges (each extra range costs a partial
 // tile round trip).  Measured on decode shapes: small tiles with 4 K ranges
-// beat both one big tile and 16-32 K ranges.
+// beat both one big tile and 16-32 K ranges.  Grids that are already large
+// enough take whole-K tiles, except batches of short segments with few rank
+// rows and a long K, which take 64-token tiles with K split (below).
 ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments, int chunk,
                                   bool gemm_ok, bool pair_ok) {
   ShrinkTiling t{};
@@ -86,19 +88,19 @@ ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments
   // faster: 119 us against 176-212 us for such tiles.)
   if (!long_segments && CR <= 32 && K >= 8192) {
     const int nf = (CR + 15) / 16;
-    const int64_t ks = (kgroups + 6) / 7;
-    const int64_t kps = (kgroups + ks - 1) / ks * 256;
-    const int64_t ksplit2 = (K + kps - 1) / kps;
-    const int64_t counters2 = (s / 64 + num_segments + 1);
-    const int64_t partial = round_up(ksplit2 * s * CR * 4, 256);
-    if (ksplit2 > 1 && counters2 <= kCounterCap && partial < (int64_t{1} << 32) - 256) {
+    const int64_t ranges = (kgroups + 6) / 7;
+    const int64_t kps = (kgroups + ranges - 1) / ranges * 256;
+    const int64_t nsplit = (K + kps - 1) / kps;
+    const int64_t ncounters = s / 64 + num_segments + 1;   // one per 64-token tile
+    const int64_t partial = round_up(nsplit * s * CR * 4, 256);
+    if (nsplit > 1 && ncounters <= kCounterCap && partial < (int64_t{1} << 32) - 256) {
       t.mf = 4;
       t.nf = nf;
       t.nblocks = 1;
       t.mblocks = (chunk + 63) / 64;
       if (t.mblocks < 1) t.mblocks = 1;
       t.kps = kps;
-      t.ksplit = static_cast<int>(ksplit2);
+      t.ksplit = static_cast<int>(nsplit);
       t.gemm = 0;
       t.grid = grid_for(num_segments, static_cast<int64_t>(t.ksplit) * t.mblocks);
       t.partial_bytes = partial;
