@@ -297,6 +297,15 @@ def test_workspace_sizes():
     finally:
         L.lora_set_option(b"shrink_pair_tiles", old)
     assert L.lora_shrink_workspace_bytes(0, 4096, 3, 16, 8, 128) == 0
+    # short segments with c*R <= 32 and a long K: 64-token tiles with K split
+    # in ranges of 1792 (8 for the full-layer down_proj), the split-K
+    # counters then the f32 partials [8][s][c*R]
+    s, cr = 4288, 32
+    assert (L.lora_shrink_workspace_bytes(s, 14336, 1, 32, 93, 128)
+            == 65536 + (8 * s * cr * 4 + 255) // 256 * 256)
+    # ... but not with K = 4096 (one range) nor with c*R = 64 (GEMM tiles)
+    assert L.lora_shrink_workspace_bytes(s, 4096, 1, 32, 93, 128) == 0
+    assert L.lora_shrink_workspace_bytes(8192, 14336, 1, 64, 185, 128) == 0
 
 
 def test_error_is_thread_local():
