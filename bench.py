@@ -17,8 +17,9 @@ events on the stream the kernels run on.  Every run also times the other
 workloads, each under its own key: the prefill chunk sweep (16 / 32 / 64 /
 128), the skewed batch (o_proj, down_proj), the Llama-3-8B-shaped layer
 sweep with the embedding gather, the pruned lm_head pass of the decode batch,
-the device-side planner, the shrink's MFMA and VALU forms on short segments
-and the MoE LoRA add; `--legs` picks some, `--quick` skips them all.
+the device-side planner, the shrink's MFMA and VALU forms on short segments,
+the MoE LoRA add and decode-shaped batches of 1024-16384 tokens; `--legs`
+picks some, `--quick` skips them all.
 """
 
 import argparse
@@ -37,7 +38,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_prefill_kernels_hbm_traffic.txt")
-LEGS = ("prefill", "skewed", "full", "lm_head", "device_plan", "short", "moe")
+LEGS = ("prefill", "skewed", "full", "lm_head", "device_plan", "short", "moe", "decode_sizes")
 
 
 def parse():
@@ -667,6 +668,28 @@ def run_skewed(device, steps=20, warmup=4, n_sets=4):
     return res
 
 
+def run_decode_sizes(device, sizes=(1024, 4096, 16384), steps=20, warmup=4, n_sets=3):
+    """The decode batch's shape at more requests: n one-token requests on 8
+    adapters drawn uniformly, rank 16, stacked qkv 4096 -> [4096, 1024, 1024];
+    shrink, expand and the stacked call with their HBM fractions, to show
+    where the kernels leave the launch-and-latency regime of 256 tokens."""
+    import torch
+    from synth.workloads import Batch, Projection
+    from synth import draw_projection
+    res = {"workload": "decode-shaped batches: n x 1 token, 8 adapters uniform, r=16, "
+                       "stacked qkv 4096 -> [4096,1024,1024]"}
+    for n in sizes:
+        rng = np.random.default_rng(1002 + n)
+        b = Batch(f"decode_{n}", 1002 + n, [1] * n, rng.integers(0, 8, n).tolist(), True, 8,
+                  [16] * 8, [1.0] * 8, 128, [Projection("qkv", 4096, [0, 4096, 5120, 6144], 16)])
+        proj = b.projections[0]
+        sets = rotated(_to(device, draw_projection(b, proj)), n_sets)
+        res[str(n)] = measure_projection(device, b, proj, sets, 128, steps, warmup)
+        del sets
+        torch.cuda.empty_cache()
+    return res
+
+
 def run_full(device, layers, steps=5, warmup=1):
     """Full layer sweep, Llama-3-8B shapes: per layer qkv, o, gate_up, down
     over 4288 tokens (192 decode + 8 x 512), 64 adapters r=32, one plan.
@@ -1193,7 +1216,9 @@ def main():
                "device_plan": ("device planner", lambda: run_device_plan(device)),
                "short": ("short segments: MFMA and VALU shrink",
                          lambda: run_short_segments(device)),
-               "moe": ("MoE LoRA add", lambda: run_moe(device))}
+               "moe": ("MoE LoRA add", lambda: run_moe(device)),
+               "decode_sizes": ("decode-shaped batches of 1024-16384 tokens",
+                                lambda: run_decode_sizes(device))}
     for leg in legs:
         print(f"# {runners[leg][0]}", file=sys.stderr, flush=True)
         line[leg] = runners[leg][1]()
