@@ -60,6 +60,30 @@ ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments
     if (ksplit > 4) ksplit = 4;
     if (ksplit > kgroups) ksplit = kgroups;
   }
+  // Tiles of 16 tokens over all the rank rows (33-48 of them: x read once
+  // per K range instead of once per column block) with the fewest K ranges
+  // (1, 2 or 4) that still give every CU a workgroup, for batches that had to
+  // shrink their tiles to 16 tokens and whose segments hold 16 tokens or
+  // more on average.  Measured on decode-shaped batches (stacked qkv, r = 16,
+  // 8 adapters), stacked call: 1024 tokens 28.9 -> 25.9 us (K in 4), 2048
+  // tokens 36.4 -> 31.5 us (K in 2).  Left out: 256 tokens (too few such
+  // tiles: 10.1 vs 8.9 us), 4096 tokens (32-token tiles already fill the GPU;
+  // such tiles 44.7-51 vs 42.6 us) and segments of a few tokens (decode over
+  // 128 adapters: 35.0 vs 32.5 us).
+  if (need_n == 3 && t.mf == 1 && t.nf < need_n &&
+      s >= 16 * static_cast<int64_t>(num_segments)) {
+    const int64_t u_all = units_for(need_n, 1);
+    const int64_t c_all = s / 16 + num_segments + 1;
+    for (int64_t ks : {int64_t{1}, int64_t{2}, int64_t{4}}) {
+      if (ks > kgroups) break;
+      if (u_all * ks >= 256 && (ks == 1 || c_all <= kCounterCap)) {
+        t.nf = need_n;
+        t.nblocks = 1;
+        ksplit = ks;
+        break;
+      }
+    }
+  }
   t.kps = (kgroups + ksplit - 1) / ksplit * 256;
   t.ksplit = static_cast<int>((K + t.kps - 1) / t.kps);
   if (t.ksplit < 1) t.ksplit = 1;

@@ -306,6 +306,13 @@ def test_workspace_sizes():
     # ... but not with K = 4096 (one range) nor with c*R = 64 (GEMM tiles)
     assert L.lora_shrink_workspace_bytes(s, 4096, 1, 32, 93, 128) == 0
     assert L.lora_shrink_workspace_bytes(8192, 14336, 1, 64, 185, 128) == 0
+    # decode-shaped qkv (c*R = 48) of 1024 / 2048 tokens over 8 adapters:
+    # 16-token tiles over all 48 rank rows with K in 4 / 2 ranges; 256 and
+    # 4096 tokens keep 16 x 16 tiles in 4 ranges and 32 x 16 tiles over all K
+    assert L.lora_shrink_workspace_bytes(1024, 4096, 3, 16, 11, 128) == 65536 + 4 * 1024 * 48 * 4
+    assert L.lora_shrink_workspace_bytes(2048, 4096, 3, 16, 20, 128) == 65536 + 2 * 2048 * 48 * 4
+    assert L.lora_shrink_workspace_bytes(256, 4096, 3, 16, 8, 40) == 65536 + 4 * 256 * 48 * 4
+    assert L.lora_shrink_workspace_bytes(4096, 4096, 3, 16, 36, 128) == 0
 
 
 def test_error_is_thread_local():

@@ -923,6 +923,39 @@ def test_long_k_short_segments(case):
     assert not ws[:COUNTER_BYTES].any()
 
 
+@pytest.mark.parametrize("n, ranges", [(1024, 4), (2048, 2)])
+def test_decode_mid_sizes(n, ranges):
+    """Decode-shaped batches of 1024 and 2048 tokens (8 adapters, stacked
+    qkv, r = 16) take 16-token tiles over all 48 rank rows with K in 4 or 2
+    ranges: shrink and expand against the oracle on every element, the
+    stacked call bit for bit against the separate calls."""
+    sgg = _sgg()
+    from segmented_gather_gemm_amd._lib import calls
+    rng = np.random.default_rng(1002 + n)
+    b = Batch(f"decode_{n}", 1002 + n, [1] * n, rng.integers(0, 8, n).tolist(), True, 8,
+              [16] * 8, [1.0] * 8, 128, [Projection("qkv", 4096, [0, 4096, 5120, 6144], 16)])
+    proj = b.projections[0]
+    t = draw_projection(b, proj)
+    be = backend(b)
+    info = plan_on(be, b)
+    check_plan(info, b, 128)
+    ind, sl, nseg, hint, perm = info.kernel_segments()
+    need = calls().lora_shrink_workspace_bytes(n, 4096, 3, 16, nseg, hint)
+    assert need == COUNTER_BYTES + ranges * n * 48 * 4
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    h = sgg.lora_shrink(x, A, info, 3, workspace=ws)
+    y_sep = sgg.lora_expand(h, Bw, info, proj.slice_offsets, proj.max_slice, base.clone())
+    y = sgg.lora_qkv(x, A, Bw, info, proj.slice_offsets, proj.max_slice, base.clone(),
+                     workspace=ws)
+    torch.cuda.synchronize()
+    want_h, want_y = oracle_forward(t, b, proj)
+    assert_close(h, want_h, f"decode {n} h")
+    assert_close(y_sep, want_y, f"decode {n} y")
+    assert torch.equal(y, y_sep)
+    assert not ws[:COUNTER_BYTES].any()
+
+
 def test_short_segments_in_groups():
     """Many short segments (forced chunk 8) on few slots: the planner merges
     consecutive segments of one slot into work segments of up to
