@@ -668,7 +668,7 @@ def run_skewed(device, steps=20, warmup=4, n_sets=4):
     return res
 
 
-def run_decode_sizes(device, sizes=(1024, 4096, 16384), steps=20, warmup=4, n_sets=3):
+def run_decode_sizes(device, sizes=(1024, 2048, 4096, 16384), steps=20, warmup=4, n_sets=3):
     """The decode batch's shape at more requests: n one-token requests on 8
     adapters drawn uniformly, rank 16, stacked qkv 4096 -> [4096, 1024, 1024];
     shrink, expand and the stacked call with their HBM fractions, to show
