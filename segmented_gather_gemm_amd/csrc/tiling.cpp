@@ -148,8 +148,11 @@ ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments
   // 128 tokens per tile and rank rows the smallest of 32 / 64 / 128 covering
   // c*R; batches of short segments (decode mixed in, many adapters, a long
   // tail of one-request adapters) take 64 x 32 tiles, whose larger grid
-  // spreads the long segments over more CUs.  Then halve the rows, then the
-  // tokens, while the grid has fewer work items than CUs.  Measured: 64 x 32
+  // spreads the long segments over more CUs.  Then, while the grid has
+  // fewer work items than CUs, halve the tokens if that alone fills the GPU
+  // (x stays read once per column block; decode-shaped 16384 tokens, c*R =
+  // 48: 64 x 64 tiles 48.9 us against 59.2 us for 128 x 32), else halve the
+  // rows, then the tokens.  Measured: 64 x 32
   // beats 128 x 32 by 10-20 % on the mixed and skewed batches (full-layer
   // qkv 44 -> 39 us, skewed down_proj 202 -> 185 us), 128 x 128 beats every
   // smaller tile by 25 % or more on prefill; the split-K kernel is faster on
@@ -162,6 +165,7 @@ ShrinkTiling choose_shrink_tiling(int64_t s, int64_t K, int CR, int num_segments
     const int64_t real_units = (s + m - 1) / m + num_segments;
     return (grid_units < real_units ? grid_units : real_units) * nbk;
   };
+  if (gemm_units(gm, gn) < 256 && gm > 64 && gemm_units(gm / 2, gn) >= 256) gm /= 2;
   while (gemm_units(gm, gn) < 256 && gn > 32) gn /= 2;
   while (gemm_units(gm, gn) < 256 && gm > 64) gm /= 2;
   // Too few workgroups for whole-K tiles (each workgroup has one K step of

@@ -956,6 +956,36 @@ def test_decode_mid_sizes(n, ranges):
     assert not ws[:COUNTER_BYTES].any()
 
 
+def test_decode_16384_gemm_tiles():
+    """A decode-shaped batch of 16384 tokens (8 adapters, stacked qkv, r =
+    16) takes 64 x 64 GEMM tiles: sampled rows (every segment boundary plus a
+    seeded sample) against the oracle, the stacked call bit for bit against
+    the separate calls on every row."""
+    sgg = _sgg()
+    n = 16384
+    rng = np.random.default_rng(1002 + n)
+    b = Batch(f"decode_{n}", 1002 + n, [1] * n, rng.integers(0, 8, n).tolist(), True, 8,
+              [16] * 8, [1.0] * 8, 128, [Projection("qkv", 4096, [0, 4096, 5120, 6144], 16)])
+    proj = b.projections[0]
+    t = draw_projection(b, proj)
+    be = backend(b)
+    info = plan_on(be, b)
+    ref = check_plan(info, b, 128)
+    rows = sample_rows(ref, n, seed=16384)
+    x, A, Bw, base = (t[k].to(DEV) for k in ("x", "A", "B", "base"))
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    h = sgg.lora_shrink(x, A, info, 3, workspace=ws)
+    y_sep = sgg.lora_expand(h, Bw, info, proj.slice_offsets, proj.max_slice, base.clone())
+    y = sgg.lora_qkv(x, A, Bw, info, proj.slice_offsets, proj.max_slice, base.clone(),
+                     workspace=ws)
+    torch.cuda.synchronize()
+    want_h, want_y = oracle_forward(t, b, proj, rows)
+    rows_t = torch.as_tensor(rows, device=DEV)
+    assert_close(h.index_select(0, rows_t), want_h, "decode 16384 h")
+    assert_close(y_sep.index_select(0, rows_t), want_y, "decode 16384 y")
+    assert torch.equal(y, y_sep)
+
+
 def test_short_segments_in_groups():
     """Many short segments (forced chunk 8) on few slots: the planner merges
     consecutive segments of one slot into work segments of up to
