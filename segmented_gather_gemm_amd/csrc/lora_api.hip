@@ -98,15 +98,20 @@ int check_expand(const void* h, int64_t ldh, const void* B, int64_t N, const voi
 }
 
 // Columns per workgroup: 128 * pairs; 256 when that still gives at least 16
-// workgroups per CU, else 128.  Measured: 256 wins on the 28672-wide gate_up
-// of prefill (1014 -> 825 us) and of the full-layer batch (192 -> 147 us);
-// 128 wins by 1-3 us on the 4096- and 6144-wide outputs of the full-layer and
-// skewed batches, whose grids are 5-10x smaller; 512 is slower everywhere.
+// workgroups per CU, or at least 4 when the segments average 96 tokens or
+// more; else 128.  Measured: 256 wins on the 28672-wide gate_up of prefill
+// (1014 -> 825 us) and of the full-layer batch (192 -> 147 us), and on
+// decode-shaped qkv batches of long segments (stacked call, 8192 tokens 96.9
+// -> 90.5 us, 16384 tokens 162.7 -> 146.2 us; 4096 tokens, under 4 per CU,
+// 44.3 vs 45.0 us); 128 wins by 1-3 us on the 4096- and 6144-wide outputs of
+// the full-layer and skewed batches (segments of 44-46 tokens on average),
+// whose grids are 5-10x smaller; 512 is slower everywhere.
 // Rank steps of 32.
 // `pairs` > 0 forces the column tile (128 * pairs).  `deal_tiles`: column
 // tiles dealt to the XCDs (expand_item_of); *tiles_per_xcd gets their count
 // per XCD (0: segments dealt instead).
-sgg::ExpandTiling choose_expand_tiling(const int32_t* offs, int c, int num_segments, int R,
+sgg::ExpandTiling choose_expand_tiling(const int32_t* offs, int c, int num_segments, int64_t s,
+                                       int R,
                                        int32_t* tile_start, int32_t* total,
                                        int32_t* tiles_per_xcd, int pairs = 0,
                                        bool deal_tiles = false) {
@@ -116,7 +121,8 @@ sgg::ExpandTiling choose_expand_tiling(const int32_t* offs, int c, int num_segme
   for (int cand : {2}) {
     int64_t tiles = 0;
     for (int k = 0; k < c; ++k) tiles += (offs[k + 1] - offs[k] + 128 * cand - 1) / (128 * cand);
-    if (tiles * num_segments >= 4096) {
+    const bool long_segments = num_segments > 0 && s >= 96 * static_cast<int64_t>(num_segments);
+    if (tiles * num_segments >= 4096 || (long_segments && tiles * num_segments >= 1024)) {
       t.pairs = cand;
       break;
     }
@@ -238,7 +244,7 @@ sgg::ExpandParams expand_params(const void* h, int64_t ldh, const void* B, int64
                                 bool segment_dealing = false) {
   sgg::ExpandParams p{};
   const bool deal = !segment_dealing && g_expand_deal_tiles.load(std::memory_order_relaxed) != 0;
-  *tiling = choose_expand_tiling(offs, c, num_segments, R, p.tile_start, &p.total_tiles,
+  *tiling = choose_expand_tiling(offs, c, num_segments, s, R, p.tile_start, &p.total_tiles,
                                  &p.tiles_per_xcd, pairs, deal);
   bool vec8 = sgg::aligned16(out) && ldo % 8 == 0;
   for (int k = 0; k <= c; ++k) {
