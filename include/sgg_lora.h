@@ -292,7 +292,10 @@ int lora_shrink(const void* x, int64_t ldx, const void* A, void* h, int64_t ldh,
  *   out[t, o_k + n] += sigma_a * sum_{j < rho_a} B[a, o_k + n, j] * h[t, k*R + j]
  * for slice k < c and n < o_{k+1} - o_k.  Columns at or past o_c and every
  * row of a rank-0 slot are left bit-for-bit unchanged.  Rank padding of B
- * and h is never read.
+ * and h never reaches the result (it may hold anything, NaN included): with
+ * R <= 32 the B fragments are loaded before the slot's rank is known and
+ * their columns past the rank discarded, h rows are staged whole, and only
+ * the columns below the rank are used.
  *
  *   h          (s, c*R) bf16, row stride ldh >= c*R.
  *   B          (L, N, R) bf16 dense, N >= o_c.
