@@ -3,9 +3,10 @@
 A step is one pass of the whole path over one batch: host plan (native
 planner) -> one async upload of the plan -> LoRA-A shrink -> LoRA-B expand
 (scaling, stacked slice offsets, in place into base) -> LoRA-A embedding
-gather.  The timed steps are eager: one native call plans and uploads, one
-call runs the embedding gather and one runs lora_qkv (the stacked shrink and
-expand).  Graph mode is timed too and reported beside it.  The headline
+gather.  The timed steps are eager: one native call plans, uploads and runs
+the embedding gather (one launch for a decode batch), one runs lora_qkv (the
+stacked shrink and expand).  The same step with the upload and the gather as
+separate calls, and graph mode, are timed too and reported beside it.  The headline
 workload is the decode batch: 256 one-token requests on 8 adapters drawn
 uniformly, rank 16, stacked qkv 4096 -> [4096, 1024, 1024], bf16; the
 embedding gather uses vocab 128256 and rank 16.  Inputs rotate over 48
@@ -238,6 +239,17 @@ def run_decode(args, device):
     be = sgg.ChunkedSgmvLoRA(b0.num_loras, b0.max_chunk_size, device)
 
     def eager_step(i):
+        # plan + upload and the embedding gather in one C call (one launch)
+        st = sets[i % len(sets)]
+        proj = st["proj"]
+        info = be.prepare_lora_batch_with_embedding(None, st["slots"], st["ranks"], st["scal"],
+                                                    st["ids"], st["A_emb"], vocab,
+                                                    is_decode=True, out=st["e"])[0]
+        sgg.lora_qkv(st["x"], st["A"], st["B"], info, proj.slice_offsets, proj.max_slice,
+                     st["base"], workspace=ws)
+
+    def eager_step_separate(i):
+        # the same step with the upload and the embedding gather as two calls
         st = sets[i % len(sets)]
         proj = st["proj"]
         info = be.prepare_lora_batch(None, st["slots"], st["ranks"], st["scal"], is_decode=True)
@@ -271,6 +283,14 @@ def run_decode(args, device):
         eager_step(i)
     torch.cuda.synchronize()
     eager_wall = time.perf_counter() - t0
+    for i in range(args.warmup):
+        eager_step_separate(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        eager_step_separate(i)
+    torch.cuda.synchronize()
+    separate_wall = time.perf_counter() - t0
 
     # ---- kernel durations, same plans and launch configuration, HIP events
     # on the launch stream.  The plans are made first; then, per kernel, a
@@ -318,6 +338,33 @@ def run_decode(args, device):
         sgg.lora_set_option("fused_stacked", fused)
         dur[n] = e0.elapsed_time(e1) * 1e3 / args.steps   # microseconds per launch
     del infos
+
+    # the upload launch alone (plan copy) and with the embedding gather, one
+    # per prepared batch, back to back: at most one ring's worth of batches,
+    # so no prepare waits for a slot while the delay kernel holds the stream
+    def prep(n, i):
+        st = sets[i % len(sets)]
+        if n == "copy":
+            be.prepare_lora_batch(None, st["slots"], st["ranks"], st["scal"], is_decode=True)
+        else:
+            be.prepare_lora_batch_with_embedding(None, st["slots"], st["ranks"], st["scal"],
+                                                 st["ids"], st["A_emb"], vocab, is_decode=True,
+                                                 out=st["e"])
+    n_up = min(args.steps, be._staging.n)
+    upload = {"launches": n_up}
+    for n in ("copy", "copy_and_embedding"):
+        for i in range(n_up):
+            prep(n, i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        held = hold_stream(stream, 5.0)
+        e0.record(stream)
+        for i in range(n_up):
+            prep(n, i)
+        e1.record(stream)
+        back_to_back &= not held.query()
+        torch.cuda.synchronize()
+        upload[n + "_us"] = round(e0.elapsed_time(e1) * 1e3 / n_up, 3)
 
     # ---- graph mode (secondary)
     bg = sgg.ChunkedSgmvLoRA(b0.num_loras, b0.max_chunk_size, device)
@@ -452,6 +499,11 @@ def run_decode(args, device):
     se_flops = per["shrink"]["algo_flops"] + per["expand"]["algo_flops"]
     return {
         "wall_s": eager_wall, "graph_wall_s": graph_wall, "tokens": b0.num_tokens,
+        "separate": {"ms_per_step": round(separate_wall / args.steps * 1e3, 4),
+                     "tokens_per_s": round(b0.num_tokens * args.steps / separate_wall, 1),
+                     "step": "host plan + upload (copy kernel), embedding gather, lora_qkv "
+                             "(two launches)"},
+        "upload_launch": upload,
         "graph_device_plan": {
             "ms_per_step": round(dgraph_wall / args.steps * 1e3, 4),
             "tokens_per_s": round(b0.num_tokens * args.steps / dgraph_wall, 1),
@@ -1187,7 +1239,10 @@ def main():
                      "traffic": traffic_for(dom_name, "decode"),
                      "algo_bytes_per_launch": k[dom_name]["algo_bytes"],
                      "avg_launch_us": dom["us"]},
-        "mode": "eager: host plan + one upload, embedding gather, lora_qkv (two launches)",
+        "mode": "eager: host plan, then one launch that uploads the plan and does the "
+                "embedding gather, then lora_qkv (two launches)",
+        "separate_upload_and_embedding": res["separate"],
+        "upload_launch": res["upload_launch"],
         "graph_tokens_per_s": round(graph, 1),
         "graph_ms_per_step": round(res["graph_wall_s"] / args.steps * 1e3, 4),
         "graph_device_plan": res["graph_device_plan"],

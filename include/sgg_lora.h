@@ -177,6 +177,42 @@ int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slots, int32_t 
                      int32_t* out_info, int32_t* done_flag, int32_t done_value, void* stream);
 
 /*
+ * lora_plan_upload_embedding -- lora_plan_upload, then lora_a_embedding of
+ * the uploaded batch, with the same results as those two calls: the plan in
+ * device_plan, out_info and done_flag exactly as lora_plan_upload, and
+ * out[t, j] = A_emb[a(t), j, input_ids[t]] for j < rho_a and in-vocabulary
+ * ids (else 0) for the num_tokens tokens of the batch.
+ * (chunked_backend.py page: prepare_lora_batch, then run_lora_a_embedding,
+ *  the first LoRA call of a forward pass.)
+ *
+ * For a decode-shaped batch (decode mode, or every seq_lens[r] == 1) of at
+ * most 3072 tokens with max_loras <= 64, both are one launch: one workgroup
+ * copies the plan while the others do the lookup, taking each token's slot
+ * (token t is request t) and the slots' ranks from the call's arguments
+ * instead of the plan.  Any other batch gets the two launches of the
+ * separate calls.
+ *
+ *   Plan arguments as lora_plan_upload (same ownership and the same staging
+ *   rules: the done flag is raised once the staging buffer has been read).
+ *   input_ids  (num_tokens,) int64 (device).
+ *   A_emb      (max_loras, R, V) bf16 dense, V >= vocab_size.
+ *   out        (num_tokens, R) bf16, row stride ldo >= R.
+ *   Ranks above R are taken as R, negative ranks as 0.
+ * Errors: as lora_plan_upload and lora_a_embedding; the embedding arguments
+ * are checked before anything is planned or enqueued.
+ */
+int lora_plan_upload_embedding(const int32_t* seq_lens, const int32_t* req_slots,
+                               int32_t num_reqs, const int32_t* lora_ranks,
+                               const float* scalings, int32_t max_loras, int32_t is_decode,
+                               int32_t max_chunk_size, int32_t chunk_size_override,
+                               int64_t token_capacity, int32_t seg_capacity,
+                               int32_t req_capacity, void* host_staging, void* device_plan,
+                               int64_t buffer_bytes, int32_t* out_info, int32_t* done_flag,
+                               int32_t done_value, const int64_t* input_ids, const void* A_emb,
+                               int64_t V, void* out, int64_t ldo, int32_t R,
+                               int64_t vocab_size, void* stream);
+
+/*
  * lora_plan_device -- the batch plan computed on the GPU, as one kernel on
  * `stream`, from request lengths and slots already in device memory.
  * (chunked_backend.py page: the steps of lora_plan_upload -- chunk size,

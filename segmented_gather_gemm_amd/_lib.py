@@ -28,6 +28,10 @@ SIGNATURES = {
     "lora_plan_upload": (ctypes.c_int, [
         _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
         _i64, _i32, _i32, _vp, _vp, _i64, _vp, _vp, _i32, _vp]),
+    "lora_plan_upload_embedding": (ctypes.c_int, [
+        _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+        _i64, _i32, _i32, _vp, _vp, _i64, _vp, _vp, _i32,
+        _vp, _vp, _i64, _vp, _i64, _i32, _i64, _vp]),
     "lora_plan_device": (ctypes.c_int, [
         _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
         _i64, _i32, _i32, _vp, _i64, _vp, _vp]),

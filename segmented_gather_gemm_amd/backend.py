@@ -211,9 +211,43 @@ class ChunkedSgmvLoRA:
         weight_indices: slot per request; lora_ranks / scalings: per slot
         (``max_loras_per_batch`` entries, rank 0 = no adapter).
         """
+        return self._prepare(seq_lens, weight_indices, lora_ranks, scalings, is_decode,
+                             use_cuda_graph, chunk_size_override, None)
+
+    def prepare_lora_batch_with_embedding(self, seq_lens, weight_indices, lora_ranks, scalings,
+                                          input_ids, weights, vocab_size, is_decode=False,
+                                          use_cuda_graph=False, chunk_size_override=0,
+                                          out=None):
+        """prepare_lora_batch, then run_lora_a_embedding(input_ids, weights,
+        vocab_size) over that batch -- the first LoRA call of a forward pass
+        -- with the same results.  For decode-shaped batches (one token per
+        request) the upload and the lookup are one launch.  Returns
+        (batch_info, embedding output of shape (num_tokens, R))."""
+        if input_ids.dtype is not torch.int64 or not input_ids.is_cuda:
+            raise TypeError("input_ids must be an int64 tensor on a ROCm device")
+        B._need_bf16_dense("weights", weights, 3)
+        L, R, V = weights.shape
+        if L != self.max_loras_per_batch:
+            raise ValueError(f"weights hold {L} slots, the backend {self.max_loras_per_batch}")
+        ids = input_ids.contiguous()
+        s = ids.shape[0]
+        if out is None:
+            out = torch.empty((s, R), dtype=torch.bfloat16, device=weights.device)
+        ost = B._need_bf16("out", out, 2)
+        B._need_rows_cols("out", out, s, R)
+        emb = (s, ids.data_ptr(), weights.data_ptr(), V, out.data_ptr(), ost[0], R,
+               int(vocab_size))
+        info = self._prepare(seq_lens, weight_indices, lora_ranks, scalings, is_decode,
+                             use_cuda_graph, chunk_size_override, emb)
+        return info, out
+
+    def _prepare(self, seq_lens, weight_indices, lora_ranks, scalings, is_decode,
+                 use_cuda_graph, chunk_size_override, emb):
         L = self.max_loras_per_batch
         lens, slots, ranks, scal, s = batch_arrays(seq_lens, weight_indices, lora_ranks,
                                                    scalings, L)
+        if emb is not None and emb[0] != s:
+            raise ValueError(f"{emb[0]} ids, the batch has {s} tokens")
         bs = len(slots)
         if use_cuda_graph:
             if self._graph_cap is None:
@@ -242,10 +276,16 @@ class ChunkedSgmvLoRA:
         idx = self._dev_index if self._dev_index is not None else torch.cuda.current_device()
         stream = torch._C._cuda_getCurrentRawStream(idx)
         flag, flag_value = stg.signal(ring)
-        check(calls().lora_plan_upload(
-            lens, slots, bs, ranks, scal, L, 1 if is_decode else 0, self.max_chunk_size,
-            int(chunk_size_override), s_cap, seg_cap, req_cap, stg.host_addr[ring], dev_addr,
-            dev_bytes, self._info_addr, flag, flag_value, stream))
+        if emb is None:
+            check(calls().lora_plan_upload(
+                lens, slots, bs, ranks, scal, L, 1 if is_decode else 0, self.max_chunk_size,
+                int(chunk_size_override), s_cap, seg_cap, req_cap, stg.host_addr[ring],
+                dev_addr, dev_bytes, self._info_addr, flag, flag_value, stream))
+        else:
+            check(calls().lora_plan_upload_embedding(
+                lens, slots, bs, ranks, scal, L, 1 if is_decode else 0, self.max_chunk_size,
+                int(chunk_size_override), s_cap, seg_cap, req_cap, stg.host_addr[ring],
+                dev_addr, dev_bytes, self._info_addr, flag, flag_value, *emb[1:], stream))
         stg.done(ring)
         n_seg, chunk, longest, _, n_work, longest_work = self._info_np.tolist()
         if use_cuda_graph:

@@ -198,28 +198,28 @@ namespace {
 constexpr int kCopyThreads = 1024;
 constexpr int kCopyDepth = 8;  // 8-byte loads in flight per thread
 
-// One workgroup copies the whole plan.  Each thread requests kCopyDepth
-// 8-byte pieces before storing any, so a plan of up to 64 KB costs one
+// One workgroup copies the whole plan.  Each thread requests DEPTH 8-byte
+// pieces before storing any, so THREADS * DEPTH * 8 bytes of plan cost one
 // host-memory round trip.  Once every thread has stored its pieces the
 // staging buffer has been read in full; thread 0 then writes `done_value` to
 // `done` (host memory, system scope), if given, so the host can reuse the
 // staging buffer without an event.
-__global__ __launch_bounds__(kCopyThreads) void plan_copy_kernel(const int32_t* src, int32_t* dst,
-                                                                 int64_t n, int32_t* done,
-                                                                 int32_t done_value) {
+template <int THREADS, int DEPTH>
+__device__ __forceinline__ void copy_plan_block(const int32_t* src, int32_t* dst, int64_t n,
+                                                int32_t* done, int32_t done_value) {
   const int64_t n2 = n >> 1;
   const uint64_t* s2 = reinterpret_cast<const uint64_t*>(src);
   uint64_t* d2 = reinterpret_cast<uint64_t*>(dst);
-  for (int64_t i0 = threadIdx.x; i0 < n2; i0 += static_cast<int64_t>(kCopyThreads) * kCopyDepth) {
-    uint64_t v[kCopyDepth];
+  for (int64_t i0 = threadIdx.x; i0 < n2; i0 += static_cast<int64_t>(THREADS) * DEPTH) {
+    uint64_t v[DEPTH];
 #pragma unroll
-    for (int u = 0; u < kCopyDepth; ++u) {
-      const int64_t i = i0 + static_cast<int64_t>(u) * kCopyThreads;
+    for (int u = 0; u < DEPTH; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * THREADS;
       v[u] = i < n2 ? __hip_atomic_load(s2 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : 0;
     }
 #pragma unroll
-    for (int u = 0; u < kCopyDepth; ++u) {
-      const int64_t i = i0 + static_cast<int64_t>(u) * kCopyThreads;
+    for (int u = 0; u < DEPTH; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * THREADS;
       if (i < n2) d2[i] = v[u];
     }
   }
@@ -232,6 +232,45 @@ __global__ __launch_bounds__(kCopyThreads) void plan_copy_kernel(const int32_t* 
   }
 }
 
+__global__ __launch_bounds__(kCopyThreads) void plan_copy_kernel(const int32_t* src, int32_t* dst,
+                                                                 int64_t n, int32_t* done,
+                                                                 int32_t done_value) {
+  copy_plan_block<kCopyThreads, kCopyDepth>(src, dst, n, done, done_value);
+}
+
+// Plan copy and the decode-shaped embedding lookup in one launch.  Workgroup
+// 0 copies the plan (16 KB per host-memory round trip: the plan of 256
+// decode tokens takes one, of 3072 three; deeper unrolling spills scalar
+// registers).  Each other
+// workgroup takes 128 consecutive (token, j) pairs, the position-major
+// embedding's spread over the CUs: the token's slot comes from the kernel
+// arguments at the same time as its id from the device, then the table
+// value and the slot's rank (also an argument) together -- two dependent
+// round trips, and no read of the plan, which is still in flight.  As in
+// the other forms, the value is requested for every j < R and kept only
+// below the rank.
+constexpr int kEmbedUploadThreads = 128;
+constexpr int kEmbedUploadDepth = 16;
+
+__global__ __launch_bounds__(kEmbedUploadThreads) void plan_copy_embedding_kernel(
+    EmbedUploadParams p) {
+  if (blockIdx.x == 0) {
+    copy_plan_block<kEmbedUploadThreads, kEmbedUploadDepth>(p.src, p.dst, p.n, p.done,
+                                                            p.done_value);
+    return;
+  }
+  const int q = static_cast<int>(blockIdx.x - 1) * kEmbedUploadThreads + threadIdx.x;
+  const int t = q / p.R;
+  if (t >= p.s) return;
+  const int j = q - t * p.R;
+  const int slot = p.slot[t];
+  const int64_t id = p.ids[t];
+  const int rho = p.rank[slot];
+  uint16_t v = 0;
+  if (id >= 0 && id < p.vocab) v = p.A[(static_cast<int64_t>(slot) * p.R + j) * p.V + id];
+  p.out[static_cast<int64_t>(t) * p.ldo + j] = j < rho ? v : 0;
+}
+
 }  // namespace
 
 hipError_t launch_plan_copy(const int32_t* src_dev_view, int32_t* dst, int64_t n,
@@ -239,6 +278,14 @@ hipError_t launch_plan_copy(const int32_t* src_dev_view, int32_t* dst, int64_t n
   if (n <= 0 && done_dev_view == nullptr) return hipSuccess;
   hipLaunchKernelGGL(plan_copy_kernel, dim3(1), dim3(kCopyThreads), 0, stream, src_dev_view, dst,
                      n < 0 ? 0 : n, done_dev_view, done_value);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_copy_embedding(const EmbedUploadParams& p, hipStream_t stream) {
+  const int64_t pairs = static_cast<int64_t>(p.s) * p.R;
+  const int64_t grid = 1 + (pairs + kEmbedUploadThreads - 1) / kEmbedUploadThreads;
+  hipLaunchKernelGGL(plan_copy_embedding_kernel, dim3(static_cast<unsigned>(grid)),
+                     dim3(kEmbedUploadThreads), 0, stream, p);
   return hipGetLastError();
 }
 

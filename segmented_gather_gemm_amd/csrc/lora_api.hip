@@ -707,15 +707,28 @@ extern "C" int64_t lora_plan_layout(int64_t token_capacity, int32_t seg_capacity
 
 namespace {
 
+// The LoRA-A embedding lookup that lora_plan_upload_embedding runs over the
+// batch it uploads (arguments as lora_a_embedding's, already checked).
+struct EmbedRequest {
+  const int64_t* ids;
+  const void* A;
+  int64_t V;
+  void* out;
+  int64_t ldo;
+  int32_t R;
+  int64_t vocab;
+};
+
 // Plan into the staging buffer (`lm_head`: the pruned lm_head plan, else the
-// chunked plan), add the tables and the work segments, then one transfer.
+// chunked plan), add the tables and the work segments, then one transfer
+// (and, given `emb`, the embedding lookup over the uploaded plan).
 int plan_upload(bool lm_head, const int32_t* seq_lens, const int32_t* req_slots,
                 int32_t num_reqs, const int32_t* lora_ranks, const float* scalings,
                 int32_t max_loras, int32_t is_decode, int32_t max_chunk_size,
                 int32_t chunk_size_override, int64_t token_capacity, int32_t seg_capacity,
                 int32_t req_capacity, void* host_staging, void* device_plan,
                 int64_t buffer_bytes, int32_t* out_info, int32_t* done_flag,
-                int32_t done_value, void* stream) {
+                int32_t done_value, void* stream, const EmbedRequest* emb = nullptr) {
 
   int64_t off[SGG_PLAN_REGIONS];
   const int64_t total = lora_plan_layout(token_capacity, seg_capacity, req_capacity, max_loras, off);
@@ -816,11 +829,45 @@ int plan_upload(bool lm_head, const int32_t* seq_lens, const int32_t* req_slots,
   // One transfer (region 9 only for the lm_head plan): a copy kernel reading
   // the pinned buffer through its device mapping (it also raises the done
   // flag); a runtime copy only if the buffer has no device mapping, followed
-  // by an empty copy that raises the flag.
+  // by an empty copy that raises the flag.  With an embedding request over a
+  // decode-shaped batch (token t is request t) of at most
+  // kEmbedUploadMaxTokens tokens and kEmbedUploadMaxLoras slots, the copy
+  // kernel also does the lookup, from slots and ranks passed as kernel
+  // arguments; otherwise the lookup runs after the copy, over the device plan.
   const int64_t n_copy = lm_head ? total : off[9];
   void* src = nullptr;
   hipError_t e = hipHostGetDevicePointer(&src, host_staging, 0);
-  if (e == hipSuccess && src != nullptr) {
+  const bool mapped = e == hipSuccess && src != nullptr;
+  bool decode_shaped = is_decode != 0 || n_tok == num_reqs;
+  for (int32_t r = 0; !is_decode && decode_shaped && r < num_reqs; ++r)
+    decode_shaped = seq_lens[r] == 1;
+  const bool fused_embed = emb != nullptr && mapped && !lm_head && decode_shaped && n_tok > 0 &&
+                           n_tok <= sgg::kEmbedUploadMaxTokens &&
+                           max_loras <= sgg::kEmbedUploadMaxLoras;
+  if (fused_embed) {
+    sgg::EmbedUploadParams ep;
+    ep.src = static_cast<const int32_t*>(src);
+    ep.dst = static_cast<int32_t*>(device_plan);
+    ep.done = done_dev;
+    ep.ids = emb->ids;
+    ep.A = static_cast<const uint16_t*>(emb->A);
+    ep.out = static_cast<uint16_t*>(emb->out);
+    ep.n = n_copy;
+    ep.V = emb->V;
+    ep.vocab = emb->vocab;
+    ep.ldo = emb->ldo;
+    ep.done_value = done_value;
+    ep.s = static_cast<int32_t>(n_tok);
+    ep.R = emb->R;
+    ep.pad_ = 0;
+    for (int32_t a = 0; a < sgg::kEmbedUploadMaxLoras; ++a) {
+      const int32_t rho = a < max_loras ? lora_ranks[a] : 0;
+      ep.rank[a] = rho < 0 ? 0 : (rho > emb->R ? emb->R : rho);
+    }
+    // the planner has checked every slot against max_loras (<= 64)
+    for (int32_t t = 0; t < ep.s; ++t) ep.slot[t] = static_cast<uint8_t>(req_slots[t]);
+    e = sgg::launch_plan_copy_embedding(ep, static_cast<hipStream_t>(stream));
+  } else if (mapped) {
     e = sgg::launch_plan_copy(static_cast<const int32_t*>(src), static_cast<int32_t*>(device_plan),
                               n_copy, done_dev, done_value, static_cast<hipStream_t>(stream));
   } else {
@@ -839,6 +886,12 @@ int plan_upload(bool lm_head, const int32_t* seq_lens, const int32_t* req_slots,
   out_info[3] = static_cast<int32_t>(n_tok);
   out_info[4] = n_work;
   out_info[5] = longest_work;
+  if (emb != nullptr && !fused_embed && n_tok > 0) {
+    const int32_t* d = static_cast<const int32_t*>(device_plan);
+    return lora_a_embedding(emb->ids, emb->A, emb->V, emb->out, emb->ldo, n_tok, max_loras,
+                            emb->R, emb->vocab, d + off[1], d + off[2], n_seg, d + off[0],
+                            d + off[5], 0, stream);
+  }
   return sgg::ok();
 }
 
@@ -856,6 +909,32 @@ extern "C" int lora_plan_upload(const int32_t* seq_lens, const int32_t* req_slot
                      is_decode, max_chunk_size, chunk_size_override, token_capacity,
                      seg_capacity, req_capacity, host_staging, device_plan, buffer_bytes,
                      out_info, done_flag, done_value, stream);
+}
+
+extern "C" int lora_plan_upload_embedding(
+    const int32_t* seq_lens, const int32_t* req_slots, int32_t num_reqs,
+    const int32_t* lora_ranks, const float* scalings, int32_t max_loras, int32_t is_decode,
+    int32_t max_chunk_size, int32_t chunk_size_override, int64_t token_capacity,
+    int32_t seg_capacity, int32_t req_capacity, void* host_staging, void* device_plan,
+    int64_t buffer_bytes, int32_t* out_info, int32_t* done_flag, int32_t done_value,
+    const int64_t* input_ids, const void* A_emb, int64_t V, void* out, int64_t ldo, int32_t R,
+    int64_t vocab_size, void* stream) {
+  // the lookup's arguments are checked before anything is planned or enqueued
+  SGG_CHECK(A_emb && ((input_ids && out) || num_reqs == 0), SGG_ERR_INVALID,
+            "input_ids, A_emb or out is NULL");
+  SGG_CHECK(R > 0, SGG_ERR_INVALID, "R=%d must be positive", R);
+  SGG_CHECK(vocab_size >= 0 && vocab_size <= V, SGG_ERR_INVALID,
+            "vocab_size=%" PRId64 " outside [0, V=%" PRId64 "]", vocab_size, V);
+  SGG_CHECK(ldo >= R, SGG_ERR_INVALID, "ldo=%" PRId64 " < R=%d", ldo, R);
+  SGG_CHECK((reinterpret_cast<uintptr_t>(out) & 1u) == 0 &&
+                (reinterpret_cast<uintptr_t>(A_emb) & 1u) == 0 &&
+                (reinterpret_cast<uintptr_t>(input_ids) & 7u) == 0,
+            SGG_ERR_UNSUPPORTED, "misaligned pointer");
+  const EmbedRequest emb{input_ids, A_emb, V, out, ldo, R, vocab_size};
+  return plan_upload(false, seq_lens, req_slots, num_reqs, lora_ranks, scalings, max_loras,
+                     is_decode, max_chunk_size, chunk_size_override, token_capacity,
+                     seg_capacity, req_capacity, host_staging, device_plan, buffer_bytes,
+                     out_info, done_flag, done_value, stream, &emb);
 }
 
 extern "C" int lora_plan_device(const int32_t* seq_lens, const int32_t* req_slots,

@@ -96,6 +96,7 @@ static int convert(const char* name, const char* sig, PyObject* const* args, Py_
  * SIGNATURES dict. */
 #define SIG_lora_plan_max_segments "lii"
 #define SIG_lora_plan_upload "ppippiiiiliipplppip"
+#define SIG_lora_plan_upload_embedding "ppippiiiiliipplppipplplilp"
 #define SIG_lora_plan_lm_head_upload "ppippiiiliipplppip"
 #define SIG_lora_plan_device "ppippiiiiliiplpp"
 #define SIG_lora_shrink_workspace_bytes "lliiii"
@@ -133,6 +134,15 @@ static PyObject* py_lora_plan_upload(PyObject* self, PyObject* const* args, Py_s
   RETURN_INT(lora_plan_upload(
       I32P(0), I32P(1), I(2), I32P(3), (const float*)P(4), I(5), I(6), I(7), I(8), L(9), I(10),
       I(11), P(12), P(13), L(14), I32P(15), I32P(16), I(17), P(18)));
+}
+
+static PyObject* py_lora_plan_upload_embedding(PyObject* self, PyObject* const* args,
+                                               Py_ssize_t n) {
+  CONVERT(lora_plan_upload_embedding);
+  RETURN_INT(lora_plan_upload_embedding(
+      I32P(0), I32P(1), I(2), I32P(3), (const float*)P(4), I(5), I(6), I(7), I(8), L(9), I(10),
+      I(11), P(12), P(13), L(14), I32P(15), I32P(16), I(17), (const int64_t*)P(18), P(19),
+      L(20), P(21), L(22), I(23), L(24), P(25)));
 }
 
 static PyObject* py_lora_plan_device(PyObject* self, PyObject* const* args, Py_ssize_t n) {
@@ -195,6 +205,7 @@ static PyObject* py_lora_a_embedding(PyObject* self, PyObject* const* args, Py_s
 static PyMethodDef methods[] = {
     ENTRY(lora_plan_max_segments),
     ENTRY(lora_plan_upload),
+    ENTRY(lora_plan_upload_embedding),
     ENTRY(lora_plan_lm_head_upload),
     ENTRY(lora_plan_device),
     ENTRY(lora_shrink_workspace_bytes),
@@ -215,8 +226,9 @@ PyMODINIT_FUNC PyInit__sggcall(void) {
   PyObject* m = PyModule_Create(&module);
   if (m == NULL) return NULL;
   PyObject* sigs = Py_BuildValue(
-      "{ssssssssssssssssssss}", "lora_plan_max_segments", SIG_lora_plan_max_segments,
-      "lora_plan_device", SIG_lora_plan_device,
+      "{ssssssssssssssssssssss}", "lora_plan_max_segments", SIG_lora_plan_max_segments,
+      "lora_plan_device", SIG_lora_plan_device, "lora_plan_upload_embedding",
+      SIG_lora_plan_upload_embedding,
       "lora_plan_upload", SIG_lora_plan_upload, "lora_plan_lm_head_upload",
       SIG_lora_plan_lm_head_upload, "lora_shrink_workspace_bytes",
       SIG_lora_shrink_workspace_bytes, "lora_qkv_workspace_bytes", SIG_lora_qkv_workspace_bytes,

@@ -199,4 +199,26 @@ hipError_t launch_plan_device(const int32_t* seq_lens, const int32_t* req_slots,
 hipError_t launch_plan_copy(const int32_t* src_dev_view, int32_t* dst, int64_t n,
                             int32_t* done_dev_view, int32_t done_value, hipStream_t stream);
 
+// The plan copy above and the LoRA-A embedding lookup of a decode-shaped
+// batch (token t is request t) in one launch: workgroup 0 copies the plan,
+// the others gather the embedding rows.  The per-token slots and the per-slot
+// ranks travel in the kernel arguments, so the gather reads neither the plan
+// nor the staging buffer: the done flag still means that every read of the
+// staging buffer has returned.
+constexpr int kEmbedUploadMaxTokens = 3072;
+constexpr int kEmbedUploadMaxLoras = 64;
+struct EmbedUploadParams {
+  const int32_t* src;         // staging buffer, device-side address
+  int32_t* dst;               // device plan
+  int32_t* done;              // host flag, device-side address (or null)
+  const int64_t* ids;
+  const uint16_t* A;          // (L, R, V) bf16
+  uint16_t* out;              // (s, R) bf16, row stride ldo
+  int64_t n, V, vocab, ldo;
+  int32_t done_value, s, R, pad_;
+  int32_t rank[kEmbedUploadMaxLoras];    // clamped to [0, R]
+  uint8_t slot[kEmbedUploadMaxTokens];   // slot of token t
+};
+hipError_t launch_plan_copy_embedding(const EmbedUploadParams& p, hipStream_t stream);
+
 }  // namespace sgg

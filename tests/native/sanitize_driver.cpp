@@ -14,6 +14,10 @@
 //   U lm_head decode max_chunk override max_loras tok_cap seg_cap req_cap has_lens n
 //     lens[n] slots[n] ranks[max_loras] scaling_bits[max_loras]
 //       -> rc info[6] | staging[total words]
+//   E decode max_chunk L tok_cap seg_cap req_cap has_lens n lens[n] slots[n]
+//     ranks[L] scaling_bits[L] R
+//       -> rc info[6] | staging[total words] | fused s R n_copy
+//          | slot[s] | rank[64]          (the last two only when fused is 1)
 //   V   -> "name rc" for each built-in validation case, then "end"
 // Every host buffer the library writes is allocated at exactly the size the
 // call is told, so an overrun is a heap-buffer-overflow report.
@@ -58,6 +62,15 @@ hipError_t launch_plan_device(const int32_t*, const int32_t*, int32_t, const int
 }
 hipError_t launch_plan_copy(const int32_t*, int32_t*, int64_t, int32_t*, int32_t, hipStream_t) {
   ++g_launches;
+  return hipSuccess;
+}
+// The one-launch upload + embedding: its arguments are kept for the E command.
+static int g_fused_embeds = 0;
+static EmbedUploadParams g_last_embed;
+hipError_t launch_plan_copy_embedding(const EmbedUploadParams& p, hipStream_t) {
+  ++g_launches;
+  ++g_fused_embeds;
+  g_last_embed = p;
   return hipSuccess;
 }
 hipError_t launch_moe_route(const MoeRouteParams&, hipStream_t) {
@@ -188,6 +201,59 @@ void cmd_upload(std::istringstream& in) {
   std::free(pf);
 }
 
+// lora_plan_upload_embedding over stand-in device buffers: the staging
+// buffer as U, and whether the one-launch form was taken, with the slots
+// and ranks it was given.
+void cmd_upload_embedding(std::istringstream& in) {
+  alignas(256) static int64_t ids[4096];       // stand-ins for device tensors (never read)
+  alignas(256) static uint16_t emb_a[1 << 12];
+  alignas(256) static uint16_t emb_out[1 << 12];
+  int decode, max_chunk, L, seg_cap, req_cap, has_lens, n, R;
+  int64_t tok_cap;
+  in >> decode >> max_chunk >> L >> tok_cap >> seg_cap >> req_cap >> has_lens >> n;
+  std::vector<int32_t> lens = has_lens ? read_ints(in, n) : std::vector<int32_t>();
+  std::vector<int32_t> slots = read_ints(in, n);
+  std::vector<int32_t> ranks = read_ints(in, L);
+  std::vector<int32_t> sbits = read_ints(in, L);
+  in >> R;
+  std::vector<float> scal(static_cast<size_t>(L));
+  std::memcpy(scal.data(), sbits.data(), sizeof(float) * L);
+  const int64_t total = lora_plan_layout(tok_cap, seg_cap, req_cap, L, nullptr);
+  int32_t* staging = static_cast<int32_t*>(std::malloc(sizeof(int32_t) * total));
+  std::memset(staging, 0xff, sizeof(int32_t) * total);
+  int32_t* device = static_cast<int32_t*>(std::malloc(sizeof(int32_t) * total));
+  int32_t* pl = exact(lens);
+  int32_t* ps = exact(slots);
+  int32_t* pr = exact(ranks);
+  float* pf = exact(scal);
+  int32_t info[6] = {-1, -1, -1, -1, -1, -1};
+  const int before = sgg::g_fused_embeds;
+  const int rc = lora_plan_upload_embedding(pl, ps, n, pr, pf, L, decode, max_chunk, 0, tok_cap,
+                                            seg_cap, req_cap, staging, device, total * 4, info,
+                                            nullptr, 0, ids, emb_a, 1000, emb_out, R, R, 1000,
+                                            nullptr);
+  const bool fused = sgg::g_fused_embeds != before;
+  std::ostringstream out;
+  out << rc;
+  put(out, info, 6);
+  put(out, staging, total);
+  const sgg::EmbedUploadParams& e = sgg::g_last_embed;
+  out << " | " << (fused ? 1 : 0) << ' ' << (fused ? e.s : 0) << ' ' << (fused ? e.R : 0) << ' '
+      << (fused ? e.n : 0);
+  if (fused) {
+    out << " |";
+    for (int32_t t = 0; t < e.s; ++t) out << ' ' << static_cast<int>(e.slot[t]);
+    put(out, e.rank, sgg::kEmbedUploadMaxLoras);
+  }
+  std::cout << out.str() << '\n';
+  std::free(staging);
+  std::free(device);
+  std::free(pl);
+  std::free(ps);
+  std::free(pr);
+  std::free(pf);
+}
+
 // Validation cases: every entry point with arguments its host checks reject,
 // and with arguments it accepts (the stub launchers enqueue nothing).
 void cmd_validate() {
@@ -283,6 +349,7 @@ int main() {
     if (cmd == 'P') cmd_plan(in, false);
     else if (cmd == 'H') cmd_plan(in, true);
     else if (cmd == 'U') cmd_upload(in);
+    else if (cmd == 'E') cmd_upload_embedding(in);
     else if (cmd == 'V') cmd_validate();
     else if (cmd != 0) std::cout << "unknown " << cmd << '\n';
   }

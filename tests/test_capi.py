@@ -240,6 +240,28 @@ def test_embedding_rejects():
     assert emb(s=0) == 0
 
 
+def test_plan_upload_embedding_rejects():
+    """The lookup's arguments are checked before the batch is planned or
+    anything enqueued; the plan's own checks follow (all on the host)."""
+    C = _lib.calls()
+    f = FAKE.value
+    slots = np.zeros(4, np.int32)
+    ranks = np.full(2, 16, np.int32)
+    scal = np.ones(2, np.float32)
+    info = np.zeros(6, np.int32)
+
+    def call(staging=f, ids=f, A=f, V=1000, out=f, ldo=16, R=16, vocab=1000):
+        return C.lora_plan_upload_embedding(None, slots, 4, ranks, scal, 2, 1, 128, 0, 4, 8, 4,
+                                            staging, f, 1 << 16, info, None, 0, ids, A, V, out,
+                                            ldo, R, vocab, None)
+    assert call(R=0) == -1 and "R=0" in _err()
+    assert call(vocab=1001) == -1 and "vocab_size" in _err()
+    assert call(ldo=8) == -1 and "ldo" in _err()
+    assert call(ids=0) == -1 and "NULL" in _err()
+    assert call(out=f + 1) == -2 and "misaligned" in _err()
+    assert call(staging=0) == -1 and "host_staging" in _err()
+
+
 def test_qkv_rejects():
     offs = (ctypes.c_int32 * 4)(0, 4096, 5120, 6144)
     args = [FAKE, 4096, FAKE, FAKE, 6144, FAKE, 6144, 256, 4096, 8, 16, offs, 3, 4096,
@@ -428,6 +450,7 @@ def _header_signature(name):
 def test_call_module_signatures_match_header():
     C = _lib.calls()
     assert set(C.SIGNATURES) == {"lora_plan_max_segments", "lora_plan_upload", "lora_plan_device",
+                                 "lora_plan_upload_embedding",
                                  "lora_plan_lm_head_upload", "lora_shrink_workspace_bytes",
                                  "lora_qkv_workspace_bytes", "lora_shrink", "lora_expand",
                                  "lora_qkv", "lora_a_embedding"}

@@ -1220,11 +1220,74 @@ def test_embedding_edges():
         sgg.lora_a_embedding(ids.to(DEV), A_emb.to(DEV), be.batch_info, V, extra_embeddings=1)
 
 
-def test_staging_ring_reuse_while_gpu_lags():
+UPLOAD_EMBED_CASES = [
+    # (name, lens (None: decode mode), L, ranks, R): decode-shaped batches of
+    # at most 3072 tokens over at most 64 slots take the one-launch form;
+    # the others (more tokens or slots, longer requests) the two launches.
+    ("decode256_L8", None, 256, 8, [16, 8, 0, 16, 4, 16, 1, 16], 16),
+    ("unit_lens_extend", "ones", 200, 5, [16, 0, 9, 16, 3], 16),
+    ("decode1_rank_above_R", None, 1, 2, [40, 3], 32),
+    ("decode3072_L64", None, 3072, 64, "mixed", 16),
+    ("decode3073_two_launches", None, 3073, 8, "mixed", 16),
+    ("decode100_L65_two_launches", None, 100, 65, "mixed", 16),
+    ("extend_two_launches", "random", 40, 6, [16, 8, 0, 16, 2, 11], 16),
+]
+
+
+@pytest.mark.parametrize("case", UPLOAD_EMBED_CASES, ids=[c[0] for c in UPLOAD_EMBED_CASES])
+def test_plan_upload_embedding(case):
+    """prepare_lora_batch_with_embedding: the same device plan as
+    prepare_lora_batch (every region, bit for bit) and the same embedding
+    rows as the oracle, in the one-launch form and in the two-launch one."""
+    name, lens_kind, bs, L, ranks, R = case
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    if ranks == "mixed":
+        ranks = [int(v) for v in rng.choice([0, 4, 8, 16], L)]
+    slots = [int(v) for v in rng.integers(0, L, bs)]
+    if lens_kind is None:
+        lens, is_decode = [1] * bs, True
+    elif lens_kind == "ones":
+        lens, is_decode = [1] * bs, False
+    else:
+        lens, is_decode = [int(v) for v in rng.integers(0, 9, bs)], False
+    s = sum(lens)
+    V = 1000
+    ids = torch.tensor(rng.integers(-3, V + 4, s), dtype=torch.int64)
+    A_emb = torch.randn(L, R, V).to(torch.bfloat16)
+    scal = [float(v) for v in rng.uniform(0.5, 2.0, L)]
+    b = Batch(name, 0, lens, slots, is_decode, L, ranks, scal, 128)
+    sgg = _sgg()
+    be = sgg.ChunkedSgmvLoRA(L, 128, DEV)
+    info, e = be.prepare_lora_batch_with_embedding(
+        None if is_decode else lens, slots, ranks, scal, ids.to(DEV), A_emb.to(DEV), V,
+        is_decode=is_decode)
+    torch.cuda.synchronize()
+    stg = be._staging
+    assert list(stg.flag_view) == stg.seq   # the upload raised its done flag
+    want = ol.embedding_a(ids.numpy(), to_f64(A_emb), lens, slots, ranks, V)
+    assert np.array_equal(to_f64(e), want)
+    check_plan(info, b, 128)
+    ref = sgg.ChunkedSgmvLoRA(L, 128, DEV)
+    rinfo = plan_on(ref, b)
+    torch.cuda.synchronize()
+    for f in ("permutation", "seg_indptr", "weight_indices", "req_seg_indptr",
+              "req_weight_indices", "lora_ranks", "scalings", "work_indptr", "work_slots"):
+        assert torch.equal(getattr(info, f), getattr(rinfo, f)), f
+    assert (info.num_segments, info.max_len, info.num_work_segments) == \
+        (rinfo.num_segments, rinfo.max_len, rinfo.num_work_segments)
+    with pytest.raises(ValueError, match="ids"):
+        be.prepare_lora_batch_with_embedding(None if is_decode else lens, slots, ranks, scal,
+                                             ids[:-1].to(DEV), A_emb.to(DEV), V,
+                                             is_decode=is_decode)
+
+
+@pytest.mark.parametrize("form", ["separate", "one_call"])
+def test_staging_ring_reuse_while_gpu_lags(form):
     """More batches than staging slots are planned while a delay kernel holds
     the stream, so the host must wait for each slot's done flag before
     reusing it; every batch's embedding gather (enqueued right after its
-    upload) must still see its own plan."""
+    upload, or in the same launch for the decode-shaped batches of the
+    one-call form) must still see its own plan."""
     rng = np.random.default_rng(44)
     L, V, Re = 4, 300, 16
     ranks = [16, 8, 0, 16]
@@ -1235,14 +1298,21 @@ def test_staging_ring_reuse_while_gpu_lags():
     for i in range(30):
         bs = int(rng.integers(1, 13))
         lens = [int(v) for v in rng.integers(1, 41, bs)]
+        if form == "one_call" and i % 2 == 0:
+            lens = [1] * int(rng.integers(1, 300))   # decode-shaped: one launch
+            bs = len(lens)
         slots = [int(v) for v in rng.integers(0, L, bs)]
         ids = torch.as_tensor(rng.integers(-5, V + 5, sum(lens)), dtype=torch.int64)
         cases.append([lens, slots, ids, ids.to(DEV)])
     torch.cuda.synchronize()
     torch.cuda._sleep(50_000_000)   # tens of milliseconds: the host runs ahead
-    for case in cases:
-        be.prepare_lora_batch(case[0], case[1], ranks, [1.0] * L)
-        case[3] = be.run_lora_a_embedding(case[3], A_dev, V)
+    for i, case in enumerate(cases):
+        if form == "separate":
+            be.prepare_lora_batch(case[0], case[1], ranks, [1.0] * L)
+            case[3] = be.run_lora_a_embedding(case[3], A_dev, V)
+        else:
+            case[3] = be.prepare_lora_batch_with_embedding(case[0], case[1], ranks, [1.0] * L,
+                                                           case[3], A_dev, V)[1]
     torch.cuda.synchronize()
     stg = be._staging
     assert list(stg.flag_view) == stg.seq   # every upload raised its flag

@@ -233,6 +233,51 @@ def test_plan_upload_staging_under_sanitizers(driver):
         assert reg[8][n_work:] == [0] * (seg_cap - n_work)
 
 
+def test_plan_upload_embedding_under_sanitizers(driver):
+    """lora_plan_upload_embedding writes the same staging buffer and plan
+    info as lora_plan_upload, and takes the one-launch form exactly for
+    decode-shaped batches of at most 3072 tokens over at most 64 slots,
+    handing that launch each token's slot and the slots' ranks clamped to
+    [0, R]."""
+    rng = random.Random(5)
+    cases = []   # (lens or None, slots, ranks, L, decode, R, fused)
+    for bs, L, decode, fused in [(256, 8, True, True), (3072, 64, True, True),
+                                 (3073, 8, True, False), (100, 65, True, False),
+                                 (1, 1, True, True), (0, 4, True, False)]:
+        cases.append((None, [rng.randrange(L) for _ in range(bs)],
+                      [rng.choice([-3, 0, 4, 16, 40]) for _ in range(L)], L, decode, 16, fused))
+    cases.append(([1] * 50, [rng.randrange(5) for _ in range(50)], [16, 0, 8, 20, 3], 5, False,
+                  16, True))
+    cases.append(([1, 2, 1], [0, 1, 0], [16, 8], 2, False, 16, False))
+    cases.append(([1, 0, 1], [0, 1, 0], [16, 8], 2, False, 16, False))
+    lines = []
+    for lens, slots, ranks, L, decode, R, _ in cases:
+        s = len(slots) if lens is None else sum(lens)
+        cap = max(_capacity(s, L, 0), 1)
+        scal = [1.0 + 0.25 * a for a in range(L)]
+        u = _upload_cmd(False, lens, slots, ranks, scal, L, decode, 128, s, cap, len(slots))
+        lines.append(u)
+        lines.append(" ".join(["E"] + u.split()[2:3] + u.split()[3:4] + u.split()[5:]
+                              + [str(R)]))
+    out = _run(driver, lines)
+    assert len(out) == 2 * len(cases)
+    for (lens, slots, ranks, L, decode, R, fused), u, e in zip(cases, out[0::2], out[1::2]):
+        uhead, (uinfo, ustaging) = _fields(u)
+        parts = e.split("|")
+        assert int(parts[0].split()[0]) == 0 and uhead[0] == 0, (e[:200], u[:200])
+        assert [int(v) for v in parts[1].split()] == uinfo
+        assert [int(v) for v in parts[2].split()] == ustaging
+        flag, s_k, R_k, n_k = [int(v) for v in parts[3].split()]
+        assert flag == int(fused), (len(slots), L, lens)
+        if fused:
+            s = len(slots)
+            offs, _ = _layout(s, max(_capacity(s, L, 0), 1), len(slots), L)
+            assert (s_k, R_k, n_k) == (s, R, offs[9])
+            assert [int(v) for v in parts[4].split()] == list(slots)
+            want = [min(max(r, 0), R) for r in ranks] + [0] * (64 - L)
+            assert [int(v) for v in parts[5].split()] == want
+
+
 EXPECTED = {
     "shrink_ok": 0, "shrink_null_x": -1, "shrink_k0": -1, "shrink_c9": -1, "shrink_k_odd": -2,
     "shrink_ldh_small": -1, "shrink_misaligned": -2, "shrink_empty_plan": 0,
