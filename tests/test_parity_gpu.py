@@ -1221,10 +1221,14 @@ def test_embedding_edges():
 
 
 UPLOAD_EMBED_CASES = [
-    # (name, lens (None: decode mode), L, ranks, R): decode-shaped batches of
-    # at most 3072 tokens over at most 64 slots take the one-launch form;
-    # the others (more tokens or slots, longer requests) the two launches.
+    # (name, lens (None: decode mode), bs, L, ranks, R): decode-shaped
+    # batches of at most 3072 tokens over at most 64 slots take the one-launch
+    # form (slots and ranks, clamped to [0, R], in the kernel arguments); the
+    # others (more tokens or slots, longer requests) the two launches.
     ("decode256_L8", None, 256, 8, [16, 8, 0, 16, 4, 16, 1, 16], 16),
+    ("decode256_negative_rank", None, 256, 8, [-3, 8, 0, 16, 4, 16, 1, 16], 16),
+    ("decode385_mixed_ranks", None, 385, 8, "mixed", 16),
+    ("rank_above_16_bits", None, 64, 4, [70000, 8, 16, 0], 16),
     ("unit_lens_extend", "ones", 200, 5, [16, 0, 9, 16, 3], 16),
     ("decode1_rank_above_R", None, 1, 2, [40, 3], 32),
     ("decode3072_L64", None, 3072, 64, "mixed", 16),
@@ -1267,6 +1271,9 @@ def test_plan_upload_embedding(case):
     want = ol.embedding_a(ids.numpy(), to_f64(A_emb), lens, slots, ranks, V)
     assert np.array_equal(to_f64(e), want)
     check_plan(info, b, 128)
+    assert info.lora_ranks.cpu().tolist() == list(ranks)
+    assert info.req_weight_indices.cpu().tolist() == slots
+    assert np.array_equal(info.scalings.cpu().numpy(), np.asarray(scal, np.float32))
     ref = sgg.ChunkedSgmvLoRA(L, 128, DEV)
     rinfo = plan_on(ref, b)
     torch.cuda.synchronize()
@@ -1608,12 +1615,14 @@ def test_device_plan_captured_with_kernels(form):
         assert torch.equal(base[s:].view(torch.int16), base0[s:].view(torch.int16))
 
 
-def test_plan_upload_from_pageable_staging():
+@pytest.mark.parametrize("lens", [[3, 0, 5, 2, 7], [400, 0, 500, 600, 700]],
+                         ids=["small", "large"])
+def test_plan_upload_from_pageable_staging(lens):
     """lora_plan_upload with a staging buffer that has no device mapping
     (pageable memory) takes the runtime-copy path and still raises the done
-    flag; the uploaded plan is the oracle's."""
+    flag; every region of the uploaded plan is the oracle's or the input's."""
     from segmented_gather_gemm_amd import _lib
-    lens, slots, L = [3, 0, 5, 2, 7], [2, 1, 0, 2, 1], 3
+    slots, L = [2, 1, 0, 2, 1], 3
     ranks = np.array([8, 16, 4], np.int32)
     scal = np.array([1.0, 0.5, 2.0], np.float32)
     s, bs = sum(lens), len(lens)
@@ -1636,7 +1645,10 @@ def test_plan_upload_from_pageable_staging():
     assert got[offs[0]:offs[0] + s].tolist() == ref["permutation"]
     assert got[offs[1]:offs[1] + cap + 1].tolist() == ref["seg_indptr"]
     assert got[offs[2]:offs[2] + cap].tolist() == ref["seg_slots"]
+    assert got[offs[3]:offs[3] + bs + 1].tolist() == ref["req_seg_indptr"]
+    assert got[offs[4]:offs[4] + bs].tolist() == slots
     assert got[offs[5]:offs[5] + L].tolist() == ranks.tolist()
+    assert got[offs[6]:offs[6] + L].view(np.float32).tolist() == scal.tolist()
     assert info[0] == ref["num_segments"] and info[1] == ref["chunk_size"] and info[3] == s
 
 
