@@ -24,6 +24,7 @@ picks some, `--quick` skips them all.
 """
 
 import argparse
+import ctypes
 import gc
 import hashlib
 import json
@@ -938,9 +939,11 @@ def run_short_segments(device, steps=50, warmup=5, n_sets=8):
 def run_moe(device, steps=50, warmup=5, n_sets=8):
     """MoE LoRA add on a decode batch (256 one-token requests, 8 adapters,
     r=16) routed top-2 over 8 experts, LoRA on the experts' up projection
-    (4096 -> 14336): per step, lora_moe_route + lora_plan_device (the copies'
-    plan on the GPU) and lora_moe_add into the fused-MoE intermediate
-    (512 rows).  HIP events around each call, back to back."""
+    (4096 -> 14336): per step, the routing and the copies' plan on the GPU
+    in one launch (lora_moe_plan) and lora_moe_add into the fused-MoE
+    intermediate (512 rows); the routing and the plan as two launches
+    (lora_moe_route, then lora_plan_device) are timed beside them.  HIP
+    events around each call, back to back."""
     import torch
     import segmented_gather_gemm_amd as sgg
     rng = np.random.default_rng(20261204)
@@ -970,10 +973,30 @@ def run_moe(device, steps=50, warmup=5, n_sets=8):
         sgg.lora_moe_add(st["x"], st["A"], st["B"], be.moe_batch_info, k, st["out"],
                          workspace=ws)
 
+    # the same routing and plan as two launches, into buffers of their own
+    nv, copies = L * E + 1, s * k
+    seg_cap = sgg.lora_plan_max_segments(copies, nv, 16)
+    offs = (ctypes.c_int64 * 10)()
+    total = int(sgg.lib().lora_plan_layout(copies, seg_cap, copies, nv, offs))
+    two = {"slots": torch.zeros(copies, dtype=torch.int32, device=device),
+           "vranks": torch.zeros(nv, dtype=torch.int32, device=device),
+           "vscal": torch.zeros(nv, dtype=torch.float32, device=device),
+           "plan": torch.zeros(total, dtype=torch.int32, device=device),
+           "info": torch.zeros(8, dtype=torch.int32, device=device)}
+
+    def route_then_plan(i):
+        bi = be.batch_info
+        sgg.lora_moe_route(bi.req_seg_indptr, bi.req_weight_indices, bi.bs,
+                           sets[i % n_sets]["topk"], E, bi.lora_ranks, bi.scalings, L,
+                           two["slots"], two["vranks"], two["vscal"])
+        sgg.lora_plan_device(None, two["slots"], two["vranks"], two["vscal"], nv, True, 128, 0,
+                             copies, seg_cap, copies, two["plan"], two["info"])
+
     res = {"workload": f"MoE LoRA add: decode {s} x 1 token, {L} adapters r={R}, top-{k} of "
                        f"{E} experts, expert up projection {K} -> {N}; {s * k} copies over "
                        f"{L * E} virtual experts", "input_sets": n_sets}
-    for name, fn in (("route_and_plan", plan), ("plan_then_add", None)):
+    for name, fn in (("route_and_plan", plan), ("route_then_plan_two_launches", route_then_plan),
+                     ("plan_then_add", None)):
         if fn is None:
             def fn(i):
                 plan(i)

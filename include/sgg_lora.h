@@ -421,6 +421,28 @@ int lora_moe_route(const int32_t* req_seg_indptr, const int32_t* req_weight_indi
                    float* virtual_scalings, void* stream);
 
 /*
+ * lora_moe_plan -- lora_moe_route and then lora_plan_device over the copies
+ * (decode mode: one-token requests, max_loras = num_loras * num_experts + 1,
+ * token and request capacity num_tokens * top_k, no chunk override), in one
+ * launch of the device planner, with the same plan: regions 0-8 of the
+ * lora_plan_layout(num_tokens * top_k, seg_capacity, num_tokens * top_k,
+ * num_loras * num_experts + 1) layout in device_plan, the virtual rank and
+ * scaling tables in regions 5 and 6 (no separate virtual arrays), and the
+ * counts and status in device_info as lora_plan_device.  Routing inputs as
+ * lora_moe_route.
+ * (PR #24007 report page: the MoE layer's routing from the per-request
+ *  fields; chunked_backend.py page: the plan of prepare_lora_batch.)
+ * Limits of the device planner: num_tokens * top_k <= 4096 copies,
+ * num_loras * num_experts + 1 <= 1024 (else SGG_ERR_UNSUPPORTED).  Errors
+ * as lora_moe_route and lora_plan_device.
+ */
+int lora_moe_plan(const int32_t* req_seg_indptr, const int32_t* req_weight_indices,
+                  int32_t num_reqs, const int32_t* topk_ids, int64_t num_tokens, int32_t top_k,
+                  int32_t num_experts, const int32_t* lora_ranks, const float* scalings,
+                  int32_t num_loras, int32_t max_chunk_size, int32_t seg_capacity,
+                  void* device_plan, int64_t buffer_bytes, int32_t* device_info, void* stream);
+
+/*
  * lora_moe_add -- the MoE LoRA add on a fused-MoE intermediate (reading as in
  * lora_moe_route): for every copy m = t * top_k + j of a plan over the
  * num_tokens * top_k copies (segments by virtual expert v),

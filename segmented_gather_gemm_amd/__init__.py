@@ -14,6 +14,7 @@ from .binding import (
     lora_a_embedding,
     lora_expand,
     lora_moe_add,
+    lora_moe_plan,
     lora_moe_route,
     lora_plan_device,
     lora_plan_lm_head,
@@ -30,7 +31,7 @@ calls()
 
 __all__ = [
     "ChunkedSgmvLoRA", "LoRABatchInfo", "SggError", "default_workspace", "lora_a_embedding",
-    "lora_expand", "lora_moe_add", "lora_moe_route", "lora_plan_device", "lora_plan_lm_head",
+    "lora_expand", "lora_moe_add", "lora_moe_plan", "lora_moe_route", "lora_plan_device", "lora_plan_lm_head",
     "lora_plan_max_segments", "lora_plan_segments", "lora_qkv", "lora_qkv_noalloc",
     "lora_set_option", "lora_shrink",
 ]

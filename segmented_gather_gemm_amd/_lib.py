@@ -55,6 +55,8 @@ SIGNATURES = {
     "lora_set_option": (_i64, [ctypes.c_char_p, _i64]),
     "lora_moe_route": (ctypes.c_int, [
         _vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp]),
+    "lora_moe_plan": (ctypes.c_int, [
+        _vp, _vp, _i32, _vp, _i64, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _vp, _vp]),
     "lora_moe_add": (ctypes.c_int, [
         _vp, _i64, _i64, _i32, _vp, _vp, _i64, _vp, _i64, _i64, _i32, _i32,
         _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i64, _vp]),

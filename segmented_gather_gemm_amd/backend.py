@@ -440,9 +440,10 @@ class ChunkedSgmvLoRA:
         reads each token's adapter from the per-request fields
         req_seg_indptr / req_weight_indices and combines it with the
         router's experts into "virtual experts").  On the GPU, with no host
-        round trip: lora_moe_route gives every top-k copy t*k + j of a token
-        its virtual expert a(t) * E + topk_ids[t, j], then lora_plan_device
-        plans the copies like a decode batch of one-token requests.
+        round trip, in one launch (lora_moe_plan): every top-k copy t*k + j of
+        a token gets its virtual expert a(t) * E + topk_ids[t, j], and the
+        copies are planned like a decode batch of one-token requests (the
+        copies' virtual experts are the plan's req_weight_indices).
         topk_ids: int32 (num_tokens, k) device tensor of the batch's tokens
         (batch_info: the current plan unless given).  The result's arrays
         are padded to a fixed capacity, so a graph may capture this call
@@ -471,17 +472,11 @@ class ChunkedSgmvLoRA:
             plan = torch.zeros(max(total, 1), dtype=torch.int32, device=self.device)
             v = {name: plan[int(o):int(o) + n] for name, o, n in zip(_NAMES, offs, sizes)}
             bufs = {"plan": plan, "v": v,
-                    "slots": torch.zeros(max(copies, 1), dtype=torch.int32, device=self.device),
-                    "vranks": torch.zeros(nv, dtype=torch.int32, device=self.device),
-                    "vscal": torch.zeros(nv, dtype=torch.float32, device=self.device),
                     "info": torch.zeros(8, dtype=torch.int32, device=self.device)}
             self._moe[key] = bufs
-        B.lora_moe_route(info.req_seg_indptr, info.req_weight_indices, info.bs, topk_ids, E,
-                         info.lora_ranks, info.scalings, L, bufs["slots"], bufs["vranks"],
-                         bufs["vscal"])
-        B.lora_plan_device(None, bufs["slots"][:copies], bufs["vranks"], bufs["vscal"], nv, True,
-                           self.max_chunk_size, 0, copies, seg_cap, copies, bufs["plan"],
-                           bufs["info"])
+        B.lora_moe_plan(info.req_seg_indptr, info.req_weight_indices, info.bs, topk_ids, E,
+                        info.lora_ranks, info.scalings, L, self.max_chunk_size, seg_cap,
+                        bufs["plan"], bufs["info"])
         v = bufs["v"]
         # typical segment length: copies per virtual expert, in whole 16-token
         # tiles between 16 and 128 (longer segments are still covered)
@@ -491,8 +486,10 @@ class ChunkedSgmvLoRA:
         self.moe_batch_info = LoRABatchInfo(
             bs=copies, num_tokens=copies, num_segments=seg_cap, max_len=hint,
             seg_indptr=v["seg_indptr"], weight_indices=v["seg_slots"],
-            permutation=v["permutation"], lora_ranks=bufs["vranks"], scalings=bufs["vscal"],
-            use_cuda_graph=True, max_seg_len=hint, work_indptr=v["work_indptr"],
+            permutation=v["permutation"], lora_ranks=v["ranks"],
+            scalings=v["scalings"].view(torch.float32), req_seg_indptr=v["req_seg_indptr"],
+            req_weight_indices=v["req_slots"], use_cuda_graph=True, max_seg_len=hint,
+            work_indptr=v["work_indptr"],
             work_slots=v["work_slots"], num_work_segments=seg_cap, max_work_len=hint)
         return self.moe_batch_info
 

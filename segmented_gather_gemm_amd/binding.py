@@ -440,6 +440,37 @@ def lora_moe_route(req_seg_indptr, req_weight_indices, num_reqs, topk_ids, num_e
         virtual_ranks.data_ptr(), virtual_scalings.data_ptr(), _stream(topk_ids)))
 
 
+def lora_moe_plan(req_seg_indptr, req_weight_indices, num_reqs, topk_ids, num_experts,
+                  lora_ranks, scalings, num_loras, max_chunk_size, seg_capacity, device_plan,
+                  device_info):
+    """lora_moe_route and lora_plan_device over the copies in one launch (all
+    device tensors; see include/sgg_lora.h): the copies' plan in device_plan
+    (int32, lora_plan_layout(s * k, seg_capacity, s * k, L * E + 1)), the
+    virtual rank / scaling tables in its regions 5 and 6, counts and status
+    in device_info (int32 [8])."""
+    def dev(name, t, dtype, n):
+        if t.dtype != dtype or not t.is_cuda or not t.is_contiguous() or t.numel() < n:
+            raise ValueError(f"{name} must be a contiguous {dtype} device tensor of >= {n} "
+                             f"entries")
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be (num_tokens, top_k)")
+    s, k = topk_ids.shape
+    dev("req_seg_indptr", req_seg_indptr, torch.int32, num_reqs + 1)
+    if num_reqs:
+        dev("req_weight_indices", req_weight_indices, torch.int32, num_reqs)
+    dev("topk_ids", topk_ids, torch.int32, s * k)
+    dev("lora_ranks", lora_ranks, torch.int32, num_loras)
+    dev("scalings", scalings, torch.float32, num_loras)
+    dev("device_plan", device_plan, torch.int32, 1)
+    dev("device_info", device_info, torch.int32, 8)
+    check(lib().lora_moe_plan(
+        req_seg_indptr.data_ptr(), req_weight_indices.data_ptr() if num_reqs else None,
+        int(num_reqs), topk_ids.data_ptr(), s, k, int(num_experts), lora_ranks.data_ptr(),
+        scalings.data_ptr(), int(num_loras), int(max_chunk_size), int(seg_capacity),
+        device_plan.data_ptr(), 4 * device_plan.numel(), device_info.data_ptr(),
+        _stream(topk_ids)))
+
+
 def lora_moe_add(x, A, B, moe_info: LoRABatchInfo, top_k, out, workspace=None):
     """MoE LoRA add: out (tokens * top_k, N) += per copy t*top_k + j the LoRA
     delta of its virtual expert (include/sgg_lora.h).  x (tokens, K);

@@ -531,6 +531,57 @@ extern "C" int lora_moe_route(const int32_t* req_seg_indptr, const int32_t* req_
   return rc ? rc : sgg::ok();
 }
 
+extern "C" int lora_moe_plan(const int32_t* req_seg_indptr, const int32_t* req_weight_indices,
+                             int32_t num_reqs, const int32_t* topk_ids, int64_t num_tokens,
+                             int32_t top_k, int32_t num_experts, const int32_t* lora_ranks,
+                             const float* scalings, int32_t num_loras, int32_t max_chunk_size,
+                             int32_t seg_capacity, void* device_plan, int64_t buffer_bytes,
+                             int32_t* device_info, void* stream) {
+  SGG_CHECK(num_reqs >= 0 && num_tokens >= 0, SGG_ERR_INVALID,
+            "num_reqs=%d and num_tokens=%" PRId64 " must be non-negative", num_reqs, num_tokens);
+  SGG_CHECK(top_k >= 1 && num_experts >= 1 && num_loras >= 1, SGG_ERR_INVALID,
+            "top_k=%d, num_experts=%d and num_loras=%d must be positive", top_k, num_experts,
+            num_loras);
+  const int64_t copies = num_tokens * top_k;
+  const int64_t nv = static_cast<int64_t>(num_loras) * num_experts + 1;
+  SGG_CHECK(copies <= sgg::kDevicePlanMaxReqs, SGG_ERR_UNSUPPORTED,
+            "%" PRId64 " copies above the device planner's %d", copies, sgg::kDevicePlanMaxReqs);
+  SGG_CHECK(nv <= sgg::kDevicePlanMaxLoras, SGG_ERR_UNSUPPORTED,
+            "num_loras * num_experts + 1 = %" PRId64 " above the device planner's %d", nv,
+            sgg::kDevicePlanMaxLoras);
+  SGG_CHECK(seg_capacity >= 0, SGG_ERR_INVALID, "seg_capacity=%d is negative", seg_capacity);
+  SGG_CHECK(req_seg_indptr && lora_ranks && scalings && device_plan && device_info,
+            SGG_ERR_INVALID,
+            "req_seg_indptr, lora_ranks, scalings, device_plan or device_info is NULL");
+  SGG_CHECK(req_weight_indices || num_reqs == 0, SGG_ERR_INVALID, "req_weight_indices is NULL");
+  SGG_CHECK(topk_ids || num_tokens == 0, SGG_ERR_INVALID, "topk_ids is NULL");
+  SGG_CHECK((reinterpret_cast<uintptr_t>(device_plan) & 3) == 0, SGG_ERR_INVALID,
+            "device_plan must be 4-byte aligned");
+  int64_t off[SGG_PLAN_REGIONS];
+  lora_plan_layout(copies, seg_capacity, static_cast<int32_t>(copies),
+                   static_cast<int32_t>(nv), off);
+  SGG_CHECK(buffer_bytes >= off[9] * 4, SGG_ERR_CAPACITY,
+            "plan buffer of %" PRId64 " bytes, regions 0-8 need %" PRId64, buffer_bytes,
+            off[9] * 4);
+  sgg::MoeRouteParams r{};
+  r.req_seg_indptr = req_seg_indptr;
+  r.req_weight_indices = req_weight_indices;
+  r.topk_ids = topk_ids;
+  r.ranks = lora_ranks;
+  r.scalings = scalings;
+  r.copies = copies;
+  r.bs = num_reqs;
+  r.top_k = top_k;
+  r.E = num_experts;
+  r.L = num_loras;
+  const int rc = launch_status(
+      sgg::launch_moe_plan(r, max_chunk_size, seg_capacity, off,
+                           static_cast<int32_t*>(device_plan), device_info,
+                           static_cast<hipStream_t>(stream)),
+      "MoE routing and plan");
+  return rc ? rc : sgg::ok();
+}
+
 extern "C" int lora_moe_add(const void* x, int64_t ldx, int64_t num_tokens, int32_t top_k,
                             const void* A, const void* B, int64_t N, void* out, int64_t ldo,
                             int64_t in_dim, int32_t num_virtual, int32_t R,
@@ -841,9 +892,11 @@ int plan_upload(bool lm_head, const int32_t* seq_lens, const int32_t* req_slots,
   bool decode_shaped = is_decode != 0 || n_tok == num_reqs;
   for (int32_t r = 0; !is_decode && decode_shaped && r < num_reqs; ++r)
     decode_shaped = seq_lens[r] == 1;
+  // (the launch indexes its (token, j) pairs and blocks with 32-bit ints)
   const bool fused_embed = emb != nullptr && mapped && !lm_head && decode_shaped && n_tok > 0 &&
                            n_tok <= sgg::kEmbedUploadMaxTokens &&
-                           max_loras <= sgg::kEmbedUploadMaxLoras;
+                           max_loras <= sgg::kEmbedUploadMaxLoras &&
+                           n_tok * emb->R <= int64_t{INT32_MAX} - 256;
   if (fused_embed) {
     sgg::EmbedUploadParams ep;
     ep.src = static_cast<const int32_t*>(src);

@@ -9,13 +9,12 @@
 // stacked shrink + expand adds each copy's LoRA delta into its row t*k + j of
 // the fused-MoE intermediate.
 //
-// One thread per copy: the token's request -- request t itself when it holds
-// token t (one-token requests: one round trip), else by binary search over
-// the request boundaries -- then the virtual expert; copies whose request, adapter
-// or expert is out of range go to the extra virtual slot L*E, whose rank is 0
-// (the kernels leave such rows unchanged).  The first L*E + 1 threads also
-// write the virtual rank and scaling tables (adapter a's values for every
-// expert).
+// One thread per copy writes its virtual expert (moe_virtual_slot); copies
+// whose request, adapter or expert is out of range go to the extra virtual
+// slot L*E, whose rank is 0 (the kernels leave such rows unchanged).  The
+// first L*E + 1 threads also write the virtual rank and scaling tables
+// (adapter a's values for every expert).  lora_moe_plan does the same inside
+// the device planner's launch.
 #include "sgg_device.h"
 #include "sgg_kernels.h"
 
@@ -32,28 +31,8 @@ __global__ __launch_bounds__(256) void moe_route_kernel(MoeRouteParams p) {
     p.vscalings[m] = m < nv ? p.scalings[a] : 0.f;
   }
   if (m >= p.copies) return;
-  const int64_t t = m / p.top_k;
-  const int e = p.topk_ids[m];
-  // the request holding token t: the last r with req_seg_indptr[r] <= t,
-  // valid if t also lies before its end.  Request t itself when it holds the
-  // token (then it is that last r); else a binary search.
-  int r = -1;
-  if (t < p.bs && p.req_seg_indptr[t] <= t && t < p.req_seg_indptr[t + 1]) {
-    r = static_cast<int>(t);
-  } else {
-    int lo = 0, hi = p.bs;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.req_seg_indptr[mid] <= t) lo = mid;
-      else hi = mid - 1;
-    }
-    if (lo < p.bs && p.req_seg_indptr[lo] <= t && t < p.req_seg_indptr[lo + 1]) r = lo;
-  }
-  int v = static_cast<int>(nv);
-  if (r >= 0) {
-    const int a = p.req_weight_indices[r];
-    if (a >= 0 && a < p.L && e >= 0 && e < p.E) v = a * p.E + e;
-  }
+  const int v = moe_virtual_slot(p.req_seg_indptr, p.req_weight_indices, p.bs, p.topk_ids,
+                                 p.top_k, p.E, p.L, m);
   p.slots[m] = v;
 }
 

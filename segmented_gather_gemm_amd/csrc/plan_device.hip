@@ -51,6 +51,15 @@ struct DevicePlanParams {
   int64_t off[SGG_PLAN_REGIONS];
   int64_t token_capacity;
   int32_t bs, L, is_decode, max_chunk, chunk_override, seg_capacity;
+  // MoE routing (the ROUTE instance, decode mode): request m is top-k copy m
+  // and its slot the copy's virtual expert (moe_virtual_slot over these
+  // fields); ranks / scalings are the route_L adapters' tables, and the plan's
+  // tables those of the L = route_L * route_E + 1 virtual slots (adapter
+  // v / route_E for v < route_L * route_E, rank 0 and scaling 0 for the last).
+  const int32_t* route_topk;
+  const int32_t* route_req_indptr;
+  const int32_t* route_req_slots;
+  int32_t route_bs, route_top_k, route_E, route_L;
 };
 
 __device__ __forceinline__ int chunk_for(int64_t n, int max_chunk) {
@@ -169,6 +178,7 @@ __device__ __forceinline__ int last_at_most(const int32_t* v, int n, int x) {
   return lo;
 }
 
+template <bool ROUTE>
 __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanParams p) {
   __shared__ int32_t count[kDevicePlanMaxLoras];      // tokens per slot
   __shared__ int32_t first_pos[kDevicePlanMaxLoras];  // first sorted position per slot
@@ -205,7 +215,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
   // the rank and scaling tables, requested now so that their round trip
   // overlaps the planning (written out in step 5; L <= kPlanThreads)
   int32_t rank_of_tid = 0, scal_of_tid = 0;
-  if (tid < L) {
+  if constexpr (ROUTE) {
+    if (tid < L - 1) {
+      rank_of_tid = p.ranks[tid / p.route_E];
+      scal_of_tid = __float_as_int(p.scalings[tid / p.route_E]);
+    }
+  } else if (tid < L) {
     rank_of_tid = p.ranks[tid];
     scal_of_tid = __float_as_int(p.scalings[tid]);
   }
@@ -218,7 +233,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
     int len = 0;
     if (r < bs) {
       len = p.seq_lens ? p.seq_lens[r] : 1;
-      const int a = p.req_slots[r];
+      const int a = ROUTE ? moe_virtual_slot(p.route_req_indptr, p.route_req_slots, p.route_bs,
+                                             p.route_topk, p.route_top_k, p.route_E,
+                                             p.route_L, r)
+                          : p.req_slots[r];
       if (len < 0 || (p.is_decode && len != 1)) atomicOr(&status, 1);
       if (a < 0 || a >= L) atomicOr(&status, 2);
       else if (len > 0) atomicAdd(&count[a], len);
@@ -487,7 +505,35 @@ hipError_t launch_plan_device(const int32_t* seq_lens, const int32_t* req_slots,
   p.max_chunk = max_chunk;
   p.chunk_override = chunk_override;
   p.seg_capacity = seg_capacity;
-  hipLaunchKernelGGL(plan_device_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+  hipLaunchKernelGGL(plan_device_kernel<false>, dim3(1), dim3(kPlanThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_plan(const MoeRouteParams& r, int32_t max_chunk, int32_t seg_capacity,
+                           const int64_t* off, int32_t* plan, int32_t* info, hipStream_t stream) {
+  DevicePlanParams p{};
+  p.seq_lens = nullptr;
+  p.req_slots = nullptr;
+  p.ranks = r.ranks;
+  p.scalings = r.scalings;
+  p.plan = plan;
+  p.info = info;
+  for (int i = 0; i < SGG_PLAN_REGIONS; ++i) p.off[i] = off[i];
+  p.token_capacity = r.copies;
+  p.bs = static_cast<int32_t>(r.copies);
+  p.L = r.L * r.E + 1;
+  p.is_decode = 1;
+  p.max_chunk = max_chunk;
+  p.chunk_override = 0;
+  p.seg_capacity = seg_capacity;
+  p.route_topk = r.topk_ids;
+  p.route_req_indptr = r.req_seg_indptr;
+  p.route_req_slots = r.req_weight_indices;
+  p.route_bs = r.bs;
+  p.route_top_k = r.top_k;
+  p.route_E = r.E;
+  p.route_L = r.L;
+  hipLaunchKernelGGL(plan_device_kernel<true>, dim3(1), dim3(kPlanThreads), 0, stream, p);
   return hipGetLastError();
 }
 

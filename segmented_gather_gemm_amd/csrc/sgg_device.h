@@ -106,4 +106,37 @@ __device__ __forceinline__ void segment_round_robin(int b, int per, int* seg, in
   *item = l % per;
 }
 
+// MoE routing (PR #24007 report page, implementation breakdown items 2-4):
+// the virtual expert a(t) * E + topk_ids[m] of top-k copy m of token
+// t = m / top_k, where a(t) is the slot of the request r with
+// req_seg_indptr[r] <= t < req_seg_indptr[r + 1] -- request t itself when it
+// holds the token (one-token requests: one round trip), else found by binary
+// search.  A copy whose request, adapter or expert is out of range goes to
+// the extra virtual slot L * E.
+__device__ __forceinline__ int moe_virtual_slot(const int32_t* req_seg_indptr,
+                                                const int32_t* req_weight_indices, int bs,
+                                                const int32_t* topk_ids, int top_k, int E, int L,
+                                                int64_t m) {
+  const int64_t t = m / top_k;
+  const int e = topk_ids[m];
+  int r = -1;
+  if (t < bs && req_seg_indptr[t] <= t && t < req_seg_indptr[t + 1]) {
+    r = static_cast<int>(t);
+  } else {
+    int lo = 0, hi = bs;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (req_seg_indptr[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    if (lo < bs && req_seg_indptr[lo] <= t && t < req_seg_indptr[lo + 1]) r = lo;
+  }
+  int v = L * E;
+  if (r >= 0) {
+    const int a = req_weight_indices[r];
+    if (a >= 0 && a < L && e >= 0 && e < E) v = a * E + e;
+  }
+  return v;
+}
+
 }  // namespace sgg

@@ -191,6 +191,12 @@ hipError_t launch_plan_device(const int32_t* seq_lens, const int32_t* req_slots,
                               int32_t is_decode, int32_t max_chunk, int32_t chunk_override,
                               int64_t token_capacity, int32_t seg_capacity, const int64_t* off,
                               int32_t* plan, int32_t* info, hipStream_t stream);
+// The MoE routing of `r` (its output arrays unused) and the device plan of the
+// r.copies one-token copies over the r.L * r.E + 1 virtual slots, in one
+// launch of the device planner: regions 0-8 as launch_plan_device over the
+// routed slots, the virtual rank / scaling tables in regions 5 and 6.
+hipError_t launch_moe_plan(const MoeRouteParams& r, int32_t max_chunk, int32_t seg_capacity,
+                           const int64_t* off, int32_t* plan, int32_t* info, hipStream_t stream);
 
 // Copy n int32 from pinned host memory (given by its device-side address) to
 // device memory, as a kernel on `stream`; src and dst 8-byte aligned.  When

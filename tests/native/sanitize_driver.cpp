@@ -73,6 +73,11 @@ hipError_t launch_plan_copy_embedding(const EmbedUploadParams& p, hipStream_t) {
   g_last_embed = p;
   return hipSuccess;
 }
+hipError_t launch_moe_plan(const MoeRouteParams&, int32_t, int32_t, const int64_t*, int32_t*,
+                           int32_t*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_moe_route(const MoeRouteParams&, hipStream_t) {
   ++g_launches;
   return hipSuccess;
@@ -332,6 +337,17 @@ void cmd_validate() {
   cases.push_back({"plan_device_buffer_small",
                    lora_plan_device(nullptr, dslots, 4, ranks, scal, 2, 1, 128, 0, 4, 4, 4, dplan,
                                     16, dinfo, nullptr)});
+  alignas(16) static int32_t mind[3] = {0, 2, 4};
+  alignas(16) static int32_t mtopk[8] = {0, 1, 1, 0, 0, 1, 1, 0};
+  auto moe_plan = [&](int64_t tokens, int32_t experts, int64_t bytes, int32_t* plan) {
+    return lora_moe_plan(mind, sl, 2, mtopk, tokens, 2, experts, ranks, scal, 2, 128, 16, plan,
+                         bytes, dinfo, nullptr);
+  };
+  cases.push_back({"moe_plan_ok", moe_plan(4, 2, sizeof(dplan), dplan)});
+  cases.push_back({"moe_plan_too_many_copies", moe_plan(4096, 2, sizeof(dplan), dplan)});
+  cases.push_back({"moe_plan_too_many_virtual", moe_plan(4, 512, sizeof(dplan), dplan)});
+  cases.push_back({"moe_plan_buffer_small", moe_plan(4, 2, 16, dplan)});
+  cases.push_back({"moe_plan_null_plan", moe_plan(4, 2, sizeof(dplan), nullptr)});
   for (const Case& c : cases) std::cout << c.name << ' ' << c.rc << '\n';
   std::cout << "launches " << sgg::g_launches << '\n';
   std::cout << "end\n";

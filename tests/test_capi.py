@@ -290,6 +290,22 @@ def test_moe_route_rejects():
     assert route(L=1 << 20, E=1 << 12) == -2 and "int32" in _err()
 
 
+def test_moe_plan_rejects():
+    """Host checks of the one-launch routing + plan: the device planner's
+    limits, the plan buffer's size, NULL pointers (nothing is enqueued)."""
+    def plan(tokens=4, k=2, E=2, L=2, buf=FAKE, nbytes=1 << 16, info=FAKE, topk=FAKE):
+        return L_.lora_moe_plan(FAKE, FAKE, 2, topk, tokens, k, E, FAKE, FAKE, L, 128, 16, buf,
+                                nbytes, info, NULL)
+    L_ = L
+    assert plan(tokens=2049) == -2 and "copies" in _err()
+    assert plan(E=512) == -2 and "1024" in _err()
+    assert plan(nbytes=64) == -3 and "plan buffer" in _err()
+    assert plan(buf=NULL) == -1
+    assert plan(info=NULL) == -1
+    assert plan(topk=NULL) == -1 and "topk_ids" in _err()
+    assert plan(k=0) == -1
+
+
 def test_moe_add_rejects():
     def add(ws=NULL, wsb=0, **kw):
         a = dict(x=FAKE, ldx=512, s=64, k=2, A=FAKE, B=FAKE, N=256, out=FAKE, ldo=256, K=512,

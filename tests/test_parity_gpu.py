@@ -1692,8 +1692,9 @@ def _moe_want(t, lens, slots, ranks, scal, topk, E):
     ("bench_shape", [1] * 256, 8, [16] * 8, 8, 2, 4096, 14336, 16, 0),
 ], ids=lambda c: c[0])
 def test_moe_lora_add_matches_oracle(case):
-    """Per-request routing to virtual experts (lora_moe_route, bit-exact
-    against the oracle), the copies planned on the GPU, and the MoE LoRA add
+    """Per-request routing to virtual experts (bit-exact against the oracle)
+    and the copies planned on the GPU in one launch (lora_moe_plan), and the
+    MoE LoRA add
     into the fused-MoE intermediate against the oracle; copies whose expert
     id is out of range keep their rows bit for bit."""
     name, lens, L, ranks, E, k, K, N, R, bad = case
@@ -1713,12 +1714,71 @@ def test_moe_lora_add_matches_oracle(case):
     ok = (topk >= 0) & (topk < E)
     v_want = om.virtual_experts(indptr, slots, np.where(ok, topk, 0), E)
     v_want[~ok.reshape(-1)] = L * E
-    got_v = be._moe[(len(topk) * k, E)]["slots"][:len(topk) * k].cpu().numpy()
+    got_v = info.req_weight_indices[:len(topk) * k].cpu().numpy()
     assert np.array_equal(got_v, v_want)
+    assert info.lora_ranks.cpu().tolist() == [r for r in ranks for _ in range(E)] + [0]
+    assert np.array_equal(info.scalings.cpu().numpy(),
+                          np.append(np.repeat(np.asarray(scal, np.float32), E), 0))
     keep = ~ok.reshape(-1)
     assert torch.equal(out[torch.from_numpy(keep).to(DEV)].view(torch.int16),
                        t["out"][torch.from_numpy(keep)].to(DEV).view(torch.int16))
     assert_close(out, want, f"MoE LoRA add ({name})")
+
+
+@pytest.mark.parametrize("case", [
+    ("extend", [3, 1, 5, 2, 1, 4, 37, 60, 9, 128], 4, [16, 8, 0, 16], 8, 2, 0, 0),
+    ("decode_bad_experts", [1] * 300, 6, [16, 16, 12, 8, 16, 4], 8, 2, 7, 0),
+    ("top4", [2, 7, 1, 30, 5], 3, [32, 0, 24], 4, 4, 5, 0),
+    ("limits_4096_copies_1017_slots", [1] * 2048, 8, [16] * 8, 127, 2, 3, 0),
+    ("tokens_past_the_requests", [4, 6, 2], 3, [16, 8, 4], 5, 2, 0, 9),
+], ids=lambda c: c[0])
+def test_moe_plan_one_launch_matches_route_then_plan(case):
+    """lora_moe_plan gives every region of the copies' plan, the virtual
+    tables and the info words bit for bit as lora_moe_route followed by
+    lora_plan_device; copies of tokens outside every request (the request
+    boundaries end early) go to the extra virtual slot in both."""
+    from segmented_gather_gemm_amd import binding as Bn
+    name, lens, L, ranks, E, k, bad, extra_tokens = case
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    slots = rng.integers(0, L, size=len(lens)).astype(np.int32)
+    scal = rng.uniform(0.5, 2.0, size=L).astype(np.float32)
+    s = int(sum(lens)) + extra_tokens
+    topk = rng.integers(0, E, size=(s, k)).astype(np.int32)
+    for i in range(bad):
+        topk[rng.integers(0, s), rng.integers(0, k)] = [-1, E, E + 7][i % 3]
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    indptr_d, slots_d, topk_d = d(indptr), d(slots), d(topk)
+    ranks_d, scal_d = d(np.asarray(ranks, np.int32)), d(scal)
+    copies, nv = s * k, L * E + 1
+    lib = _sgg()._lib.lib()
+    seg_cap = int(lib.lora_plan_max_segments(copies, nv, 16))
+    offs = (ctypes.c_int64 * 10)()
+    total = int(lib.lora_plan_layout(copies, seg_cap, copies, nv, offs))
+    plans = [torch.full((total,), -7, dtype=torch.int32, device=DEV) for _ in range(2)]
+    infos = [torch.full((8,), -7, dtype=torch.int32, device=DEV) for _ in range(2)]
+    vslots = torch.empty(copies, dtype=torch.int32, device=DEV)
+    vranks = torch.empty(nv, dtype=torch.int32, device=DEV)
+    vscal = torch.empty(nv, dtype=torch.float32, device=DEV)
+    Bn.lora_moe_route(indptr_d, slots_d, len(lens), topk_d, E, ranks_d, scal_d, L, vslots,
+                      vranks, vscal)
+    Bn.lora_plan_device(None, vslots, vranks, vscal, nv, True, 128, 0, copies, seg_cap, copies,
+                        plans[0], infos[0])
+    Bn.lora_moe_plan(indptr_d, slots_d, len(lens), topk_d, E, ranks_d, scal_d, L, 128, seg_cap,
+                     plans[1], infos[1])
+    torch.cuda.synchronize()
+    assert torch.equal(infos[0], infos[1]) and int(infos[1][6]) == 0
+    assert torch.equal(plans[0][:offs[9]], plans[1][:offs[9]])
+    got = plans[1].cpu().numpy()
+    assert got[offs[5]:offs[5] + nv].tolist() == vranks.cpu().tolist()
+    assert np.array_equal(got[offs[6]:offs[6] + nv].view(np.float32), vscal.cpu().numpy())
+    ok = (topk >= 0) & (topk < E)
+    inside = int(sum(lens))   # tokens past the last request have none: the extra slot
+    v_want = np.full(copies, L * E, dtype=np.int64)
+    v_want[:inside * k] = om.virtual_experts(indptr.astype(np.int64), slots.tolist(),
+                                             np.where(ok, topk, 0)[:inside], E)
+    v_want[~ok.reshape(-1)] = L * E
+    assert np.array_equal(got[offs[4]:offs[4] + copies], v_want)
 
 
 def test_moe_lora_add_in_a_graph():

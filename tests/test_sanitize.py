@@ -249,6 +249,11 @@ def test_plan_upload_embedding_under_sanitizers(driver):
     cases.append(([1] * 50, [rng.randrange(5) for _ in range(50)], [16, 0, 8, 20, 3], 5, False,
                   16, True))
     cases.append(([1, 2, 1], [0, 1, 0], [16, 8], 2, False, 16, False))
+    # (token, j) pairs past 2^31: the two launches (the fused launch indexes them in int32)
+    cases.append((None, [rng.randrange(8) for _ in range(3072)], [16] * 8, 8, True, 1 << 20,
+                  False))
+    cases.append((None, [rng.randrange(8) for _ in range(2048)], [16] * 8, 8, True, 1 << 19,
+                  True))
     cases.append(([1, 0, 1], [0, 1, 0], [16, 8], 2, False, 16, False))
     lines = []
     for lens, slots, ranks, L, decode, R, _ in cases:
@@ -286,6 +291,8 @@ EXPECTED = {
     "expand_null_base": -1, "qkv_ok": 0, "qkv_workspace_small": -3, "workspace_sizes": 0,
     "embedding_ok": 0, "embedding_extra_vocab": -2, "embedding_vocab_above_v": -1,
     "plan_device_ok": 0, "plan_device_too_many_loras": -2, "plan_device_buffer_small": -3,
+    "moe_plan_ok": 0, "moe_plan_too_many_copies": -2, "moe_plan_too_many_virtual": -2,
+    "moe_plan_buffer_small": -3, "moe_plan_null_plan": -1,
 }
 
 
