@@ -216,10 +216,12 @@ def rotated(t, n):
 
 
 def run_decode(args, device):
-    """Decode steps.  Headline (eager): host plan + one upload, then the
-    embedding gather and the stacked shrink + expand (lora_qkv), one C call
-    each.  Secondary: graph mode (the three launches captured once per input
-    set over a fixed-capacity plan, replayed after each plan upload)."""
+    """Decode steps.  Headline (eager): the host plan, its upload and the
+    embedding gather in one C call and one launch, then the stacked shrink +
+    expand (lora_qkv).  Beside it: the same step with the upload and the
+    gather as two calls, and graph mode (the gather and the stacked call's
+    launches captured once per input set over a fixed-capacity plan,
+    replayed after each plan upload)."""
     import torch
     import segmented_gather_gemm_amd as sgg
 
