@@ -12,7 +12,8 @@
 //      the index itself), validation;
 //   2. tokens per slot (LDS histogram), the chunk size, each slot's first
 //      sorted position and first segment (scans over the slots: across the
-//      lanes of one wave when there are at most 64 slots);
+//      lanes of one wave when there are at most 64 slots, of two when there
+//      are at most 128);
 //   3. each request's first sorted position: the stable counting sort.  For
 //      one-token requests every wave places 64 at once (slots matched by one
 //      ballot per slot bit, a per-wave count table for the offsets); else one
@@ -191,6 +192,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
   __shared__ int64_t wave_sums[kPlanThreads / 64 + 1][2];
   __shared__ int32_t status, longest, longest_work, all_unit;
   __shared__ uint32_t slot_totals[2];
+  __shared__ uint32_t wave0_totals[3];  // step 2, 65-128 slots
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -302,6 +304,40 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(DevicePlanPar
         slot_totals[0] = ty;
         slot_totals[1] = tz;
         if (static_cast<int64_t>(ty) > p.seg_capacity) atomicOr(&status, 8);
+      }
+    }
+    __syncthreads();
+    n_seg = slot_totals[0];
+    n_work = slot_totals[1];
+  } else if (L <= 128) {
+    // The slots fit the first two waves: each scans its 64 slots, then wave
+    // 1 adds wave 0's totals (one barrier; no block-level pass).
+    uint32_t x = static_cast<uint32_t>(n_slot), y = static_cast<uint32_t>(segs);
+    uint32_t z = static_cast<uint32_t>(works);
+    if (wave < 2) {
+      wave_inclusive_scan3(x, y, z);
+      if (wave == 0 && lane == 63) {
+        wave0_totals[0] = x;
+        wave0_totals[1] = y;
+        wave0_totals[2] = z;
+      }
+    }
+    __syncthreads();
+    if (wave == 1) {
+      x += wave0_totals[0];
+      y += wave0_totals[1];
+      z += wave0_totals[2];
+    }
+    if (wave < 2) {
+      if (tid < L) {
+        first_pos[tid] = static_cast<int32_t>(x - static_cast<uint32_t>(n_slot));
+        first_seg[tid] = static_cast<int32_t>(y - static_cast<uint32_t>(segs));
+        first_work[tid] = static_cast<int32_t>(z - static_cast<uint32_t>(works));
+      }
+      if (wave == 1 && lane == 63) {
+        slot_totals[0] = y;
+        slot_totals[1] = z;
+        if (static_cast<int64_t>(y) > p.seg_capacity) atomicOr(&status, 8);
       }
     }
     __syncthreads();

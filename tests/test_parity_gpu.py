@@ -1459,6 +1459,12 @@ DEVICE_PLAN_CASES = [
     ("L1024_bs4096", 4096, 4096, 3, 1024, (0, 3), 128, 0),
     ("decode_L1024_bs4096", 4096, 4096, 1, 1024, None, 128, 0),
     ("unit_L1024_bs4096", 4096, 4096, 1, 1024, (1, 1), 128, 0),
+    # slot counts around the one- and two-wave slot scans (64, 128)
+    ("decode500_L64", 500, 512, 1, 64, None, 128, 0),
+    ("decode500_L65", 500, 512, 1, 65, None, 128, 0),
+    ("extend_L100", 120, 128, 40, 100, (0, 40), 128, 0),
+    ("decode700_L128", 700, 700, 1, 128, None, 128, 0),
+    ("extend_L129", 150, 160, 30, 129, (1, 30), 32, 0),
 ]
 
 
