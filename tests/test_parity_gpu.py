@@ -1288,6 +1288,34 @@ def test_plan_upload_embedding(case):
                                              is_decode=is_decode)
 
 
+def test_plan_upload_embedding_graph_capacity():
+    """The one-call upload + embedding into the graph-capacity plan buffer
+    (init_cuda_graph_batch_info, a batch below the capacity): the embedding
+    rows are the oracle's and every plan region is what
+    prepare_lora_batch(use_cuda_graph=True) writes."""
+    sgg = _sgg()
+    rng = np.random.default_rng(77)
+    L, V, R, bs, cap_bs = 8, 1000, 16, 200, 256
+    slots = rng.integers(0, L, bs).tolist()
+    ranks = [16, 8, 0, 16, 4, 16, 1, 16]
+    scal = rng.uniform(0.5, 2.0, L).astype(np.float32).tolist()
+    ids = torch.tensor(rng.integers(-3, V + 4, bs), dtype=torch.int64)
+    A_emb = torch.randn(L, R, V).to(torch.bfloat16)
+    be = sgg.ChunkedSgmvLoRA(L, 128, DEV)
+    ref = sgg.ChunkedSgmvLoRA(L, 128, DEV)
+    be.init_cuda_graph_batch_info(cap_bs, 1)
+    ref.init_cuda_graph_batch_info(cap_bs, 1)
+    _, e = be.prepare_lora_batch_with_embedding(None, slots, ranks, scal, ids.to(DEV),
+                                                A_emb.to(DEV), V, is_decode=True,
+                                                use_cuda_graph=True)
+    ref.prepare_lora_batch(None, slots, ranks, scal, is_decode=True, use_cuda_graph=True)
+    torch.cuda.synchronize()
+    want = ol.embedding_a(ids.numpy(), to_f64(A_emb), [1] * bs, slots, ranks, V)
+    assert np.array_equal(to_f64(e), want)
+    cap = be._graph_cap[2]
+    assert _plan_regions(be, bs, bs, cap) == _plan_regions(ref, bs, bs, cap)
+
+
 @pytest.mark.parametrize("form", ["separate", "one_call"])
 def test_staging_ring_reuse_while_gpu_lags(form):
     """More batches than staging slots are planned while a delay kernel holds
