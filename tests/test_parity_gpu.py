@@ -1288,6 +1288,43 @@ def test_plan_upload_embedding(case):
                                              is_decode=is_decode)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_upload_embedding_random(seed):
+    """Seeded random batches through prepare_lora_batch_with_embedding:
+    decode mode, one-token extend batches and mixed lengths; 1-80 slots
+    (the one-launch form takes at most 64), ranks anywhere in [0, R + 8],
+    R of 8-64, ids partly out of vocabulary.  Embedding rows bit-exact
+    against the oracle, every plan region equal to the plain upload's."""
+    sgg = _sgg()
+    rng = np.random.default_rng(9000 + seed)
+    L = int(rng.integers(1, 81))
+    R = int(rng.choice([8, 16, 32, 64]))
+    bs = int(rng.integers(1, 700))
+    kind = ["decode", "ones", "mixed"][seed % 3]
+    lens = [1] * bs if kind != "mixed" else [int(v) for v in rng.integers(0, 5, bs)]
+    is_decode = kind == "decode"
+    slots = [int(v) for v in rng.integers(0, L, bs)]
+    ranks = [int(v) for v in rng.integers(0, R + 9, L)]
+    scal = [float(v) for v in rng.uniform(0.25, 2.0, L)]
+    V = 500
+    s = sum(lens)
+    ids = torch.tensor(rng.integers(-4, V + 5, s), dtype=torch.int64)
+    A_emb = torch.randn(L, R, V).to(torch.bfloat16)
+    be = sgg.ChunkedSgmvLoRA(L, 128, DEV)
+    info, e = be.prepare_lora_batch_with_embedding(
+        None if is_decode else lens, slots, ranks, scal, ids.to(DEV), A_emb.to(DEV), V,
+        is_decode=is_decode)
+    ref = sgg.ChunkedSgmvLoRA(L, 128, DEV)
+    rinfo = ref.prepare_lora_batch(None if is_decode else lens, slots, ranks, scal,
+                                   is_decode=is_decode)
+    torch.cuda.synchronize()
+    want = ol.embedding_a(ids.numpy(), to_f64(A_emb), lens, slots, ranks, V)
+    assert np.array_equal(to_f64(e), want)
+    for f in ("permutation", "seg_indptr", "weight_indices", "req_seg_indptr",
+              "req_weight_indices", "lora_ranks", "scalings", "work_indptr", "work_slots"):
+        assert torch.equal(getattr(info, f), getattr(rinfo, f)), f
+
+
 def test_plan_upload_embedding_graph_capacity():
     """The one-call upload + embedding into the graph-capacity plan buffer
     (init_cuda_graph_batch_info, a batch below the capacity): the embedding
