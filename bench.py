@@ -354,6 +354,20 @@ def run_decode(args, device):
                                                  st["ids"], st["A_emb"], vocab, is_decode=True,
                                                  out=st["e"])
     n_up = min(args.steps, be._staging.n)
+    # GPU time of whole eager steps: one ring's worth queued behind a delay
+    # kernel (the host's planning hidden), against the wall-clock step
+    for i in range(n_up):
+        eager_step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    held = hold_stream(stream, 5.0)
+    e0.record(stream)
+    for i in range(n_up):
+        eager_step(i)
+    e1.record(stream)
+    back_to_back &= not held.query()
+    torch.cuda.synchronize()
+    step_gpu_us = e0.elapsed_time(e1) * 1e3 / n_up
     upload = {"launches": n_up}
     for n in ("copy", "copy_and_embedding"):
         for i in range(n_up):
@@ -507,6 +521,7 @@ def run_decode(args, device):
                      "step": "host plan + upload (copy kernel), embedding gather, lora_qkv "
                              "(two launches)"},
         "upload_launch": upload,
+        "step_gpu_us": round(step_gpu_us, 2),
         "graph_device_plan": {
             "ms_per_step": round(dgraph_wall / args.steps * 1e3, 4),
             "tokens_per_s": round(b0.num_tokens * args.steps / dgraph_wall, 1),
@@ -1268,6 +1283,7 @@ def main():
                 "embedding gather, then lora_qkv (two launches)",
         "separate_upload_and_embedding": res["separate"],
         "upload_launch": res["upload_launch"],
+        "step_gpu_us": res["step_gpu_us"],
         "graph_tokens_per_s": round(graph, 1),
         "graph_ms_per_step": round(res["graph_wall_s"] / args.steps * 1e3, 4),
         "graph_device_plan": res["graph_device_plan"],
